@@ -1,0 +1,320 @@
+"""Benchmark of the compressed-key indexer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
+
+Headline step: decode scoring of 32 requests x 65,536 bf16 compressed entries (256K-token
+context at 4:1 compression, 1,024 pages of 64 per request, pages scattered by a permuted block
+table, 10% planted hot pages), i.e. fm_index_logits followed by fm_topk512 (k = 512) on the
+same stream.  The pool is replicated on the device and the replicas rotate from step to step
+so that no step finds its keys in the 256 MB Infinity Cache.  The metric is compressed entries
+scored and selected per second over the whole call; every input is resident in HBM before the
+timed region starts.
+
+Per-kernel durations come from HIP events recorded on the stream the kernels run on.  The
+roofline object reports the scoring kernel against HBM peak (8 TB/s) with its algorithmic
+bytes: keys once, q/w once, block table, logits written.  Secondary entries measure the other
+workloads (three-layer fp8 mask, two-level fp8 scoring over 384 resident pages, causal fp8
+prefill) the same way.  cpu_baseline times the fp64 oracle on a bounded sample of the
+headline workload on the host cores.
+
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+FLOP_PER_PAIR = 2 * 64 * 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "top_selection_fm_amd", "csrc"))):
+        with open(os.path.join(ROOT, "top_selection_fm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources") != digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Events around each kernel launch, on the current (launch) stream."""
+
+    def __init__(self, torch, names, steps):
+        self.torch = torch
+        self.names = names
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+                   for _ in range(steps)]
+
+    def mark(self, step, i):
+        self.ev[step][i].record()
+
+    def per_kernel_ms(self):
+        out = {}
+        for i, n in enumerate(self.names):
+            out[n] = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in self.ev]))
+        return out
+
+
+def timed(torch, names, fn, steps, warmup):
+    for s in range(warmup):
+        fn(s, None)
+    torch.cuda.synchronize()
+    tm = Timer(torch, names, steps)
+    t0 = time.perf_counter()
+    for s in range(steps):
+        fn(s, tm)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, tm.per_kernel_ms()
+
+
+# ----------------------------------------------------------------------------- workloads
+def run_decode(torch, api, W, steps, warmup, replicas=3):
+    wl = W.decode_bf16()
+    dw = api.DeviceWorkload(wl, "cuda:0", pool_copies=replicas)
+    B = wl.kv.B
+    ld = wl.kv.block_table.shape[1] * 64
+    logits = torch.empty((B, ld), dtype=torch.float32, device="cuda:0")
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda:0")
+    q = dw.query()
+    kvs = [dw.kv(r) for r in range(replicas)]
+
+    def step(s, tm):
+        if tm: tm.mark(s, 0)
+        api.fm_index_logits(q, kvs[s % replicas], logits, ld)
+        if tm: tm.mark(s, 1)
+        api.fm_topk512(logits, ld, B, None, None, 0, None, 512, idx)
+        if tm: tm.mark(s, 2)
+
+    wall, per = timed(torch, ["score", "topk"], step, steps, warmup)
+    entries = int(wl.kv.seq_lens.sum())
+    key_bytes = entries * 256
+    alg_bytes = key_bytes + B * 64 * 128 * 2 + B * 64 * 2 + wl.kv.block_table.nbytes + \
+        wl.kv.seq_lens.nbytes + B * ld * 4
+    return wl, dict(entries=entries, wall_s=wall, per=per, alg_bytes=alg_bytes,
+                    flops=entries * FLOP_PER_PAIR)
+
+
+def run_mask(torch, api, W, steps, warmup, replicas=2):
+    wl = W.three_layer_mask_fp8()
+    dw = api.DeviceWorkload(wl, "cuda:0", pool_copies=replicas)
+    B = wl.kv.B
+    ld = wl.kv.block_table.shape[1] * 64
+    n_pages = ld // 64
+    mask = torch.empty((B, ld), dtype=torch.uint8, device="cuda:0")
+    cnt = torch.empty(B, dtype=torch.int32, device="cuda:0")
+    plist = torch.empty((B, n_pages), dtype=torch.int32, device="cuda:0")
+    qs = [dw.query(l) for l in range(3)]
+    kvs = [dw.kv(r) for r in range(replicas)]
+
+    def step(s, tm):
+        if tm: tm.mark(s, 0)
+        api.fm_resident_mask(qs, kvs[s % replicas], api.FM_UNION_MAX, 0.5, 0, 0, mask, ld, cnt,
+                             plist, n_pages)
+        if tm: tm.mark(s, 1)
+
+    wall, per = timed(torch, ["mask+compact"], step, steps, warmup)
+    entries = int(wl.kv.seq_lens.sum())
+    alg = 3 * entries * 132 + 3 * B * (64 * 128 * 2 + 64 * 2) + wl.kv.block_table.nbytes + \
+        B * ld + B * n_pages * 4
+    return dict(workload=wl.name, entries=entries, layers=3, ms=per["mask+compact"],
+                entries_per_s=entries / (per["mask+compact"] * 1e-3),
+                hbm_gbs=alg / (per["mask+compact"] * 1e-3) / 1e9,
+                hbm_frac=alg / (per["mask+compact"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes=alg, resident_pages_mean=None)
+
+
+def run_two_level(torch, api, W, steps, warmup, replicas=12):
+    wl = W.two_level_resident_fp8()
+    dw = api.DeviceWorkload(wl, "cuda:0", pool_copies=replicas)
+    T = wl.queries[0].T
+    res_ld = wl.resident_pages.shape[1]
+    nb = api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, T, res_ld * 64)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    idx = torch.empty((T, 512), dtype=torch.int32, device="cuda:0")
+    q = dw.query()
+    kvs = [dw.kv(r) for r in range(replicas)]
+
+    def step(s, tm):
+        if tm: tm.mark(s, 0)
+        api.fm_score_resident(q, kvs[s % replicas], dw.resident_pages, dw.n_resident, res_ld,
+                              512, idx, None, ws, nb)
+        if tm: tm.mark(s, 1)
+
+    wall, per = timed(torch, ["score_resident"], step, steps, warmup)
+    entries = int(wl.n_resident.sum()) * 64
+    alg = entries * 132 + T * (64 * 128 * 2 + 64 * 2) + wl.resident_pages.nbytes + \
+        int(wl.n_resident.sum()) * 4 + T * 512 * 4
+    ms = per["score_resident"]
+    return dict(workload=wl.name, entries=entries, ms=ms, entries_per_s=entries / (ms * 1e-3),
+                hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes=alg, note="score + top-512 in one call (two kernels)")
+
+
+def run_prefill(torch, api, W, steps, warmup):
+    wl = W.prefill_causal_fp8()
+    dw = api.DeviceWorkload(wl, "cuda:0")
+    T = wl.queries[0].T
+    ld = wl.kv.max_seq_len
+    logits = torch.empty((T, ld), dtype=torch.float32, device="cuda:0")
+    idx = torch.empty((T, 512), dtype=torch.int32, device="cuda:0")
+    q, kv = dw.query(), dw.kv()
+
+    def step(s, tm):
+        if tm: tm.mark(s, 0)
+        api.fm_index_logits(q, kv, logits, ld)
+        if tm: tm.mark(s, 1)
+        api.fm_topk512(logits, ld, T, None, None, 0, None, 512, idx)
+        if tm: tm.mark(s, 2)
+
+    wall, per = timed(torch, ["score", "topk"], step, steps, warmup)
+    pairs = int(sum(min(ld, p // 4) for p in wl.queries[0].q_pos.tolist()))
+    flops = pairs * FLOP_PER_PAIR
+    return dict(workload=wl.name, visible_pairs=pairs, score_ms=per["score"],
+                topk_ms=per["topk"], pairs_per_s=pairs / ((per["score"] + per["topk"]) * 1e-3),
+                mfma_tflops=flops / (per["score"] * 1e-3) / 1e12,
+                mfma_frac=flops / (per["score"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS)
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, budget_s=12.0):
+    import oracle
+
+    oracle.lib()
+    done_entries = 0
+    t0 = time.perf_counter()
+    rows = 0
+    for b in range(wl.kv.B):
+        L = oracle.logits(wl, rows=[b])
+        oracle.topk_rows(L)
+        done_entries += int(wl.kv.seq_lens[b])
+        rows += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done_entries / dt, unit="entries/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=f"{rows} of {wl.kv.B} requests of the headline workload "
+                       f"({done_entries} entries, fp64 logits + top-512), {dt:.1f} s")
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the indexer path shards by request with no communication; see the design "
+              f"notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from top_selection_fm_amd import api
+    from top_selection_fm_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    api.lib()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    log("headline: decode bf16 B=32 x 65536 ...")
+    wl, h = run_decode(torch, api, W, args.steps, args.warmup)
+    ms_step = h["wall_s"] / args.steps * 1e3
+    score_ms = h["per"]["score"]
+    digest = kernel_source_digest()
+    achieved = h["alg_bytes"] / (score_ms * 1e-3) / 1e9
+    traffic = read_traffic("score_decode_bf16_b32_s65536_counters.txt", digest)
+    line = {
+        "metric": "compressed-key entries scored+selected/sec (decode, bf16 keys)",
+        "value": h["entries"] * args.steps / h["wall_s"],
+        "unit": "entries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_bf16_b32_s65536_top512", "requests": 32,
+                   "entries_per_request": 65536, "page": 64, "heads": 64, "head_dim": 128,
+                   "k": 512, "pool_replicas_rotated": 3},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "score_kernel<bf16 keys, bf16 q>",
+                     "alg_bytes_per_launch": h["alg_bytes"], "avg_kernel_ms": score_ms},
+        "kernels_ms": h["per"],
+        "kernel_sources": digest,
+    }
+    if not args.headline_only:
+        sec = []
+        for name, fn in (("mask", run_mask), ("two_level", run_two_level),
+                         ("prefill", run_prefill)):
+            log(f"secondary: {name} ...")
+            try:
+                sec.append(fn(torch, api, W, max(5, args.steps // 2), 2))
+            except Exception as e:  # report and keep the headline
+                sec.append(dict(workload=name, error=repr(e)))
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * fm.h -- C ABI of libfm.so: compressed-key indexer scoring and selection on MI355X (gfx950).
+ *
+ * The indexer scores every compressed KV entry s of a request for a query row t as
+ *
+ *     L[t,s] = sum_h w[t,h] * ReLU( q[t,h,:] . k[s,:] )          (64 heads, head_dim 128)
+ *
+ * (FlashMemory-DeepSeek-V4 paper summary, section 3, the Memory-Indexer score I = sigmoid(L);
+ * README "Retriever architecture"; DeepSeek-V4 CSA page, section 3, formula CSA-1 for the
+ * native lightning indexer, which has the same form).  On top of the logits the library
+ * provides the two decisions the pages build on them:
+ *   - a Level-1 resident mask: sigmoid(L) >= p per query encoder, OR-ed over up to three
+ *     encoders (paper summary, section 3, the threshold set and the R_t equation), compacted
+ *     into 64-entry resident pages (README, page-granular recall);
+ *   - a Level-2 top-k (k = 512 in DeepSeek-V4) per query row, optionally restricted to a
+ *     resident mask or to a list of resident pages (paper summary, section 3, the C^CoreComp
+ *     set; README "Two-level recall": non-resident logits are -inf before the native top-512,
+ *     and decode scores only the resident set).
+ *
+ * Conventions for every entry point:
+ *   - Descriptors are host structs; every pointer inside them and every buffer argument is a
+ *     DEVICE pointer unless stated otherwise.  The caller owns all memory.  The library never
+ *     allocates, frees, or keeps a pointer after the call returns.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
+ *     asynchronously; nothing synchronises the host.  Buffers must stay alive until the
+ *     stream reaches the work.  Calls are stateless and thread-safe.
+ *   - Errors are detected on the host before anything is enqueued; on error nothing is
+ *     launched and fm_last_error() (per thread) describes the problem.  No exception crosses
+ *     the ABI.
+ *   - Device-side preconditions that are NOT checked on the host: seq_lens[b] <=
+ *     kv->max_seq_len; per-entry and per-token scales finite and > 0; q, w, keys free of NaN;
+ *     resident page ids distinct.  Block-table and resident-list entries are bounds-checked
+ *     on the device: an out-of-range physical page (e.g. -1) is never dereferenced and its
+ *     entries score NaN, which no selection picks.
+ */
+#ifndef FM_H
+#define FM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FM_VERSION 100          /* 1.0.0 */
+#define FM_MAX_LAYERS 4
+#define FM_PAGE_SIZE 64         /* compressed entries per page */
+#define FM_HEAD_DIM 128
+#define FM_N_HEADS 64
+#define FM_MAX_K 1024
+
+typedef enum {
+    FM_OK = 0,
+    FM_ERR_INVALID_ARG = 1,     /* null / negative / inconsistent argument */
+    FM_ERR_UNSUPPORTED = 2,     /* valid but not implemented (dtype combination, n_heads...) */
+    FM_ERR_WORKSPACE = 3,       /* workspace missing or smaller than fm_workspace_bytes() */
+    FM_ERR_LAUNCH = 4           /* the HIP runtime refused a launch */
+} fm_status;
+
+typedef enum {
+    FM_F32 = 0,                 /* float32 */
+    FM_BF16 = 1,                /* bfloat16 bit patterns (uint16) */
+    FM_FP8_E4M3 = 2,            /* OCP E4M3FN codes (uint8); a separate float32 scale applies */
+    FM_FP8_E4M3_SCALED132 = 3   /* 132-byte compressed key: 128 E4M3FN codes + float32 scale */
+} fm_dtype;
+
+typedef enum { FM_UNION_MAX = 0, FM_UNION_MEAN = 1 } fm_union_mode;
+
+typedef enum {
+    FM_OP_INDEX_LOGITS = 0,
+    FM_OP_TOPK = 1,
+    FM_OP_RESIDENT_MASK = 2,
+    FM_OP_SCORE_RESIDENT = 3
+} fm_op;
+
+/*
+ * Paged compressed-key pool(s).  Entry s of request b lives in logical page s / 64 at slot
+ * s % 64; its physical page is block_table[b * bt_ld + s / 64].  Pool layer l is an array
+ * [n_phys_pages][64][row] where row is 512 B (FM_F32), 256 B (FM_BF16) or 132 B
+ * (FM_FP8_E4M3_SCALED132: bytes 0..127 E4M3FN codes, bytes 128..131 little-endian float32
+ * scale; key = code * scale -- README "compressed_k format").  All layers share the block
+ * table (each encoder scores its own keys at the same entry positions).  Pool bases must be
+ * 16-byte aligned.  Requires bt_ld >= ceil(max_seq_len / 64).
+ */
+typedef struct {
+    const void *pool[FM_MAX_LAYERS];
+    int n_pools;
+    fm_dtype key_dtype;         /* FM_F32, FM_BF16 or FM_FP8_E4M3_SCALED132 */
+    int page_size;              /* must be 64 */
+    int head_dim;               /* must be 128 */
+    const int32_t *block_table; /* [B, bt_ld] */
+    int64_t bt_ld;
+    const int32_t *seq_lens;    /* [B] valid entries per request */
+    int B;
+    int64_t max_seq_len;        /* host-side upper bound of every seq_lens[b] */
+    int64_t n_phys_pages;
+} fm_kv_desc;
+
+/*
+ * Query rows of one encoder / layer.  q is [T, n_heads, head_dim] row-major; w is
+ * [T, n_heads] and already includes any weight scale (the library applies none).
+ * row_req maps a row to its request (NULL: row t is request t when T == B, or request 0
+ * when B == 1).  With q_pos, row t may only use entries s < floor(q_pos[t] / compress_ratio)
+ * (DeepSeek-V4 CSA page, section 10: a token position maps to compressed block
+ * floor(pos / ratio)); without it, every s < seq_len is visible.
+ * Supported (q_dtype, key_dtype): (F32, F32), (BF16, BF16), (BF16, SCALED132),
+ * (FP8_E4M3 with q_scale[T], SCALED132).  w_dtype: F32 or BF16.
+ */
+typedef struct {
+    const void *q;
+    fm_dtype q_dtype;
+    const float *q_scale;       /* [T], FP8_E4M3 q only; q = code * q_scale[t] */
+    const void *w;
+    fm_dtype w_dtype;
+    int T;
+    int n_heads;                /* must be 64 */
+    const int32_t *row_req;     /* [T] or NULL */
+    const int32_t *q_pos;       /* [T] or NULL */
+    int compress_ratio;         /* > 0; used only with q_pos (4 for CSA) */
+} fm_query_desc;
+
+/*
+ * Index logits.  For every row t and 0 <= s < ld:
+ *   logits[t * ld + s] = L[t,s] (float32) if s < n_vis(t), else -inf,
+ * where n_vis(t) = seq_len[b] (cut to floor(q_pos / ratio) with positions).  Entries of an
+ * unmapped page score NaN.  Key layer 0 of `kv` is used.
+ */
+fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *logits,
+                          int64_t ld, void *stream);
+
+/*
+ * Level-1 resident mask over n_layers encoders (1..FM_MAX_LAYERS), one query row per request
+ * per encoder (q_layers[l].T == kv->B, row b = request b), encoder l scoring pool[l].
+ *   FM_UNION_MAX : u[b,s] = max_l L_l[b,s]; resident iff u >= ln(p / (1 - p)), i.e.
+ *                  max_l sigmoid(L_l) >= p (the OR of the per-encoder decisions);
+ *   FM_UNION_MEAN: u[b,s] = mean_l sigmoid(L_l[b,s]); resident iff u >= p.
+ * Entries s < n_sink or s >= seq_len[b] - n_recent are forced resident (README: threshold +
+ * recent + sink).  mask[b * mask_ld + s] is 1/0 (torch.bool compatible) for s < mask_ld, 0
+ * for s >= seq_len[b].  Pages are the 64-entry blocks of [0, mask_ld):
+ *   page_count[b]   number of pages with >= 1 resident entry;
+ *   page_list       (nullable) [B, page_list_ld]: those pages ascending, then -1;
+ *   page_density    (nullable) [B, ceil(mask_ld / 64)]: resident entries per page;
+ *   union_score     (nullable) [B, mask_ld] float32: u (-inf for s >= seq_len).
+ * 0 < threshold < 1.  No workspace.
+ */
+fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm_kv_desc *kv,
+                           fm_union_mode mode, float threshold, int32_t n_sink,
+                           int32_t n_recent, uint8_t *mask, int64_t mask_ld,
+                           int32_t *page_count, int32_t *page_list, int64_t page_list_ld,
+                           int32_t *page_density, float *union_score, void *stream);
+
+/*
+ * Top-k per row of a logit matrix logits[T, ld].  Candidates of row t are the entries
+ * s < n_valid[t] (n_valid NULL: s < ld) whose logit is finite (not -inf, not NaN) and, when
+ * mask is given, with mask[row_req[t] * mask_ld + s] != 0 (row_req NULL: mask row t).
+ * Selects the k candidates of largest logit, ties broken by lower s (-0.0 == +0.0); with
+ * fewer than k candidates, all of them.  out_idx[t * k + i] lists the selected s in
+ * ascending order, padded with -1; out_val (nullable) holds their logits, padded with -inf.
+ * 1 <= k <= FM_MAX_K.  ws may be NULL (fm_workspace_bytes(FM_OP_TOPK, ...) == 0).
+ */
+fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_valid,
+                     const uint8_t *mask, int64_t mask_ld, const int32_t *row_req, int k,
+                     int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * Two-level scoring: for every row t (request b), score only the entries of the listed
+ * resident logical pages resident_pages[b * res_ld + j], j < n_resident[b] (distinct ids,
+ * any order), that are valid and visible, then select the top-k exactly as fm_topk512 over
+ * those candidates (ties by lower logical index).  Indices are logical entry positions
+ * 64 * page + slot, ascending, -1 padded.  Pages outside the list are never dereferenced.
+ * Needs ws_bytes >= fm_workspace_bytes(FM_OP_SCORE_RESIDENT, T, res_ld * 64).
+ */
+fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
+                            const int32_t *resident_pages, const int32_t *n_resident,
+                            int64_t res_ld, int k, int32_t *out_idx, float *out_val,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes an operation needs for T rows of up to max_candidates entries each. */
+size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates);
+
+/* Static description of a status code. */
+const char *fm_status_string(fm_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *fm_last_error(void);
+
+/* FM_VERSION of the library. */
+int fm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FM_H */

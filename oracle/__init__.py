@@ -66,6 +66,8 @@ def lib():
         L.fmo_n_visible.argtypes = [P, P, C.c_int]
         L.fmo_logits.restype = None
         L.fmo_logits.argtypes = [P, P, C.c_int, P, C.c_int, C.c_int64, C.c_int64, P, C.c_int64]
+        L.fmo_logits_at.restype = None
+        L.fmo_logits_at.argtypes = [P, P, C.c_int, P, P, C.c_int64, P]
         L.fmo_topk.restype = C.c_int
         L.fmo_topk.argtypes = [P, P, P, C.c_int64, C.c_int, P, P]
         L.fmo_topk_rows.restype = None
@@ -164,6 +166,19 @@ def logits(wl, layer: int = 0, rows=None, s_begin: int = 0, s_end: int | None = 
     kvl.pool[0] = b.kv.pool[layer]
     lib().fmo_logits(b.qref(), C.byref(kvl), 0, rows.ctypes.data, int(rows.size),
                      int(s_begin), int(s_end), out.ctypes.data, out.shape[1])
+    return out
+
+
+def logits_at(wl, rows, ents, layer: int = 0):
+    """fp64 logits at the listed (row, entry) points; -inf where not visible."""
+    b = _Bound(wl, [layer])
+    kvl = _KV.from_buffer_copy(b.kv)
+    kvl.pool[0] = b.kv.pool[layer]
+    r = np.ascontiguousarray(rows, np.int32).reshape(-1)
+    e = np.ascontiguousarray(ents, np.int64).reshape(-1)
+    out = np.empty(r.size, np.float64)
+    lib().fmo_logits_at(b.qref(), C.byref(kvl), 0, r.ctypes.data, e.ctypes.data, r.size,
+                        out.ctypes.data)
     return out
 
 

@@ -102,6 +102,7 @@ static int load_key(const fmo_kv *kv, int layer, int b, int64_t s, double *k)
 {
     int D = kv->head_dim;
     int64_t page = s / kv->page_size, off = s % kv->page_size;
+    if (s < 0 || page >= kv->bt_ld) return 0;
     int32_t phys = kv->block_table[(int64_t)b * kv->bt_ld + page];
     if (phys < 0 || phys >= kv->n_phys_pages) return 0;
     int64_t row = (int64_t)phys * kv->page_size + off;
@@ -192,6 +193,32 @@ void fmo_logits(const fmo_q *q, const fmo_kv *kv, int layer, const int32_t *rows
             if (s < fmo_n_visible(q, kv, t) && load_key(kv, layer, b, s, k))
                 L = logit_one(qv, wv, k, H, D);
             out[(int64_t)i * ld + (s - s_begin)] = L;
+        }
+        free(qv); free(wv); free(k);
+    }
+}
+
+/* the same logit at listed points: out[i] = L[rows[i], ents[i]] (-inf if not visible) */
+void fmo_logits_at(const fmo_q *q, const fmo_kv *kv, int layer, const int32_t *rows,
+                   const int64_t *ents, int64_t n, double *out)
+{
+    int H = q->n_heads, D = kv->head_dim;
+#pragma omp parallel
+    {
+        double *qv = (double *)malloc(sizeof(double) * H * D);
+        double *wv = (double *)malloc(sizeof(double) * H);
+        double *k = (double *)malloc(sizeof(double) * D);
+        int last = -1;
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            int t = rows[i];
+            if (t != last) { load_query(q, t, D, qv, wv); last = t; }
+            int b = fmo_row_request(q, kv, t);
+            double L = -INFINITY;
+            if (ents[i] >= 0 && ents[i] < fmo_n_visible(q, kv, t) &&
+                load_key(kv, layer, b, ents[i], k))
+                L = logit_one(qv, wv, k, H, D);
+            out[i] = L;
         }
         free(qv); free(wv); free(k);
     }

@@ -1,0 +1,148 @@
+"""Helpers for the GPU tests: run the C-ABI entry points on a DeviceWorkload and compare with
+the oracle under the parity rule.
+
+Parity rule:
+  * logits: per row, max|L_gpu - L_ref| / max|L_ref| <= tol over the visible entries
+    (tol 1e-5 for fp32 inputs, 2e-2 for bf16 / fp8), and -inf exactly where the oracle has -inf;
+  * decisions (mask bits, selected index sets): bit-exact except for entries whose oracle logit
+    lies within 1e-3 * max|L_ref| of the decision boundary (the logit cut for masks, the
+    oracle's k-th value for top-k).  Those band entries are counted and reported.  When a row
+    has at most k candidates there is no band: the sets must be equal.  Set sizes always match.
+"""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from top_selection_fm_amd import api
+
+BAND = 1e-3
+
+
+def note(tag: str, **kv) -> None:
+    """Print a one-line parity report (and append it to $FM_PARITY_REPORT if set)."""
+    line = json.dumps(dict(tag=tag, **kv), default=float)
+    print(line, file=sys.stderr, flush=True)
+    path = os.environ.get("FM_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
+# ----------------------------------------------------------------------------- runners
+def index_logits(dw, layer=0, ld=None, replica=0):
+    T = dw.wl.queries[layer].T
+    ld = dw.wl.kv.block_table.shape[1] * 64 if ld is None else ld
+    out = torch.empty((T, ld), dtype=torch.float32, device=dw.device)
+    api.fm_index_logits(dw.query(layer), dw.kv(replica, [layer]), out, ld)
+    return out
+
+
+def topk(logits, k=512, n_valid=None, mask=None, row_req=None):
+    T, ld = logits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    val = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    api.fm_topk512(logits, ld, T, n_valid, mask, 0 if mask is None else mask.shape[1], row_req,
+                   k, idx, val)
+    return idx, val
+
+
+def score_resident(dw, k=512, resident_pages=None, n_resident=None, replica=0):
+    rp = dw.resident_pages if resident_pages is None else resident_pages
+    nr = dw.n_resident if n_resident is None else n_resident
+    T = dw.wl.queries[0].T
+    res_ld = rp.shape[1]
+    nb = api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, T, res_ld * 64)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dw.device)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dw.device)
+    val = torch.empty((T, k), dtype=torch.float32, device=dw.device)
+    api.fm_score_resident(dw.query(0), dw.kv(replica), rp, nr, res_ld, k, idx, val, ws, nb)
+    return idx, val
+
+
+def resident_mask(dw, mode=api.FM_UNION_MAX, threshold=0.5, n_sink=0, n_recent=0,
+                  mask_ld=None, layers=None):
+    layers = list(range(len(dw.wl.queries))) if layers is None else layers
+    B = dw.wl.kv.B
+    mask_ld = dw.wl.kv.block_table.shape[1] * 64 if mask_ld is None else mask_ld
+    n_pages = -(-mask_ld // 64)
+    dev = dw.device
+    out = dict(mask=torch.empty((B, mask_ld), dtype=torch.uint8, device=dev),
+               page_count=torch.empty(B, dtype=torch.int32, device=dev),
+               page_list=torch.empty((B, n_pages), dtype=torch.int32, device=dev),
+               page_density=torch.empty((B, n_pages), dtype=torch.int32, device=dev),
+               union=torch.empty((B, mask_ld), dtype=torch.float32, device=dev))
+    api.fm_resident_mask([dw.query(l) for l in layers], dw.kv(0, layers), mode, threshold,
+                         n_sink, n_recent, out["mask"], mask_ld, out["page_count"],
+                         out["page_list"], n_pages, out["page_density"], out["union"])
+    return out
+
+
+# ----------------------------------------------------------------------------- parity checks
+def check_logits(L_gpu: np.ndarray, L_ref: np.ndarray, tol: float, tag: str) -> float:
+    """Row-wise relative max error; -inf must coincide.  Returns the worst row error."""
+    L_gpu = np.asarray(L_gpu, np.float64)
+    assert L_gpu.shape == L_ref.shape
+    ninf_ref = np.isneginf(L_ref)
+    assert np.array_equal(np.isneginf(L_gpu), ninf_ref), f"{tag}: -inf pattern differs"
+    fin = ~ninf_ref
+    assert np.all(np.isfinite(L_gpu[fin])), f"{tag}: non-finite GPU logits"
+    worst = 0.0
+    for t in range(L_ref.shape[0]):
+        f = fin[t]
+        if not f.any():
+            continue
+        scale = np.max(np.abs(L_ref[t, f]))
+        err = np.max(np.abs(L_gpu[t, f] - L_ref[t, f])) / max(scale, 1e-30)
+        worst = max(worst, err)
+    assert worst <= tol, f"{tag}: logit error {worst:.3g} > {tol}"
+    return worst
+
+
+def check_topk_row(idx_gpu, val_gpu, ref_idx, ref_cnt, ref_val_of, row_scale, k, tag):
+    """One row.  ref_val_of(list of entries) -> oracle logits of those entries."""
+    g = np.asarray(idx_gpu)
+    sel = g[g >= 0]
+    assert np.all(g[len(sel):] == -1) and np.all(g[:len(sel)] >= 0), f"{tag}: padding"
+    assert np.all(np.diff(sel) > 0), f"{tag}: not ascending / duplicates"
+    assert len(sel) == ref_cnt, f"{tag}: {len(sel)} selected, oracle {ref_cnt}"
+    r = np.asarray(ref_idx[:ref_cnt])
+    diff = np.setxor1d(sel, r)
+    if diff.size == 0:
+        return 0, 0
+    assert ref_cnt >= k, f"{tag}: sets differ with fewer than k candidates"
+    ref_vals = ref_val_of(r)
+    thr = np.min(ref_vals)
+    dv = ref_val_of(diff)
+    band = BAND * row_scale
+    bad = np.abs(dv - thr) > band
+    assert not bad.any(), (f"{tag}: {int(bad.sum())} disagreements outside the band "
+                           f"(thr {thr:.6g}, band {band:.3g}, e.g. {diff[bad][:5]} "
+                           f"-> {dv[bad][:5]})")
+    return int(diff.size), int(np.sum(np.abs(ref_vals - thr) <= band))
+
+
+def check_mask(mask_gpu, mask_ref, union_ref, cut, seq_lens, tag):
+    """Bit-exact outside the band |u_ref - cut| <= 1e-3 * max|u_ref| (per request)."""
+    mask_gpu = np.asarray(mask_gpu).astype(bool)
+    mask_ref = np.asarray(mask_ref).astype(bool)
+    dis = 0
+    band_n = 0
+    for b in range(mask_ref.shape[0]):
+        n = int(seq_lens[b])
+        u = union_ref[b, :n]
+        scale = np.max(np.abs(u[np.isfinite(u)])) if np.isfinite(u).any() else 1.0
+        inband = np.abs(u - cut) <= BAND * scale
+        d = mask_gpu[b] != mask_ref[b]
+        assert not d[n:].any(), f"{tag}: mask set past seq_len"
+        assert not (d[:n] & ~inband).any(), (f"{tag}: request {b}: "
+                                             f"{int((d[:n] & ~inband).sum())} mask bits "
+                                             f"differ outside the band")
+        dis += int(d.sum())
+        band_n += int(inband.sum())
+    return dis, band_n

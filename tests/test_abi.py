@@ -1,0 +1,207 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/fm.h declares, and
+rejects bad arguments on the host (status codes) before anything is launched.
+
+Pointers passed here are fake, aligned device addresses: every call below fails validation
+(or is a T = 0 no-op) and never reaches the HIP runtime.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from top_selection_fm_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fm.h")
+FAKE = 0x10000   # 64 KiB: aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = api.lib()
+    names = declared_functions()
+    assert set(names) >= {"fm_index_logits", "fm_resident_mask", "fm_topk512",
+                          "fm_score_resident"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(api.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    m = re.search(r"#define FM_VERSION (\d+)", open(HEADER).read())
+    assert api.fm_version() == int(m.group(1))
+    for s, name in enumerate(["FM_OK", "FM_ERR_INVALID_ARG", "FM_ERR_UNSUPPORTED",
+                              "FM_ERR_WORKSPACE", "FM_ERR_LAUNCH"]):
+        assert api.fm_status_string(s) == name
+    assert api.fm_status_string(99) == "FM_ERR_UNKNOWN"
+
+
+def test_workspace_bytes():
+    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 30, 384 * 64) == 30 * 384 * 64 * 4
+    assert api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 10 ** 6) == 0
+    assert api.fm_workspace_bytes(api.FM_OP_INDEX_LOGITS, 4, 100) == 0
+    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 0, 100) == 0
+
+
+class _Shape:
+    def __init__(self, *shape):
+        self.shape = shape
+
+
+def good_kv(key_dtype="bf16", B=2, max_seq_len=1000, n_pools=1):
+    d = api.KvDesc()
+    for i in range(n_pools):
+        d.pool[i] = FAKE * (i + 1)
+    d.n_pools = n_pools
+    d.key_dtype = api.KEY_DTYPES[key_dtype]
+    d.page_size = 64
+    d.head_dim = 128
+    d.block_table = FAKE
+    d.bt_ld = (max_seq_len + 63) // 64
+    d.seq_lens = FAKE
+    d.B = B
+    d.max_seq_len = max_seq_len
+    d.n_phys_pages = 100
+    return d
+
+
+def good_q(q_dtype="bf16", T=2, w_dtype="bf16"):
+    d = api.QueryDesc()
+    d.q = FAKE
+    d.q_dtype = api.Q_DTYPES[q_dtype]
+    d.q_scale = FAKE if q_dtype == "fp8" else None
+    d.w = FAKE
+    d.w_dtype = api.Q_DTYPES[w_dtype]
+    d.T = T
+    d.n_heads = 64
+    d.compress_ratio = 4
+    return d
+
+
+def status_of(fn, *args):
+    with pytest.raises(api.FmError) as e:
+        fn(*args)
+    return e.value.status, str(e.value)
+
+
+def logits_call(q, kv, ld=1000):
+    return status_of(api.fm_index_logits, q, kv, FAKE, ld, 0)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda q, kv: setattr(q, "n_heads", 128), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: setattr(kv, "page_size", 32), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: setattr(kv, "head_dim", 64), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: setattr(kv, "key_dtype", api.FM_FP8_E4M3), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: setattr(q, "q_dtype", api.FM_F32), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: setattr(q, "w_dtype", api.FM_FP8_E4M3), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: kv.pool.__setitem__(0, FAKE + 4), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: kv.pool.__setitem__(0, None), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "bt_ld", 10), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "B", 0), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "max_seq_len", -1), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "n_phys_pages", 0), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "block_table", None), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(q, "T", -1), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(q, "T", 3), api.FM_ERR_INVALID_ARG),      # T != B, no row_req
+    (lambda q, kv: setattr(q, "q", FAKE + 8), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(q, "w", None), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: (setattr(q, "q_pos", FAKE), setattr(q, "compress_ratio", 0)),
+     api.FM_ERR_INVALID_ARG),
+])
+def test_index_logits_validation(mutate, status):
+    q, kv = good_q(), good_kv()
+    mutate(q, kv)
+    got, msg = logits_call(q, kv)
+    assert got == status, msg
+    assert api.fm_last_error() and api.fm_last_error() in msg
+
+
+def test_fp8_query_needs_scale_and_fp8_keys():
+    q, kv = good_q("fp8"), good_kv("fp8x132")
+    q.q_scale = None
+    assert logits_call(q, kv)[0] == api.FM_ERR_INVALID_ARG
+    q2, kv2 = good_q("fp8"), good_kv("bf16")
+    assert logits_call(q2, kv2)[0] == api.FM_ERR_UNSUPPORTED
+
+
+def test_index_logits_bad_output():
+    assert status_of(api.fm_index_logits, good_q(), good_kv(), None, 1000, 0)[0] == \
+        api.FM_ERR_INVALID_ARG
+    assert logits_call(good_q(), good_kv(), ld=0)[0] == api.FM_ERR_INVALID_ARG
+    assert status_of(api.fm_index_logits, good_q(), good_kv(), FAKE + 2, 1000, 0)[0] == \
+        api.FM_ERR_INVALID_ARG
+
+
+def test_zero_rows_is_a_noop():
+    api.fm_index_logits(good_q(T=0), good_kv(), FAKE, 1000, 0)
+    api.fm_topk512(FAKE, 100, 0, None, None, 0, None, 512, FAKE)
+    assert api.fm_last_error() == ""
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(k=0), api.FM_ERR_UNSUPPORTED),
+    (dict(k=1025), api.FM_ERR_UNSUPPORTED),
+    (dict(T=-1), api.FM_ERR_INVALID_ARG),
+    (dict(ld=0), api.FM_ERR_INVALID_ARG),
+    (dict(logits=None), api.FM_ERR_INVALID_ARG),
+    (dict(out_idx=None), api.FM_ERR_INVALID_ARG),
+    (dict(mask=FAKE, mask_ld=99), api.FM_ERR_INVALID_ARG),
+])
+def test_topk_validation(args, status):
+    a = dict(logits=FAKE, ld=100, T=2, n_valid=None, mask=None, mask_ld=0, row_req=None, k=512,
+             out_idx=FAKE)
+    a.update(args)
+    got, _ = status_of(api.fm_topk512, a["logits"], a["ld"], a["T"], a["n_valid"], a["mask"],
+                       a["mask_ld"], a["row_req"], a["k"], a["out_idx"])
+    assert got == status
+
+
+def test_score_resident_validation():
+    q, kv = good_q(), good_kv("fp8x132")
+    need = api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 2, 10 * 64)
+    st = lambda **kw: status_of(api.fm_score_resident, q, kv, kw.get("rp", FAKE),
+                                kw.get("nr", FAKE), kw.get("res_ld", 10), kw.get("k", 512),
+                                FAKE, None, kw.get("ws", FAKE), kw.get("ws_bytes", need - 4))[0]
+    assert st() == api.FM_ERR_WORKSPACE
+    assert st(ws=None, ws_bytes=need) == api.FM_ERR_WORKSPACE
+    assert st(ws=FAKE + 4, ws_bytes=need) == api.FM_ERR_WORKSPACE
+    assert st(rp=None, ws_bytes=need) == api.FM_ERR_INVALID_ARG
+    assert st(res_ld=0, ws_bytes=need) == api.FM_ERR_INVALID_ARG
+    assert st(k=4096, ws_bytes=need) == api.FM_ERR_UNSUPPORTED
+
+
+def mask_call(qs, kv, **kw):
+    arr = (api.QueryDesc * len(qs))(*qs) if qs else None
+    L = api.lib()
+    return L.fm_resident_mask(arr, kw.get("n_layers", len(qs)), C.byref(kv),
+                              kw.get("mode", api.FM_UNION_MAX), kw.get("threshold", 0.5),
+                              kw.get("n_sink", 0), kw.get("n_recent", 0),
+                              kw.get("mask", FAKE), kw.get("mask_ld", 1000),
+                              kw.get("page_count", FAKE), kw.get("page_list", None),
+                              kw.get("page_list_ld", 0), None, None, None)
+
+
+def test_resident_mask_validation():
+    kv = good_kv("fp8x132", n_pools=3)
+    qs = [good_q() for _ in range(3)]
+    assert mask_call(qs, kv, threshold=0.0) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, threshold=1.0) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, n_layers=0) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, n_layers=5) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, mode=7) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, n_sink=-1) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, mask=None) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, page_count=None) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, kv, page_list=FAKE, page_list_ld=0) == api.FM_ERR_INVALID_ARG
+    assert mask_call(qs, good_kv("fp8x132", n_pools=2)) == api.FM_ERR_INVALID_ARG
+    bad = [good_q(), good_q(T=3), good_q()]
+    assert mask_call(bad, kv) == api.FM_ERR_INVALID_ARG
+    fp8 = [good_q("fp8") for _ in range(3)]
+    assert mask_call(fp8, kv) == api.FM_ERR_UNSUPPORTED

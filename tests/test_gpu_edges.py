@@ -1,0 +1,135 @@
+"""GPU edge cases and invariants of the C-ABI entry points.
+
+Top-k on constructed logit rows (ties, signed zeros, -inf / NaN, fewer candidates than k,
+k from 1 to 1024, n_valid, masks, empty rows) is compared bit-exactly with the oracle's
+selection on the same float32 values.  Scoring invariants: two runs are bit-identical, a
+permuted block table with the pool permuted alike gives bit-identical logits, and poisoned
+pages outside the resident list never reach a result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import gpu_util as G
+from top_selection_fm_amd import api
+from top_selection_fm_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_topk(L: np.ndarray, k, n_valid=None, mask=None, row_req=None):
+    Lt = torch.from_numpy(np.ascontiguousarray(L, np.float32)).cuda()
+    nv = None if n_valid is None else torch.from_numpy(np.asarray(n_valid, np.int32)).cuda()
+    mk = None if mask is None else torch.from_numpy(np.asarray(mask, np.uint8)).cuda()
+    rr = None if row_req is None else torch.from_numpy(np.asarray(row_req, np.int32)).cuda()
+    idx, val = G.topk(Lt, k=k, n_valid=nv, mask=mk, row_req=rr)
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+def ref_topk(L, k, n_valid=None, mask=None, row_req=None):
+    ri, rv, rc = oracle.topk_rows(np.asarray(L, np.float32).astype(np.float64), k=k,
+                                  n_valid=n_valid, mask=mask, row_req=row_req)
+    return ri, rv
+
+
+def constructed_rows(rng, T, n):
+    L = rng.standard_normal((T, n)).astype(np.float32)
+    L[0] = 1.0                                        # all tie
+    L[1] = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0))   # signed zeros
+    L[2] = np.round(L[2] * 2) / 2                     # few distinct values
+    L[3, rng.random(n) < 0.3] = -np.inf
+    L[4, rng.random(n) < 0.3] = np.nan
+    L[5] = -np.inf                                    # no candidate at all
+    L[6, :] = -np.inf
+    L[6, [3, n // 2, n - 1]] = [2.0, -1.0, 0.0]       # three candidates
+    L[7] = np.float32(3.4e38) * np.sign(L[7])         # extremes
+    return L
+
+
+@pytest.mark.parametrize("k", [1, 7, 512, 1000, 1024])
+@pytest.mark.parametrize("n", [1, 600, 5000])
+def test_topk_constructed_rows_bit_exact(k, n):
+    rng = np.random.default_rng(k * 10007 + n)
+    L = constructed_rows(rng, 12, n)
+    ig, vg = gpu_topk(L, k)
+    ri, rv = ref_topk(L, k)
+    assert np.array_equal(ig, ri)
+    sel = ri >= 0
+    assert np.array_equal(vg[sel], rv[sel].astype(np.float32))
+    assert np.all(np.isneginf(vg[~sel]))
+
+
+def test_topk_n_valid_mask_and_row_req():
+    rng = np.random.default_rng(5)
+    T, n = 9, 3000
+    L = constructed_rows(rng, T, n)
+    nv = rng.integers(0, n + 1, T).astype(np.int32)
+    nv[0] = 0
+    mask = (rng.random((3, n)) < 0.4).astype(np.uint8)
+    row_req = (np.arange(T) % 3).astype(np.int32)
+    ig, _ = gpu_topk(L, 512, n_valid=nv, mask=mask, row_req=row_req)
+    ri, _ = ref_topk(L, 512, n_valid=nv, mask=mask, row_req=row_req)
+    assert np.array_equal(ig, ri)
+    assert np.all(ig[0] == -1)
+
+
+def test_topk_long_rows_262144_candidates():
+    """Mode-A sized rows: 262,144 candidates, with planted duplicates of the 512th value."""
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((3, 262144)).astype(np.float32)
+    L[1, rng.choice(262144, 5000, replace=False)] = np.float32(2.5)   # a huge tie group
+    mask = (rng.random((3, 262144)) < 0.12).astype(np.uint8)
+    ig, _ = gpu_topk(L, 512)
+    ri, _ = ref_topk(L, 512)
+    assert np.array_equal(ig, ri)
+    ig, _ = gpu_topk(L, 512, mask=mask)
+    ri, _ = ref_topk(L, 512, mask=mask)
+    assert np.array_equal(ig, ri)
+
+
+def test_scoring_is_deterministic_and_placement_invariant():
+    wl = W.decode_bf16(seed=3001, B=4, seq_len=64 * 33 + 9, ragged=True)
+    dw = api.DeviceWorkload(wl, "cuda:0")
+    L1 = G.index_logits(dw)
+    L2 = G.index_logits(dw)
+    assert torch.equal(L1, L2)
+    i1, v1 = G.topk(L1)
+    i2, v2 = G.topk(L2)
+    assert torch.equal(i1, i2) and torch.equal(v1, v2)
+    # move every physical page elsewhere and remap the block table alike
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(wl.kv.n_phys_pages)
+    pool = np.empty_like(wl.kv.pools[0])
+    pool[perm] = wl.kv.pools[0]
+    wl2 = W.Workload(wl.name, W.KeyPool([pool], "bf16", perm[wl.kv.block_table].astype(np.int32),
+                                        wl.kv.seq_lens), wl.queries)
+    L3 = G.index_logits(api.DeviceWorkload(wl2, "cuda:0"))
+    assert torch.equal(torch.nan_to_num(L1, nan=7.0), torch.nan_to_num(L3, nan=7.0))
+
+
+def test_unmapped_pages_score_nan_and_are_never_selected():
+    wl = W.decode_bf16(seed=3002, B=2, seq_len=64 * 20, ragged=False)
+    bt = wl.kv.block_table.copy()
+    bt[0, [2, 5]] = -1
+    bt[1, 7] = 10 ** 8                        # out of range: bounds-checked on the device
+    wl2 = W.Workload(wl.name, W.KeyPool(wl.kv.pools, "bf16", bt, wl.kv.seq_lens), wl.queries)
+    dw = api.DeviceWorkload(wl2, "cuda:0")
+    L = G.index_logits(dw).cpu().numpy()
+    assert np.all(np.isnan(L[0, 2 * 64:3 * 64])) and np.all(np.isnan(L[1, 7 * 64:8 * 64]))
+    assert np.isfinite(L[0, :128]).all()
+    idx, _ = G.topk(torch.from_numpy(L).cuda())
+    ig = idx.cpu().numpy()
+    assert not np.isin(ig[0] // 64, [2, 5]).any() and not np.any(ig[1] // 64 == 7)
+
+
+def test_resident_pages_out_of_range_are_skipped():
+    wl = W.two_level_resident_fp8(seed=3003, B=2, seq_len=64 * 40, kmax=6, poison=True)
+    rp = wl.resident_pages.copy()
+    rp[1, 2] = 10 ** 6                         # not a page of this request
+    dw = api.DeviceWorkload(wl, "cuda:0")
+    idx, val = G.score_resident(dw, resident_pages=torch.from_numpy(rp).cuda())
+    ig, vg = idx.cpu().numpy(), val.cpu().numpy()
+    sel = ig[1][ig[1] >= 0]
+    assert sel.size == 5 * 64 and np.all(np.isfinite(vg[1][:sel.size]))
+    assert set((sel // 64).tolist()) == set(rp[1].tolist()) - {10 ** 6}

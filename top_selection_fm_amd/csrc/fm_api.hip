@@ -1,0 +1,320 @@
+// fm_api.hip -- the C ABI of libfm.so (declared and documented in include/fm.h).
+//
+// Host layer only: validate every argument, fill the kernel argument blocks, enqueue the
+// kernels on the caller's stream.  Nothing here allocates device memory, synchronises, or
+// keeps state beyond a thread-local error message.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fm_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+fm_status fail(fm_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fm_status ok() {
+    g_err[0] = 0;
+    return FM_OK;
+}
+
+#define REQUIRE(cond, status, ...)                     \
+    do {                                               \
+        if (!(cond)) return fail((status), __VA_ARGS__); \
+    } while (0)
+
+#define CHECK(expr)                           \
+    do {                                      \
+        fm_status s_ = (expr);                \
+        if (s_ != FM_OK) return s_;           \
+    } while (0)
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int key_fmt(fm_dtype d) {
+    return d == FM_F32 ? fm::KEY_F32 : d == FM_BF16 ? fm::KEY_BF16 : fm::KEY_FP8;
+}
+
+fm_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(FM_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return FM_OK;
+}
+
+fm_status check_kv(const fm_kv_desc *kv, int n_pools_needed) {
+    REQUIRE(kv, FM_ERR_INVALID_ARG, "kv descriptor is NULL");
+    REQUIRE(kv->page_size == FM_PAGE_SIZE, FM_ERR_UNSUPPORTED, "page_size %d (only %d)",
+            kv->page_size, FM_PAGE_SIZE);
+    REQUIRE(kv->head_dim == FM_HEAD_DIM, FM_ERR_UNSUPPORTED, "head_dim %d (only %d)",
+            kv->head_dim, FM_HEAD_DIM);
+    REQUIRE(kv->key_dtype == FM_F32 || kv->key_dtype == FM_BF16 ||
+                kv->key_dtype == FM_FP8_E4M3_SCALED132,
+            FM_ERR_UNSUPPORTED, "key dtype %d", (int)kv->key_dtype);
+    REQUIRE(kv->B >= 1, FM_ERR_INVALID_ARG, "B = %d", kv->B);
+    REQUIRE(kv->n_pools >= n_pools_needed && kv->n_pools <= FM_MAX_LAYERS, FM_ERR_INVALID_ARG,
+            "n_pools = %d, need %d..%d", kv->n_pools, n_pools_needed, FM_MAX_LAYERS);
+    for (int l = 0; l < n_pools_needed; ++l) {
+        REQUIRE(kv->pool[l], FM_ERR_INVALID_ARG, "pool[%d] is NULL", l);
+        REQUIRE(aligned(kv->pool[l], 16), FM_ERR_INVALID_ARG, "pool[%d] not 16-byte aligned", l);
+    }
+    REQUIRE(kv->block_table && kv->seq_lens, FM_ERR_INVALID_ARG, "block_table / seq_lens NULL");
+    REQUIRE(kv->max_seq_len >= 0 && kv->max_seq_len <= (int64_t)INT32_MAX, FM_ERR_INVALID_ARG,
+            "max_seq_len = %lld", (long long)kv->max_seq_len);
+    REQUIRE(kv->bt_ld >= 1 && kv->bt_ld >= (kv->max_seq_len + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE,
+            FM_ERR_INVALID_ARG, "bt_ld = %lld < ceil(max_seq_len / 64)", (long long)kv->bt_ld);
+    REQUIRE(kv->n_phys_pages >= 1 && kv->n_phys_pages <= (int64_t)INT32_MAX, FM_ERR_INVALID_ARG,
+            "n_phys_pages = %lld", (long long)kv->n_phys_pages);
+    return FM_OK;
+}
+
+fm_status check_q(const fm_query_desc *q, const fm_kv_desc *kv, const char *name) {
+    REQUIRE(q, FM_ERR_INVALID_ARG, "%s: query descriptor is NULL", name);
+    REQUIRE(q->T >= 0, FM_ERR_INVALID_ARG, "%s: T = %d", name, q->T);
+    REQUIRE(q->n_heads == FM_N_HEADS, FM_ERR_UNSUPPORTED, "%s: n_heads %d (only %d)", name,
+            q->n_heads, FM_N_HEADS);
+    REQUIRE(q->w_dtype == FM_F32 || q->w_dtype == FM_BF16, FM_ERR_UNSUPPORTED,
+            "%s: w dtype %d", name, (int)q->w_dtype);
+    const fm_dtype k = kv->key_dtype;
+    const bool combo = (q->q_dtype == FM_F32 && k == FM_F32) ||
+                       (q->q_dtype == FM_BF16 && (k == FM_BF16 || k == FM_FP8_E4M3_SCALED132)) ||
+                       (q->q_dtype == FM_FP8_E4M3 && k == FM_FP8_E4M3_SCALED132);
+    REQUIRE(combo, FM_ERR_UNSUPPORTED, "%s: q dtype %d with key dtype %d", name, (int)q->q_dtype,
+            (int)k);
+    if (q->T == 0) return FM_OK;
+    REQUIRE(q->q && q->w, FM_ERR_INVALID_ARG, "%s: q / w NULL", name);
+    REQUIRE(aligned(q->q, 16), FM_ERR_INVALID_ARG, "%s: q not 16-byte aligned", name);
+    REQUIRE(q->q_dtype != FM_FP8_E4M3 || q->q_scale, FM_ERR_INVALID_ARG,
+            "%s: fp8 q needs q_scale", name);
+    REQUIRE(q->row_req || q->T == kv->B || kv->B == 1, FM_ERR_INVALID_ARG,
+            "%s: row_req NULL needs T == B or B == 1 (T = %d, B = %d)", name, q->T, kv->B);
+    REQUIRE(!q->q_pos || q->compress_ratio >= 1, FM_ERR_INVALID_ARG,
+            "%s: compress_ratio = %d", name, q->compress_ratio);
+    return FM_OK;
+}
+
+fm::QArgs make_q(const fm_query_desc *q, const fm_kv_desc *kv) {
+    fm::QArgs a;
+    a.q = q->q;
+    a.q_scale = q->q_scale;
+    a.w = q->w;
+    a.w_bf16 = q->w_dtype == FM_BF16;
+    a.T = q->T;
+    a.row_req = q->row_req;
+    a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
+    a.q_pos = q->q_pos;
+    a.ratio = q->compress_ratio >= 1 ? q->compress_ratio : 1;
+    return a;
+}
+
+fm::KvArgs make_kv(const fm_kv_desc *kv) {
+    fm::KvArgs a;
+    for (int l = 0; l < FM_MAX_LAYERS; ++l)
+        a.pool[l] = l < kv->n_pools ? (const uint8_t *)kv->pool[l] : nullptr;
+    a.bt = kv->block_table;
+    a.bt_ld = kv->bt_ld;
+    a.seq_lens = kv->seq_lens;
+    a.n_phys = kv->n_phys_pages;
+    a.B = kv->B;
+    return a;
+}
+
+// page slots per wave: enough waves to fill 256 CUs several times, at most 16 slots each
+int pages_per_wave(int64_t total_slots) {
+    int64_t p = total_slots / 4096;
+    if (p < 2) p = 2;
+    if (p > 16) p = 16;
+    return (int)p;
+}
+
+fm_status run_score(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t *res_pages,
+                    const int32_t *n_res, int64_t res_ld, float *out, int64_t out_ld,
+                    int64_t n_slots, hipStream_t st) {
+    fm::ScoreArgs a;
+    a.q = make_q(q, kv);
+    a.kv = make_kv(kv);
+    a.res_pages = res_pages;
+    a.n_res = n_res;
+    a.res_ld = res_ld;
+    a.out = out;
+    a.out_ld = out_ld;
+    a.n_slots = n_slots;
+    a.ppw = pages_per_wave((int64_t)q->T * n_slots);
+    if (kv->key_dtype == FM_F32) return launched(fm::launch_score_f32(a, st), "score_f32");
+    const int qf = q->q_dtype == FM_FP8_E4M3 ? fm::Q_FP8 : fm::Q_BF16;
+    return launched(fm::launch_score(a, key_fmt(kv->key_dtype), qf, st), "score");
+}
+
+}  // namespace
+
+extern "C" {
+
+fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *logits,
+                          int64_t ld, void *stream) {
+    CHECK(check_kv(kv, 1));
+    CHECK(check_q(q, kv, "q"));
+    REQUIRE(logits, FM_ERR_INVALID_ARG, "logits is NULL");
+    REQUIRE(ld >= 1, FM_ERR_INVALID_ARG, "ld = %lld", (long long)ld);
+    REQUIRE(aligned(logits, 4), FM_ERR_INVALID_ARG, "logits not 4-byte aligned");
+    if (q->T == 0) return ok();
+    CHECK(run_score(q, kv, nullptr, nullptr, 0, logits, ld, (ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE,
+                    (hipStream_t)stream));
+    return ok();
+}
+
+fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_valid,
+                     const uint8_t *mask, int64_t mask_ld, const int32_t *row_req, int k,
+                     int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    REQUIRE(T >= 0, FM_ERR_INVALID_ARG, "T = %d", T);
+    REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
+    REQUIRE(ld >= 1 && ld <= (int64_t)INT32_MAX, FM_ERR_INVALID_ARG, "ld = %lld", (long long)ld);
+    if (T == 0) return ok();
+    REQUIRE(logits && out_idx, FM_ERR_INVALID_ARG, "logits / out_idx NULL");
+    REQUIRE(!mask || mask_ld >= ld, FM_ERR_INVALID_ARG, "mask_ld %lld < ld %lld",
+            (long long)mask_ld, (long long)ld);
+    fm::TopkArgs a;
+    a.logits = logits;
+    a.ld = ld;
+    a.T = T;
+    a.n_valid = n_valid;
+    a.mask = mask;
+    a.mask_ld = mask_ld;
+    a.row_req = row_req;
+    a.b_is_zero = 0;
+    a.res_pages = nullptr;
+    a.n_res = nullptr;
+    a.res_ld = 0;
+    a.B = INT32_MAX;   // mask rows are the caller's: row_req[t] must index one
+    a.k = k;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    CHECK(launched(fm::launch_topk(a, (hipStream_t)stream), "topk"));
+    return ok();
+}
+
+fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
+                            const int32_t *resident_pages, const int32_t *n_resident,
+                            int64_t res_ld, int k, int32_t *out_idx, float *out_val, void *ws,
+                            size_t ws_bytes, void *stream) {
+    CHECK(check_kv(kv, 1));
+    CHECK(check_q(q, kv, "q"));
+    REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
+    REQUIRE(res_ld >= 1 && res_ld * FM_PAGE_SIZE <= (int64_t)INT32_MAX, FM_ERR_INVALID_ARG,
+            "res_ld = %lld", (long long)res_ld);
+    if (q->T == 0) return ok();
+    REQUIRE(resident_pages && n_resident && out_idx, FM_ERR_INVALID_ARG,
+            "resident_pages / n_resident / out_idx NULL");
+    const size_t need = fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T, res_ld * FM_PAGE_SIZE);
+    REQUIRE(ws && ws_bytes >= need && aligned(ws, 16), FM_ERR_WORKSPACE,
+            "workspace %zu bytes at %p, need %zu (16-byte aligned)", ws_bytes, ws, need);
+    hipStream_t st = (hipStream_t)stream;
+    float *wl = (float *)ws;
+    const int64_t ld = res_ld * FM_PAGE_SIZE;
+    CHECK(run_score(q, kv, resident_pages, n_resident, res_ld, wl, ld, res_ld, st));
+    fm::TopkArgs a;
+    a.logits = wl;
+    a.ld = ld;
+    a.T = q->T;
+    a.n_valid = nullptr;
+    a.mask = nullptr;
+    a.mask_ld = 0;
+    a.row_req = q->row_req;
+    a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
+    a.res_pages = resident_pages;
+    a.n_res = n_resident;
+    a.res_ld = res_ld;
+    a.B = kv->B;
+    a.k = k;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    CHECK(launched(fm::launch_topk(a, st), "topk"));
+    return ok();
+}
+
+fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm_kv_desc *kv,
+                           fm_union_mode mode, float threshold, int32_t n_sink,
+                           int32_t n_recent, uint8_t *mask, int64_t mask_ld,
+                           int32_t *page_count, int32_t *page_list, int64_t page_list_ld,
+                           int32_t *page_density, float *union_score, void *stream) {
+    REQUIRE(n_layers >= 1 && n_layers <= FM_MAX_LAYERS, FM_ERR_INVALID_ARG, "n_layers = %d",
+            n_layers);
+    CHECK(check_kv(kv, n_layers));
+    REQUIRE(q_layers, FM_ERR_INVALID_ARG, "q_layers is NULL");
+    for (int l = 0; l < n_layers; ++l) {
+        CHECK(check_q(&q_layers[l], kv, "q_layers[l]"));
+        REQUIRE(q_layers[l].T == kv->B, FM_ERR_INVALID_ARG,
+                "q_layers[%d].T = %d, must equal B = %d (one row per request)", l,
+                q_layers[l].T, kv->B);
+        REQUIRE(q_layers[l].q_dtype == q_layers[0].q_dtype, FM_ERR_UNSUPPORTED,
+                "layers mix q dtypes");
+        REQUIRE(q_layers[l].q_dtype != FM_FP8_E4M3, FM_ERR_UNSUPPORTED,
+                "fp8 queries are not supported for the resident mask");
+    }
+    REQUIRE(mode == FM_UNION_MAX || mode == FM_UNION_MEAN, FM_ERR_INVALID_ARG, "mode = %d",
+            (int)mode);
+    REQUIRE(threshold > 0.f && threshold < 1.f, FM_ERR_INVALID_ARG,
+            "threshold %g outside (0, 1)", (double)threshold);
+    REQUIRE(n_sink >= 0 && n_recent >= 0, FM_ERR_INVALID_ARG, "n_sink / n_recent negative");
+    REQUIRE(mask && page_count, FM_ERR_INVALID_ARG, "mask / page_count NULL");
+    REQUIRE(mask_ld >= 1 && mask_ld <= (int64_t)INT32_MAX, FM_ERR_INVALID_ARG, "mask_ld = %lld",
+            (long long)mask_ld);
+    REQUIRE(!page_list || page_list_ld >= 1, FM_ERR_INVALID_ARG, "page_list_ld = %lld",
+            (long long)page_list_ld);
+    hipStream_t st = (hipStream_t)stream;
+    fm::MaskArgs a;
+    for (int l = 0; l < FM_MAX_LAYERS; ++l)
+        a.q[l] = l < n_layers ? make_q(&q_layers[l], kv) : fm::QArgs{};
+    a.kv = make_kv(kv);
+    a.n_layers = n_layers;
+    a.mean_mode = mode == FM_UNION_MEAN;
+    const double p = (double)threshold;
+    a.cut = mode == FM_UNION_MEAN ? threshold : (p == 0.5 ? 0.0f : (float)log(p / (1.0 - p)));
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    a.mask = mask;
+    a.mask_ld = mask_ld;
+    a.union_score = union_score;
+    a.n_pages = (mask_ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE;
+    CHECK(launched(fm::launch_mask(a, key_fmt(kv->key_dtype), kv->B, st), "resident_mask"));
+    fm::CompactArgs c;
+    c.mask = mask;
+    c.mask_ld = mask_ld;
+    c.n_pages = a.n_pages;
+    c.page_count = page_count;
+    c.page_list = page_list;
+    c.page_list_ld = page_list_ld;
+    c.page_density = page_density;
+    CHECK(launched(fm::launch_compact(c, kv->B, st), "page_compact"));
+    return ok();
+}
+
+size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates) {
+    if (op != FM_OP_SCORE_RESIDENT || T <= 0 || max_candidates <= 0) return 0;
+    return (size_t)T * (size_t)max_candidates * sizeof(float);
+}
+
+const char *fm_status_string(fm_status s) {
+    switch (s) {
+    case FM_OK: return "FM_OK";
+    case FM_ERR_INVALID_ARG: return "FM_ERR_INVALID_ARG";
+    case FM_ERR_UNSUPPORTED: return "FM_ERR_UNSUPPORTED";
+    case FM_ERR_WORKSPACE: return "FM_ERR_WORKSPACE";
+    case FM_ERR_LAUNCH: return "FM_ERR_LAUNCH";
+    }
+    return "FM_ERR_UNKNOWN";
+}
+
+const char *fm_last_error(void) { return g_err; }
+
+int fm_version(void) { return FM_VERSION; }
+
+}  // extern "C"

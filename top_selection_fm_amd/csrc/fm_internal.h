@@ -1,0 +1,107 @@
+// fm_internal.h -- kernel argument blocks and launch entry points shared by the HIP sources of
+// libfm.so.  Host code validates every argument before it fills one of these blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fm.h"
+
+namespace fm {
+
+constexpr int kPage = FM_PAGE_SIZE;  // compressed entries per page
+constexpr int kDim = FM_HEAD_DIM;    // head dimension
+constexpr int kHeads = FM_N_HEADS;   // heads of one query row
+constexpr int kRowFp8 = kDim + 4;    // 132-byte compressed-key row
+constexpr int kRowBf16 = kDim * 2;
+constexpr int kRowF32 = kDim * 4;
+
+// key / query element formats the kernels are instantiated for
+enum KeyFmt { KEY_F32 = 0, KEY_BF16 = 1, KEY_FP8 = 3 };
+enum QFmt { Q_F32 = 0, Q_BF16 = 1, Q_FP8 = 2 };
+
+// One query layer as the kernels see it.
+struct QArgs {
+    const void *q;          // [T, 64, 128]
+    const float *q_scale;   // [T] (fp8 q)
+    const void *w;          // [T, 64]
+    int w_bf16;             // 1: w is bf16, 0: float32
+    int T;
+    const int32_t *row_req; // [T] or null
+    int b_is_zero;          // row_req null and B == 1: every row is request 0
+    const int32_t *q_pos;   // [T] or null
+    int ratio;
+};
+
+struct KvArgs {
+    const uint8_t *pool[FM_MAX_LAYERS];
+    const int32_t *bt;
+    int64_t bt_ld;
+    const int32_t *seq_lens;
+    int64_t n_phys;
+    int B;
+};
+
+// Scoring of query rows over pages, writing one float per entry.
+//   res_pages == null: slot j of row t is logical page j; out column = 64 j + e.
+//   res_pages != null: slot j is resident_pages[b, j] (j < n_res[b]); out column = 64 j + e.
+struct ScoreArgs {
+    QArgs q;
+    KvArgs kv;
+    const int32_t *res_pages;
+    const int32_t *n_res;
+    int64_t res_ld;
+    float *out;
+    int64_t out_ld;      // floats per output row
+    int64_t n_slots;     // page slots per row covered by the grid
+    int ppw;             // page slots per wave
+};
+
+struct MaskArgs {
+    QArgs q[FM_MAX_LAYERS];
+    KvArgs kv;
+    int n_layers;
+    int mean_mode;
+    float cut;           // MAX: logit cut ln(p/(1-p)); MEAN: probability p
+    int32_t n_sink, n_recent;
+    uint8_t *mask;
+    int64_t mask_ld;
+    float *union_score;  // nullable
+    int64_t n_pages;     // ceil(mask_ld / 64)
+};
+
+struct CompactArgs {
+    const uint8_t *mask;
+    int64_t mask_ld;
+    int64_t n_pages;
+    int32_t *page_count;
+    int32_t *page_list;  // nullable
+    int64_t page_list_ld;
+    int32_t *page_density;  // nullable
+};
+
+struct TopkArgs {
+    const float *logits;
+    int64_t ld;
+    int T;
+    const int32_t *n_valid;    // [T] or null
+    const uint8_t *mask;       // nullable
+    int64_t mask_ld;
+    const int32_t *row_req;    // request of row t (mask row and resident list), or null
+    int b_is_zero;
+    const int32_t *res_pages;  // two-level index map (nullable)
+    const int32_t *n_res;
+    int64_t res_ld;
+    int B;                     // requests (bounds row_req in two-level mode)
+    int k;
+    int32_t *out_idx;
+    float *out_val;            // nullable
+};
+
+hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s);
+hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);
+hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s);
+hipError_t launch_compact(const CompactArgs &a, int B, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+
+}  // namespace fm

@@ -1,0 +1,492 @@
+// score.hip -- index-logit kernels for gfx950.
+//
+// L[t,s] = sum_h w[t,h] * ReLU(q[t,h,:] . k[s,:]) over 64 heads of dimension 128
+// (FlashMemory-DeepSeek-V4 paper summary, section 3, the Memory-Indexer score; DeepSeek-V4 CSA
+// page, section 3, formula CSA-1).  All 64 heads of a query row share one key row, so a page of
+// 64 entries is a dense [64 heads x 128] . [128 x 64 entries] contraction: it runs on MFMA.
+//
+// Operand layout (v_mfma_f32_16x16x32_bf16, wave64): lane l = 16 g + r holds row r of the A
+// tile (a head) and column r of the B tile (an entry), eight k-values each; the accumulator
+// lane holds rows 4 g .. 4 g + 3 of column r.  A dot product does not depend on the order of
+// its terms, so the eight dimensions a lane carries are chosen per key format to make its
+// loads contiguous; queries are loaded with the same assignment:
+//   bf16 keys: lane group g, k-step kk -> dims (4 kk + g) * 8 .. +8   (16 B of the 256-B row)
+//   fp8  keys: lane group g, k-step kk -> dims 32 g + 8 kk .. +8      (32 B of the 132-B row)
+// fp8 keys are widened to bf16 with v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value is a
+// bf16 value); the per-entry scale is applied after the head sum, which is valid because the
+// scale is positive (ReLU(c x) = c ReLU(x) for c > 0).  fp8 queries against fp8 keys use the
+// gfx950 v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales.
+//
+// The head sum: each lane weights and sums its 16 accumulator values (4 head tiles x 4 rows),
+// then two cross-lane adds (lane xor 16, xor 32) complete the 64-head sum for its column.
+#include <math.h>
+
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// page-slot states (wave-uniform), besides a non-negative physical page id
+constexpr int kSlotInvisible = -1;  // every entry of the page is past the visible length
+constexpr int kSlotUnmapped = -2;   // the block table (or resident list) points nowhere valid
+constexpr int kSlotEmpty = -3;      // resident-list slot beyond n_resident: nothing to write
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// request of row t; -1 when row_req points outside [0, B)
+__device__ __forceinline__ int row_request(const QArgs &q, const KvArgs &kv, int t) {
+    const int b = q.row_req ? q.row_req[t] : (q.b_is_zero ? 0 : t);
+    return (b >= 0 && b < kv.B) ? b : -1;
+}
+
+// entries row t may use (0 for a row whose request is out of range)
+__device__ __forceinline__ int64_t n_visible(const QArgs &q, const KvArgs &kv, int t, int b) {
+    if (b < 0) return 0;
+    int64_t n = kv.seq_lens[b];
+    if (q.q_pos) {
+        int64_t c = (int64_t)q.q_pos[t] / q.ratio;
+        n = c < n ? c : n;
+    }
+    return n < 0 ? 0 : n;
+}
+
+template <int KF>
+__device__ __forceinline__ int dim_base(int g, int kk) {
+    return KF == KEY_BF16 ? (kk * 4 + g) * 8 : g * 32 + kk * 8;
+}
+
+// ---------------------------------------------------------------- query operands
+struct QBf16 { u32x4 a[4][4]; };   // [head tile m][k-step kk]: 8 bf16
+struct QFp8 { i32x8 a[4]; };       // [head tile m]: 32 E4M3 codes
+
+template <int KF>
+__device__ __forceinline__ void load_q(QBf16 &Q, const uint8_t *qrow, int r, int g) {
+    const uint16_t *q = (const uint16_t *)qrow;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            Q.a[m][kk] = *(const u32x4 *)(q + (16 * m + r) * kDim + dim_base<KF>(g, kk));
+}
+
+__device__ __forceinline__ void load_q(QFp8 &Q, const uint8_t *qrow, int r, int g) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Q.a[m] = *(const i32x8 *)(qrow + (16 * m + r) * kDim + g * 32);
+}
+
+// w[t, 16 m + 4 g + i] for the accumulator rows this lane holds
+__device__ __forceinline__ void load_w(float (&wv)[16], const void *w, int w_bf16, int t, int g) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int h = 16 * m + 4 * g + i;
+            wv[m * 4 + i] = w_bf16 ? bf16f(((const uint16_t *)w)[(int64_t)t * kHeads + h])
+                                   : ((const float *)w)[(int64_t)t * kHeads + h];
+        }
+}
+
+// ---------------------------------------------------------------- key pages in registers
+struct PgBf16 { u32x4 b[4][4]; };              // [entry tile j][k-step kk]
+struct PgFp8 { u32x4 b[4][2]; float scale; };  // [entry tile j][half]: 16 codes; own-row scale
+
+__device__ __forceinline__ u32x4 load16(const uint8_t *p) {  // 4-byte aligned
+    const uint32_t *w = (const uint32_t *)p;
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ void load_page(PgBf16 &P, const uint8_t *page, int r, int g, int) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            P.b[j][kk] = *(const u32x4 *)(page + (16 * j + r) * kRowBf16 + (kk * 4 + g) * 16);
+}
+
+__device__ __forceinline__ void load_page(PgFp8 &P, const uint8_t *page, int r, int g, int ln) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) P.b[j][h] = load16(page + (16 * j + r) * kRowFp8 + g * 32 + h * 16);
+    P.scale = *(const float *)(page + ln * kRowFp8 + kDim);
+}
+
+__device__ __forceinline__ u32x4 b_operand(const PgBf16 &P, int j, int kk) { return P.b[j][kk]; }
+
+__device__ __forceinline__ u32x4 b_operand(const PgFp8 &P, int j, int kk) {
+    u32x4 v = P.b[j][kk >> 1];
+    uint32_t d0 = (kk & 1) ? v[2] : v[0];
+    uint32_t d1 = (kk & 1) ? v[3] : v[1];
+    u32x4 o;
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+    return o;
+}
+
+__device__ __forceinline__ float page_scale(const PgBf16 &) { return 1.0f; }
+__device__ __forceinline__ float page_scale(const PgFp8 &P) { return P.scale; }
+
+// weighted ReLU head sum of one 16-entry tile; every lane of column r returns the total
+__device__ __forceinline__ float head_sum(const f32x4 (&acc)[4], const float (&wv)[16]) {
+    float p = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p = fmaf(wv[m * 4 + i], fmaxf(acc[m][i], 0.f), p);
+    p += __shfl_xor(p, 16);
+    p += __shfl_xor(p, 32);
+    return p;
+}
+
+// logit (before key/query scales) of page entry `lane` for one query row
+template <class Pg>
+__device__ __forceinline__ float page_logit(const QBf16 &Q, const float (&wv)[16], const Pg &P, int g) {
+    float tot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 bk = __builtin_bit_cast(bf16x8, b_operand(P, j, kk));
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, Q.a[m][kk]), bk, acc[m], 0, 0, 0);
+        }
+        tot[j] = head_sum(acc, wv);
+    }
+    return g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+}
+
+__device__ __forceinline__ float page_logit(const QFp8 &Q, const float (&wv)[16], const PgFp8 &P, int g) {
+    float tot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        i32x8 bk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bk[e] = (int)P.b[j][0][e];
+            bk[4 + e] = (int)P.b[j][1][e];
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                Q.a[m], bk, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        tot[j] = head_sum(acc, wv);
+    }
+    return g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+}
+
+template <int KF> struct PageOf;
+template <> struct PageOf<KEY_BF16> { typedef PgBf16 T; static constexpr int row = kRowBf16; };
+template <> struct PageOf<KEY_FP8> { typedef PgFp8 T; static constexpr int row = kRowFp8; };
+template <int QF> struct QOf;
+template <> struct QOf<Q_BF16> { typedef QBf16 T; static constexpr int elem = 2; };
+template <> struct QOf<Q_FP8> { typedef QFp8 T; static constexpr int elem = 1; };
+
+template <int KF>
+__device__ __forceinline__ void load_qrow(QBf16 &Q, const QArgs &q, int t, int r, int g) {
+    load_q<KF>(Q, (const uint8_t *)q.q + (int64_t)t * kHeads * kDim * 2, r, g);
+}
+template <int KF>
+__device__ __forceinline__ void load_qrow(QFp8 &Q, const QArgs &q, int t, int r, int g) {
+    load_q(Q, (const uint8_t *)q.q + (int64_t)t * kHeads * kDim, r, g);
+}
+
+// Resolve a page slot to a physical page id or a slot state.
+__device__ __forceinline__ int resolve_slot(const ScoreArgs &A, int b, int64_t nvis, int64_t nres,
+                                            int64_t j, int &lp_out) {
+    int64_t lp;
+    if (A.res_pages) {
+        if (j >= nres) { lp_out = -1; return kSlotEmpty; }
+        lp = A.res_pages[(int64_t)b * A.res_ld + j];
+    } else {
+        lp = j;
+    }
+    lp_out = (int)lp;
+    if (lp < 0 || lp >= A.kv.bt_ld) return lp * kPage >= nvis && lp >= 0 ? kSlotInvisible : kSlotUnmapped;
+    if (lp * kPage >= nvis) return kSlotInvisible;
+    int phys = A.kv.bt[(int64_t)b * A.kv.bt_ld + lp];
+    if (phys < 0 || phys >= A.kv.n_phys) return kSlotUnmapped;
+    return phys;
+}
+
+// ---------------------------------------------------------------- row scoring kernel
+// grid (ceil(n_slots / (4 ppw)), T), 4 waves; wave w of block x scores slots
+// [(4 x + w) ppw, +ppw) of row blockIdx.y, two pages in flight at a time.
+template <int KF, int QF>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs A) {
+    typedef typename PageOf<KF>::T Pg;
+    typedef typename QOf<QF>::T Qf;
+    const int t = blockIdx.y;
+    const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
+    if (slot0 >= A.n_slots) return;
+    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
+    const int braw = row_request(A.q, A.kv, t);
+    const int64_t nvis = n_visible(A.q, A.kv, t, braw);
+    const int b = braw < 0 ? 0 : braw;
+    const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
+    float *out = A.out + (int64_t)t * A.out_ld;
+    const uint8_t *pool = A.kv.pool[0];
+
+    int lp_l = -1, phys_l = kSlotEmpty;
+    if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
+
+    Qf Q;
+    float wv[16];
+    load_qrow<KF>(Q, A.q, t, r, g);
+    load_w(wv, A.q.w, A.q.w_bf16, t, g);
+    const float qscale = (QF == Q_FP8) ? A.q.q_scale[t] : 1.0f;
+
+    auto fetch = [&](Pg &P, int i) {
+        int phys = __builtin_amdgcn_readlane(phys_l, i);
+        if (phys >= 0) load_page(P, pool + (int64_t)phys * (kPage * PageOf<KF>::row), r, g, ln);
+    };
+    auto emit = [&](const Pg &P, int i) {
+        int phys = __builtin_amdgcn_readlane(phys_l, i);
+        if (phys == kSlotEmpty) return;
+        int lp = __builtin_amdgcn_readlane(lp_l, i);
+        int64_t s = (int64_t)lp * kPage + ln;
+        int64_t col = (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
+        float v;
+        if (phys >= 0) {
+            v = page_logit(Q, wv, P, g) * page_scale(P) * qscale;
+            if (s >= nvis) v = -INFINITY;
+        } else if (phys == kSlotInvisible) {
+            v = -INFINITY;
+        } else {
+            v = s < nvis ? __builtin_nanf("") : -INFINITY;
+        }
+        if (col < A.out_ld) out[col] = v;
+    };
+
+    Pg P0, P1;
+    fetch(P0, 0);
+    for (int i = 0; i < nslot; i += 2) {
+        if (i + 1 < nslot) fetch(P1, i + 1);
+        emit(P0, i);
+        if (i + 1 < nslot) {
+            if (i + 2 < nslot) fetch(P0, i + 2);
+            emit(P1, i + 1);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- fp32 path (VALU)
+// One thread per output column; fp32 products and sums.  For fp32 inputs only.
+__global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
+    __shared__ float qs[kHeads * kDim];
+    __shared__ float wsm[kHeads];
+    const int t = blockIdx.y;
+    const float *qrow = (const float *)A.q.q + (int64_t)t * kHeads * kDim;
+    for (int i = threadIdx.x; i < kHeads * kDim; i += blockDim.x) qs[i] = qrow[i];
+    for (int i = threadIdx.x; i < kHeads; i += blockDim.x)
+        wsm[i] = A.q.w_bf16 ? bf16f(((const uint16_t *)A.q.w)[(int64_t)t * kHeads + i])
+                            : ((const float *)A.q.w)[(int64_t)t * kHeads + i];
+    __syncthreads();
+    const int64_t col = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= A.n_slots * kPage || col >= A.out_ld) return;
+    const int braw = row_request(A.q, A.kv, t);
+    const int64_t nvis = n_visible(A.q, A.kv, t, braw);
+    const int b = braw < 0 ? 0 : braw;
+    const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
+    int lp;
+    int phys = resolve_slot(A, b, nvis, nres, col / kPage, lp);
+    if (phys == kSlotEmpty) return;
+    const int64_t s = (int64_t)lp * kPage + col % kPage;
+    float v;
+    if (phys >= 0 && s < nvis) {
+        const float *k = (const float *)A.kv.pool[0] + ((int64_t)phys * kPage + col % kPage) * kDim;
+        float kr[kDim];
+#pragma unroll
+        for (int d = 0; d < kDim; ++d) kr[d] = k[d];
+        v = 0.f;
+        for (int h = 0; h < kHeads; ++h) {
+            float x = 0.f;
+#pragma unroll
+            for (int d = 0; d < kDim; ++d) x = fmaf(qs[h * kDim + d], kr[d], x);
+            v = fmaf(wsm[h], fmaxf(x, 0.f), v);
+        }
+    } else if (phys == kSlotUnmapped && s < nvis) {
+        v = __builtin_nanf("");
+    } else {
+        v = -INFINITY;
+    }
+    A.out[(int64_t)t * A.out_ld + col] = v;
+}
+
+// ---------------------------------------------------------------- Level-1 mask
+// Union of n_layers encoders per entry (paper summary, section 3, R_t equation; README "Joint
+// checkpoint + ensemble": max or mean of the per-layer sigmoids).  Grid (ceil(n_pages /
+// (4 PPW)), B); each wave owns PPW consecutive pages of request blockIdx.y and walks the layers
+// one after another, keeping the running union of its PPW x 64 entries in registers.
+template <int KF, int PPW>
+__global__ __launch_bounds__(256) void mask_kernel(MaskArgs A) {
+    typedef typename PageOf<KF>::T Pg;
+    const int b = blockIdx.y;
+    const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int64_t page0 = ((int64_t)blockIdx.x * 4 + wave) * PPW;
+    if (page0 >= A.n_pages) return;
+    const int np = (int)min((int64_t)PPW, A.n_pages - page0);
+    const int64_t seq = A.kv.seq_lens[b];
+    const float inv_n = 1.0f / (float)A.n_layers;
+
+    int phys_l = kSlotInvisible;
+    if (ln < np) {
+        int64_t lp = page0 + ln;
+        if (lp * kPage >= seq) phys_l = kSlotInvisible;
+        else if (lp >= A.kv.bt_ld) phys_l = kSlotUnmapped;
+        else {
+            int p = A.kv.bt[(int64_t)b * A.kv.bt_ld + lp];
+            phys_l = (p < 0 || p >= A.kv.n_phys) ? kSlotUnmapped : p;
+        }
+    }
+
+    float u[PPW];
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) u[i] = A.mean_mode ? 0.f : -INFINITY;
+
+    for (int l = 0; l < A.n_layers; ++l) {
+        QBf16 Q;
+        float wv[16];
+        load_q<KF>(Q, (const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, r, g);
+        load_w(wv, A.q[l].w, A.q[l].w_bf16, b, g);
+        const uint8_t *pool = A.kv.pool[l];
+        Pg P0, P1;
+        auto fetch = [&](Pg &P, int i) {
+            int phys = __builtin_amdgcn_readlane(phys_l, i);
+            if (phys >= 0) load_page(P, pool + (int64_t)phys * (kPage * PageOf<KF>::row), r, g, ln);
+        };
+        auto take = [&](const Pg &P, int i) {
+            int phys = __builtin_amdgcn_readlane(phys_l, i);
+            float L;
+            if (phys >= 0) L = page_logit(Q, wv, P, g) * page_scale(P);
+            else if (phys == kSlotUnmapped) L = __builtin_nanf("");
+            else return;
+            u[i] = A.mean_mode ? u[i] + inv_n / (1.0f + expf(-L))
+                               : ((L != L || u[i] != u[i]) ? __builtin_nanf("") : fmaxf(u[i], L));
+        };
+        fetch(P0, 0);
+#pragma unroll
+        for (int i = 0; i < PPW; i += 2) {
+            if (i < np) {
+                if (i + 1 < np) fetch(P1, i + 1);
+                take(P0, i);
+                if (i + 1 < np) {
+                    if (i + 2 < np) fetch(P0, i + 2);
+                    take(P1, i + 1);
+                }
+            }
+        }
+    }
+
+    uint8_t *mrow = A.mask + (int64_t)b * A.mask_ld;
+#pragma unroll
+    for (int i = 0; i < PPW; ++i) {
+        if (i >= np) break;
+        int64_t s = (page0 + i) * kPage + ln;
+        if (s >= A.mask_ld) continue;
+        bool valid = s < seq;
+        bool m = valid && (u[i] >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
+        mrow[s] = m ? 1 : 0;
+        if (A.union_score) A.union_score[(int64_t)b * A.mask_ld + s] = valid ? u[i] : -INFINITY;
+    }
+}
+
+// fp32 keys: one thread per entry, fp32 VALU arithmetic.
+__global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
+    __shared__ float qs[kHeads * kDim];
+    __shared__ float wsm[kHeads];
+    const int b = blockIdx.y;
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t seq = A.kv.seq_lens[b];
+    const float inv_n = 1.0f / (float)A.n_layers;
+    float u = A.mean_mode ? 0.f : -INFINITY;
+    for (int l = 0; l < A.n_layers; ++l) {
+        __syncthreads();
+        const float *qrow = (const float *)A.q[l].q + (int64_t)b * kHeads * kDim;
+        for (int i = threadIdx.x; i < kHeads * kDim; i += blockDim.x) qs[i] = qrow[i];
+        for (int i = threadIdx.x; i < kHeads; i += blockDim.x)
+            wsm[i] = A.q[l].w_bf16 ? bf16f(((const uint16_t *)A.q[l].w)[(int64_t)b * kHeads + i])
+                                   : ((const float *)A.q[l].w)[(int64_t)b * kHeads + i];
+        __syncthreads();
+        if (s >= seq || s >= A.mask_ld) continue;
+        int64_t lp = s / kPage;
+        int phys = lp < A.kv.bt_ld ? A.kv.bt[(int64_t)b * A.kv.bt_ld + lp] : -1;
+        float L;
+        if (phys < 0 || phys >= A.kv.n_phys) {
+            L = __builtin_nanf("");
+        } else {
+            const float *k = (const float *)A.kv.pool[l] + ((int64_t)phys * kPage + s % kPage) * kDim;
+            float kr[kDim];
+#pragma unroll
+            for (int d = 0; d < kDim; ++d) kr[d] = k[d];
+            L = 0.f;
+            for (int h = 0; h < kHeads; ++h) {
+                float x = 0.f;
+#pragma unroll
+                for (int d = 0; d < kDim; ++d) x = fmaf(qs[h * kDim + d], kr[d], x);
+                L = fmaf(wsm[h], fmaxf(x, 0.f), L);
+            }
+        }
+        u = A.mean_mode ? u + inv_n / (1.0f + expf(-L))
+                        : ((L != L || u != u) ? __builtin_nanf("") : fmaxf(u, L));
+    }
+    if (s >= A.mask_ld) return;
+    bool valid = s < seq;
+    bool m = valid && (u >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
+    A.mask[(int64_t)b * A.mask_ld + s] = m ? 1 : 0;
+    if (A.union_score) A.union_score[(int64_t)b * A.mask_ld + s] = valid ? u : -INFINITY;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s) {
+    dim3 grid((unsigned)((a.n_slots + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)a.q.T);
+    if (key_fmt == KEY_BF16 && q_fmt == Q_BF16)
+        score_kernel<KEY_BF16, Q_BF16><<<grid, 256, 0, s>>>(a);
+    else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16)
+        score_kernel<KEY_FP8, Q_BF16><<<grid, 256, 0, s>>>(a);
+    else if (key_fmt == KEY_FP8 && q_fmt == Q_FP8)
+        score_kernel<KEY_FP8, Q_FP8><<<grid, 256, 0, s>>>(a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s) {
+    dim3 grid((unsigned)((a.n_slots * kPage + 255) / 256), (unsigned)a.q.T);
+    score_f32_kernel<<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s) {
+    constexpr int PPW = 8;
+    if (key_fmt == KEY_F32) {
+        dim3 grid((unsigned)((a.mask_ld + 255) / 256), (unsigned)B);
+        mask_f32_kernel<<<grid, 256, 0, s>>>(a);
+    } else {
+        dim3 grid((unsigned)((a.n_pages + 4 * PPW - 1) / (4 * PPW)), (unsigned)B);
+        if (key_fmt == KEY_BF16)
+            mask_kernel<KEY_BF16, PPW><<<grid, 256, 0, s>>>(a);
+        else
+            mask_kernel<KEY_FP8, PPW><<<grid, 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fm
