@@ -110,6 +110,8 @@ def run_decode(torch, api, W, steps, warmup, replicas=3):
     ld = wl.kv.block_table.shape[1] * 64
     logits = torch.empty((B, ld), dtype=torch.float32, device="cuda:0")
     idx = torch.empty((B, 512), dtype=torch.int32, device="cuda:0")
+    nb = api.fm_workspace_bytes(api.FM_OP_TOPK, B, ld)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
     q = dw.query()
     kvs = [dw.kv(r) for r in range(replicas)]
 
@@ -117,7 +119,7 @@ def run_decode(torch, api, W, steps, warmup, replicas=3):
         if tm: tm.mark(s, 0)
         api.fm_index_logits(q, kvs[s % replicas], logits, ld)
         if tm: tm.mark(s, 1)
-        api.fm_topk512(logits, ld, B, None, None, 0, None, 512, idx)
+        api.fm_topk512(logits, ld, B, None, None, 0, None, 512, idx, None, ws, nb)
         if tm: tm.mark(s, 2)
 
     wall, per = timed(torch, ["score", "topk"], step, steps, warmup)
@@ -192,13 +194,15 @@ def run_prefill(torch, api, W, steps, warmup):
     ld = wl.kv.max_seq_len
     logits = torch.empty((T, ld), dtype=torch.float32, device="cuda:0")
     idx = torch.empty((T, 512), dtype=torch.int32, device="cuda:0")
+    nb = api.fm_workspace_bytes(api.FM_OP_TOPK, T, ld)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
     q, kv = dw.query(), dw.kv()
 
     def step(s, tm):
         if tm: tm.mark(s, 0)
         api.fm_index_logits(q, kv, logits, ld)
         if tm: tm.mark(s, 1)
-        api.fm_topk512(logits, ld, T, None, None, 0, None, 512, idx)
+        api.fm_topk512(logits, ld, T, None, None, 0, None, 512, idx, None, ws, nb)
         if tm: tm.mark(s, 2)
 
     wall, per = timed(torch, ["score", "topk"], step, steps, warmup)

@@ -43,12 +43,15 @@ def index_logits(dw, layer=0, ld=None, replica=0):
     return out
 
 
-def topk(logits, k=512, n_valid=None, mask=None, row_req=None):
+def topk(logits, k=512, n_valid=None, mask=None, row_req=None, workspace=True):
+    """fm_topk512; with workspace=True the two-stage path gets the bytes it asks for."""
     T, ld = logits.shape
     idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     val = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    nb = api.fm_workspace_bytes(api.FM_OP_TOPK, T, ld) if workspace else 0
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=logits.device) if nb else None
     api.fm_topk512(logits, ld, T, n_valid, mask, 0 if mask is None else mask.shape[1], row_req,
-                   k, idx, val)
+                   k, idx, val, ws, nb)
     return idx, val
 
 

@@ -43,9 +43,13 @@ def test_version_and_status_strings():
 
 
 def test_workspace_bytes():
-    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 30, 384 * 64) == 30 * 384 * 64 * 4
-    assert api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 10 ** 6) == 0
+    topk = api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 384 * 64)
+    assert topk >= 30 * 6 * 512 * 8          # six 4096-entry chunks of <= 512 survivors
+    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 30, 384 * 64) >= \
+        30 * 384 * 64 * 4 + topk
+    assert api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 10 ** 6) > topk
     assert api.fm_workspace_bytes(api.FM_OP_INDEX_LOGITS, 4, 100) == 0
+    assert api.fm_workspace_bytes(api.FM_OP_RESIDENT_MASK, 4, 100) == 0
     assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 0, 100) == 0
 
 
@@ -171,7 +175,7 @@ def test_score_resident_validation():
                                 FAKE, None, kw.get("ws", FAKE), kw.get("ws_bytes", need - 4))[0]
     assert st() == api.FM_ERR_WORKSPACE
     assert st(ws=None, ws_bytes=need) == api.FM_ERR_WORKSPACE
-    assert st(ws=FAKE + 4, ws_bytes=need) == api.FM_ERR_WORKSPACE
+    assert st(ws=FAKE + 16, ws_bytes=need) == api.FM_ERR_WORKSPACE   # needs 256-byte alignment
     assert st(rp=None, ws_bytes=need) == api.FM_ERR_INVALID_ARG
     assert st(res_ld=0, ws_bytes=need) == api.FM_ERR_INVALID_ARG
     assert st(k=4096, ws_bytes=need) == api.FM_ERR_UNSUPPORTED

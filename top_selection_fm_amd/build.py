@@ -26,21 +26,22 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = SO, defines=()) -> str:
+    """Compile every csrc/*.hip into `out`; `defines` are extra -D options (tuning knobs)."""
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
-    tmp = SO + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *srcs, "-o", tmp]
+           *[f"-D{d}" for d in defines], *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, SO)
-    return SO
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

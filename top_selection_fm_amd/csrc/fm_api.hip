@@ -126,9 +126,12 @@ fm::KvArgs make_kv(const fm_kv_desc *kv) {
     return a;
 }
 
+#ifndef FM_TARGET_WAVES
+#define FM_TARGET_WAVES 4096
+#endif
 // page slots per wave: enough waves to fill 256 CUs several times, at most 16 slots each
 int pages_per_wave(int64_t total_slots) {
-    int64_t p = total_slots / 4096;
+    int64_t p = total_slots / FM_TARGET_WAVES;
     if (p < 2) p = 2;
     if (p > 16) p = 16;
     return (int)p;
@@ -172,8 +175,6 @@ fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *l
 fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_valid,
                      const uint8_t *mask, int64_t mask_ld, const int32_t *row_req, int k,
                      int32_t *out_idx, float *out_val, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     REQUIRE(T >= 0, FM_ERR_INVALID_ARG, "T = %d", T);
     REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
     REQUIRE(ld >= 1 && ld <= (int64_t)INT32_MAX, FM_ERR_INVALID_ARG, "ld = %lld", (long long)ld);
@@ -197,7 +198,12 @@ fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_va
     a.k = k;
     a.out_idx = out_idx;
     a.out_val = out_val;
-    CHECK(launched(fm::launch_topk(a, (hipStream_t)stream), "topk"));
+    // with enough workspace and k <= 512, the two-stage (chunk, then merge) path runs
+    fm::TopkWs W;
+    const bool two = ws && aligned(ws, 16) && k <= fm::kTopkWsK &&
+                     ws_bytes >= fm::topk_ws_bytes(T, ld);
+    if (two) W = fm::topk_ws_carve(ws, T, ld);
+    CHECK(launched(fm::launch_topk(a, two ? &W : nullptr, (hipStream_t)stream), "topk"));
     return ok();
 }
 
@@ -214,11 +220,12 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     REQUIRE(resident_pages && n_resident && out_idx, FM_ERR_INVALID_ARG,
             "resident_pages / n_resident / out_idx NULL");
     const size_t need = fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T, res_ld * FM_PAGE_SIZE);
-    REQUIRE(ws && ws_bytes >= need && aligned(ws, 16), FM_ERR_WORKSPACE,
-            "workspace %zu bytes at %p, need %zu (16-byte aligned)", ws_bytes, ws, need);
+    REQUIRE(ws && ws_bytes >= need && aligned(ws, 256), FM_ERR_WORKSPACE,
+            "workspace %zu bytes at %p, need %zu (256-byte aligned)", ws_bytes, ws, need);
     hipStream_t st = (hipStream_t)stream;
     float *wl = (float *)ws;
     const int64_t ld = res_ld * FM_PAGE_SIZE;
+    const size_t logit_bytes = fm::align_up((size_t)q->T * (size_t)ld * sizeof(float), 256);
     CHECK(run_score(q, kv, resident_pages, n_resident, res_ld, wl, ld, res_ld, st));
     fm::TopkArgs a;
     a.logits = wl;
@@ -236,7 +243,8 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     a.k = k;
     a.out_idx = out_idx;
     a.out_val = out_val;
-    CHECK(launched(fm::launch_topk(a, st), "topk"));
+    fm::TopkWs W = fm::topk_ws_carve((uint8_t *)ws + logit_bytes, q->T, ld);
+    CHECK(launched(fm::launch_topk(a, k <= fm::kTopkWsK ? &W : nullptr, st), "topk"));
     return ok();
 }
 
@@ -298,8 +306,12 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
 }
 
 size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates) {
-    if (op != FM_OP_SCORE_RESIDENT || T <= 0 || max_candidates <= 0) return 0;
-    return (size_t)T * (size_t)max_candidates * sizeof(float);
+    if (T <= 0 || max_candidates <= 0) return 0;
+    if (op == FM_OP_TOPK) return fm::topk_ws_bytes(T, max_candidates);
+    if (op == FM_OP_SCORE_RESIDENT)
+        return fm::align_up((size_t)T * (size_t)max_candidates * sizeof(float), 256) +
+               fm::topk_ws_bytes(T, max_candidates);
+    return 0;
 }
 
 const char *fm_status_string(fm_status s) {

@@ -98,10 +98,24 @@ struct TopkArgs {
     float *out_val;            // nullable
 };
 
+// Two-stage top-k workspace: per (row, 4096-entry chunk) up to kTopkWsK survivors.
+constexpr int kTopkChunk = 4096;
+constexpr int kTopkWsK = 512;
+struct TopkWs {
+    float *val;      // [T, n_chunks, kTopkWsK]
+    int32_t *idx;    // [T, n_chunks, kTopkWsK]
+    int32_t *cnt;    // [T, n_chunks]
+    int n_chunks;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+size_t topk_ws_bytes(int T, int64_t n);          // bytes for rows of up to n entries
+TopkWs topk_ws_carve(void *ws, int T, int64_t n);
+
 hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, int B, hipStream_t s);
-hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s);
 
 }  // namespace fm

@@ -19,9 +19,28 @@
 //
 // The head sum: each lane weights and sums its 16 accumulator values (4 head tiles x 4 rows),
 // then two cross-lane adds (lane xor 16, xor 32) complete the 64-head sum for its column.
+//
+// Streaming: keys are read once, straight into registers in the layout above.  A decode call
+// is HBM-bound, so what matters is the number of bytes in flight per CU: every wave keeps
+// NBUF - 1 pages loading while it computes one, and the query fragments (the MFMA A operands)
+// can live in LDS, shared by the four waves of a workgroup (they score the same row), which
+// frees the registers for deeper prefetch and two waves per SIMD.
 #include <math.h>
 
 #include "fm_internal.h"
+
+#ifndef FM_NBUF_BF16
+#define FM_NBUF_BF16 3
+#endif
+#ifndef FM_NBUF_FP8
+#define FM_NBUF_FP8 4
+#endif
+#ifndef FM_QLDS
+#define FM_QLDS 1
+#endif
+#ifndef FM_WAVES_PER_EU
+#define FM_WAVES_PER_EU 2
+#endif
 
 namespace fm {
 namespace {
@@ -60,23 +79,45 @@ __device__ __forceinline__ int dim_base(int g, int kk) {
     return KF == KEY_BF16 ? (kk * 4 + g) * 8 : g * 32 + kk * 8;
 }
 
-// ---------------------------------------------------------------- query operands
-struct QBf16 { u32x4 a[4][4]; };   // [head tile m][k-step kk]: 8 bf16
-struct QFp8 { i32x8 a[4]; };       // [head tile m]: 32 E4M3 codes
-
+// ---------------------------------------------------------------- query operands (A)
+// bf16 q: fragment (m, kk) = 8 bf16 of head 16 m + r at dims dim_base(g, kk)
+// fp8  q: fragment m      = 32 E4M3 codes of head 16 m + r at dims 32 g .. 32 g + 31
 template <int KF>
-__device__ __forceinline__ void load_q(QBf16 &Q, const uint8_t *qrow, int r, int g) {
+__device__ __forceinline__ u32x4 q_frag_bf16(const uint8_t *qrow, int m, int kk, int r, int g) {
     const uint16_t *q = (const uint16_t *)qrow;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            Q.a[m][kk] = *(const u32x4 *)(q + (16 * m + r) * kDim + dim_base<KF>(g, kk));
+    return *(const u32x4 *)(q + (16 * m + r) * kDim + dim_base<KF>(g, kk));
 }
 
-__device__ __forceinline__ void load_q(QFp8 &Q, const uint8_t *qrow, int r, int g) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) Q.a[m] = *(const i32x8 *)(qrow + (16 * m + r) * kDim + g * 32);
+__device__ __forceinline__ i32x8 q_frag_fp8(const uint8_t *qrow, int m, int r, int g) {
+    return *(const i32x8 *)(qrow + (16 * m + r) * kDim + g * 32);
+}
+
+struct QRegBf16 {
+    u32x4 a[4][4];
+    __device__ __forceinline__ u32x4 get(int m, int kk, int) const { return a[m][kk]; }
+};
+struct QLdsBf16 {           // 16 fragments x 64 lanes x 16 B, lane-contiguous (conflict free)
+    const u32x4 *s;
+    int ln;
+    __device__ __forceinline__ u32x4 get(int m, int kk, int z) const { return s[(m * 4 + kk) * 64 + ln + z]; }
+};
+struct QRegFp8 {
+    i32x8 a[4];
+    __device__ __forceinline__ i32x8 get(int m, int) const { return a[m]; }
+};
+struct QLdsFp8 {            // 4 fragments x 64 lanes x 32 B
+    const i32x8 *s;
+    int ln;
+    __device__ __forceinline__ i32x8 get(int m, int z) const { return s[m * 64 + ln + z]; }
+};
+
+// A zero the compiler cannot see through.  Adding it to an LDS index once per entry tile makes
+// the query fragments be re-read for every tile instead of being kept live across a page, which
+// leaves the registers to the key pages in flight.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    return z;
 }
 
 // w[t, 16 m + 4 g + i] for the accumulator rows this lane holds
@@ -100,20 +141,29 @@ __device__ __forceinline__ u32x4 load16(const uint8_t *p) {  // 4-byte aligned
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// bf16 page: a buffer descriptor spanning exactly the page (so no lane can read past it), one
+// VGPR offset per lane (row r, 16-byte chunk g), entry tile j in the scalar offset, k-step kk in
+// the immediate offset.
 __device__ __forceinline__ void load_page(PgBf16 &P, const uint8_t *page, int r, int g, int) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, kPage * kRowBf16, 0x00020000);
+    const uint32_t off = (uint32_t)(r * kRowBf16 + g * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            P.b[j][kk] = *(const u32x4 *)(page + (16 * j + r) * kRowBf16 + (kk * 4 + g) * 16);
+            P.b[j][kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + kk * 64, j * 16 * kRowBf16, 0);
 }
 
+// fp8 page: 132-byte rows are only 4-byte aligned, so plain global loads (which accept that)
+// from the wave-uniform page base plus a 32-bit lane offset.
 __device__ __forceinline__ void load_page(PgFp8 &P, const uint8_t *page, int r, int g, int ln) {
+    const uint32_t off = (uint32_t)(r * kRowFp8 + g * 32);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) P.b[j][h] = load16(page + (16 * j + r) * kRowFp8 + g * 32 + h * 16);
-    P.scale = *(const float *)(page + ln * kRowFp8 + kDim);
+        for (int h = 0; h < 2; ++h) P.b[j][h] = load16(page + (off + (uint32_t)(j * 16 * kRowFp8 + h * 16)));
+    P.scale = *(const float *)(page + (uint32_t)(ln * kRowFp8 + kDim));
 }
 
 __device__ __forceinline__ u32x4 b_operand(const PgBf16 &P, int j, int kk) { return P.b[j][kk]; }
@@ -133,24 +183,31 @@ __device__ __forceinline__ u32x4 b_operand(const PgFp8 &P, int j, int kk) {
 __device__ __forceinline__ float page_scale(const PgBf16 &) { return 1.0f; }
 __device__ __forceinline__ float page_scale(const PgFp8 &P) { return P.scale; }
 
-// weighted ReLU head sum of one 16-entry tile; every lane of column r returns the total
+// weighted ReLU head sum of one 16-entry tile; every lane of column r returns the total.
+// The four lane groups (rows of 16 lanes) are combined with the gfx950 row swaps: after
+// permlane16_swap each row holds its pair's two partials, after permlane32_swap the two pair
+// sums; both operands are the same register, and every lane adds in the same order.
 __device__ __forceinline__ float head_sum(const f32x4 (&acc)[4], const float (&wv)[16]) {
     float p = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) p = fmaf(wv[m * 4 + i], fmaxf(acc[m][i], 0.f), p);
-    p += __shfl_xor(p, 16);
-    p += __shfl_xor(p, 32);
-    return p;
+    const uint32_t u = __float_as_uint(p);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    p = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const uint32_t v = __float_as_uint(p);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
-// logit (before key/query scales) of page entry `lane` for one query row
-template <class Pg>
-__device__ __forceinline__ float page_logit(const QBf16 &Q, const float (&wv)[16], const Pg &P, int g) {
+// logit (before key/query scales) of page entry `lane` for one bf16 query row
+template <class QS, class Pg>
+__device__ __forceinline__ float page_logit_bf16q(const QS &Q, const float (&wv)[16], const Pg &P, int g) {
     float tot[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        const int z = opaque_zero();
         f32x4 acc[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -160,17 +217,20 @@ __device__ __forceinline__ float page_logit(const QBf16 &Q, const float (&wv)[16
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, Q.a[m][kk]), bk, acc[m], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, Q.get(m, kk, z)), bk, acc[m], 0, 0, 0);
         }
         tot[j] = head_sum(acc, wv);
     }
     return g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
 }
 
-__device__ __forceinline__ float page_logit(const QFp8 &Q, const float (&wv)[16], const PgFp8 &P, int g) {
+// same for an fp8 query row against fp8 keys (one 16x16x128 MFMA per head tile)
+template <class QS>
+__device__ __forceinline__ float page_logit_fp8q(const QS &Q, const float (&wv)[16], const PgFp8 &P, int g) {
     float tot[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+        const int z = opaque_zero();
         i32x8 bk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -181,7 +241,7 @@ __device__ __forceinline__ float page_logit(const QFp8 &Q, const float (&wv)[16]
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                Q.a[m], bk, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                Q.get(m, z), bk, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
         tot[j] = head_sum(acc, wv);
     }
     return g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
@@ -190,18 +250,68 @@ __device__ __forceinline__ float page_logit(const QFp8 &Q, const float (&wv)[16]
 template <int KF> struct PageOf;
 template <> struct PageOf<KEY_BF16> { typedef PgBf16 T; static constexpr int row = kRowBf16; };
 template <> struct PageOf<KEY_FP8> { typedef PgFp8 T; static constexpr int row = kRowFp8; };
-template <int QF> struct QOf;
-template <> struct QOf<Q_BF16> { typedef QBf16 T; static constexpr int elem = 2; };
-template <> struct QOf<Q_FP8> { typedef QFp8 T; static constexpr int elem = 1; };
 
-template <int KF>
-__device__ __forceinline__ void load_qrow(QBf16 &Q, const QArgs &q, int t, int r, int g) {
-    load_q<KF>(Q, (const uint8_t *)q.q + (int64_t)t * kHeads * kDim * 2, r, g);
-}
-template <int KF>
-__device__ __forceinline__ void load_qrow(QFp8 &Q, const QArgs &q, int t, int r, int g) {
-    load_q(Q, (const uint8_t *)q.q + (int64_t)t * kHeads * kDim, r, g);
-}
+// Query operand source of one row: registers, or the workgroup's LDS copy.
+template <int KF, int QF, bool QLDS> struct QSource;
+
+template <int KF> struct QSource<KF, Q_BF16, false> {
+    QRegBf16 q;
+    __device__ void init(const uint8_t *qrow, void *, int r, int g, int) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) q.a[m][kk] = q_frag_bf16<KF>(qrow, m, kk, r, g);
+    }
+    template <class Pg>
+    __device__ float logit(const float (&wv)[16], const Pg &P, int g) const {
+        return page_logit_bf16q(q, wv, P, g);
+    }
+};
+
+template <int KF> struct QSource<KF, Q_BF16, true> {
+    QLdsBf16 q;
+    // every wave of the block writes 4 of the 16 fragments; the caller then syncs the block
+    __device__ void init(const uint8_t *qrow, void *lds, int r, int g, int ln) {
+        u32x4 *s = (u32x4 *)lds;
+        const int w = threadIdx.x >> 6;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int fi = w * 4 + f, m = fi >> 2, kk = fi & 3;
+            s[fi * 64 + ln] = q_frag_bf16<KF>(qrow, m, kk, r, g);
+        }
+        q.s = s;
+        q.ln = ln;
+    }
+    template <class Pg>
+    __device__ float logit(const float (&wv)[16], const Pg &P, int g) const {
+        return page_logit_bf16q(q, wv, P, g);
+    }
+};
+
+template <int KF> struct QSource<KF, Q_FP8, false> {
+    QRegFp8 q;
+    __device__ void init(const uint8_t *qrow, void *, int r, int g, int) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) q.a[m] = q_frag_fp8(qrow, m, r, g);
+    }
+    __device__ float logit(const float (&wv)[16], const PgFp8 &P, int g) const {
+        return page_logit_fp8q(q, wv, P, g);
+    }
+};
+
+template <int KF> struct QSource<KF, Q_FP8, true> {
+    QLdsFp8 q;
+    __device__ void init(const uint8_t *qrow, void *lds, int r, int g, int ln) {
+        i32x8 *s = (i32x8 *)lds;
+        const int m = threadIdx.x >> 6;          // wave m writes fragment m
+        s[m * 64 + ln] = q_frag_fp8(qrow, m, r, g);
+        q.s = s;
+        q.ln = ln;
+    }
+    __device__ float logit(const float (&wv)[16], const PgFp8 &P, int g) const {
+        return page_logit_fp8q(q, wv, P, g);
+    }
+};
 
 // Resolve a page slot to a physical page id or a slot state.
 __device__ __forceinline__ int resolve_slot(const ScoreArgs &A, int b, int64_t nvis, int64_t nres,
@@ -222,31 +332,35 @@ __device__ __forceinline__ int resolve_slot(const ScoreArgs &A, int b, int64_t n
 }
 
 // ---------------------------------------------------------------- row scoring kernel
-// grid (ceil(n_slots / (4 ppw)), T), 4 waves; wave w of block x scores slots
-// [(4 x + w) ppw, +ppw) of row blockIdx.y, two pages in flight at a time.
-template <int KF, int QF>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs A) {
+// grid (ceil(n_slots / (4 ppw)), T), 4 waves per workgroup, all on row blockIdx.y; wave w of
+// workgroup x scores slots [(4 x + w) ppw, +ppw), with NBUF - 1 pages loading ahead.
+template <int KF, int QF, int NBUF, bool QLDS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
+void score_kernel(ScoreArgs A) {
     typedef typename PageOf<KF>::T Pg;
-    typedef typename QOf<QF>::T Qf;
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[QLDS ? (QF == Q_FP8 ? 4 * 64 * 32 : 16 * 64 * 16) : 16];
     const int t = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int wave = threadIdx.x >> 6;
     const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
-    if (slot0 >= A.n_slots) return;
-    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
     const int braw = row_request(A.q, A.kv, t);
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
     float *out = A.out + (int64_t)t * A.out_ld;
     const uint8_t *pool = A.kv.pool[0];
+    const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * (QF == Q_FP8 ? 1 : 2);
+
+    QSource<KF, QF, QLDS> Q;
+    Q.init(qrow, q_lds, r, g, ln);
+    if (QLDS) __syncthreads();
+    if (slot0 >= A.n_slots) return;
+    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
 
     int lp_l = -1, phys_l = kSlotEmpty;
     if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
 
-    Qf Q;
     float wv[16];
-    load_qrow<KF>(Q, A.q, t, r, g);
     load_w(wv, A.q.w, A.q.w_bf16, t, g);
     const float qscale = (QF == Q_FP8) ? A.q.q_scale[t] : 1.0f;
 
@@ -262,7 +376,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs A) {
         int64_t col = (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
         float v;
         if (phys >= 0) {
-            v = page_logit(Q, wv, P, g) * page_scale(P) * qscale;
+            v = Q.logit(wv, P, g) * page_scale(P) * qscale;
             if (s >= nvis) v = -INFINITY;
         } else if (phys == kSlotInvisible) {
             v = -INFINITY;
@@ -272,14 +386,18 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs A) {
         if (col < A.out_ld) out[col] = v;
     };
 
-    Pg P0, P1;
-    fetch(P0, 0);
-    for (int i = 0; i < nslot; i += 2) {
-        if (i + 1 < nslot) fetch(P1, i + 1);
-        emit(P0, i);
-        if (i + 1 < nslot) {
-            if (i + 2 < nslot) fetch(P0, i + 2);
-            emit(P1, i + 1);
+    Pg P[NBUF];
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u)
+        if (u < nslot) fetch(P[u], u);
+    for (int i0 = 0; i0 < nslot; i0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            const int i = i0 + u;
+            if (i < nslot) {
+                if (i + NBUF - 1 < nslot) fetch(P[(u + NBUF - 1) % NBUF], i + NBUF - 1);
+                emit(P[u], i);
+            }
         }
     }
 }
@@ -331,14 +449,24 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
 // Union of n_layers encoders per entry (paper summary, section 3, R_t equation; README "Joint
 // checkpoint + ensemble": max or mean of the per-layer sigmoids).  Grid (ceil(n_pages /
 // (4 PPW)), B); each wave owns PPW consecutive pages of request blockIdx.y and walks the layers
-// one after another, keeping the running union of its PPW x 64 entries in registers.
-template <int KF, int PPW>
-__global__ __launch_bounds__(256) void mask_kernel(MaskArgs A) {
+// one after another, keeping the running union of its PPW x 64 entries in registers.  The
+// layers' query fragments sit in LDS, shared by the workgroup (same request).
+template <int KF, int PPW, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
+void mask_kernel(MaskArgs A) {
     typedef typename PageOf<KF>::T Pg;
+    __shared__ __attribute__((aligned(16))) uint8_t q_lds[FM_MAX_LAYERS][16 * 64 * 16];
     const int b = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int wave = threadIdx.x >> 6;
     const int64_t page0 = ((int64_t)blockIdx.x * 4 + wave) * PPW;
+
+    QSource<KF, Q_BF16, true> Qs[FM_MAX_LAYERS];
+#pragma unroll
+    for (int l = 0; l < FM_MAX_LAYERS; ++l)
+        if (l < A.n_layers)
+            Qs[l].init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, q_lds[l], r, g, ln);
+    __syncthreads();
     if (page0 >= A.n_pages) return;
     const int np = (int)min((int64_t)PPW, A.n_pages - page0);
     const int64_t seq = A.kv.seq_lens[b];
@@ -360,35 +488,32 @@ __global__ __launch_bounds__(256) void mask_kernel(MaskArgs A) {
     for (int i = 0; i < PPW; ++i) u[i] = A.mean_mode ? 0.f : -INFINITY;
 
     for (int l = 0; l < A.n_layers; ++l) {
-        QBf16 Q;
         float wv[16];
-        load_q<KF>(Q, (const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, r, g);
         load_w(wv, A.q[l].w, A.q[l].w_bf16, b, g);
         const uint8_t *pool = A.kv.pool[l];
-        Pg P0, P1;
-        auto fetch = [&](Pg &P, int i) {
+        const QSource<KF, Q_BF16, true> &Q = Qs[l];
+        Pg P[NBUF];
+        auto fetch = [&](Pg &Pp, int i) {
             int phys = __builtin_amdgcn_readlane(phys_l, i);
-            if (phys >= 0) load_page(P, pool + (int64_t)phys * (kPage * PageOf<KF>::row), r, g, ln);
+            if (phys >= 0) load_page(Pp, pool + (int64_t)phys * (kPage * PageOf<KF>::row), r, g, ln);
         };
-        auto take = [&](const Pg &P, int i) {
+        auto take = [&](const Pg &Pp, int i) {
             int phys = __builtin_amdgcn_readlane(phys_l, i);
             float L;
-            if (phys >= 0) L = page_logit(Q, wv, P, g) * page_scale(P);
+            if (phys >= 0) L = Q.logit(wv, Pp, g) * page_scale(Pp);
             else if (phys == kSlotUnmapped) L = __builtin_nanf("");
             else return;
             u[i] = A.mean_mode ? u[i] + inv_n / (1.0f + expf(-L))
                                : ((L != L || u[i] != u[i]) ? __builtin_nanf("") : fmaxf(u[i], L));
         };
-        fetch(P0, 0);
 #pragma unroll
-        for (int i = 0; i < PPW; i += 2) {
+        for (int v = 0; v < NBUF - 1; ++v)
+            if (v < np) fetch(P[v], v);
+#pragma unroll
+        for (int i = 0; i < PPW; ++i) {
             if (i < np) {
-                if (i + 1 < np) fetch(P1, i + 1);
-                take(P0, i);
-                if (i + 1 < np) {
-                    if (i + 2 < np) fetch(P0, i + 2);
-                    take(P1, i + 1);
-                }
+                if (i + NBUF - 1 < np) fetch(P[(i + NBUF - 1) % NBUF], i + NBUF - 1);
+                take(P[i % NBUF], i);
             }
         }
     }
@@ -457,12 +582,13 @@ __global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s) {
     dim3 grid((unsigned)((a.n_slots + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)a.q.T);
+    constexpr bool QL = FM_QLDS != 0;
     if (key_fmt == KEY_BF16 && q_fmt == Q_BF16)
-        score_kernel<KEY_BF16, Q_BF16><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_BF16, Q_BF16, FM_NBUF_BF16, QL><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16)
-        score_kernel<KEY_FP8, Q_BF16><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_FP8, Q_BF16, FM_NBUF_FP8, QL><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_FP8)
-        score_kernel<KEY_FP8, Q_FP8><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_FP8, Q_FP8, FM_NBUF_FP8, QL><<<grid, 256, 0, s>>>(a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -482,9 +608,9 @@ hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s) {
     } else {
         dim3 grid((unsigned)((a.n_pages + 4 * PPW - 1) / (4 * PPW)), (unsigned)B);
         if (key_fmt == KEY_BF16)
-            mask_kernel<KEY_BF16, PPW><<<grid, 256, 0, s>>>(a);
+            mask_kernel<KEY_BF16, PPW, 2><<<grid, 256, 0, s>>>(a);
         else
-            mask_kernel<KEY_FP8, PPW><<<grid, 256, 0, s>>>(a);
+            mask_kernel<KEY_FP8, PPW, FM_NBUF_FP8><<<grid, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }
