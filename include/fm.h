@@ -157,10 +157,10 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
  * Selects the k candidates of largest logit, ties broken by lower s (-0.0 == +0.0); with
  * fewer than k candidates, all of them.  out_idx[t * k + i] lists the selected s in
  * ascending order, padded with -1; out_val (nullable) holds their logits, padded with -inf.
- * 1 <= k <= FM_MAX_K.  Workspace is optional: with ws 16-byte aligned, k <= 512 and
- * ws_bytes >= fm_workspace_bytes(FM_OP_TOPK, T, ld), a two-stage path runs (chunk-local
- * selection across many workgroups, then a per-row merge); otherwise (ws NULL or smaller)
- * one workgroup per row does the whole selection.  Both give the same result.
+ * 1 <= k <= FM_MAX_K.  The workspace is optional.  With ws 256-byte aligned and ws_bytes >=
+ * fm_workspace_bytes(FM_OP_TOPK, T, ld) (0 for ld <= 4096), rows longer than 4,096 entries
+ * are first filtered by one workgroup per 8,192-entry chunk, then selected by one workgroup
+ * per row; otherwise one workgroup per row does everything.  Both give the same result.
  */
 fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_valid,
                      const uint8_t *mask, int64_t mask_ld, const int32_t *row_req, int k,
@@ -174,7 +174,7 @@ fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_va
  * those candidates (ties by lower logical index).  Indices are logical entry positions
  * 64 * page + slot, ascending, -1 padded.  Pages outside the list are never dereferenced.
  * Needs ws 256-byte aligned with ws_bytes >= fm_workspace_bytes(FM_OP_SCORE_RESIDENT, T,
- * res_ld * 64) (the logits of the listed pages plus the top-k workspace).
+ * res_ld * 64) (the logits of the listed pages, then the top-k workspace).
  */
 fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
                             const int32_t *resident_pages, const int32_t *n_resident,

@@ -49,7 +49,7 @@ def constructed_rows(rng, T, n):
 
 @pytest.mark.parametrize("workspace", [True, False])
 @pytest.mark.parametrize("k", [1, 7, 512, 1000, 1024])
-@pytest.mark.parametrize("n", [1, 600, 5000, 9000])
+@pytest.mark.parametrize("n", [1, 600, 4096, 4097, 9000, 70000])
 def test_topk_constructed_rows_bit_exact(k, n, workspace):
     rng = np.random.default_rng(k * 10007 + n)
     L = constructed_rows(rng, 12, n)
@@ -89,6 +89,26 @@ def test_topk_long_rows_262144_candidates(workspace):
     ig, _ = gpu_topk(L, 512, mask=mask, workspace=workspace)
     ri, _ = ref_topk(L, 512, mask=mask)
     assert np.array_equal(ig, ri)
+
+
+@pytest.mark.parametrize("workspace", [True, False])
+def test_topk_sampled_cut_and_its_fallbacks(workspace):
+    """Long rows go through a sampled cut; rows where the cut cannot hold fall back to the exact
+    selection over the whole row.  Every case must match the oracle bit for bit."""
+    n = 65536
+    stride = n // 4096                              # the sample reads every 16th entry here
+    rng = np.random.default_rng(11)
+    L = np.zeros((4, n), np.float32)
+    L[0] = rng.standard_normal(n)                   # ordinary row: the cut holds
+    L[1] = 0.25                                     # constant row: everything passes, overflow
+    L[2] = 0.5                                      # sampled entries look hotter than the row:
+    L[2, np.arange(100) * stride] = 1.0             # only 100 pass the cut (< k), fallback
+    L[3] = rng.standard_normal(n)                   # the top values sit between sample points
+    L[3, np.arange(700) * stride + 1] = 5.0 + rng.random(700)
+    ig, vg = gpu_topk(L, 512, workspace=workspace)
+    ri, rv = ref_topk(L, 512)
+    assert np.array_equal(ig, ri)
+    assert np.array_equal(vg[ri >= 0], rv[ri >= 0].astype(np.float32))
 
 
 def test_scoring_is_deterministic_and_placement_invariant():

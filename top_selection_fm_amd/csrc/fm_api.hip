@@ -198,12 +198,12 @@ fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_va
     a.k = k;
     a.out_idx = out_idx;
     a.out_val = out_val;
-    // with enough workspace and k <= 512, the two-stage (chunk, then merge) path runs
+    // with the workspace it asks for, long rows are filtered by many workgroups first
+    const size_t need = fm::topk_ws_bytes(T, ld);
     fm::TopkWs W;
-    const bool two = ws && aligned(ws, 16) && k <= fm::kTopkWsK &&
-                     ws_bytes >= fm::topk_ws_bytes(T, ld);
-    if (two) W = fm::topk_ws_carve(ws, T, ld);
-    CHECK(launched(fm::launch_topk(a, two ? &W : nullptr, (hipStream_t)stream), "topk"));
+    const bool staged = need > 0 && ws && aligned(ws, 256) && ws_bytes >= need;
+    if (staged) W = fm::topk_ws_carve(ws, T, ld);
+    CHECK(launched(fm::launch_topk(a, staged ? &W : nullptr, (hipStream_t)stream), "topk"));
     return ok();
 }
 
@@ -225,7 +225,6 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     hipStream_t st = (hipStream_t)stream;
     float *wl = (float *)ws;
     const int64_t ld = res_ld * FM_PAGE_SIZE;
-    const size_t logit_bytes = fm::align_up((size_t)q->T * (size_t)ld * sizeof(float), 256);
     CHECK(run_score(q, kv, resident_pages, n_resident, res_ld, wl, ld, res_ld, st));
     fm::TopkArgs a;
     a.logits = wl;
@@ -243,8 +242,11 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     a.k = k;
     a.out_idx = out_idx;
     a.out_val = out_val;
-    fm::TopkWs W = fm::topk_ws_carve((uint8_t *)ws + logit_bytes, q->T, ld);
-    CHECK(launched(fm::launch_topk(a, k <= fm::kTopkWsK ? &W : nullptr, st), "topk"));
+    const size_t logit_bytes = fm::align_up((size_t)q->T * (size_t)ld * sizeof(float), 256);
+    fm::TopkWs W;
+    const bool staged = fm::topk_ws_bytes(q->T, ld) > 0;
+    if (staged) W = fm::topk_ws_carve((uint8_t *)ws + logit_bytes, q->T, ld);
+    CHECK(launched(fm::launch_topk(a, staged ? &W : nullptr, st), "topk"));
     return ok();
 }
 

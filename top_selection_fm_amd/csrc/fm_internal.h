@@ -98,18 +98,19 @@ struct TopkArgs {
     float *out_val;            // nullable
 };
 
-// Two-stage top-k workspace: per (row, 4096-entry chunk) up to kTopkWsK survivors.
-constexpr int kTopkChunk = 4096;
-constexpr int kTopkWsK = 512;
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Top-k workspace: stage-1 survivors of every (row, kTopkChunk-entry chunk), kTopkCap each.
+constexpr int kTopkChunk = 8192;
+constexpr int kTopkCap = 1024;
+constexpr int kTopkMaxChunks = 256;   // staged path for rows of up to 2M entries
 struct TopkWs {
-    float *val;      // [T, n_chunks, kTopkWsK]
-    int32_t *idx;    // [T, n_chunks, kTopkWsK]
-    int32_t *cnt;    // [T, n_chunks]
+    float *val;      // [T, n_chunks, kTopkCap]
+    int32_t *idx;    // [T, n_chunks, kTopkCap]
+    int32_t *cnt;    // [T, n_chunks]; > kTopkCap: overflow or no cut
     int n_chunks;
 };
-
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-size_t topk_ws_bytes(int T, int64_t n);          // bytes for rows of up to n entries
+size_t topk_ws_bytes(int T, int64_t n);   // bytes for T rows of up to n entries (0: not used)
 TopkWs topk_ws_carve(void *ws, int T, int64_t n);
 
 hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s);

@@ -33,7 +33,10 @@
 #define FM_NBUF_BF16 3
 #endif
 #ifndef FM_NBUF_FP8
-#define FM_NBUF_FP8 4
+#define FM_NBUF_FP8 3
+#endif
+#ifndef FM_NBUF_MASK
+#define FM_NBUF_MASK 2
 #endif
 #ifndef FM_QLDS
 #define FM_QLDS 1
@@ -449,24 +452,16 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
 // Union of n_layers encoders per entry (paper summary, section 3, R_t equation; README "Joint
 // checkpoint + ensemble": max or mean of the per-layer sigmoids).  Grid (ceil(n_pages /
 // (4 PPW)), B); each wave owns PPW consecutive pages of request blockIdx.y and walks the layers
-// one after another, keeping the running union of its PPW x 64 entries in registers.  The
-// layers' query fragments sit in LDS, shared by the workgroup (same request).
+// one after another, keeping the running union of its PPW x 64 entries in registers, and
+// holds the current layer's query fragments in registers.
 template <int KF, int PPW, int NBUF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
 void mask_kernel(MaskArgs A) {
     typedef typename PageOf<KF>::T Pg;
-    __shared__ __attribute__((aligned(16))) uint8_t q_lds[FM_MAX_LAYERS][16 * 64 * 16];
     const int b = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int wave = threadIdx.x >> 6;
     const int64_t page0 = ((int64_t)blockIdx.x * 4 + wave) * PPW;
-
-    QSource<KF, Q_BF16, true> Qs[FM_MAX_LAYERS];
-#pragma unroll
-    for (int l = 0; l < FM_MAX_LAYERS; ++l)
-        if (l < A.n_layers)
-            Qs[l].init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, q_lds[l], r, g, ln);
-    __syncthreads();
     if (page0 >= A.n_pages) return;
     const int np = (int)min((int64_t)PPW, A.n_pages - page0);
     const int64_t seq = A.kv.seq_lens[b];
@@ -491,7 +486,8 @@ void mask_kernel(MaskArgs A) {
         float wv[16];
         load_w(wv, A.q[l].w, A.q[l].w_bf16, b, g);
         const uint8_t *pool = A.kv.pool[l];
-        const QSource<KF, Q_BF16, true> &Q = Qs[l];
+        QSource<KF, Q_BF16, false> Q;       // this layer's query fragments, in registers
+        Q.init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, nullptr, r, g, ln);
         Pg P[NBUF];
         auto fetch = [&](Pg &Pp, int i) {
             int phys = __builtin_amdgcn_readlane(phys_l, i);
@@ -582,13 +578,14 @@ __global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s) {
     dim3 grid((unsigned)((a.n_slots + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)a.q.T);
-    constexpr bool QL = FM_QLDS != 0;
+    // bf16 pages are 16 KB: the query fragments go to LDS to leave registers for prefetch.
+    // fp8 pages are 8.25 KB: registers hold both, and LDS re-reads would outweigh the page bytes.
     if (key_fmt == KEY_BF16 && q_fmt == Q_BF16)
-        score_kernel<KEY_BF16, Q_BF16, FM_NBUF_BF16, QL><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_BF16, Q_BF16, FM_NBUF_BF16, FM_QLDS != 0><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16)
-        score_kernel<KEY_FP8, Q_BF16, FM_NBUF_FP8, QL><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_FP8, Q_BF16, FM_NBUF_FP8, false><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_FP8)
-        score_kernel<KEY_FP8, Q_FP8, FM_NBUF_FP8, QL><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_FP8, Q_FP8, FM_NBUF_FP8, false><<<grid, 256, 0, s>>>(a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -610,7 +607,7 @@ hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s) {
         if (key_fmt == KEY_BF16)
             mask_kernel<KEY_BF16, PPW, 2><<<grid, 256, 0, s>>>(a);
         else
-            mask_kernel<KEY_FP8, PPW, FM_NBUF_FP8><<<grid, 256, 0, s>>>(a);
+            mask_kernel<KEY_FP8, PPW, FM_NBUF_MASK><<<grid, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }

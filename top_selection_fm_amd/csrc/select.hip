@@ -5,20 +5,21 @@
 // DeepSeek-V4 CSA page, section 8: with fewer than 512 entries every entry is kept).
 // The order is "logit descending, then entry index ascending".  Each candidate gets a unique
 // 64-bit key: the order-preserving uint32 image of its logit (-0 folded onto +0) above the
-// bitwise complement of its entry index.  The k-th largest key is found by radix selection,
-// six digits (11/11/10 bits of the logit word, then of the index word), most significant
+// bitwise complement of its entry index.  An exact radix selection finds the k-th largest
+// key: six digits (11/11/10 bits of the logit word, then of the index word), most significant
 // first, with an LDS histogram per digit; a level stops early when the bin holding the k-th
 // key contains exactly the number still needed.  The result is a rule "decided key prefix >=
 // P", which selects exactly min(k, |C|) candidates.  Selected entries are gathered in LDS and
 // bitonic-sorted by index, so the output is ascending and deterministic.
 //
-// Two paths:
-//   * single pass (no workspace): one 1024-thread workgroup per row runs the digit passes
-//     over the row in global memory;
-//   * two stages (workspace): stage 1 cuts every row into 4,096-entry chunks, one 256-thread
-//     workgroup per chunk stages its chunk in LDS and keeps the chunk's own top-k (every
-//     element of the row's top-k is in the top-k of its chunk, so nothing is lost); stage 2
-//     runs one workgroup per row over the <= ceil(n / 4096) * k survivors.
+// One workgroup per row.  Rows longer than the LDS candidate buffer are first cut down: a
+// strided sample of 4,096 entries is binned linearly in value (2,048 bins over the sample's
+// range), and the bin at which the sample's count from the top reaches about 1.3 k n / 4096
+// becomes the cut.  One pass over the row appends every candidate whose bin is at or above the
+// cut to the LDS buffer; the exact selection then runs on the buffer.  Binning is monotone in
+// the value, so when at least k candidates pass, every member of the row's top-k passed too
+// (a candidate in a lower bin has k larger ones above it) and the result is exact.  If fewer
+// than k pass, or the buffer overflows, the exact selection runs over the whole row instead.
 //
 // Compaction (README, page-granular recall): a page of 64 entries is resident when any entry
 // of the mask is; a block-wide exclusive scan of the page flags yields the ascending list.
@@ -30,8 +31,11 @@ namespace fm {
 namespace {
 
 constexpr int kBins = 2048;
-constexpr int kRowThreads = 1024;
-constexpr int kChunkThreads = 256;
+constexpr int kRowThreads = 1024;     // page compaction
+constexpr int kTopkThreads = 512;
+constexpr int kSample = 2048;         // sampled entries of a long row
+constexpr int kBnd = 1024;            // boundary-bin capacity of the final selection
+constexpr int kBuf = 4096;            // LDS candidate buffer
 
 template <int NT>
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
@@ -86,42 +90,48 @@ struct RowSrc {   // one row of a logit matrix (optionally through a resident-pa
     __device__ int64_t entry(int64_t j) const {
         return rp ? (int64_t)rp[j >> 6] * kPage + (j & 63) : j;
     }
+    __device__ bool cand(int64_t j, float &v, int64_t &s) const {
+        v = row[j];
+        if (!(v > -INFINITY)) return false;           // -inf and NaN are never candidates
+        s = entry(j);
+        return !(mrow && !mrow[s]);
+    }
     template <int NT, class F>
     __device__ void each(F f) const {
-        for (int64_t j = threadIdx.x; j < n; j += NT) {
-            const float v = row[j];
-            if (!(v > -INFINITY)) continue;          // -inf and NaN are never candidates
-            const int64_t s = entry(j);
-            if (mrow && !mrow[s]) continue;
-            f(v, s);
+        for (int64_t j0 = threadIdx.x; j0 < n; j0 += 4 * NT) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (j0 + u * NT < n) ? row[j0 + u * NT] : -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (!(v[u] > -INFINITY)) continue;     // -inf and NaN are never candidates
+                const int64_t s = entry(j0 + u * NT);
+                if (mrow && !mrow[s]) continue;
+                f(v[u], s);
+            }
         }
     }
 };
 
-struct LdsChunk {  // a staged chunk: non-candidates already turned into NaN
+struct LdsBuf {     // candidates already filtered into LDS
     const float *v;
     const int32_t *e;
     int m;
     template <int NT, class F>
     __device__ void each(F f) const {
-        for (int i = threadIdx.x; i < m; i += NT) {
-            const float x = v[i];
-            if (x > -INFINITY) f(x, (int64_t)e[i]);
-        }
+        for (int i = threadIdx.x; i < m; i += NT) f(v[i], (int64_t)e[i]);
     }
 };
 
-struct ChunkList {  // stage-1 survivors of one row: n_chunks lists of up to k entries
-    const float *V;
-    const int32_t *E;
-    const int32_t *C;
-    int n_chunks, k;
-    template <int NT, class F>
-    __device__ void each(F f) const {
-        for (int c = 0; c < n_chunks; ++c) {
-            const int cnt = C[c];
-            for (int i = threadIdx.x; i < cnt; i += NT) f(V[(int64_t)c * k + i], (int64_t)E[(int64_t)c * k + i]);
-        }
+// Monotone linear binning of values over [lo, hi] into kBins bins (-1 below lo).
+struct LinBins {
+    float lo, inv_w;
+    bool flat;
+    __device__ int operator()(float v) const {
+        if (v < lo) return -1;
+        if (flat) return v > lo ? kBins - 1 : 0;
+        const float x = (v - lo) * inv_w;
+        return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
     }
 };
 
@@ -250,76 +260,414 @@ __device__ RowSrc row_source(const TopkArgs &A, int t) {
     return R;
 }
 
-// ---------------------------------------------------------------- single pass
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(TopkArgs A) {
-    __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t sh[kRowThreads / 64 + 1];
-    __shared__ uint32_t misc[2];
-    __shared__ uint32_t s_count;
-    __shared__ int32_t sel_idx[FM_MAX_K];
-    __shared__ float sel_val[FM_MAX_K];
-    const int t = blockIdx.x;
-    const RowSrc src = row_source(A, t);
-    const Rule rule = radix_rule<kRowThreads>(src, (uint32_t)A.k, hist, sh, misc);
-    if (threadIdx.x == 0) s_count = 0u;
+// ---------------------------------------------------------------- top-k kernel
+template <int NT>
+__device__ float block_reduce(float x, bool take_max, float *shf) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float y = __shfl_xor(x, o);
+        x = take_max ? fmaxf(x, y) : fminf(x, y);
+    }
+    const int w = threadIdx.x >> 6;
+    if (__lane_id() == 0) shf[w] = x;
     __syncthreads();
-    gather<kRowThreads>(src, rule, sel_val, sel_idx, &s_count, FM_MAX_K);
+    x = shf[0];
+    for (int i = 1; i < NT / 64; ++i) x = take_max ? fmaxf(x, shf[i]) : fminf(x, shf[i]);
     __syncthreads();
-    sort_and_write<kRowThreads>(sel_idx, sel_val, (int)min(s_count, (uint32_t)A.k), A.k,
-                                A.out_idx + (int64_t)t * A.k,
-                                A.out_val ? A.out_val + (int64_t)t * A.k : nullptr);
+    return x;
 }
 
-// ---------------------------------------------------------------- two stages
-__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(TopkArgs A, TopkWs W) {
-    __shared__ float cv[kTopkChunk];
-    __shared__ int32_t ce[kTopkChunk];
-    __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t sh[kChunkThreads / 64 + 1];
-    __shared__ uint32_t misc[2];
-    __shared__ uint32_t s_count;
-    const int c = blockIdx.x, t = blockIdx.y;
-    const RowSrc R = row_source(A, t);
-    const int64_t j0 = (int64_t)c * kTopkChunk;
-    const int m = (int)max((int64_t)0, min((int64_t)kTopkChunk, R.n - j0));
-    for (int i = threadIdx.x; i < m; i += kChunkThreads) {
-        const int64_t j = j0 + i;
-        float v = R.row[j];
-        const int64_t s = R.entry(j);
-        if (R.mrow && !R.mrow[s]) v = __builtin_nanf("");
-        cv[i] = v;
-        ce[i] = (int32_t)s;
+// The cut of a row: candidates with bins(v) >= b pass.  b < 0 means "no cut" (all pass).
+struct Cut {
+    LinBins bins;
+    int b;
+};
+
+// Sample position i of a row of n > kBuf entries: kSample / 16 runs of 16 contiguous entries
+// spread evenly over the row (few cache lines, many pages).
+__device__ __forceinline__ int64_t sample_pos(int i, int64_t n) {
+    return (int64_t)(i >> 4) * n / (kSample / 16) + (i & 15);
+}
+
+// Cut of row R from its sample (block-uniform).  Aims at the sample's (2 k m / n + 16)-th
+// largest value (m = sample size), i.e. about 2 k + 16 n / m candidates of the row passing:
+// comfortably more than k, far fewer than the buffer holds.
+template <int NT>
+__device__ Cut row_cut(const RowSrc &R, uint32_t k, float *sval, uint32_t *hist, uint32_t *sh,
+                       uint32_t *misc, float *shf) {
+    const int tid = threadIdx.x;
+    Cut c;
+    c.bins = LinBins{-INFINITY, 0.f, true};
+    c.b = -1;
+    if (R.n <= kBuf) return c;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int i = tid; i < kSample; i += NT) {
+        float v;
+        int64_t s;
+        const bool ok = R.cand(sample_pos(i, R.n), v, s);
+        sval[i] = ok ? v : __builtin_nanf("");
+        if (ok) {
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+        }
+    }
+    lo = block_reduce<NT>(lo, false, shf);
+    hi = block_reduce<NT>(hi, true, shf);
+    if (!(lo <= hi)) return c;                               // no sampled candidate
+    const uint32_t r = 2u * (uint32_t)(((uint64_t)k * kSample + R.n - 1) / R.n) + 16u;
+    LinBins bins{lo, 0.f, !(hi > lo)};
+    bins.inv_w = bins.flat ? 0.f : (float)kBins / (hi - lo);
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < kSample; i += NT) {
+        const float v = sval[i];
+        if (v == v) atomicAdd(&hist[bins(v)], 1u);
     }
     __syncthreads();
-    const LdsChunk src{cv, ce, m};
-    const Rule rule = radix_rule<kChunkThreads>(src, (uint32_t)A.k, hist, sh, misc);
-    if (threadIdx.x == 0) s_count = 0u;
+    constexpr int BPT = kBins / NT;
+    const int top = kBins - 1 - BPT * tid;
+    uint32_t h[BPT], sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        h[i] = hist[top - i];
+        sum += h[i];
+    }
+    uint32_t total;
+    uint32_t above = block_excl_scan<NT>(sum, sh, total);
+    if (total < r) return c;                                 // too few sampled to cut: all pass
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        if (above < r && r <= above + h[i]) misc[0] = (uint32_t)(top - i);
+        above += h[i];
+    }
     __syncthreads();
-    const int64_t slot = (int64_t)t * W.n_chunks + c;
-    gather<kChunkThreads>(src, rule, W.val + slot * A.k, W.idx + slot * A.k, &s_count,
-                          (uint32_t)A.k);
+    c.bins = bins;
+    c.b = (int)misc[0];
     __syncthreads();
-    if (threadIdx.x == 0) W.cnt[slot] = (int32_t)min(s_count, (uint32_t)A.k);
+    return c;
 }
 
-__global__ __launch_bounds__(kRowThreads) void topk_merge_kernel(TopkArgs A, TopkWs W) {
+// Append the candidates of entries [j0, j1) that pass the cut to (bv, be), keeping the first
+// `cap`; returns how many passed.  Each thread has 16 values in flight per step (four 16-byte
+// loads; element j = base + 4 (u NT + tid) + c, so every load instruction covers 8 KB).
+template <int NT>
+__device__ uint32_t filter_range(const RowSrc &R, int64_t j0, int64_t j1, const Cut &cut,
+                                 float *bv, int32_t *be, uint32_t cap, uint32_t *s_count) {
+    const int tid = threadIdx.x, ln = __lane_id();
+    if (tid == 0) *s_count = 0u;
+    __syncthreads();
+    const uint64_t lt = (ln == 0) ? 0ull : (~0ull >> (64 - ln));
+    const bool vec = !R.rp && ((uintptr_t)(R.row + j0) % 16 == 0);
+    constexpr int U = 4;
+    for (int64_t base = j0; base < j1; base += (int64_t)NT * U * 4) {
+        float v[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = base + 4 * ((int64_t)u * NT + tid);
+            if (vec && j + 4 <= j1) {
+                const float4 x = *(const float4 *)(R.row + j);
+                v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[u][c] = (j + c < j1) ? R.row[j + c] : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t j = base + 4 * ((int64_t)u * NT + tid) + c;
+                const float x = v[u][c];
+                int64_t s = 0;
+                bool hit = x > -INFINITY && cut.bins(x) >= cut.b;
+                if (hit) {
+                    s = R.entry(j);
+                    hit = !(R.mrow && !R.mrow[s]);
+                }
+                const uint64_t mask = __ballot(hit);
+                if (mask) {
+                    const int leader = (int)__builtin_ctzll(mask);
+                    uint32_t b0 = 0;
+                    if (ln == leader) b0 = atomicAdd(s_count, (uint32_t)__popcll(mask));
+                    b0 = __shfl(b0, leader);
+                    const uint32_t pos = b0 + (uint32_t)__popcll(mask & lt);
+                    if (hit && pos < cap) {
+                        bv[pos] = x;
+                        be[pos] = (int32_t)s;
+                    }
+                }
+            }
+    }
+    __syncthreads();
+    const uint32_t n = *s_count;
+    __syncthreads();
+    return n;
+}
+
+// Final selection of the top-k among m buffered candidates (values bval, entries bent), written
+// to the output row in ascending entry order.  One linear-bin histogram over the buffer's value
+// range finds the bin holding the k-th largest value; the entries of higher bins are all
+// selected, and the few in that bin are ranked exactly by the full key.  When that bin holds
+// more than kBnd entries (many near-equal values) the radix selection takes over.
+template <int NT>
+__device__ void select_buffer(const float *bval, const int32_t *bent, int m, uint32_t k,
+                              uint32_t *hist, uint32_t *sh, uint32_t *misc, float *shf,
+                              int32_t *bnd, int32_t *sel_idx, float *sel_val, uint32_t *cnt2,
+                              int32_t *oi, float *ov, int k_out) {
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        cnt2[0] = 0u;
+        cnt2[1] = 0u;
+    }
+    if ((uint32_t)m <= k) {
+        for (int i = tid; i < m; i += NT) {
+            sel_idx[i] = bent[i];
+            sel_val[i] = bval[i];
+        }
+        if (tid == 0) cnt2[0] = (uint32_t)m;
+        __syncthreads();
+    } else {
+        float lo = INFINITY, hi = -INFINITY;
+        for (int i = tid; i < m; i += NT) {
+            lo = fminf(lo, bval[i]);
+            hi = fmaxf(hi, bval[i]);
+        }
+        lo = block_reduce<NT>(lo, false, shf);
+        hi = block_reduce<NT>(hi, true, shf);
+        LinBins bins{lo, 0.f, !(hi > lo)};
+        bins.inv_w = bins.flat ? 0.f : (float)kBins / (hi - lo);
+        for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < m; i += NT) atomicAdd(&hist[bins(bval[i])], 1u);
+        __syncthreads();
+        constexpr int BPT = kBins / NT;
+        const int top = kBins - 1 - BPT * tid;
+        uint32_t h[BPT], sum = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            h[i] = hist[top - i];
+            sum += h[i];
+        }
+        uint32_t total;
+        uint32_t above = block_excl_scan<NT>(sum, sh, total);
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            if (above < k && k <= above + h[i]) {
+                misc[0] = (uint32_t)(top - i);
+                misc[1] = above;
+            }
+            above += h[i];
+        }
+        __syncthreads();
+        const int bstar = (int)misc[0];
+        const uint32_t need = k - misc[1];
+        const uint32_t nb = hist[bstar];
+        if (nb <= (uint32_t)kBnd) {
+            for (int i = tid; i < m; i += NT) {
+                const int b = bins(bval[i]);
+                if (b > bstar) {
+                    const uint32_t p = atomicAdd(&cnt2[0], 1u);
+                    sel_idx[p] = bent[i];
+                    sel_val[p] = bval[i];
+                } else if (b == bstar) {
+                    bnd[atomicAdd(&cnt2[1], 1u)] = i;
+                }
+            }
+            __syncthreads();
+            for (uint32_t a = tid; a < nb; a += NT) {
+                const int ia = bnd[a];
+                const uint64_t ka = full_key(bval[ia], bent[ia]);
+                uint32_t rank = 0;
+                for (uint32_t c = 0; c < nb; ++c) rank += full_key(bval[bnd[c]], bent[bnd[c]]) > ka;
+                if (rank < need) {
+                    const uint32_t p = atomicAdd(&cnt2[0], 1u);
+                    sel_idx[p] = bent[ia];
+                    sel_val[p] = bval[ia];
+                }
+            }
+            __syncthreads();
+        } else {
+            const LdsBuf src{bval, bent, m};
+            const Rule rule = radix_rule<NT>(src, k, hist, sh, misc);
+            __syncthreads();
+            gather<NT>(src, rule, sel_val, sel_idx, &cnt2[0], FM_MAX_K);
+            __syncthreads();
+        }
+    }
+    // ascending entry order: each selected entry's position is the number of smaller entries
+    const int cnt = (int)min(cnt2[0], k);
+    for (int i = tid; i < cnt; i += NT) {
+        const int32_t e = sel_idx[i];
+        int pos = 0;
+        for (int c = 0; c < cnt; ++c) pos += sel_idx[c] < e;
+        oi[pos] = e;
+        if (ov) ov[pos] = sel_val[i];
+    }
+    for (int i = cnt + tid; i < k_out; i += NT) {
+        oi[i] = -1;
+        if (ov) ov[i] = -INFINITY;
+    }
+}
+
+// Stage 1 of the workspace path: grid (n_chunks, T).  Every chunk of a long row recomputes the
+// row's cut from the same sample (identical result in every workgroup) and filters its own
+// kTopkChunk entries into its workspace slot.
+__global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, TopkWs W) {
+    constexpr int NT = kTopkThreads;
+    static_assert(kTopkChunk == NT * 16, "one chunk = 16 values per thread");
+    __shared__ float sval[kSample];
     __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t sh[kRowThreads / 64 + 1];
+    __shared__ uint32_t sh[NT / 64 + 1];
     __shared__ uint32_t misc[2];
+    __shared__ float shf[NT / 64];
+    __shared__ uint32_t s_count;
+    const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, ln = __lane_id();
+    const RowSrc R = row_source(A, t);
+    const int64_t slot = (int64_t)t * W.n_chunks + c;
+    if (R.n <= kBuf) {                  // the select kernel handles short rows on its own
+        if (tid == 0) W.cnt[slot] = 0;
+        return;
+    }
+    // the chunk's 16 values per thread are requested first and stay in flight while the cut
+    // is computed from the sample (element j = j0 + 4 (u NT + tid) + e)
+    const int64_t j0 = (int64_t)c * kTopkChunk, j1 = min(j0 + kTopkChunk, R.n);
+    const bool vec = !R.rp && ((uintptr_t)(R.row + j0) % 16 == 0);
+    float v[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t j = j0 + 4 * ((int64_t)u * NT + tid);
+        if (vec && j + 4 <= j1) {
+            const float4 x = *(const float4 *)(R.row + j);
+            v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[u][e] = (j + e < j1) ? R.row[j + e] : -INFINITY;
+        }
+    }
+    const Cut cut = row_cut<NT>(R, (uint32_t)A.k, sval, hist, sh, misc, shf);
+    if (tid == 0) s_count = 0u;
+    __syncthreads();
+    float *bv = W.val + slot * kTopkCap;
+    int32_t *be = W.idx + slot * kTopkCap;
+    const uint64_t lt = (ln == 0) ? 0ull : (~0ull >> (64 - ln));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t j = j0 + 4 * ((int64_t)u * NT + tid) + e;
+            const float x = v[u][e];
+            int64_t sidx = 0;
+            bool hit = x > -INFINITY && cut.bins(x) >= cut.b;
+            if (hit) {
+                sidx = R.entry(j);
+                hit = !(R.mrow && !R.mrow[sidx]);
+            }
+            const uint64_t mask = __ballot(hit);
+            if (mask) {
+                const int leader = (int)__builtin_ctzll(mask);
+                uint32_t b0 = 0;
+                if (ln == leader) b0 = atomicAdd(&s_count, (uint32_t)__popcll(mask));
+                b0 = __shfl(b0, leader);
+                const uint32_t pos = b0 + (uint32_t)__popcll(mask & lt);
+                if (hit && pos < (uint32_t)kTopkCap) {
+                    bv[pos] = x;
+                    be[pos] = (int32_t)sidx;
+                }
+            }
+        }
+    __syncthreads();
+    if (tid == 0) W.cnt[slot] = cut.b < 0 ? (int32_t)(kTopkCap + 1) : (int32_t)s_count;
+}
+
+// Final selection, one workgroup per row.  With stage-1 survivors (W != null and a long row)
+// the buffer is filled from the workspace; otherwise the workgroup cuts and filters the row
+// itself.  When the cut did not hold (fewer than k passed) or the buffer overflowed, the exact
+// selection runs over the whole row.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs A, TopkWs W, int has_ws) {
+    constexpr int NT = kTopkThreads;
+    __shared__ float bval[kBuf];
+    __shared__ int32_t bent[kBuf];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t sh[NT / 64 + 1];
+    __shared__ uint32_t misc[2];
+    __shared__ float shf[NT / 64];
     __shared__ uint32_t s_count;
     __shared__ int32_t sel_idx[FM_MAX_K];
     __shared__ float sel_val[FM_MAX_K];
-    const int t = blockIdx.x;
-    const int64_t base = (int64_t)t * W.n_chunks;
-    const ChunkList src{W.val + base * A.k, W.idx + base * A.k, W.cnt + base, W.n_chunks, A.k};
-    const Rule rule = radix_rule<kRowThreads>(src, (uint32_t)A.k, hist, sh, misc);
-    if (threadIdx.x == 0) s_count = 0u;
-    __syncthreads();
-    gather<kRowThreads>(src, rule, sel_val, sel_idx, &s_count, FM_MAX_K);
-    __syncthreads();
-    sort_and_write<kRowThreads>(sel_idx, sel_val, (int)min(s_count, (uint32_t)A.k), A.k,
-                                A.out_idx + (int64_t)t * A.k,
-                                A.out_val ? A.out_val + (int64_t)t * A.k : nullptr);
+    __shared__ int32_t bnd[kBnd];
+    __shared__ uint32_t cnt2[2];
+    __shared__ uint32_t offs[kTopkMaxChunks + 1];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const RowSrc R = row_source(A, t);
+    const uint32_t k = (uint32_t)A.k;
+
+    bool from_buf;
+    uint32_t total = 0;
+    if (has_ws && R.n > kBuf) {
+        // survivors of the row's chunks: offsets first, then one round of loads
+        const int64_t base = (int64_t)t * W.n_chunks;
+        if (tid == 0) {
+            uint32_t acc = 0, over = 0;
+            for (int c = 0; c < W.n_chunks; ++c) {
+                const uint32_t n = (uint32_t)W.cnt[base + c];
+                offs[c] = acc;
+                over |= n > (uint32_t)kTopkCap;
+                acc += n;
+            }
+            offs[W.n_chunks] = acc;
+            misc[0] = over;
+        }
+        __syncthreads();
+        total = offs[W.n_chunks];
+        from_buf = !misc[0] && total >= k && total <= (uint32_t)kBuf;
+        __syncthreads();
+        if (from_buf) {
+            constexpr int U = kBuf / NT;
+            float xv[U];
+            int32_t xe[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t g = tid + u * NT;
+                if (g < total) {
+                    int lo = 0, hi = W.n_chunks;            // offs[lo] <= g < offs[hi]
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (offs[mid] <= g) lo = mid; else hi = mid;
+                    }
+                    const int64_t at = (base + lo) * kTopkCap + (g - offs[lo]);
+                    xv[u] = W.val[at];
+                    xe[u] = W.idx[at];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t g = tid + u * NT;
+                if (g < total) {
+                    bval[g] = xv[u];
+                    bent[g] = xe[u];
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+        const Cut cut = row_cut<NT>(R, k, bval, hist, sh, misc, shf);
+        total = filter_range<NT>(R, 0, R.n, cut, bval, bent, kBuf, &s_count);
+        from_buf = total <= (uint32_t)kBuf && !(cut.b >= 0 && total < k);
+    }
+
+    int32_t *oi = A.out_idx + (int64_t)t * A.k;
+    float *ov = A.out_val ? A.out_val + (int64_t)t * A.k : nullptr;
+    if (from_buf) {
+        select_buffer<NT>(bval, bent, (int)total, k, hist, sh, misc, shf, bnd, sel_idx, sel_val,
+                          cnt2, oi, ov, A.k);
+    } else {
+        const Rule rule = radix_rule<NT>(R, k, hist, sh, misc);
+        if (tid == 0) s_count = 0u;
+        __syncthreads();
+        gather<NT>(R, rule, sel_val, sel_idx, &s_count, FM_MAX_K);
+        __syncthreads();
+        sort_and_write<NT>(sel_idx, sel_val, (int)min(s_count, k), A.k, oi, ov);
+    }
 }
 
 // ---------------------------------------------------------------- page compaction
@@ -372,12 +720,10 @@ __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
 }  // namespace
 
 size_t topk_ws_bytes(int T, int64_t n) {
-    if (T <= 0 || n <= 0) return 0;
-    const int64_t chunks = (n + kTopkChunk - 1) / kTopkChunk;
-    const size_t slots = (size_t)T * (size_t)chunks;
-    return align_up(slots * kTopkWsK * sizeof(float), 256) +
-           align_up(slots * kTopkWsK * sizeof(int32_t), 256) +
-           align_up(slots * sizeof(int32_t), 256);
+    if (T <= 0 || n <= kBuf || n > (int64_t)kTopkMaxChunks * kTopkChunk) return 0;
+    const size_t slots = (size_t)T * (size_t)((n + kTopkChunk - 1) / kTopkChunk);
+    return align_up(slots * kTopkCap * sizeof(float), 256) +
+           align_up(slots * kTopkCap * sizeof(int32_t), 256) + align_up(slots * sizeof(int32_t), 256);
 }
 
 TopkWs topk_ws_carve(void *ws, int T, int64_t n) {
@@ -387,22 +733,22 @@ TopkWs topk_ws_carve(void *ws, int T, int64_t n) {
     TopkWs W;
     W.n_chunks = (int)chunks;
     W.val = (float *)p;
-    p += align_up(slots * kTopkWsK * sizeof(float), 256);
+    p += align_up(slots * kTopkCap * sizeof(float), 256);
     W.idx = (int32_t *)p;
-    p += align_up(slots * kTopkWsK * sizeof(int32_t), 256);
+    p += align_up(slots * kTopkCap * sizeof(int32_t), 256);
     W.cnt = (int32_t *)p;
     return W;
 }
 
 hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s) {
-    if (ws && a.k <= kTopkWsK) {
-        topk_chunk_kernel<<<dim3((unsigned)ws->n_chunks, (unsigned)a.T), dim3(kChunkThreads), 0, s>>>(a, *ws);
-        hipError_t e = hipGetLastError();
+    TopkWs W{};
+    if (ws) {
+        W = *ws;
+        topk_filter_kernel<<<dim3((unsigned)W.n_chunks, (unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, W);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        topk_merge_kernel<<<dim3((unsigned)a.T), dim3(kRowThreads), 0, s>>>(a, *ws);
-    } else {
-        topk_row_kernel<<<dim3((unsigned)a.T), dim3(kRowThreads), 0, s>>>(a);
     }
+    topk_kernel<<<dim3((unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, W, ws ? 1 : 0);
     return hipGetLastError();
 }
 
