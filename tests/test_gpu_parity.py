@@ -311,3 +311,44 @@ def test_prefill_full_sampled_rows(prefill_full):
     assert not np.any(ig == 33791), "entry 33,791 is visible to no row"
     assert np.all(ig < 33791)
     G.note("prefill full sampled", rows=rows.tolist(), logit_err=err, topk_dis=dis)
+
+
+@pytest.mark.parametrize("T,pos0,seq_len,extra_ld", [
+    (16, 4 * 700, 64 * 12 + 3, 0),       # exactly one 16-row tile
+    (17, 4 * 700, 64 * 12 + 3, 70),      # a ragged second tile; columns past seq_len
+    (15, 4 * 700, 64 * 12 + 3, 0),       # fewer rows than a tile: one row at a time
+    (40, 0, 64 * 5, 0),                  # the first rows see nothing (pos < ratio)
+    (300, 4 * 9000, 64 * 140 + 17, 5),   # many tiles and chunks, no causal cut inside
+])
+def test_prefill_edge_shapes(T, pos0, seq_len, extra_ld):
+    wl = W.prefill_causal_fp8(seed=2008 + T, T=T, pos0=pos0, seq_len=seq_len)
+    dw = dev(wl)
+    ld = seq_len + extra_ld
+    L = G.index_logits(dw, ld=ld)
+    L2 = G.index_logits(dw, ld=ld)
+    assert torch.equal(L, L2), "prefill logits are not deterministic"
+    idx, val = G.topk(L)
+    torch.cuda.synchronize()
+    rows = np.arange(T)
+    Lr = oracle.logits(wl, rows=rows, s_end=ld)
+    err = G.check_logits(L.cpu().numpy(), Lr, TOL_LOW, f"prefill T={T}")
+    dis = topk_parity(f"prefill T={T} top-512", Lr, idx.cpu().numpy(), val.cpu().numpy())
+    G.note(f"prefill edge T={T}", logit_err=err, topk_dis=dis)
+
+
+def test_prefill_unmapped_pages_score_nan():
+    wl = W.prefill_causal_fp8(seed=2030, T=32, pos0=4 * 1300, seq_len=64 * 20)
+    bt = wl.kv.block_table.copy()
+    bt[0, 3] = -1
+    bt[0, 9] = 10 ** 8                       # out of range: bounds-checked on the device
+    wl2 = W.Workload(wl.name, W.KeyPool(wl.kv.pools, "fp8x132", bt, wl.kv.seq_lens),
+                     wl.queries)
+    L = G.index_logits(dev(wl2), ld=64 * 20).cpu().numpy()
+    assert np.all(np.isnan(L[:, 3 * 64:4 * 64])) and np.all(np.isnan(L[:, 9 * 64:10 * 64]))
+    Lr = oracle.logits(wl, rows=np.arange(32), s_end=64 * 20)
+    keep = np.ones(64 * 20, bool)
+    keep[3 * 64:4 * 64] = keep[9 * 64:10 * 64] = False
+    G.check_logits(L[:, keep], Lr[:, keep], TOL_LOW, "prefill unmapped")
+    idx, _ = G.topk(torch.from_numpy(L).cuda())
+    ig = idx.cpu().numpy()
+    assert not np.isin(ig // 64, [3, 9]).any()

@@ -167,8 +167,19 @@ fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *l
     REQUIRE(ld >= 1, FM_ERR_INVALID_ARG, "ld = %lld", (long long)ld);
     REQUIRE(aligned(logits, 4), FM_ERR_INVALID_ARG, "logits not 4-byte aligned");
     if (q->T == 0) return ok();
-    CHECK(run_score(q, kv, nullptr, nullptr, 0, logits, ld, (ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE,
-                    (hipStream_t)stream));
+    const int64_t n_pages = (ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE;
+    if (q->q_dtype == FM_FP8_E4M3 && kv->B == 1 && q->T >= 16) {
+        // many rows over one request's keys (prefill): tiled for key reuse across rows
+        fm::PrefillArgs a;
+        a.q = make_q(q, kv);
+        a.kv = make_kv(kv);
+        a.out = logits;
+        a.out_ld = ld;
+        fm::prefill_plan(a, q->T, n_pages);
+        CHECK(launched(fm::launch_prefill(a, (hipStream_t)stream), "prefill"));
+        return ok();
+    }
+    CHECK(run_score(q, kv, nullptr, nullptr, 0, logits, ld, n_pages, (hipStream_t)stream));
     return ok();
 }
 

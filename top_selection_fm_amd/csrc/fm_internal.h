@@ -57,6 +57,18 @@ struct ScoreArgs {
     int ppw;             // page slots per wave
 };
 
+// Tiled scoring of many query rows of one request (prefill), fp8 queries and fp8 keys.
+struct PrefillArgs {
+    QArgs q;
+    KvArgs kv;           // B == 1: every row reads request 0's block table
+    float *out;
+    int64_t out_ld;      // floats per output row (columns 0 .. out_ld - 1 are written)
+    int64_t n_pages;     // ceil(out_ld / 64)
+    int64_t chunk_pages; // pages per workgroup chunk
+    int n_chunks;
+    int n_rowblocks;     // ceil(T / 8)
+};
+
 struct MaskArgs {
     QArgs q[FM_MAX_LAYERS];
     KvArgs kv;
@@ -114,6 +126,8 @@ size_t topk_ws_bytes(int T, int64_t n);   // bytes for T rows of up to n entries
 TopkWs topk_ws_carve(void *ws, int T, int64_t n);
 
 hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s);
+void prefill_plan(PrefillArgs &a, int T, int64_t n_pages);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, int B, hipStream_t s);

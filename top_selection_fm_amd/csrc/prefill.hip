@@ -1,0 +1,300 @@
+// prefill.hip -- index logits for many query rows of one request: fp8 queries x fp8 keys.
+//
+// L[t,s] = sum_h w[t,h] * ReLU(q[t,h,:] . k[s,:]) over 64 heads of dimension 128
+// (FlashMemory-DeepSeek-V4 paper summary, section 3, the Memory-Indexer score; DeepSeek-V4 CSA
+// page, section 3, formula CSA-1), with the causal cut s < floor(pos_t / ratio) (CSA page,
+// section 10).  Prefill has thousands of rows over the same keys, so the work is a real dense
+// contraction: it is tiled for operand reuse and runs on the fp8 MFMA.
+//
+// Tiling.  A workgroup (8 waves) owns 8 consecutive query rows, one per wave, and a chunk of
+// key pages.  Each wave keeps the fp8 queries of its row in registers; the key pages stream
+// through a ring of three LDS buffers (one page of 64 entries per step) and every key fragment
+// read from LDS feeds 4 MFMAs.  A page's global loads go out two steps before it is scored.
+// The workgroup's linear id is split as (chunk = id % n_chunks, row block = id / n_chunks):
+// workgroups are dealt to the 8 XCDs round-robin, so with n_chunks a multiple of 8 each XCD
+// only ever reads the key chunks that belong to it, and they stay in its L2.
+//
+// MFMA layout (v_mfma_scale_f32_16x16x128_f8f6f4, wave64).  Row i of fragment n of the A tile
+// is head 16 n + i of the wave's query row, so the accumulator lane 16 g + j holds heads
+// 16 n + 4 g + 0..3 for key entry j of a 16-entry block; the head sum is 16 in-lane terms plus
+// two row swaps across the four lane groups.  The K dimension (128 head dims) is split the same
+// way for queries and keys (32 consecutive bytes per lane), so the dot products are exact
+// whatever order the hardware walks K in.  The MFMAs of block u + 1 are issued between the
+// epilogue steps of block u, across page boundaries too.
+//
+// Epilogue.  The MFMA's power-of-two block scale multiplies every dot product of E4M3 codes by
+// 2^-25, which puts any possible value (|S| <= 448^2 * 128 < 2^25) strictly inside (-1, 1).
+// Each pair of head results is rounded to f16 with the conversion's clamp to [0, 1] (packed),
+// which on that range is exactly ReLU, and multiplied by the head weights with v_dot2c_f32_f16
+// into float accumulators: two VALU instructions per four head results.  The weights are
+// scaled per row by a power of two into [2^14, 2^15) first, so a bf16 weight converts to f16
+// exactly.  The only rounding beyond float accumulation is the f16 rounding of each ReLU(S)
+// term (relative 2^-11 for terms >= 2^-14, absolute 2^-25 of the largest possible S below).
+// The per-token query scale, the per-entry key scale and the powers of two are applied to the
+// sum, which is valid because the scales are positive.
+#include <math.h>
+
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+constexpr int kLdsRow = 144;                       // a key row's 128 codes, padded (bank spread)
+constexpr int kSExp = 25;                          // dot products of codes are scaled by 2^-25
+constexpr int kScaleA = 127 - kSExp;               // E8M0 block scale of the A operand
+constexpr int kMaxChunkPages = 128;                // pages of one workgroup's key chunk, at most
+constexpr int kWaves = 8;                          // one query row per wave
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ u32x4 load16(const uint8_t *p) {  // 4-byte aligned
+    const uint32_t *w = (const uint32_t *)p;
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ int row_request(const QArgs &q, const KvArgs &kv, int t) {
+    const int b = q.row_req ? q.row_req[t] : (q.b_is_zero ? 0 : t);
+    return (b >= 0 && b < kv.B) ? b : -1;
+}
+
+__device__ __forceinline__ int64_t n_visible(const QArgs &q, const KvArgs &kv, int t, int b) {
+    if (b < 0) return 0;
+    int64_t n = kv.seq_lens[b];
+    if (q.q_pos) {
+        const int64_t c = (int64_t)q.q_pos[t] / q.ratio;
+        n = c < n ? c : n;
+    }
+    return n < 0 ? 0 : n;
+}
+
+// Physical page of logical page p of request 0, or -1 when it is not mapped.
+__device__ __forceinline__ int page_phys(const KvArgs &kv, int64_t p) {
+    if (p >= kv.bt_ld) return -1;
+    const int phys = kv.bt[p];
+    return (phys < 0 || phys >= kv.n_phys) ? -1 : phys;
+}
+
+// ReLU(f16(x)), x in (-1, 1): the clamp to [0, 1] folds into the conversion instruction
+__device__ __forceinline__ h2 relu16(float a, float b) {
+    const h2 x = __builtin_convertvector(f32x2{a, b}, h2);
+    return __builtin_elementwise_min(__builtin_elementwise_max(x, h2{0, 0}), h2{1, 1});
+}
+
+// One fp8 accumulator tile of the epilogue: heads 8 n + 4 (g % 2) + 0..3 of this lane's row.
+__device__ __forceinline__ void epi_step(const f32x4 &c, h2 w01, h2 w23, float &a0, float &a1) {
+    a0 = __builtin_amdgcn_fdot2(relu16(c[0], c[1]), w01, a0, false);
+    a1 = __builtin_amdgcn_fdot2(relu16(c[2], c[3]), w23, a1, false);
+}
+
+// This lane's half of its row's 64-head sum plus the partner lane group's (lane xor 16), by a
+// row swap; both lanes of a pair add in the same order.
+__device__ __forceinline__ float pair_total(float p) {
+    const uint32_t u = __float_as_uint(p);
+    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void prefill_fp8_kernel(PrefillArgs A) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_codes[3][kPage * kLdsRow];
+    __shared__ float s_scale[3][kPage];
+    __shared__ int s_phys[kMaxChunkPages];
+
+    const int tid = threadIdx.x, ln = __lane_id(), wave = tid >> 6;
+    const int j = ln & 15, g = ln >> 4;
+    const int chunk = (int)(blockIdx.x % (unsigned)A.n_chunks);
+    const int rblk = (int)(blockIdx.x / (unsigned)A.n_chunks);
+    const int t0 = rblk * kWaves;
+    const int T = A.q.T;
+
+    int nv8 = 0;
+    if (j < kWaves && t0 + j < T)
+        nv8 = (int)n_visible(A.q, A.kv, t0 + j, row_request(A.q, A.kv, t0 + j));
+    int tile_nvis = nv8;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) tile_nvis = max(tile_nvis, __shfl_xor(tile_nvis, o));
+    const int t = t0 + wave;
+    const bool row_ok = t < T;
+    const int nvis_t = __shfl(nv8, wave);
+    float *orow = A.out + (int64_t)(row_ok ? t : 0) * A.out_ld;
+
+    // queries: fragment n, A row i = head 16 n + i, bytes 32 g .. 32 g + 31
+    i32x8 qf[4];
+    {
+        const uint8_t *qb = (const uint8_t *)A.q.q + (int64_t)(row_ok ? t : 0) * kHeads * kDim;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const uint8_t *p = qb + (16 * n + j) * kDim + 32 * g;
+            const u32x4 a = row_ok ? *(const u32x4 *)p : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 b = row_ok ? *(const u32x4 *)(p + 16) : u32x4{0u, 0u, 0u, 0u};
+            qf[n] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                          (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        }
+    }
+    // this lane's 16 head weights (heads 16 n + 4 g + 0..3) as f16 pairs scaled by 2^ew
+    h2 wp[8];
+    float row_factor;
+    {
+        const int64_t base = (int64_t)(row_ok ? t : 0) * kHeads + 4 * g;
+        float wl[4][4];
+        if (A.q.w_bf16) {
+            const uint16_t *w16 = (const uint16_t *)A.q.w + base;
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) wl[n][v] = bf16f(w16[16 * n + v]);
+        } else {
+            const float *w32 = (const float *)A.q.w + base;
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) wl[n][v] = w32[16 * n + v];
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) m = fmaxf(m, fabsf(wl[n][v]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        int ex = 0;
+        if (m > 0.f) (void)frexpf(m, &ex);
+        const int ew = m > 0.f ? 15 - ex : 0;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            wp[2 * n] = __builtin_convertvector(f32x2{ldexpf(wl[n][0], ew), ldexpf(wl[n][1], ew)}, h2);
+            wp[2 * n + 1] = __builtin_convertvector(f32x2{ldexpf(wl[n][2], ew), ldexpf(wl[n][3], ew)}, h2);
+        }
+        const float qs = row_ok ? A.q.q_scale[t] : 0.f;
+        row_factor = ldexpf(qs, kSExp - ew);
+    }
+
+    const int64_t p_begin = (int64_t)chunk * A.chunk_pages;
+    const int64_t p_end = min(p_begin + A.chunk_pages, A.n_pages);
+    const int64_t p_vis = min(p_end, ((int64_t)tile_nvis + kPage - 1) / kPage);
+    for (int i = tid; i < A.chunk_pages; i += kThreads)
+        s_phys[i] = p_begin + i < p_end ? page_phys(A.kv, p_begin + i) : -1;
+    __syncthreads();
+
+    // staging: thread tid carries entry tid / 8, code bytes 16 (tid % 8) .. + 15, and the scale
+    const int se = tid >> 3, sp = tid & 7;
+    u32x4 Rc = u32x4{0u, 0u, 0u, 0u};
+    float Rs = 0.f;
+    auto stage = [&](int64_t p) {
+        const int64_t pc = min(p, p_vis - 1);
+        const int phys = max(s_phys[pc - p_begin], 0);
+        const uint8_t *row = A.kv.pool[0] + ((int64_t)phys * kPage + se) * kRowFp8;
+        Rc = load16(row + 16 * sp);
+        Rs = *(const float *)(row + kDim);
+    };
+    auto commit = [&](int buf) {
+        *(u32x4 *)&s_codes[buf][se * kLdsRow + 16 * sp] = Rc;
+        if (sp == 0) s_scale[buf][se] = Rs;
+    };
+    auto kfrag = [&](int buf, int u) {
+        const uint8_t *kp = s_codes[buf] + (16 * u + j) * kLdsRow + 32 * g;
+        const u32x4 k0 = *(const u32x4 *)kp;
+        const u32x4 k1 = *(const u32x4 *)(kp + 16);
+        return i32x8{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                     (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+    };
+    int64_t pend_s = A.out_ld;
+    float pend_v = 0.f;
+    auto flush = [&]() {
+        if (row_ok && pend_s < A.out_ld) orow[pend_s] = pend_v;
+    };
+    // the fp8 MFMAs of the next block into `nxt`, the current block's epilogue on the vector unit
+    auto phase = [&](f32x4 (&nxt)[4], const i32x8 &kn, const f32x4 (&cur)[4]) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            nxt[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                qf[n], kn, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, kScaleA, 0, 127);
+            epi_step(cur[n], wp[2 * n], wp[2 * n + 1], a0, a1);
+            if (n & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+        // sum over the four lane groups (heads 4 g + 0..3 of every fragment)
+        const float p = pair_total(a0 + a1);
+        const uint32_t u = __float_as_uint(p);
+        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    };
+
+    if (p_begin < p_vis) {
+        stage(p_begin);
+        commit(0);
+        stage(p_begin + 1);
+        commit(1);
+        stage(p_begin + 2);
+        __syncthreads();
+        f32x4 ca[4], cb[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            ca[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                qf[n], kfrag(0, 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, kScaleA, 0, 127);
+        i32x8 k1 = kfrag(0, 1);
+        int b0 = 0;
+        for (int64_t p = p_begin; p < p_vis; ++p) {
+            const int b1 = b0 == 2 ? 0 : b0 + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+            commit(b2);
+            stage(p + 3);
+            flush();
+            f32x4 tot;
+            const i32x8 k2 = kfrag(b0, 2);
+            tot[0] = phase(cb, k1, ca);
+            const i32x8 k3 = kfrag(b0, 3);
+            tot[1] = phase(ca, k2, cb);
+            const i32x8 kn = kfrag(b1, 0);
+            tot[2] = phase(cb, k3, ca);
+            k1 = kfrag(b1, 1);
+            tot[3] = phase(ca, kn, cb);
+            // every lane holds all four block totals; lane group g stores block g
+            const int e = 16 * g + j;
+            const int64_t s = p * kPage + e;
+            const float tt = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+            const float v = s_phys[p - p_begin] >= 0 ? tt * row_factor * s_scale[b0][e]
+                                                     : __builtin_nanf("");
+            pend_s = s;
+            pend_v = s < nvis_t ? v : -INFINITY;
+            __syncthreads();
+            b0 = b1;
+        }
+        flush();
+    }
+    for (int64_t p = max(p_vis, p_begin); p < p_end; ++p) {
+        const int64_t s = p * kPage + 16 * g + j;
+        if (row_ok && s < A.out_ld) orow[s] = -INFINITY;
+    }
+}
+
+}  // namespace
+
+void prefill_plan(PrefillArgs &a, int T, int64_t n_pages) {
+    const int64_t rblocks = (T + kWaves - 1) / kWaves;
+    int64_t chunks = (4096 + rblocks - 1) / rblocks;         // about 16 workgroups per CU
+    const int64_t max_chunks = n_pages / 8 > 1 ? n_pages / 8 : 1;   // >= 8 pages per chunk
+    if (chunks > max_chunks) chunks = max_chunks;
+    if (chunks >= 8) chunks = chunks / 8 * 8;                 // one chunk set per XCD
+    const int64_t min_chunks = (n_pages + kMaxChunkPages - 1) / kMaxChunkPages;
+    if (chunks < min_chunks) chunks = min_chunks;             // the chunk's table fits in LDS
+    if (chunks < 1) chunks = 1;
+    a.n_pages = n_pages;
+    a.n_chunks = (int)chunks;
+    a.chunk_pages = (n_pages + chunks - 1) / chunks;
+    a.n_rowblocks = (int)rblocks;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s) {
+    const unsigned grid = (unsigned)((int64_t)a.n_chunks * a.n_rowblocks);
+    prefill_fp8_kernel<<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace fm
