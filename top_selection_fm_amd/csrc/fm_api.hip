@@ -164,7 +164,8 @@ fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *l
     CHECK(check_kv(kv, 1));
     CHECK(check_q(q, kv, "q"));
     REQUIRE(logits, FM_ERR_INVALID_ARG, "logits is NULL");
-    REQUIRE(ld >= 1, FM_ERR_INVALID_ARG, "ld = %lld", (long long)ld);
+    REQUIRE(ld >= 1 && ld <= (int64_t)INT32_MAX / 4, FM_ERR_INVALID_ARG, "ld = %lld (1 .. 2^29)",
+            (long long)ld);
     REQUIRE(aligned(logits, 4), FM_ERR_INVALID_ARG, "logits not 4-byte aligned");
     if (q->T == 0) return ok();
     const int64_t n_pages = (ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE;
@@ -225,7 +226,7 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     CHECK(check_kv(kv, 1));
     CHECK(check_q(q, kv, "q"));
     REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
-    REQUIRE(res_ld >= 1 && res_ld * FM_PAGE_SIZE <= (int64_t)INT32_MAX, FM_ERR_INVALID_ARG,
+    REQUIRE(res_ld >= 1 && res_ld * FM_PAGE_SIZE <= (int64_t)INT32_MAX / 4, FM_ERR_INVALID_ARG,
             "res_ld = %lld", (long long)res_ld);
     if (q->T == 0) return ok();
     REQUIRE(resident_pages && n_resident && out_idx, FM_ERR_INVALID_ARG,

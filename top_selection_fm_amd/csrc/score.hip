@@ -20,26 +20,20 @@
 // The head sum: each lane weights and sums its 16 accumulator values (4 head tiles x 4 rows),
 // then two cross-lane adds (lane xor 16, xor 32) complete the 64-head sum for its column.
 //
-// Streaming: keys are read once, straight into registers in the layout above.  A decode call
-// is HBM-bound, so what matters is the number of bytes in flight per CU: every wave keeps
-// NBUF - 1 pages loading while it computes one, and the query fragments (the MFMA A operands)
-// can live in LDS, shared by the four waves of a workgroup (they score the same row), which
-// frees the registers for deeper prefetch and two waves per SIMD.
+// Streaming: keys are read once, straight from HBM into MFMA operand registers in the layout
+// above; the query fragments stay in registers.  A decode call is HBM-bound, so what matters is
+// the number of bytes in flight per CU: every wave keeps the next page (bf16) or two (fp8)
+// loading while it scores one, with loads and stores that never sit behind a branch, so the
+// wait before a page covers that page's loads only.
 #include <math.h>
 
 #include "fm_internal.h"
 
-#ifndef FM_NBUF_BF16
-#define FM_NBUF_BF16 3
+#ifndef FM_BF16_RING
+#define FM_BF16_RING 4
 #endif
-#ifndef FM_NBUF_FP8
-#define FM_NBUF_FP8 3
-#endif
-#ifndef FM_NBUF_MASK
-#define FM_NBUF_MASK 2
-#endif
-#ifndef FM_QLDS
-#define FM_QLDS 1
+#ifndef FM_DECODE_WAVES
+#define FM_DECODE_WAVES 4
 #endif
 #ifndef FM_WAVES_PER_EU
 #define FM_WAVES_PER_EU 2
@@ -57,6 +51,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kSlotInvisible = -1;  // every entry of the page is past the visible length
 constexpr int kSlotUnmapped = -2;   // the block table (or resident list) points nowhere valid
 constexpr int kSlotEmpty = -3;      // resident-list slot beyond n_resident: nothing to write
+constexpr int kMaxPpw = 16;         // page slots per wave, at most
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -97,42 +92,28 @@ __device__ __forceinline__ i32x8 q_frag_fp8(const uint8_t *qrow, int m, int r, i
 
 struct QRegBf16 {
     u32x4 a[4][4];
-    __device__ __forceinline__ u32x4 get(int m, int kk, int) const { return a[m][kk]; }
-};
-struct QLdsBf16 {           // 16 fragments x 64 lanes x 16 B, lane-contiguous (conflict free)
-    const u32x4 *s;
-    int ln;
-    __device__ __forceinline__ u32x4 get(int m, int kk, int z) const { return s[(m * 4 + kk) * 64 + ln + z]; }
+    __device__ __forceinline__ u32x4 get(int m, int kk) const { return a[m][kk]; }
 };
 struct QRegFp8 {
     i32x8 a[4];
-    __device__ __forceinline__ i32x8 get(int m, int) const { return a[m]; }
+    __device__ __forceinline__ i32x8 get(int m) const { return a[m]; }
 };
-struct QLdsFp8 {            // 4 fragments x 64 lanes x 32 B
-    const i32x8 *s;
-    int ln;
-    __device__ __forceinline__ i32x8 get(int m, int z) const { return s[m * 64 + ln + z]; }
-};
-
-// A zero the compiler cannot see through.  Adding it to an LDS index once per entry tile makes
-// the query fragments be re-read for every tile instead of being kept live across a page, which
-// leaves the registers to the key pages in flight.
-__device__ __forceinline__ int opaque_zero() {
-    int z;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-    return z;
-}
-
 // w[t, 16 m + 4 g + i] for the accumulator rows this lane holds
 __device__ __forceinline__ void load_w(float (&wv)[16], const void *w, int w_bf16, int t, int g) {
+    const int64_t base = (int64_t)t * kHeads + 4 * g;
+    if (w_bf16) {
+        const uint16_t *w16 = (const uint16_t *)w + base;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int h = 16 * m + 4 * g + i;
-            wv[m * 4 + i] = w_bf16 ? bf16f(((const uint16_t *)w)[(int64_t)t * kHeads + h])
-                                   : ((const float *)w)[(int64_t)t * kHeads + h];
-        }
+            for (int i = 0; i < 4; ++i) wv[m * 4 + i] = bf16f(w16[16 * m + i]);
+    } else {
+        const float *w32 = (const float *)w + base;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[m * 4 + i] = w32[16 * m + i];
+    }
 }
 
 // ---------------------------------------------------------------- key pages in registers
@@ -144,12 +125,21 @@ __device__ __forceinline__ u32x4 load16(const uint8_t *p) {  // 4-byte aligned
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// bf16 page: a buffer descriptor spanning exactly the page (so no lane can read past it), one
-// VGPR offset per lane (row r, 16-byte chunk g), entry tile j in the scalar offset, k-step kk in
-// the immediate offset.
-__device__ __forceinline__ void load_page(PgBf16 &P, const uint8_t *page, int r, int g, int) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)page, (short)0, kPage * kRowBf16, 0x00020000);
+// Page loads go through a buffer descriptor spanning exactly the page, so no lane can read past
+// it; a page that is not to be read (unmapped, invisible, or padding) gets a zero-size
+// descriptor, for which the loads return zeros without touching memory.  That keeps every load
+// unconditional (no branches around memory operations, exact wait counts) while an invalid
+// page is never dereferenced.  phys is wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *pool, int phys, int bytes) {
+    const bool ok = phys >= 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(pool + (int64_t)(ok ? phys : 0) * bytes),
+                                             (short)0, ok ? bytes : 0, 0x00020000);
+}
+
+// bf16 page: one VGPR offset per lane (row r, 16-byte chunk g), entry tile j in the scalar
+// offset, k-step kk in the immediate offset.
+__device__ __forceinline__ void load_page(PgBf16 &P, const uint8_t *pool, int phys, int r, int g, int) {
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(pool, phys, kPage * kRowBf16);
     const uint32_t off = (uint32_t)(r * kRowBf16 + g * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -158,15 +148,17 @@ __device__ __forceinline__ void load_page(PgBf16 &P, const uint8_t *page, int r,
             P.b[j][kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + kk * 64, j * 16 * kRowBf16, 0);
 }
 
-// fp8 page: 132-byte rows are only 4-byte aligned, so plain global loads (which accept that)
-// from the wave-uniform page base plus a 32-bit lane offset.
-__device__ __forceinline__ void load_page(PgFp8 &P, const uint8_t *page, int r, int g, int ln) {
+// fp8 page: 132-byte rows, so the 16-byte loads are 4-byte aligned (as plain global loads of the
+// same rows are); the lane's own row scale comes along.
+__device__ __forceinline__ void load_page(PgFp8 &P, const uint8_t *pool, int phys, int r, int g, int ln) {
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(pool, phys, kPage * kRowFp8);
     const uint32_t off = (uint32_t)(r * kRowFp8 + g * 32);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) P.b[j][h] = load16(page + (off + (uint32_t)(j * 16 * kRowFp8 + h * 16)));
-    P.scale = *(const float *)(page + (uint32_t)(ln * kRowFp8 + kDim));
+        for (int h = 0; h < 2; ++h)
+            P.b[j][h] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + h * 16, j * 16 * kRowFp8, 0);
+    P.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(ln * kRowFp8 + kDim), 0, 0));
 }
 
 __device__ __forceinline__ u32x4 b_operand(const PgBf16 &P, int j, int kk) { return P.b[j][kk]; }
@@ -210,7 +202,6 @@ __device__ __forceinline__ float page_logit_bf16q(const QS &Q, const float (&wv)
     float tot[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int z = opaque_zero();
         f32x4 acc[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -220,7 +211,7 @@ __device__ __forceinline__ float page_logit_bf16q(const QS &Q, const float (&wv)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, Q.get(m, kk, z)), bk, acc[m], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, Q.get(m, kk)), bk, acc[m], 0, 0, 0);
         }
         tot[j] = head_sum(acc, wv);
     }
@@ -233,7 +224,6 @@ __device__ __forceinline__ float page_logit_fp8q(const QS &Q, const float (&wv)[
     float tot[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int z = opaque_zero();
         i32x8 bk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -244,22 +234,23 @@ __device__ __forceinline__ float page_logit_fp8q(const QS &Q, const float (&wv)[
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                Q.get(m, z), bk, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                Q.get(m), bk, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
         tot[j] = head_sum(acc, wv);
     }
     return g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
 }
 
 template <int KF> struct PageOf;
-template <> struct PageOf<KEY_BF16> { typedef PgBf16 T; static constexpr int row = kRowBf16; };
-template <> struct PageOf<KEY_FP8> { typedef PgFp8 T; static constexpr int row = kRowFp8; };
+template <> struct PageOf<KEY_BF16> { typedef PgBf16 T; static constexpr int row = kRowBf16, nbuf = 2; };
+template <> struct PageOf<KEY_FP8> { typedef PgFp8 T; static constexpr int row = kRowFp8, nbuf = 3; };
 
 // Query operand source of one row: registers, or the workgroup's LDS copy.
-template <int KF, int QF, bool QLDS> struct QSource;
+// Query operand source of one row, in registers.
+template <int KF, int QF> struct QSource;
 
-template <int KF> struct QSource<KF, Q_BF16, false> {
+template <int KF> struct QSource<KF, Q_BF16> {
     QRegBf16 q;
-    __device__ void init(const uint8_t *qrow, void *, int r, int g, int) {
+    __device__ void init(const uint8_t *qrow, int r, int g) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -271,45 +262,11 @@ template <int KF> struct QSource<KF, Q_BF16, false> {
     }
 };
 
-template <int KF> struct QSource<KF, Q_BF16, true> {
-    QLdsBf16 q;
-    // every wave of the block writes 4 of the 16 fragments; the caller then syncs the block
-    __device__ void init(const uint8_t *qrow, void *lds, int r, int g, int ln) {
-        u32x4 *s = (u32x4 *)lds;
-        const int w = threadIdx.x >> 6;
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int fi = w * 4 + f, m = fi >> 2, kk = fi & 3;
-            s[fi * 64 + ln] = q_frag_bf16<KF>(qrow, m, kk, r, g);
-        }
-        q.s = s;
-        q.ln = ln;
-    }
-    template <class Pg>
-    __device__ float logit(const float (&wv)[16], const Pg &P, int g) const {
-        return page_logit_bf16q(q, wv, P, g);
-    }
-};
-
-template <int KF> struct QSource<KF, Q_FP8, false> {
+template <int KF> struct QSource<KF, Q_FP8> {
     QRegFp8 q;
-    __device__ void init(const uint8_t *qrow, void *, int r, int g, int) {
+    __device__ void init(const uint8_t *qrow, int r, int g) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) q.a[m] = q_frag_fp8(qrow, m, r, g);
-    }
-    __device__ float logit(const float (&wv)[16], const PgFp8 &P, int g) const {
-        return page_logit_fp8q(q, wv, P, g);
-    }
-};
-
-template <int KF> struct QSource<KF, Q_FP8, true> {
-    QLdsFp8 q;
-    __device__ void init(const uint8_t *qrow, void *lds, int r, int g, int ln) {
-        i32x8 *s = (i32x8 *)lds;
-        const int m = threadIdx.x >> 6;          // wave m writes fragment m
-        s[m * 64 + ln] = q_frag_fp8(qrow, m, r, g);
-        q.s = s;
-        q.ln = ln;
     }
     __device__ float logit(const float (&wv)[16], const PgFp8 &P, int g) const {
         return page_logit_fp8q(q, wv, P, g);
@@ -334,32 +291,56 @@ __device__ __forceinline__ int resolve_slot(const ScoreArgs &A, int b, int64_t n
     return phys;
 }
 
+// Page stream of one wave: take(P, i) for i = 0 .. n - 1 in order, with the loads of the next
+// NBUF - 1 pages in flight.  fetch(P, i) must be valid (a zero-size load) for i up to
+// n + NBUF - 2, and take(P, i) harmless for i up to the next multiple of NBUF: the loop runs in
+// whole rounds of NBUF so every buffer index is a compile-time constant and the body has no
+// branches around memory operations.
+template <int NBUF, class Pg, class Fetch, class Take>
+__device__ __forceinline__ void stream_pages(int n, Pg (&P)[NBUF], Fetch fetch, Take take) {
+#pragma unroll
+    for (int v = 0; v < NBUF - 1; ++v) fetch(P[v], v);
+    for (int i0 = 0; i0 < n; i0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+            fetch(P[(u + NBUF - 1) % NBUF], i0 + u + NBUF - 1);
+            take(P[u], i0 + u);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- row scoring kernel
 // grid (ceil(n_slots / (4 ppw)), T), 4 waves per workgroup, all on row blockIdx.y; wave w of
-// workgroup x scores slots [(4 x + w) ppw, +ppw), with NBUF - 1 pages loading ahead.
-template <int KF, int QF, int NBUF, bool QLDS>
+// workgroup x scores slots [(4 x + w) ppw, +ppw).  The query fragments stay in registers; pages
+// stream from HBM straight into MFMA operand registers, the next NBUF - 1 pages loading while
+// one is scored (NBUF = 2 for 16-KB bf16 pages, 3 for 8.25-KB fp8 pages).  Slots past the
+// wave's own are empty (nothing read, nothing written); outputs go through a buffer descriptor
+// spanning the output row, so a column past out_ld (or an empty slot's) is dropped by the
+// hardware.
+template <int KF, int QF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
 void score_kernel(ScoreArgs A) {
     typedef typename PageOf<KF>::T Pg;
-    __shared__ __attribute__((aligned(16))) uint8_t q_lds[QLDS ? (QF == Q_FP8 ? 4 * 64 * 32 : 16 * 64 * 16) : 16];
+    __shared__ float s_res[4][kMaxPpw + 4][64];   // logits until the wave's loads are done
     const int t = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int wave = threadIdx.x >> 6;
     const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
+    if (slot0 >= A.n_slots) return;
+    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
     const int braw = row_request(A.q, A.kv, t);
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
-    float *out = A.out + (int64_t)t * A.out_ld;
     const uint8_t *pool = A.kv.pool[0];
     const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * (QF == Q_FP8 ? 1 : 2);
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
 
-    QSource<KF, QF, QLDS> Q;
-    Q.init(qrow, q_lds, r, g, ln);
-    if (QLDS) __syncthreads();
-    if (slot0 >= A.n_slots) return;
-    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
+    QSource<KF, QF> Q;
+    Q.init(qrow, r, g);
 
+    // lane i describes slot i of this wave: physical page (or slot state) and logical page
     int lp_l = -1, phys_l = kSlotEmpty;
     if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
 
@@ -367,41 +348,128 @@ void score_kernel(ScoreArgs A) {
     load_w(wv, A.q.w, A.q.w_bf16, t, g);
     const float qscale = (QF == Q_FP8) ? A.q.q_scale[t] : 1.0f;
 
-    auto fetch = [&](Pg &P, int i) {
-        int phys = __builtin_amdgcn_readlane(phys_l, i);
-        if (phys >= 0) load_page(P, pool + (int64_t)phys * (kPage * PageOf<KF>::row), r, g, ln);
+    auto fetch = [&](Pg &P, int i) {   // i < 64: ppw <= 16, padded by at most NBUF
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        load_page(P, pool, phys, r, g, ln);
     };
-    auto emit = [&](const Pg &P, int i) {
-        int phys = __builtin_amdgcn_readlane(phys_l, i);
-        if (phys == kSlotEmpty) return;
-        int lp = __builtin_amdgcn_readlane(lp_l, i);
-        int64_t s = (int64_t)lp * kPage + ln;
-        int64_t col = (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
-        float v;
-        if (phys >= 0) {
-            v = Q.logit(wv, P, g) * page_scale(P) * qscale;
-            if (s >= nvis) v = -INFINITY;
-        } else if (phys == kSlotInvisible) {
-            v = -INFINITY;
-        } else {
-            v = s < nvis ? __builtin_nanf("") : -INFINITY;
+    auto emit = [&](const Pg &P, int i) {    // logits to LDS; stored after the last load
+        s_res[wave][i][ln] = Q.logit(wv, P, g) * page_scale(P) * qscale;
+    };
+    Pg P[PageOf<KF>::nbuf];
+    stream_pages(nslot, P, fetch, emit);
+    for (int i = 0; i < nslot; ++i) {
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        const int lp = __builtin_amdgcn_readlane(lp_l, i);
+        const int64_t s = (int64_t)lp * kPage + ln;
+        const int64_t col = phys == kSlotEmpty ? A.out_ld
+                          : (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
+        float v = phys >= 0 ? s_res[wave][i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
+        if (s >= nvis) v = -INFINITY;
+        const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------- bf16 decode: tile ring
+// bf16 keys x bf16 queries, the decode shape.  Same work split and output as score_kernel, but
+// built for occupancy, which is what an HBM-bound gather needs: the query fragments (the MFMA A
+// operands, 16 KB per row) sit in LDS, written once by the four waves of the workgroup (they
+// score the same row) and read back per k-step, so a wave needs about 120 VGPRs and four waves
+// share each SIMD.  The unit of the load pipeline is a 16-entry tile (4 KB per wave, 16 VGPRs):
+// a ring of RING tiles keeps RING - 1 tiles loading at every moment, each tile's loads going
+// out as soon as its registers are free.
+struct TileBf16 { u32x4 b[4]; };   // [k-step kk]
+
+template <int RING>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_DECODE_WAVES)))
+void score_bf16_ring_kernel(ScoreArgs A) {
+    __shared__ u32x4 s_q[16][64];        // fragment (m, kk) = 4 m + kk, lane-contiguous
+    __shared__ float s_res[4][kMaxPpw][64];   // each wave's logits until its loads are done
+    const int t = blockIdx.y;
+    const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
+    const int wave = threadIdx.x >> 6;
+    {
+        const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int fi = wave * 4 + f;
+            s_q[fi][ln] = q_frag_bf16<KEY_BF16>(qrow, fi >> 2, fi & 3, r, g);
         }
-        if (col < A.out_ld) out[col] = v;
+    }
+    __syncthreads();
+    const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
+    if (slot0 >= A.n_slots) return;
+    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
+    const int braw = row_request(A.q, A.kv, t);
+    const int64_t nvis = n_visible(A.q, A.kv, t, braw);
+    const int b = braw < 0 ? 0 : braw;
+    const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
+    const uint8_t *pool = A.kv.pool[0];
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
+
+    int lp_l = -1, phys_l = kSlotEmpty;
+    if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
+    float wv[16];
+    load_w(wv, A.q.w, A.q.w_bf16, t, g);
+
+    const uint32_t off = (uint32_t)(r * kRowBf16 + g * 16);
+    auto fetch = [&](TileBf16 &T, int x) {       // tile x: page x / 4, entry tile x % 4
+        const __amdgpu_buffer_rsrc_t rs =
+            page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 2), kPage * kRowBf16);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            T.b[kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + kk * 64, (x & 3) * 16 * kRowBf16, 0);
+    };
+    auto tile_logit = [&](const TileBf16 &T) {
+        // a zero the compiler cannot see through: the query fragments are read from LDS for
+        // every tile instead of being hoisted into registers, which would cost occupancy
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const u32x4 *qs = &s_q[0][ln + z];
+        f32x4 acc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 bk = __builtin_bit_cast(bf16x8, T.b[kk]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, qs[(4 * m + kk) * 64]), bk, acc[m], 0, 0, 0);
+        }
+        return head_sum(acc, wv);
+    };
+    // A page's logits go to LDS; the global stores wait until every load of the wave has been
+    // issued and consumed.  (Vector memory operations complete in issue order, so a store among
+    // the loads would make each later wait for a key tile wait for the store as well.)
+    auto emit = [&](const f32x4 &tot, int i) {   // page slot i: lane = entry, tile g
+        s_res[wave][i][ln] = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
     };
 
-    Pg P[NBUF];
+    // tiles 0 .. 4 nslot - 1 in order; slots past nslot are empty (zero-size loads)
+    TileBf16 T[RING];
 #pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u)
-        if (u < nslot) fetch(P[u], u);
-    for (int i0 = 0; i0 < nslot; i0 += NBUF) {
+    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x0 = 0; x0 < 4 * nslot; x0 += 4 * RING) {
 #pragma unroll
-        for (int u = 0; u < NBUF; ++u) {
-            const int i = i0 + u;
-            if (i < nslot) {
-                if (i + NBUF - 1 < nslot) fetch(P[(u + NBUF - 1) % NBUF], i + NBUF - 1);
-                emit(P[u], i);
-            }
+        for (int u = 0; u < 4 * RING; ++u) {
+            fetch(T[(u + RING - 1) % RING], x0 + u + RING - 1);
+            tot[u & 3] = tile_logit(T[u % RING]);
+            if ((u & 3) == 3) emit(tot, (x0 + u) >> 2);
         }
+    }
+    for (int i = 0; i < nslot; ++i) {
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        const int lp = __builtin_amdgcn_readlane(lp_l, i);
+        const int64_t s = (int64_t)lp * kPage + ln;
+        const int64_t col = phys == kSlotEmpty ? A.out_ld
+                          : (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
+        float v = phys >= 0 ? s_res[wave][i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
+        if (s >= nvis) v = -INFINITY;
+        const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, 0);
     }
 }
 
@@ -450,80 +518,71 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
 
 // ---------------------------------------------------------------- Level-1 mask
 // Union of n_layers encoders per entry (paper summary, section 3, R_t equation; README "Joint
-// checkpoint + ensemble": max or mean of the per-layer sigmoids).  Grid (ceil(n_pages /
-// (4 PPW)), B); each wave owns PPW consecutive pages of request blockIdx.y and walks the layers
-// one after another, keeping the running union of its PPW x 64 entries in registers, and
-// holds the current layer's query fragments in registers.
-template <int KF, int PPW, int NBUF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
+// checkpoint + ensemble": max or mean of the per-layer sigmoids).  Grid (ceil(n_pages / PPW),
+// B), one wave per layer (blockDim = 64 n_layers): wave l streams PPW consecutive pages of
+// request blockIdx.y from pool l with layer l's query fragments in registers, and leaves its
+// logits in LDS; then the workgroup forms the union, the decision and the mask bytes.
+template <int KF, int PPW>
+__global__ __launch_bounds__(64 * FM_MAX_LAYERS) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
 void mask_kernel(MaskArgs A) {
     typedef typename PageOf<KF>::T Pg;
+    constexpr int NB = PageOf<KF>::nbuf;
+    __shared__ float s_u[FM_MAX_LAYERS][PPW + NB][kPage];
     const int b = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
-    const int wave = threadIdx.x >> 6;
-    const int64_t page0 = ((int64_t)blockIdx.x * 4 + wave) * PPW;
-    if (page0 >= A.n_pages) return;
+    const int l = threadIdx.x >> 6;              // this wave's layer
+    const int64_t page0 = (int64_t)blockIdx.x * PPW;
     const int np = (int)min((int64_t)PPW, A.n_pages - page0);
     const int64_t seq = A.kv.seq_lens[b];
-    const float inv_n = 1.0f / (float)A.n_layers;
 
+    // lane i describes page page0 + i (i < np): physical page or state; past np: invisible
     int phys_l = kSlotInvisible;
     if (ln < np) {
-        int64_t lp = page0 + ln;
+        const int64_t lp = page0 + ln;
         if (lp * kPage >= seq) phys_l = kSlotInvisible;
         else if (lp >= A.kv.bt_ld) phys_l = kSlotUnmapped;
         else {
-            int p = A.kv.bt[(int64_t)b * A.kv.bt_ld + lp];
+            const int p = A.kv.bt[(int64_t)b * A.kv.bt_ld + lp];
             phys_l = (p < 0 || p >= A.kv.n_phys) ? kSlotUnmapped : p;
         }
     }
 
-    float u[PPW];
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) u[i] = A.mean_mode ? 0.f : -INFINITY;
-
-    for (int l = 0; l < A.n_layers; ++l) {
+    {
+        const QArgs &QA = A.q[l];
         float wv[16];
-        load_w(wv, A.q[l].w, A.q[l].w_bf16, b, g);
+        load_w(wv, QA.w, QA.w_bf16, b, g);
         const uint8_t *pool = A.kv.pool[l];
-        QSource<KF, Q_BF16, false> Q;       // this layer's query fragments, in registers
-        Q.init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, nullptr, r, g, ln);
-        Pg P[NBUF];
-        auto fetch = [&](Pg &Pp, int i) {
-            int phys = __builtin_amdgcn_readlane(phys_l, i);
-            if (phys >= 0) load_page(Pp, pool + (int64_t)phys * (kPage * PageOf<KF>::row), r, g, ln);
+        QSource<KF, Q_BF16> Q;
+        Q.init((const uint8_t *)QA.q + (int64_t)b * kHeads * kDim * 2, r, g);
+        auto fetch = [&](Pg &P, int i) {
+            load_page(P, pool, __builtin_amdgcn_readlane(phys_l, i), r, g, ln);
         };
-        auto take = [&](const Pg &Pp, int i) {
-            int phys = __builtin_amdgcn_readlane(phys_l, i);
-            float L;
-            if (phys >= 0) L = Q.logit(wv, Pp, g) * page_scale(Pp);
-            else if (phys == kSlotUnmapped) L = __builtin_nanf("");
-            else return;
-            u[i] = A.mean_mode ? u[i] + inv_n / (1.0f + expf(-L))
-                               : ((L != L || u[i] != u[i]) ? __builtin_nanf("") : fmaxf(u[i], L));
+        auto take = [&](const Pg &P, int i) {
+            const int phys = __builtin_amdgcn_readlane(phys_l, i);
+            const float L = Q.logit(wv, P, g) * page_scale(P);
+            s_u[l][i][ln] = phys >= 0 ? L : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
         };
-#pragma unroll
-        for (int v = 0; v < NBUF - 1; ++v)
-            if (v < np) fetch(P[v], v);
-#pragma unroll
-        for (int i = 0; i < PPW; ++i) {
-            if (i < np) {
-                if (i + NBUF - 1 < np) fetch(P[(i + NBUF - 1) % NBUF], i + NBUF - 1);
-                take(P[i % NBUF], i);
-            }
-        }
+        Pg P[NB];
+        stream_pages(np, P, fetch, take);
     }
+    __syncthreads();
 
+    const float inv_n = 1.0f / (float)A.n_layers;
     uint8_t *mrow = A.mask + (int64_t)b * A.mask_ld;
-#pragma unroll
-    for (int i = 0; i < PPW; ++i) {
-        if (i >= np) break;
-        int64_t s = (page0 + i) * kPage + ln;
+    for (int e = threadIdx.x; e < np * kPage; e += blockDim.x) {
+        const int i = e >> 6, x = e & 63;
+        const int64_t s = (page0 + i) * kPage + x;
         if (s >= A.mask_ld) continue;
-        bool valid = s < seq;
-        bool m = valid && (u[i] >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
+        float u = A.mean_mode ? 0.f : -INFINITY;
+        for (int k = 0; k < A.n_layers; ++k) {
+            const float L = s_u[k][i][x];
+            u = A.mean_mode ? u + inv_n / (1.0f + expf(-L))
+                            : ((L != L || u != u) ? __builtin_nanf("") : fmaxf(u, L));
+        }
+        const bool valid = s < seq;
+        const bool m = valid && (u >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
         mrow[s] = m ? 1 : 0;
-        if (A.union_score) A.union_score[(int64_t)b * A.mask_ld + s] = valid ? u[i] : -INFINITY;
+        if (A.union_score) A.union_score[(int64_t)b * A.mask_ld + s] = valid ? u : -INFINITY;
     }
 }
 
@@ -578,14 +637,16 @@ __global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s) {
     dim3 grid((unsigned)((a.n_slots + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)a.q.T);
-    // bf16 pages are 16 KB: the query fragments go to LDS to leave registers for prefetch.
-    // fp8 pages are 8.25 KB: registers hold both, and LDS re-reads would outweigh the page bytes.
-    if (key_fmt == KEY_BF16 && q_fmt == Q_BF16)
-        score_kernel<KEY_BF16, Q_BF16, FM_NBUF_BF16, FM_QLDS != 0><<<grid, 256, 0, s>>>(a);
+    if (key_fmt == KEY_BF16 && q_fmt == Q_BF16) {
+        if (FM_BF16_RING)
+            score_bf16_ring_kernel<FM_BF16_RING ? FM_BF16_RING : 4><<<grid, 256, 0, s>>>(a);
+        else
+            score_kernel<KEY_BF16, Q_BF16><<<grid, 256, 0, s>>>(a);
+    }
     else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16)
-        score_kernel<KEY_FP8, Q_BF16, FM_NBUF_FP8, false><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_FP8, Q_BF16><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_FP8)
-        score_kernel<KEY_FP8, Q_FP8, FM_NBUF_FP8, false><<<grid, 256, 0, s>>>(a);
+        score_kernel<KEY_FP8, Q_FP8><<<grid, 256, 0, s>>>(a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -598,16 +659,17 @@ hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s) {
-    constexpr int PPW = 8;
+    constexpr int PPW = 16;
     if (key_fmt == KEY_F32) {
         dim3 grid((unsigned)((a.mask_ld + 255) / 256), (unsigned)B);
         mask_f32_kernel<<<grid, 256, 0, s>>>(a);
     } else {
-        dim3 grid((unsigned)((a.n_pages + 4 * PPW - 1) / (4 * PPW)), (unsigned)B);
+        dim3 grid((unsigned)((a.n_pages + PPW - 1) / PPW), (unsigned)B);
+        const unsigned threads = 64u * (unsigned)a.n_layers;
         if (key_fmt == KEY_BF16)
-            mask_kernel<KEY_BF16, PPW, 2><<<grid, 256, 0, s>>>(a);
+            mask_kernel<KEY_BF16, PPW><<<grid, threads, 0, s>>>(a);
         else
-            mask_kernel<KEY_FP8, PPW, FM_NBUF_MASK><<<grid, 256, 0, s>>>(a);
+            mask_kernel<KEY_FP8, PPW><<<grid, threads, 0, s>>>(a);
     }
     return hipGetLastError();
 }
