@@ -32,6 +32,9 @@
 #ifndef FM_BF16_RING
 #define FM_BF16_RING 4
 #endif
+#ifndef FM_F8_RING
+#define FM_F8_RING 4
+#endif
 #ifndef FM_DECODE_WAVES
 #define FM_DECODE_WAVES 4
 #endif
@@ -473,6 +476,147 @@ void score_bf16_ring_kernel(ScoreArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- fp8 keys x bf16 queries
+// 32-entry tiles on v_mfma_f32_32x32x16_bf16 (the 16x16x32 bf16 MFMA of gfx950 runs at half
+// that rate, and fp8 pages carry twice the entries per byte of bf16 ones, so here the matrix
+// core time matters).  Lane l = j + 32 h of a tile holds key entry j's codes 64 h .. 64 h + 63
+// (four 16-byte loads; 132-byte rows are 4-byte aligned) and its scale; k-step s takes the
+// 8 codes 8 s .. 8 s + 7 of that half, widened to bf16 (exact), against query dims
+// 64 h + 8 s .. + 8 of head 32 m + j (A operand, head tile m = 0, 1).  The accumulator register
+// v of lane j + 32 h is head 32 m + 8 (v / 4) + 4 h + v % 4 for entry j, so a lane sums its 32
+// heads with their weights and one row swap with lane j + 32 (1 - h) completes the 64.
+struct TileF8 { u32x4 c[4]; float scale; };
+
+struct QF8Ops {                     // one query row as A operands, and its weights
+    u32x4 a[2][8];                  // [head tile m][k-step s]
+    float w[2][16];                 // [m][accumulator register v]
+    __device__ void init(const uint8_t *qrow, const void *wp, int w_bf16, int t, int ln) {
+        const int j = ln & 31, h = ln >> 5;
+        const uint16_t *q = (const uint16_t *)qrow;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int st = 0; st < 8; ++st) a[m][st] = *(const u32x4 *)(q + (32 * m + j) * kDim + 64 * h + 8 * st);
+        const int64_t base = (int64_t)t * kHeads + 4 * h;
+        if (w_bf16) {
+            const uint16_t *w16 = (const uint16_t *)wp + base;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) w[m][v] = bf16f(w16[32 * m + 8 * (v >> 2) + (v & 3)]);
+        } else {
+            const float *w32 = (const float *)wp + base;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) w[m][v] = w32[32 * m + 8 * (v >> 2) + (v & 3)];
+        }
+    }
+};
+
+// tile (page slot, half) of a page through its buffer descriptor (zero-size: nothing read)
+__device__ __forceinline__ void load_tile_f8(TileF8 &T, const __amdgpu_buffer_rsrc_t &rs, int half, int ln) {
+    const uint32_t row = (uint32_t)((32 * half + (ln & 31)) * kRowFp8);
+    const uint32_t off = row + 64 * (ln >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0);
+    T.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, row + kDim, 0, 0));
+}
+
+// logit of entry (lane % 32) of the tile, scale applied; both lane halves return it
+__device__ __forceinline__ float tile_logit_f8(const QF8Ops &Q, const TileF8 &T) {
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    f32x16 acc[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        const uint32_t d0 = T.c[st >> 1][(st & 1) * 2], d1 = T.c[st >> 1][(st & 1) * 2 + 1];
+        u32x4 bw;
+        bw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
+        bw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
+        bw[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
+        bw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, Q.a[m][st]), b, acc[m], 0, 0, 0);
+    }
+    float p = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p = fmaf(Q.w[m][v], fmaxf(acc[m][v], 0.f), p);
+    const uint32_t u = __float_as_uint(p);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * T.scale;
+}
+
+// Tile stream of one wave over page slots 0 .. n - 1 (two tiles a page): fetch(T, x) loads
+// tile x, take(tot0, tot1, i) receives page slot i's two tile results.  A ring of RING tiles
+// keeps RING - 1 loading; fetch must be a valid (zero-size) load past the wave's pages.
+template <int RING, class Fetch, class Take>
+__device__ __forceinline__ void stream_tiles_f8(int n, const QF8Ops &Q, Fetch fetch, Take take) {
+    static_assert(RING % 2 == 0, "the ring holds whole pages");
+    TileF8 T[RING];
+#pragma unroll
+    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+    float t0 = 0.f;
+    for (int x0 = 0; x0 < 2 * n; x0 += 2 * RING) {
+#pragma unroll
+        for (int u = 0; u < 2 * RING; ++u) {
+            fetch(T[(u + RING - 1) % RING], x0 + u + RING - 1);
+            const float tl = tile_logit_f8(Q, T[u % RING]);
+            if (u & 1) take(t0, tl, (x0 + u) >> 1);
+            else t0 = tl;
+        }
+    }
+}
+
+// Two-level (and any bf16-query) scoring over fp8 pages: the work split, slot states and
+// deferred stores of score_kernel, with the tile stream above.
+template <int RING>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
+void score_f8_kernel(ScoreArgs A) {
+    __shared__ float s_res[4][kMaxPpw + RING][64];
+    const int t = blockIdx.y;
+    const int ln = __lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
+    if (slot0 >= A.n_slots) return;
+    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
+    const int braw = row_request(A.q, A.kv, t);
+    const int64_t nvis = n_visible(A.q, A.kv, t, braw);
+    const int b = braw < 0 ? 0 : braw;
+    const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
+    const uint8_t *pool = A.kv.pool[0];
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
+    int lp_l = -1, phys_l = kSlotEmpty;
+    if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
+    QF8Ops Q;
+    Q.init((const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2, A.q.w, A.q.w_bf16, t, ln);
+
+    auto fetch = [&](TileF8 &T, int x) {
+        load_tile_f8(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);
+    };
+    auto take = [&](float t0, float t1, int i) { s_res[wave][i][ln] = (ln >> 5) ? t1 : t0; };
+    stream_tiles_f8<RING>(nslot, Q, fetch, take);
+    for (int i = 0; i < nslot; ++i) {
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        const int lp = __builtin_amdgcn_readlane(lp_l, i);
+        const int64_t s = (int64_t)lp * kPage + ln;
+        const int64_t col = phys == kSlotEmpty ? A.out_ld
+                          : (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
+        float v = phys >= 0 ? s_res[wave][i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
+        if (s >= nvis) v = -INFINITY;
+        const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------- fp32 path (VALU)
 // One thread per output column; fp32 products and sums.  For fp32 inputs only.
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
@@ -527,7 +671,7 @@ __global__ __launch_bounds__(64 * FM_MAX_LAYERS) __attribute__((amdgpu_waves_per
 void mask_kernel(MaskArgs A) {
     typedef typename PageOf<KF>::T Pg;
     constexpr int NB = PageOf<KF>::nbuf;
-    __shared__ float s_u[FM_MAX_LAYERS][PPW + NB][kPage];
+    __shared__ float s_u[FM_MAX_LAYERS][PPW + FM_F8_RING][kPage];
     const int b = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int l = threadIdx.x >> 6;              // this wave's layer
@@ -547,7 +691,21 @@ void mask_kernel(MaskArgs A) {
         }
     }
 
-    {
+    if constexpr (KF == KEY_FP8) {
+        const QArgs &QA = A.q[l];
+        const uint8_t *pool = A.kv.pool[l];
+        QF8Ops Q;
+        Q.init((const uint8_t *)QA.q + (int64_t)b * kHeads * kDim * 2, QA.w, QA.w_bf16, b, ln);
+        auto fetch = [&](TileF8 &T, int x) {
+            load_tile_f8(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);
+        };
+        auto take = [&](float t0, float t1, int i) {
+            const int phys = __builtin_amdgcn_readlane(phys_l, i);
+            const float L = (ln >> 5) ? t1 : t0;
+            s_u[l][i][ln] = phys >= 0 ? L : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
+        };
+        stream_tiles_f8<FM_F8_RING>(np, Q, fetch, take);
+    } else {
         const QArgs &QA = A.q[l];
         float wv[16];
         load_w(wv, QA.w, QA.w_bf16, b, g);
@@ -644,7 +802,7 @@ hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t 
             score_kernel<KEY_BF16, Q_BF16><<<grid, 256, 0, s>>>(a);
     }
     else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16)
-        score_kernel<KEY_FP8, Q_BF16><<<grid, 256, 0, s>>>(a);
+        score_f8_kernel<FM_F8_RING><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_FP8)
         score_kernel<KEY_FP8, Q_FP8><<<grid, 256, 0, s>>>(a);
     else

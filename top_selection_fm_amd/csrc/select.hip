@@ -27,6 +27,13 @@
 
 #include "fm_internal.h"
 
+#ifndef FM_TOPK_U
+#define FM_TOPK_U 4
+#endif
+#ifndef FM_TOPK_STAGE_MIN
+#define FM_TOPK_STAGE_MIN 4096
+#endif
+
 namespace fm {
 namespace {
 
@@ -358,7 +365,7 @@ __device__ uint32_t filter_range(const RowSrc &R, int64_t j0, int64_t j1, const 
     __syncthreads();
     const uint64_t lt = (ln == 0) ? 0ull : (~0ull >> (64 - ln));
     const bool vec = !R.rp && ((uintptr_t)(R.row + j0) % 16 == 0);
-    constexpr int U = 4;
+    constexpr int U = FM_TOPK_U;
     for (int64_t base = j0; base < j1; base += (int64_t)NT * U * 4) {
         float v[U][4];
 #pragma unroll
@@ -720,7 +727,7 @@ __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
 }  // namespace
 
 size_t topk_ws_bytes(int T, int64_t n) {
-    if (T <= 0 || n <= kBuf || n > (int64_t)kTopkMaxChunks * kTopkChunk) return 0;
+    if (T <= 0 || n <= FM_TOPK_STAGE_MIN || n > (int64_t)kTopkMaxChunks * kTopkChunk) return 0;
     const size_t slots = (size_t)T * (size_t)((n + kTopkChunk - 1) / kTopkChunk);
     return align_up(slots * kTopkCap * sizeof(float), 256) +
            align_up(slots * kTopkCap * sizeof(int32_t), 256) + align_up(slots * sizeof(int32_t), 256);
