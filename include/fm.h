@@ -23,7 +23,9 @@
  *     allocates, frees, or keeps a pointer after the call returns.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
  *     asynchronously; nothing synchronises the host.  Buffers must stay alive until the
- *     stream reaches the work.  Calls are stateless and thread-safe.
+ *     stream reaches the work.  Calls are stateless and thread-safe; a workspace needs no
+ *     clearing, but work of two calls that may run at the same time on the GPU (different
+ *     streams) must not share one.
  *   - Errors are detected on the host before anything is enqueued; on error nothing is
  *     launched and fm_last_error() (per thread) describes the problem.  No exception crosses
  *     the ABI.

@@ -111,6 +111,28 @@ def test_topk_sampled_cut_and_its_fallbacks(workspace):
     assert np.array_equal(vg[ri >= 0], rv[ri >= 0].astype(np.float32))
 
 
+def test_topk_workspace_reused_and_dirty():
+    """One workspace serves consecutive calls of different shapes and data, starting from
+    arbitrary bytes: nothing in it has to be cleared between calls."""
+    rng = np.random.default_rng(21)
+    nb = api.fm_workspace_bytes(api.FM_OP_TOPK, 6, 70000)
+    for fill in (0xFF, None, 0x00):
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        if fill is None:
+            ws.copy_(torch.from_numpy(rng.integers(0, 256, nb, dtype=np.uint8)))
+        else:
+            ws.fill_(fill)
+        for T, n in ((6, 70000), (3, 20000), (6, 70000), (5, 8193)):
+            L = constructed_rows(rng, 8, n)[:T].copy()
+            Lt = torch.from_numpy(L).cuda()
+            idx = torch.empty((T, 512), dtype=torch.int32, device="cuda")
+            need = api.fm_workspace_bytes(api.FM_OP_TOPK, T, n)
+            assert need <= nb
+            api.fm_topk512(Lt, n, T, None, None, 0, None, 512, idx, None, ws, nb)
+            ri, _ = ref_topk(L, 512)
+            assert np.array_equal(idx.cpu().numpy(), ri), (fill, T, n)
+
+
 def test_scoring_is_deterministic_and_placement_invariant():
     wl = W.decode_bf16(seed=3001, B=4, seq_len=64 * 33 + 9, ragged=True)
     dw = api.DeviceWorkload(wl, "cuda:0")

@@ -487,31 +487,69 @@ void score_bf16_ring_kernel(ScoreArgs A) {
 // heads with their weights and one row swap with lane j + 32 (1 - h) completes the 64.
 struct TileF8 { u32x4 c[4]; float scale; };
 
-struct QF8Ops {                     // one query row as A operands, and its weights
-    u32x4 a[2][8];                  // [head tile m][k-step s]
-    float w[2][16];                 // [m][accumulator register v]
-    __device__ void init(const uint8_t *qrow, const void *wp, int w_bf16, int t, int ln) {
-        const int j = ln & 31, h = ln >> 5;
-        const uint16_t *q = (const uint16_t *)qrow;
+// one query row's head weights for the 32x32 accumulator layout: w[m][v] is head
+// 32 m + 8 (v / 4) + 4 h + v % 4 of lane j + 32 h
+__device__ __forceinline__ void load_w32(float (&w)[2][16], const void *wp, int w_bf16, int t, int ln) {
+    const int64_t base = (int64_t)t * kHeads + 4 * (ln >> 5);
+    if (w_bf16) {
+        const uint16_t *w16 = (const uint16_t *)wp + base;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int st = 0; st < 8; ++st) a[m][st] = *(const u32x4 *)(q + (32 * m + j) * kDim + 64 * h + 8 * st);
-        const int64_t base = (int64_t)t * kHeads + 4 * h;
-        if (w_bf16) {
-            const uint16_t *w16 = (const uint16_t *)wp + base;
+            for (int v = 0; v < 16; ++v) w[m][v] = bf16f(w16[32 * m + 8 * (v >> 2) + (v & 3)]);
+    } else {
+        const float *w32 = (const float *)wp + base;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) w[m][v] = bf16f(w16[32 * m + 8 * (v >> 2) + (v & 3)]);
-        } else {
-            const float *w32 = (const float *)wp + base;
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) w[m][v] = w32[32 * m + 8 * (v >> 2) + (v & 3)];
-        }
+            for (int v = 0; v < 16; ++v) w[m][v] = w32[32 * m + 8 * (v >> 2) + (v & 3)];
     }
+}
+
+// A operand (m, k-step s) of lane j + 32 h: dims 64 h + 8 s .. + 8 of head 32 m + j
+__device__ __forceinline__ u32x4 qa_frag(const uint8_t *qrow, int m, int st, int ln) {
+    return *(const u32x4 *)((const uint16_t *)qrow + (32 * m + (ln & 31)) * kDim + 64 * (ln >> 5) + 8 * st);
+}
+
+// One query row with its A operands in LDS, shared by the four waves of a workgroup that
+// score the same row (each wave writes 4 of the 16 fragments; the caller synchronises the
+// workgroup before the first use), and its weights in registers.
+struct QF8Lds {
+    const u32x4 *a;                 // [8 m + s][lane]
+    float w[2][16];
+    __device__ void init(u32x4 *lds, const uint8_t *qrow, const void *wp, int w_bf16, int t, int ln) {
+        const int wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int fi = 4 * wave + f;
+            lds[fi * 64 + ln] = qa_frag(qrow, fi >> 3, fi & 7, ln);
+        }
+        a = lds;
+        load_w32(w, wp, w_bf16, t, ln);
+    }
+    // fragments of one tile; the opaque zero keeps them from being hoisted into registers
+    // across tiles, which would cost occupancy
+    __device__ __forceinline__ const u32x4 *frags() const {
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        return a + __lane_id() + z;
+    }
+    __device__ __forceinline__ u32x4 get(const u32x4 *f, int m, int st) const { return f[(8 * m + st) * 64]; }
+};
+
+// The same with the A operands in registers (one wave per row).
+struct QF8Reg {
+    u32x4 a[2][8];
+    float w[2][16];
+    __device__ void init(const uint8_t *qrow, const void *wp, int w_bf16, int t, int ln) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int st = 0; st < 8; ++st) a[m][st] = qa_frag(qrow, m, st, ln);
+        load_w32(w, wp, w_bf16, t, ln);
+    }
+    __device__ __forceinline__ const u32x4 *frags() const { return nullptr; }
+    __device__ __forceinline__ u32x4 get(const u32x4 *, int m, int st) const { return a[m][st]; }
 };
 
 // tile (page slot, half) of a page through its buffer descriptor (zero-size: nothing read)
@@ -524,8 +562,10 @@ __device__ __forceinline__ void load_tile_f8(TileF8 &T, const __amdgpu_buffer_rs
 }
 
 // logit of entry (lane % 32) of the tile, scale applied; both lane halves return it
-__device__ __forceinline__ float tile_logit_f8(const QF8Ops &Q, const TileF8 &T) {
+template <class QF>
+__device__ __forceinline__ float tile_logit_f8(const QF &Q, const TileF8 &T) {
     typedef float f32x16 __attribute__((ext_vector_type(16)));
+    const u32x4 *qf = Q.frags();
     f32x16 acc[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -542,7 +582,7 @@ __device__ __forceinline__ float tile_logit_f8(const QF8Ops &Q, const TileF8 &T)
         const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, Q.a[m][st]), b, acc[m], 0, 0, 0);
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, Q.get(qf, m, st)), b, acc[m], 0, 0, 0);
     }
     float p = 0.f;
 #pragma unroll
@@ -557,8 +597,8 @@ __device__ __forceinline__ float tile_logit_f8(const QF8Ops &Q, const TileF8 &T)
 // Tile stream of one wave over page slots 0 .. n - 1 (two tiles a page): fetch(T, x) loads
 // tile x, take(tot0, tot1, i) receives page slot i's two tile results.  A ring of RING tiles
 // keeps RING - 1 loading; fetch must be a valid (zero-size) load past the wave's pages.
-template <int RING, class Fetch, class Take>
-__device__ __forceinline__ void stream_tiles_f8(int n, const QF8Ops &Q, Fetch fetch, Take take) {
+template <int RING, class QF, class Fetch, class Take>
+__device__ __forceinline__ void stream_tiles_f8(int n, const QF &Q, Fetch fetch, Take take) {
     static_assert(RING % 2 == 0, "the ring holds whole pages");
     TileF8 T[RING];
 #pragma unroll
@@ -578,12 +618,16 @@ __device__ __forceinline__ void stream_tiles_f8(int n, const QF8Ops &Q, Fetch fe
 // Two-level (and any bf16-query) scoring over fp8 pages: the work split, slot states and
 // deferred stores of score_kernel, with the tile stream above.
 template <int RING>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void score_f8_kernel(ScoreArgs A) {
     __shared__ float s_res[4][kMaxPpw + RING][64];
+    __shared__ u32x4 s_qa[16 * 64];
     const int t = blockIdx.y;
     const int ln = __lane_id();
     const int wave = threadIdx.x >> 6;
+    QF8Lds Q;
+    Q.init(s_qa, (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2, A.q.w, A.q.w_bf16, t, ln);
+    __syncthreads();
     const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
     if (slot0 >= A.n_slots) return;
     const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
@@ -596,8 +640,6 @@ void score_f8_kernel(ScoreArgs A) {
         (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
     int lp_l = -1, phys_l = kSlotEmpty;
     if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
-    QF8Ops Q;
-    Q.init((const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2, A.q.w, A.q.w_bf16, t, ln);
 
     auto fetch = [&](TileF8 &T, int x) {
         load_tile_f8(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);
@@ -694,7 +736,7 @@ void mask_kernel(MaskArgs A) {
     if constexpr (KF == KEY_FP8) {
         const QArgs &QA = A.q[l];
         const uint8_t *pool = A.kv.pool[l];
-        QF8Ops Q;
+        QF8Reg Q;
         Q.init((const uint8_t *)QA.q + (int64_t)b * kHeads * kDim * 2, QA.w, QA.w_bf16, b, ln);
         auto fetch = [&](TileF8 &T, int x) {
             load_tile_f8(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);

@@ -516,25 +516,42 @@ __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uin
     }
 }
 
-// Stage 1 of the workspace path: grid (n_chunks, T).  Every chunk of a long row recomputes the
-// row's cut from the same sample (identical result in every workgroup) and filters its own
-// kTopkChunk entries into its workspace slot.
-__global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, TopkWs W) {
+// Shared memory of a row cut and a chunk filter (the sample, the cut's histogram, reductions).
+struct CutLds {
+    float sample[kSample];
+    uint32_t hist[kBins];
+    uint32_t sh[kTopkThreads / 64 + 1];
+    uint32_t misc[2];
+    float shf[kTopkThreads / 64];
+    uint32_t s_count;
+};
+
+// Shared memory of a final selection.  The cut's sample aliases bval, which is filled only
+// after the cut is known.
+struct TopkLds {
+    float bval[kBuf];
+    int32_t bent[kBuf];
+    uint32_t hist[kBins];
+    uint32_t sh[kTopkThreads / 64 + 1];
+    uint32_t misc[2];
+    float shf[kTopkThreads / 64];
+    uint32_t s_count;
+    int32_t sel_idx[FM_MAX_K];
+    float sel_val[FM_MAX_K];
+    int32_t bnd[kBnd];
+    uint32_t cnt2[2];
+    uint32_t offs[kTopkMaxChunks + 1];
+};
+static_assert(kSample <= kBuf, "the sample fits the candidate buffer");
+
+// Filter one kTopkChunk-entry chunk of row t into its workspace slot: every chunk of a long row
+// recomputes the row's cut from the same sample (identical result in every workgroup).
+__device__ void filter_chunk(const TopkArgs &A, const TopkWs &W, const RowSrc &R, int c, int t,
+                             CutLds &L) {
     constexpr int NT = kTopkThreads;
     static_assert(kTopkChunk == NT * 16, "one chunk = 16 values per thread");
-    __shared__ float sval[kSample];
-    __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t sh[NT / 64 + 1];
-    __shared__ uint32_t misc[2];
-    __shared__ float shf[NT / 64];
-    __shared__ uint32_t s_count;
-    const int c = blockIdx.x, t = blockIdx.y, tid = threadIdx.x, ln = __lane_id();
-    const RowSrc R = row_source(A, t);
+    const int tid = threadIdx.x, ln = __lane_id();
     const int64_t slot = (int64_t)t * W.n_chunks + c;
-    if (R.n <= kBuf) {                  // the select kernel handles short rows on its own
-        if (tid == 0) W.cnt[slot] = 0;
-        return;
-    }
     // the chunk's 16 values per thread are requested first and stay in flight while the cut
     // is computed from the sample (element j = j0 + 4 (u NT + tid) + e)
     const int64_t j0 = (int64_t)c * kTopkChunk, j1 = min(j0 + kTopkChunk, R.n);
@@ -551,8 +568,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, T
             for (int e = 0; e < 4; ++e) v[u][e] = (j + e < j1) ? R.row[j + e] : -INFINITY;
         }
     }
-    const Cut cut = row_cut<NT>(R, (uint32_t)A.k, sval, hist, sh, misc, shf);
-    if (tid == 0) s_count = 0u;
+    const Cut cut = row_cut<NT>(R, (uint32_t)A.k, L.sample, L.hist, L.sh, L.misc, L.shf);
+    if (tid == 0) L.s_count = 0u;
     __syncthreads();
     float *bv = W.val + slot * kTopkCap;
     int32_t *be = W.idx + slot * kTopkCap;
@@ -573,7 +590,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, T
             if (mask) {
                 const int leader = (int)__builtin_ctzll(mask);
                 uint32_t b0 = 0;
-                if (ln == leader) b0 = atomicAdd(&s_count, (uint32_t)__popcll(mask));
+                if (ln == leader) b0 = atomicAdd(&L.s_count, (uint32_t)__popcll(mask));
                 b0 = __shfl(b0, leader);
                 const uint32_t pos = b0 + (uint32_t)__popcll(mask & lt);
                 if (hit && pos < (uint32_t)kTopkCap) {
@@ -583,50 +600,36 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, T
             }
         }
     __syncthreads();
-    if (tid == 0) W.cnt[slot] = cut.b < 0 ? (int32_t)(kTopkCap + 1) : (int32_t)s_count;
+    if (tid == 0) W.cnt[slot] = cut.b < 0 ? (int32_t)(kTopkCap + 1) : (int32_t)L.s_count;
 }
 
-// Final selection, one workgroup per row.  With stage-1 survivors (W != null and a long row)
-// the buffer is filled from the workspace; otherwise the workgroup cuts and filters the row
-// itself.  When the cut did not hold (fewer than k passed) or the buffer overflowed, the exact
-// selection runs over the whole row.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs A, TopkWs W, int has_ws) {
+// Final selection of row t.  With stage-1 survivors (staged) the buffer is filled from the
+// workspace; otherwise the workgroup cuts and filters the row itself.  When the cut did not hold
+// (fewer than k passed) or the buffer overflowed, the exact selection runs over the whole row.
+__device__ void select_row(const TopkArgs &A, const TopkWs &W, bool staged, const RowSrc &R, int t,
+                           TopkLds &L) {
     constexpr int NT = kTopkThreads;
-    __shared__ float bval[kBuf];
-    __shared__ int32_t bent[kBuf];
-    __shared__ uint32_t hist[kBins];
-    __shared__ uint32_t sh[NT / 64 + 1];
-    __shared__ uint32_t misc[2];
-    __shared__ float shf[NT / 64];
-    __shared__ uint32_t s_count;
-    __shared__ int32_t sel_idx[FM_MAX_K];
-    __shared__ float sel_val[FM_MAX_K];
-    __shared__ int32_t bnd[kBnd];
-    __shared__ uint32_t cnt2[2];
-    __shared__ uint32_t offs[kTopkMaxChunks + 1];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const RowSrc R = row_source(A, t);
+    const int tid = threadIdx.x;
     const uint32_t k = (uint32_t)A.k;
-
     bool from_buf;
     uint32_t total = 0;
-    if (has_ws && R.n > kBuf) {
+    if (staged) {
         // survivors of the row's chunks: offsets first, then one round of loads
         const int64_t base = (int64_t)t * W.n_chunks;
         if (tid == 0) {
             uint32_t acc = 0, over = 0;
             for (int c = 0; c < W.n_chunks; ++c) {
                 const uint32_t n = (uint32_t)W.cnt[base + c];
-                offs[c] = acc;
+                L.offs[c] = acc;
                 over |= n > (uint32_t)kTopkCap;
                 acc += n;
             }
-            offs[W.n_chunks] = acc;
-            misc[0] = over;
+            L.offs[W.n_chunks] = acc;
+            L.misc[0] = over;
         }
         __syncthreads();
-        total = offs[W.n_chunks];
-        from_buf = !misc[0] && total >= k && total <= (uint32_t)kBuf;
+        total = L.offs[W.n_chunks];
+        from_buf = !L.misc[0] && total >= k && total <= (uint32_t)kBuf;
         __syncthreads();
         if (from_buf) {
             constexpr int U = kBuf / NT;
@@ -639,9 +642,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs A, TopkWs W
                     int lo = 0, hi = W.n_chunks;            // offs[lo] <= g < offs[hi]
                     while (hi - lo > 1) {
                         const int mid = (lo + hi) >> 1;
-                        if (offs[mid] <= g) lo = mid; else hi = mid;
+                        if (L.offs[mid] <= g) lo = mid; else hi = mid;
                     }
-                    const int64_t at = (base + lo) * kTopkCap + (g - offs[lo]);
+                    const int64_t at = (base + lo) * kTopkCap + (g - L.offs[lo]);
                     xv[u] = W.val[at];
                     xe[u] = W.idx[at];
                 }
@@ -650,31 +653,54 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs A, TopkWs W
             for (int u = 0; u < U; ++u) {
                 const uint32_t g = tid + u * NT;
                 if (g < total) {
-                    bval[g] = xv[u];
-                    bent[g] = xe[u];
+                    L.bval[g] = xv[u];
+                    L.bent[g] = xe[u];
                 }
             }
         }
         __syncthreads();
     } else {
-        const Cut cut = row_cut<NT>(R, k, bval, hist, sh, misc, shf);
-        total = filter_range<NT>(R, 0, R.n, cut, bval, bent, kBuf, &s_count);
+        const Cut cut = row_cut<NT>(R, k, L.bval, L.hist, L.sh, L.misc, L.shf);
+        total = filter_range<NT>(R, 0, R.n, cut, L.bval, L.bent, kBuf, &L.s_count);
         from_buf = total <= (uint32_t)kBuf && !(cut.b >= 0 && total < k);
     }
 
     int32_t *oi = A.out_idx + (int64_t)t * A.k;
     float *ov = A.out_val ? A.out_val + (int64_t)t * A.k : nullptr;
     if (from_buf) {
-        select_buffer<NT>(bval, bent, (int)total, k, hist, sh, misc, shf, bnd, sel_idx, sel_val,
-                          cnt2, oi, ov, A.k);
+        select_buffer<NT>(L.bval, L.bent, (int)total, k, L.hist, L.sh, L.misc, L.shf, L.bnd,
+                          L.sel_idx, L.sel_val, L.cnt2, oi, ov, A.k);
     } else {
-        const Rule rule = radix_rule<NT>(R, k, hist, sh, misc);
-        if (tid == 0) s_count = 0u;
+        const Rule rule = radix_rule<NT>(R, k, L.hist, L.sh, L.misc);
+        if (tid == 0) L.s_count = 0u;
         __syncthreads();
-        gather<NT>(R, rule, sel_val, sel_idx, &s_count, FM_MAX_K);
+        gather<NT>(R, rule, L.sel_val, L.sel_idx, &L.s_count, FM_MAX_K);
         __syncthreads();
-        sort_and_write<NT>(sel_idx, sel_val, (int)min(s_count, k), A.k, oi, ov);
+        sort_and_write<NT>(L.sel_idx, L.sel_val, (int)min(L.s_count, k), A.k, oi, ov);
     }
+}
+
+// Stage 1 of the workspace path: grid (n_chunks, T), one workgroup per kTopkChunk-entry chunk
+// of a long row.  A chunk past its row's end records no survivors.
+__global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, TopkWs W) {
+    __shared__ CutLds L;
+    const int c = blockIdx.x, t = blockIdx.y;
+    const RowSrc R = row_source(A, t);
+    if (R.n <= kBuf) return;                 // short rows: stage 2 selects them directly
+    if ((int64_t)c * kTopkChunk >= R.n) {
+        if (threadIdx.x == 0) W.cnt[(int64_t)t * W.n_chunks + c] = 0;
+        return;
+    }
+    filter_chunk(A, W, R, c, t, L);
+}
+
+// Stage 2: one workgroup per row selects from the chunks' survivors (rows longer than kBuf
+// with a workspace) or from the row itself.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs A, TopkWs W, int staged) {
+    __shared__ TopkLds L;
+    const int t = blockIdx.x;
+    const RowSrc R = row_source(A, t);
+    select_row(A, W, staged && R.n > kBuf, R, t, L);
 }
 
 // ---------------------------------------------------------------- page compaction
@@ -748,14 +774,12 @@ TopkWs topk_ws_carve(void *ws, int T, int64_t n) {
 }
 
 hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s) {
-    TopkWs W{};
     if (ws) {
-        W = *ws;
-        topk_filter_kernel<<<dim3((unsigned)W.n_chunks, (unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, W);
+        topk_filter_kernel<<<dim3((unsigned)ws->n_chunks, (unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, *ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    topk_kernel<<<dim3((unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, W, ws ? 1 : 0);
+    topk_kernel<<<dim3((unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, ws ? *ws : TopkWs{}, ws ? 1 : 0);
     return hipGetLastError();
 }
 
