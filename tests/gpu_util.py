@@ -69,7 +69,7 @@ def score_resident(dw, k=512, resident_pages=None, n_resident=None, replica=0):
 
 
 def resident_mask(dw, mode=api.FM_UNION_MAX, threshold=0.5, n_sink=0, n_recent=0,
-                  mask_ld=None, layers=None):
+                  mask_ld=None, layers=None, with_union=True):
     layers = list(range(len(dw.wl.queries))) if layers is None else layers
     B = dw.wl.kv.B
     mask_ld = dw.wl.kv.block_table.shape[1] * 64 if mask_ld is None else mask_ld
@@ -79,7 +79,8 @@ def resident_mask(dw, mode=api.FM_UNION_MAX, threshold=0.5, n_sink=0, n_recent=0
                page_count=torch.empty(B, dtype=torch.int32, device=dev),
                page_list=torch.empty((B, n_pages), dtype=torch.int32, device=dev),
                page_density=torch.empty((B, n_pages), dtype=torch.int32, device=dev),
-               union=torch.empty((B, mask_ld), dtype=torch.float32, device=dev))
+               union=torch.empty((B, mask_ld), dtype=torch.float32, device=dev)
+               if with_union else None)
     api.fm_resident_mask([dw.query(l) for l in layers], dw.kv(0, layers), mode, threshold,
                          n_sink, n_recent, out["mask"], mask_ld, out["page_count"],
                          out["page_list"], n_pages, out["page_density"], out["union"])

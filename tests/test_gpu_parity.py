@@ -173,6 +173,20 @@ def test_mask_single_layer_and_short_mask_ld(mask_small):
         assert np.array_equal(m["page_count"].cpu().numpy(), r["page_count"])
 
 
+@pytest.mark.parametrize("mode", ["max", "mean"])
+def test_mask_two_layers(mask_small, mode):
+    wl = mask_small
+    dw = dev(wl)
+    um = api.FM_UNION_MAX if mode == "max" else api.FM_UNION_MEAN
+    m = G.resident_mask(dw, mode=um, layers=[2, 0])
+    r = oracle.resident_mask(wl, mode=mode, layers=[2, 0])
+    dis, _ = G.check_mask(m["mask"].cpu().numpy(), r["mask"], r["union"],
+                          0.0 if mode == "max" else 0.5, wl.kv.seq_lens, f"mask layers 2,0 {mode}")
+    if dis == 0:
+        assert np.array_equal(m["page_count"].cpu().numpy(), r["page_count"])
+        assert np.array_equal(m["page_list"].cpu().numpy(), r["page_list"])
+
+
 @pytest.fixture(scope="module")
 def mask_full():
     return W.three_layer_mask_fp8()
@@ -181,7 +195,7 @@ def mask_full():
 def test_mask_fp8_full(mask_full):
     wl = mask_full
     dw = dev(wl)
-    m = G.resident_mask(dw)
+    m = G.resident_mask(dw, with_union=False)      # as timed: no debug union output
     torch.cuda.synchronize()
     r = oracle.resident_mask(wl)
     dis, band = G.check_mask(m["mask"].cpu().numpy(), r["mask"], r["union"], 0.0,

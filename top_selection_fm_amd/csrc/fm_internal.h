@@ -80,6 +80,7 @@ struct MaskArgs {
     int64_t mask_ld;
     float *union_score;  // nullable
     int64_t n_pages;     // ceil(mask_ld / 64)
+    int ppw;             // pages per wave (set by the launcher)
 };
 
 struct CompactArgs {

@@ -41,6 +41,27 @@
 #ifndef FM_WAVES_PER_EU
 #define FM_WAVES_PER_EU 2
 #endif
+#ifndef FM_QLDS_AHEAD
+#define FM_QLDS_AHEAD 2   // two-level: A fragments read ahead from LDS
+#endif
+#ifndef FM_MASK_AHEAD
+#define FM_MASK_AHEAD 6   // fp8 mask: A fragments read ahead from LDS
+#endif
+#ifndef FM_MASK_RESIDENT
+#define FM_MASK_RESIDENT 2048   // fp8 mask: waves to spread the pages over (2 a SIMD)
+#endif
+#ifndef FM_MASK_RING
+#define FM_MASK_RING 4    // fp8 mask: tiles in the load ring
+#endif
+#ifndef FM_MASK_WPE
+#define FM_MASK_WPE 2     // fp8 mask: waves per SIMD the registers are sized for
+#endif
+#ifndef FM_MASK_MAXPPW
+#define FM_MASK_MAXPPW 16
+#endif
+#ifndef FM_MASK_F8
+#define FM_MASK_F8 1   // fp8 mask: layers-per-wave kernel (0: one wave per layer)
+#endif
 
 namespace fm {
 namespace {
@@ -55,6 +76,7 @@ constexpr int kSlotInvisible = -1;  // every entry of the page is past the visib
 constexpr int kSlotUnmapped = -2;   // the block table (or resident list) points nowhere valid
 constexpr int kSlotEmpty = -3;      // resident-list slot beyond n_resident: nothing to write
 constexpr int kMaxPpw = 16;         // page slots per wave, at most
+constexpr int kMaskPpw = FM_MASK_MAXPPW;   // pages per wave of the fp8 mask kernel, at most
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -535,6 +557,9 @@ struct QF8Lds {
         return a + __lane_id() + z;
     }
     __device__ __forceinline__ u32x4 get(const u32x4 *f, int m, int st) const { return f[(8 * m + st) * 64]; }
+    __device__ __forceinline__ const f32x4 *weights() const { return (const f32x4 *)&w[0][0]; }
+    static constexpr bool kLds = true;
+    static constexpr int kAhead = FM_QLDS_AHEAD;
 };
 
 // The same with the A operands in registers (one wave per row).
@@ -550,6 +575,28 @@ struct QF8Reg {
     }
     __device__ __forceinline__ const u32x4 *frags() const { return nullptr; }
     __device__ __forceinline__ u32x4 get(const u32x4 *, int m, int st) const { return a[m][st]; }
+    __device__ __forceinline__ const f32x4 *weights() const { return (const f32x4 *)&w[0][0]; }
+    static constexpr bool kLds = false;
+    static constexpr int kAhead = 4;
+};
+
+// One layer's A operands and head weights, both in LDS (weights as [h][16 m + v] per lane half).
+struct QLayerLds {
+    const u32x4 *a;                 // [8 m + s][lane]
+    const f32x4 *w;                 // [2][8]
+    __device__ __forceinline__ const u32x4 *frags() const {
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        return a + __lane_id() + z;
+    }
+    __device__ __forceinline__ u32x4 get(const u32x4 *f, int m, int st) const { return f[(8 * m + st) * 64]; }
+    __device__ __forceinline__ const f32x4 *weights() const {
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        return w + 8 * (__lane_id() >> 5) + z;
+    }
+    static constexpr bool kLds = true;
+    static constexpr int kAhead = FM_MASK_AHEAD;
 };
 
 // tile (page slot, half) of a page through its buffer descriptor (zero-size: nothing read)
@@ -561,7 +608,36 @@ __device__ __forceinline__ void load_tile_f8(TileF8 &T, const __amdgpu_buffer_rs
     T.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, row + kDim, 0, 0));
 }
 
-// logit of entry (lane % 32) of the tile, scale applied; both lane halves return it
+// max(x, 0) for a float through its bit pattern: every negative float (and -0) is a negative
+// int.  One integer max instead of the quieting max pair a float max needs in IEEE mode.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Coalesced variant for tiles that pass through LDS: instruction k of lane ln reads code bytes
+// 16 (ln % 8) .. + 15 of row 32 half + 8 k + ln / 8 (eight lanes cover a row's 128 code bytes);
+// half 0 also reads the scale of row ln of the page.  tile_to_mma_layout() then moves the codes
+// through the wave's LDS buffer (144-byte rows: aligned, no bank conflicts) into the layout
+// load_tile_f8 produces.  Row-contiguous 128-byte reads stream markedly faster from HBM than
+// sixteen-byte pieces of 64 different rows.
+constexpr int kTileLdsRow = 144;
+__device__ __forceinline__ void load_tile_rows(TileF8 &T, const __amdgpu_buffer_rsrc_t &rs, int half, int ln) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t row = (uint32_t)(32 * half + 8 * k + (ln >> 3));
+        T.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, row * kRowFp8 + 16 * (ln & 7), 0, 0);
+    }
+    if (half == 0) T.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)ln * kRowFp8 + kDim, 0, 0));
+}
+__device__ __forceinline__ void tile_to_mma_layout(TileF8 &T, uint8_t *buf, int ln) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        *(u32x4 *)(buf + (8 * k + (ln >> 3)) * kTileLdsRow + 16 * (ln & 7)) = T.c[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        T.c[k] = *(const u32x4 *)(buf + (ln & 31) * kTileLdsRow + 64 * (ln >> 5) + 16 * k);
+}
+
+// logit of entry (lane % 32) of the tile, scale applied; both lane halves return it.  The A
+// fragments are fetched QF::kAhead MFMAs ahead of their use (from LDS for the LDS sources).
 template <class QF>
 __device__ __forceinline__ float tile_logit_f8(const QF &Q, const TileF8 &T) {
     typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -571,6 +647,10 @@ __device__ __forceinline__ float tile_logit_f8(const QF &Q, const TileF8 &T) {
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
+    constexpr int D = QF::kAhead;                 // fragments in flight
+    u32x4 a[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) a[k] = Q.get(qf, k & 1, k >> 1);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
         const uint32_t d0 = T.c[st >> 1][(st & 1) * 2], d1 = T.c[st >> 1][(st & 1) * 2 + 1];
@@ -581,14 +661,23 @@ __device__ __forceinline__ float tile_logit_f8(const QF &Q, const TileF8 &T) {
         bw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
         const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, Q.get(qf, m, st)), b, acc[m], 0, 0, 0);
+        for (int m = 0; m < 2; ++m) {
+            const int k = 2 * st + m;
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[k % D]), b, acc[m], 0, 0, 0);
+            if (k + D < 16) a[k % D] = Q.get(qf, (k + D) & 1, (k + D) >> 1);
+            if (QF::kLds) __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    const f32x4 *wt = Q.weights();
     float p = 0.f;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) p = fmaf(Q.w[m][v], fmaxf(acc[m][v], 0.f), p);
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const f32x4 w4 = wt[4 * m + v4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p = fmaf(w4[e], relu_bits(acc[m][4 * v4 + e]), p);
+        }
     const uint32_t u = __float_as_uint(p);
     const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * T.scale;
@@ -786,6 +875,114 @@ void mask_kernel(MaskArgs A) {
     }
 }
 
+// Tile stream over page slots 0 .. n - 1 with coalesced row loads (load_tile_rows) moved to the
+// MFMA layout through the wave's LDS buffer: take(t0, t1, sc, i) receives page slot i's two tile
+// results and the scale of entry (lane) of the page.
+template <int RING, class QF, class Fetch, class Take>
+__device__ __forceinline__ void stream_tiles_rows(int n, const QF &Q, uint8_t *buf, Fetch fetch, Take take) {
+    static_assert(RING % 2 == 0, "the ring holds whole pages");
+    const int ln = __lane_id();
+    TileF8 T[RING];
+#pragma unroll
+    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+    float t0 = 0.f, sc = 1.f;
+    for (int x0 = 0; x0 < 2 * n; x0 += 2 * RING) {
+#pragma unroll
+        for (int u = 0; u < 2 * RING; ++u) {
+            fetch(T[(u + RING - 1) % RING], x0 + u + RING - 1);
+            TileF8 &Tu = T[u % RING];
+            if ((u & 1) == 0) sc = Tu.scale;
+            tile_to_mma_layout(Tu, buf, ln);
+            Tu.scale = 1.f;
+            const float tl = tile_logit_f8(Q, Tu);
+            if (u & 1) take(t0, tl, sc, (x0 + u) >> 1);
+            else t0 = tl;
+        }
+    }
+}
+
+// The same union over fp8 pools with bf16 queries, four waves a workgroup, every wave on its own
+// ppw pages of request blockIdx.y for all NL layers in turn: layer l's query operands and head
+// weights sit in the wave's registers while it streams its pages of pool l, and the running
+// union of each entry waits in LDS.  After the last layer the wave forms the decisions and
+// writes its pages' mask bytes.
+template <int NL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_MASK_WPE)))
+void mask_f8_kernel(MaskArgs A) {
+    constexpr int RING = FM_MASK_RING;
+    __shared__ float s_u[4][kMaskPpw][kPage];                                      // unions
+    __shared__ __attribute__((aligned(16))) uint8_t s_tile[4][32 * kTileLdsRow];   // transposes
+    const int b = blockIdx.y;
+    const int ln = __lane_id(), wave = threadIdx.x >> 6;
+    const int64_t page0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
+    if (page0 >= A.n_pages) return;
+    const int np = (int)min((int64_t)A.ppw, A.n_pages - page0);
+    const int64_t seq = A.kv.seq_lens[b];
+
+    // lane i describes page page0 + i (i < np): physical page or state; past np: invisible
+    int phys_l = kSlotInvisible;
+    if (ln < np) {
+        const int64_t lp = page0 + ln;
+        if (lp * kPage >= seq) phys_l = kSlotInvisible;
+        else if (lp >= A.kv.bt_ld) phys_l = kSlotUnmapped;
+        else {
+            const int p = A.kv.bt[(int64_t)b * A.kv.bt_ld + lp];
+            phys_l = (p < 0 || p >= A.kv.n_phys) ? kSlotUnmapped : p;
+        }
+    }
+    const float inv_n = 1.0f / (float)NL;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        QF8Reg Q;
+        Q.init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, A.q[l].w, A.q[l].w_bf16, b, ln);
+        const uint8_t *pool = A.kv.pool[l];
+        auto fetch = [&](TileF8 &T, int x) {
+            load_tile_rows(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);
+        };
+        auto take = [&](float t0, float t1, float sc, int i) {
+            if (i >= np) return;
+            const int phys = __builtin_amdgcn_readlane(phys_l, i);
+            float L = ((ln >> 5) ? t1 : t0) * sc;
+            L = phys >= 0 ? L : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
+            float &u = s_u[wave][i][ln];
+            if (A.mean_mode) {
+                const float p = inv_n / (1.0f + expf(-L));
+                u = l == 0 ? p : u + p;
+            } else {
+                u = l == 0 ? L : ((L != L || u != u) ? __builtin_nanf("") : fmaxf(u, L));
+            }
+        };
+        stream_tiles_rows<RING>(np, Q, s_tile[wave], fetch, take);
+    }
+
+    // decisions and mask bytes (0 / 1): 16-byte chunks when the span is whole and aligned, else
+    // one by one.  Chunk c covers entries 16 (c % 4) .. + 15 of page c / 4.
+    uint8_t *mrow = A.mask + (int64_t)b * A.mask_ld;
+    const int64_t s0 = page0 * kPage;
+    const int nb = (int)min((int64_t)np * kPage, A.mask_ld - s0);
+    auto decide = [&](int e) -> bool {     // entry s0 + e of the wave's span
+        const int64_t s = s0 + e;
+        const float u = s_u[wave][e >> 6][e & 63];
+        if (A.union_score) A.union_score[(int64_t)b * A.mask_ld + s] = s < seq ? u : -INFINITY;
+        return s < seq && (u >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
+    };
+    if (nb % 16 == 0 && ((uintptr_t)(mrow + s0) % 16) == 0) {
+        for (int c = ln; 16 * c < nb; c += 64) {
+            u32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w |= (decide(16 * c + 4 * q + k) ? 1u : 0u) << (8 * k);
+                v[q] = w;
+            }
+            *(u32x4 *)(mrow + s0 + 16 * c) = v;
+        }
+    } else {
+        for (int e = ln; e < nb; e += 64) mrow[s0 + e] = decide(e) ? 1 : 0;
+    }
+}
+
 // fp32 keys: one thread per entry, fp32 VALU arithmetic.
 __global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
     __shared__ float qs[kHeads * kDim];
@@ -858,11 +1055,21 @@ hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s) {
+hipError_t launch_mask(const MaskArgs &a0, int key_fmt, int B, hipStream_t s) {
     constexpr int PPW = 16;
+    MaskArgs a = a0;
+    // fp8 layers-per-wave kernel: spread the pages over FM_MASK_RESIDENT waves, at most
+    // kMaskPpw pages a wave
+    const int64_t total = a.n_pages * (int64_t)B;
+    a.ppw = (int)std::min<int64_t>(kMaskPpw, std::max<int64_t>(1, (total + FM_MASK_RESIDENT - 1) / FM_MASK_RESIDENT));
     if (key_fmt == KEY_F32) {
         dim3 grid((unsigned)((a.mask_ld + 255) / 256), (unsigned)B);
         mask_f32_kernel<<<grid, 256, 0, s>>>(a);
+    } else if (key_fmt == KEY_FP8 && FM_MASK_F8) {
+        dim3 grid((unsigned)((a.n_pages + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)B);
+        if (a.n_layers == 1) mask_f8_kernel<1><<<grid, 256, 0, s>>>(a);
+        else if (a.n_layers == 2) mask_f8_kernel<2><<<grid, 256, 0, s>>>(a);
+        else mask_f8_kernel<3><<<grid, 256, 0, s>>>(a);
     } else {
         dim3 grid((unsigned)((a.n_pages + PPW - 1) / PPW), (unsigned)B);
         const unsigned threads = 64u * (unsigned)a.n_layers;

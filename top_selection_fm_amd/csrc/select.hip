@@ -712,36 +712,59 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
     return __popc(x & 0x01010101u);
 }
 
+// One workgroup per request.  Thread t takes pages base + 4 t .. + 3 of a round of
+// 4 kRowThreads pages and loads all their mask bytes before using any (one round trip per
+// round); one block scan of the per-thread counts places the resident pages in ascending order.
 __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
+    constexpr int PPT = 4;
     __shared__ uint32_t sh[kRowThreads / 64 + 1];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const uint8_t *mrow = A.mask + (int64_t)b * A.mask_ld;
     const bool wide = ((uintptr_t)mrow % 16 == 0);
     uint32_t running = 0;
-    for (int64_t base = 0; base < A.n_pages; base += kRowThreads) {
-        const int64_t p = base + tid;
-        uint32_t dens = 0;
-        if (p < A.n_pages) {
-            const int64_t s0 = p * kPage, s1 = min(s0 + kPage, A.mask_ld);
-            if (wide && s1 - s0 == kPage) {
-                const uint4 *m4 = (const uint4 *)(mrow + s0);
+    for (int64_t base = 0; base < A.n_pages; base += PPT * kRowThreads) {
+        const int64_t p0 = base + (int64_t)PPT * tid;
+        uint32_t dens[PPT];
+        if (wide && (p0 + PPT) * kPage <= A.mask_ld) {
+            uint4 v[PPT][4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uint4 v = m4[i];
-                    dens += nonzero_bytes(v.x) + nonzero_bytes(v.y) + nonzero_bytes(v.z) +
-                            nonzero_bytes(v.w);
-                }
-            } else {
-                for (int64_t s = s0; s < s1; ++s) dens += mrow[s] != 0;
+            for (int i = 0; i < PPT; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[i][c] = ((const uint4 *)(mrow + (p0 + i) * kPage))[c];
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                dens[i] = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    dens[i] += nonzero_bytes(v[i][c].x) + nonzero_bytes(v[i][c].y) +
+                               nonzero_bytes(v[i][c].z) + nonzero_bytes(v[i][c].w);
             }
-            if (A.page_density) A.page_density[(int64_t)b * A.n_pages + p] = (int32_t)dens;
+        } else {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                dens[i] = 0;
+                const int64_t s0 = (p0 + i) * kPage, s1 = min(s0 + kPage, A.mask_ld);
+                for (int64_t s = s0; s < s1; ++s) dens[i] += mrow[s] != 0;
+            }
         }
-        const uint32_t flag = dens > 0 ? 1u : 0u;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            if (p0 + i < A.n_pages && A.page_density)
+                A.page_density[(int64_t)b * A.n_pages + p0 + i] = (int32_t)dens[i];
+            cnt += (p0 + i < A.n_pages && dens[i] > 0) ? 1u : 0u;
+        }
         uint32_t tot;
-        const uint32_t pos = running + block_excl_scan<kRowThreads>(flag, sh, tot);
-        if (flag && A.page_list && pos < A.page_list_ld)
-            A.page_list[(int64_t)b * A.page_list_ld + pos] = (int32_t)p;
+        uint32_t pos = running + block_excl_scan<kRowThreads>(cnt, sh, tot);
+        if (A.page_list) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                if (p0 + i < A.n_pages && dens[i] > 0) {
+                    if (pos < A.page_list_ld) A.page_list[(int64_t)b * A.page_list_ld + pos] = (int32_t)(p0 + i);
+                    ++pos;
+                }
+        }
         running += tot;
     }
     if (tid == 0) A.page_count[b] = (int32_t)running;
