@@ -159,10 +159,12 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
  * Selects the k candidates of largest logit, ties broken by lower s (-0.0 == +0.0); with
  * fewer than k candidates, all of them.  out_idx[t * k + i] lists the selected s in
  * ascending order, padded with -1; out_val (nullable) holds their logits, padded with -inf.
- * 1 <= k <= FM_MAX_K.  The workspace is optional.  With ws 256-byte aligned and ws_bytes >=
- * fm_workspace_bytes(FM_OP_TOPK, T, ld) (0 for ld <= 4096), rows longer than 4,096 entries
- * are first filtered by one workgroup per 8,192-entry chunk, then selected by one workgroup
- * per row; otherwise one workgroup per row does everything.  Both give the same result.
+ * 1 <= k <= FM_MAX_K.  For ld <= 65,536 one workgroup per row selects in a single pass over
+ * the row and no workspace is used (fm_workspace_bytes(FM_OP_TOPK, T, ld) is 0).  For longer
+ * rows the workspace is optional: with ws 256-byte aligned and ws_bytes >=
+ * fm_workspace_bytes(FM_OP_TOPK, T, ld), rows are first filtered by one workgroup per
+ * 8,192-entry chunk, then selected by one workgroup per row; otherwise one workgroup per row
+ * does everything.  Every path gives the same result.
  */
 fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_valid,
                      const uint8_t *mask, int64_t mask_ld, const int32_t *row_req, int k,

@@ -43,10 +43,15 @@ def test_version_and_status_strings():
 
 
 def test_workspace_bytes():
-    topk = api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 384 * 64)
-    assert topk >= 30 * 3 * 1024 * 8                 # three 8192-entry chunks per row
-    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 30, 384 * 64) >= \
-        30 * 384 * 64 * 4 + topk
+    # rows of up to 65,536 entries are selected in one pass: no top-k workspace
+    assert api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 384 * 64) == 0
+    assert api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 65536) == 0
+    topk = api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 65537)
+    assert topk >= 30 * 9 * 1024 * 8                 # nine 8192-entry chunks per row
+    assert api.fm_workspace_bytes(api.FM_OP_TOPK, 3, 262144) >= 3 * 32 * 1024 * 8
+    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 30, 384 * 64) >= 30 * 384 * 64 * 4
+    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 30, 2048 * 64) >= \
+        30 * 2048 * 64 * 4 + api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 2048 * 64)
     assert api.fm_workspace_bytes(api.FM_OP_TOPK, 30, 4096) == 0   # short rows: none
     assert api.fm_workspace_bytes(api.FM_OP_INDEX_LOGITS, 4, 100) == 0
     assert api.fm_workspace_bytes(api.FM_OP_RESIDENT_MASK, 4, 100) == 0

@@ -23,12 +23,19 @@
 //
 // Compaction (README, page-granular recall): a page of 64 entries is resident when any entry
 // of the mask is; a block-wide exclusive scan of the page flags yields the ascending list.
+#include <float.h>
 #include <math.h>
 
 #include "fm_internal.h"
 
 #ifndef FM_TOPK_U
 #define FM_TOPK_U 4
+#endif
+#ifndef FM_TOPK_ROW
+#define FM_TOPK_ROW 1   // rows of up to 65,536 entries: single-pass row kernel
+#endif
+#ifndef FM_TOPK_NT
+#define FM_TOPK_NT 1024  // threads of the single-pass row kernel
 #endif
 #ifndef FM_TOPK_STAGE_MIN
 #define FM_TOPK_STAGE_MIN 4096
@@ -37,12 +44,15 @@
 namespace fm {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kBins = 2048;
 constexpr int kRowThreads = 1024;     // page compaction
 constexpr int kTopkThreads = 512;
 constexpr int kSample = 2048;         // sampled entries of a long row
 constexpr int kBnd = 1024;            // boundary-bin capacity of the final selection
 constexpr int kBuf = 4096;            // LDS candidate buffer
+constexpr int kTopkLdsThreads = 1024; // largest workgroup sharing TopkLds
 
 template <int NT>
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
@@ -416,11 +426,16 @@ __device__ uint32_t filter_range(const RowSrc &R, int64_t j0, int64_t j1, const 
 // range finds the bin holding the k-th largest value; the entries of higher bins are all
 // selected, and the few in that bin are ranked exactly by the full key.  When that bin holds
 // more than kBnd entries (many near-equal values) the radix selection takes over.
+//
+// have_range: [rlo, rhi] bounds the buffer's values (the caller knows them; skips a reduction).  When every entry is below kOrderBits (small_entries), the output order
+// comes from a bitmap of the selected entries and prefix popcounts instead of pairwise counts.
+constexpr int kOrderBits = kBins * 32;
 template <int NT>
 __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uint32_t k,
                               uint32_t *hist, uint32_t *sh, uint32_t *misc, float *shf,
                               int32_t *bnd, int32_t *sel_idx, float *sel_val, uint32_t *cnt2,
-                              int32_t *oi, float *ov, int k_out) {
+                              int32_t *oi, float *ov, int k_out, bool have_range = false,
+                              float rlo = 0.f, float rhi = 0.f, bool small_entries = false) {
     const int tid = threadIdx.x;
     if (tid == 0) {
         cnt2[0] = 0u;
@@ -434,13 +449,20 @@ __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uin
         if (tid == 0) cnt2[0] = (uint32_t)m;
         __syncthreads();
     } else {
-        float lo = INFINITY, hi = -INFINITY;
-        for (int i = tid; i < m; i += NT) {
-            lo = fminf(lo, bval[i]);
-            hi = fmaxf(hi, bval[i]);
+        float lo, hi;
+        if (have_range) {
+            lo = rlo;
+            hi = rhi;
+        } else {
+            lo = INFINITY;
+            hi = -INFINITY;
+            for (int i = tid; i < m; i += NT) {
+                lo = fminf(lo, bval[i]);
+                hi = fmaxf(hi, bval[i]);
+            }
+            lo = block_reduce<NT>(lo, false, shf);
+            hi = block_reduce<NT>(hi, true, shf);
         }
-        lo = block_reduce<NT>(lo, false, shf);
-        hi = block_reduce<NT>(hi, true, shf);
         LinBins bins{lo, 0.f, !(hi > lo)};
         bins.inv_w = bins.flat ? 0.f : (float)kBins / (hi - lo);
         for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
@@ -469,6 +491,7 @@ __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uin
         const int bstar = (int)misc[0];
         const uint32_t need = k - misc[1];
         const uint32_t nb = hist[bstar];
+        __syncthreads();            // every thread has nb before the radix path clears hist
         if (nb <= (uint32_t)kBnd) {
             for (int i = tid; i < m; i += NT) {
                 const int b = bins(bval[i]);
@@ -501,14 +524,58 @@ __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uin
             __syncthreads();
         }
     }
-    // ascending entry order: each selected entry's position is the number of smaller entries
     const int cnt = (int)min(cnt2[0], k);
-    for (int i = tid; i < cnt; i += NT) {
-        const int32_t e = sel_idx[i];
-        int pos = 0;
-        for (int c = 0; c < cnt; ++c) pos += sel_idx[c] < e;
-        oi[pos] = e;
-        if (ov) ov[pos] = sel_val[i];
+    if (small_entries) {
+        // ascending entry order from a bitmap of the selected entries (kBins words, in hist)
+        // and the prefix popcount of each word (16-bit, in bnd)
+        static_assert(kBins % NT == 0 && kBnd * 2 >= kBins, "bitmap layout");
+        constexpr int WPT = kBins / NT;
+        __syncthreads();
+        for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += NT) atomicOr(&hist[sel_idx[i] >> 5], 1u << (sel_idx[i] & 31));
+        __syncthreads();
+        uint32_t wd[WPT], c = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            wd[i] = hist[WPT * tid + i];
+            c += (uint32_t)__popc(wd[i]);
+        }
+        uint32_t tot;
+        uint32_t pre = block_excl_scan<NT>(c, sh, tot);
+        uint16_t *pref = (uint16_t *)bnd;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            pref[WPT * tid + i] = (uint16_t)pre;
+            pre += (uint32_t)__popc(wd[i]);
+        }
+        __syncthreads();
+        for (int i = tid; i < cnt; i += NT) {
+            const int32_t e = sel_idx[i];
+            const uint32_t wv = hist[e >> 5];
+            const int pos = (int)pref[e >> 5] + __popc(wv & ((1u << (e & 31)) - 1u));
+            oi[pos] = e;
+            if (ov) ov[pos] = sel_val[i];
+        }
+    } else {
+        // ascending entry order: each selected entry's position is the number of smaller
+        // entries (sel_idx padded to a multiple of 16 with INT32_MAX, read four at a time)
+        const int cnt16 = (cnt + 15) & ~15;
+        for (int i = cnt + tid; i < cnt16; i += NT) sel_idx[i] = 0x7fffffff;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += NT) {
+            const int32_t e = sel_idx[i];
+            int pos = 0;
+            for (int c = 0; c < cnt16; c += 16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int4 x = *(const int4 *)&sel_idx[c + 4 * q];
+                    pos += (x.x < e) + (x.y < e) + (x.z < e) + (x.w < e);
+                }
+            }
+            oi[pos] = e;
+            if (ov) ov[pos] = sel_val[i];
+        }
     }
     for (int i = cnt + tid; i < k_out; i += NT) {
         oi[i] = -1;
@@ -532,17 +599,216 @@ struct TopkLds {
     float bval[kBuf];
     int32_t bent[kBuf];
     uint32_t hist[kBins];
-    uint32_t sh[kTopkThreads / 64 + 1];
+    uint32_t sh[kTopkLdsThreads / 64 + 1];
     uint32_t misc[2];
-    float shf[kTopkThreads / 64];
+    float shf[kTopkLdsThreads / 64];
     uint32_t s_count;
-    int32_t sel_idx[FM_MAX_K];
+    alignas(16) int32_t sel_idx[FM_MAX_K];
     float sel_val[FM_MAX_K];
     int32_t bnd[kBnd];
     uint32_t cnt2[2];
     uint32_t offs[kTopkMaxChunks + 1];
 };
 static_assert(kSample <= kBuf, "the sample fits the candidate buffer");
+
+// ---------------------------------------------------------------- single-pass row top-k
+// Rows of up to kRowMax entries: one workgroup of kRowNT threads per row loads the whole row
+// into registers at once (every load in flight together), takes the cut's sample from those
+// registers (a few values a thread, spread over the row), keeps the candidates
+// at or above the cut in the LDS buffer and selects exactly from it (select_buffer).  One read
+// of the row, no workspace, no second launch.  When the cut does not hold (fewer than k pass,
+// or more than the buffer holds) the exact radix selection runs over the row instead.
+constexpr int kRowNT = FM_TOPK_NT;
+constexpr int kRowMax = 65536;
+constexpr int kRowVec = kRowMax / (4 * kRowNT);
+
+__global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
+    constexpr int NT = kRowNT, NW = NT / 64;
+    constexpr int SPT = kSample / NT;               // sampled values a thread
+    static_assert(SPT * NT == kSample && SPT <= 4, "sample layout");
+    __shared__ TopkLds L;
+    __shared__ float s_max[NW];
+    const int t = blockIdx.x, tid = threadIdx.x, ln = __lane_id(), w = tid >> 6;
+    const RowSrc R = row_source(A, t);
+    const int64_t n = R.n;
+    const uint32_t k = (uint32_t)A.k;
+    for (int i = tid; i < kBins; i += NT) L.hist[i] = 0u;   // ordered by the barriers below
+
+    // the row, every non-candidate (-inf, NaN, masked, past n) as -inf.  Buffer loads bounded
+    // by the row (4-byte alignment suffices; dwords past n read as 0 and are replaced)
+    float v[kRowVec][4];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)R.row, (short)0, (int)(n * 4), 0x00020000);
+    const int n32 = (int)n;                           // n <= kRowMax here
+#pragma unroll
+    for (int u = 0; u < kRowVec; ++u) {
+        const int j = 4 * (u * NT + tid);
+        const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 4u, 0, 0));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[u][c] = (j + c < n32) ? x[c] : -INFINITY;
+    }
+    if (R.mrow) {
+        // a masked row has no resident-page map (fm_topk512): mask byte j covers position j
+        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)R.mrow, (short)0, n32, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t j = (uint32_t)(4 * (u * NT + tid) + c);
+                if (!__builtin_amdgcn_raw_buffer_load_b8(mr, j, 0, 0)) v[u][c] = -INFINITY;
+            }
+    }
+
+    // The cut: candidates x >= tau pass.  -FLT_MAX (no cut) passes every candidate and no -inf
+    // or NaN.  For rows > kBuf the cut comes from a sample of SPT register values a thread,
+    // v[(SPT tid + q) % kRowVec][q] (q < SPT: spread over the whole row), aiming at about
+    // 2 k + 16 n / kSample candidates passing.
+    float tau = -FLT_MAX, smax = 0.f;
+    if (n > kBuf) {
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < SPT; ++q) {
+            const int uq = (SPT * tid + q) & (kRowVec - 1);
+            float sq = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < kRowVec; ++u) sq = u == uq ? v[u][q] : sq;
+            L.bval[q * NT + tid] = sq > -INFINITY ? sq : __builtin_nanf("");
+            lo = sq > -INFINITY ? fminf(lo, sq) : lo;
+            hi = fmaxf(hi, sq);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            lo = fminf(lo, __shfl_xor(lo, o));
+            hi = fmaxf(hi, __shfl_xor(hi, o));
+        }
+        if (ln == 0) {
+            L.shf[w] = lo;
+            s_max[w] = hi;
+        }
+        __syncthreads();
+        lo = INFINITY;
+        hi = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            lo = fminf(lo, L.shf[i]);
+            hi = fmaxf(hi, s_max[i]);
+        }
+        const float width = hi - lo;
+        if (lo <= hi && width < INFINITY) {           // some sampled candidate, a finite range
+            const uint32_t r = 2u * (uint32_t)(((uint64_t)k * kSample + n - 1) / n) + 16u;
+            LinBins bins{lo, 0.f, !(hi > lo)};
+            bins.inv_w = bins.flat ? 0.f : (float)kBins / width;
+#pragma unroll
+            for (int q = 0; q < SPT; ++q) {
+                const float x = L.bval[q * NT + tid];
+                if (x == x) atomicAdd(&L.hist[bins(x)], 1u);
+            }
+            __syncthreads();
+            constexpr int BPT = kBins / NT;
+            const int top = kBins - 1 - BPT * tid;
+            uint32_t h[BPT], sum = 0;
+#pragma unroll
+            for (int i = 0; i < BPT; ++i) {
+                h[i] = L.hist[top - i];
+                sum += h[i];
+            }
+            uint32_t total;
+            uint32_t above = block_excl_scan<NT>(sum, L.sh, total);
+            if (total >= r) {
+#pragma unroll
+                for (int i = 0; i < BPT; ++i) {
+                    if (above < r && r <= above + h[i]) L.misc[0] = (uint32_t)(top - i);
+                    above += h[i];
+                }
+                __syncthreads();
+                // the lower edge of the cut bin; any threshold is exact once k candidates pass
+                const float e = bins.flat ? lo : lo + (float)L.misc[0] * (width / (float)kBins);
+                tau = e > -FLT_MAX ? e : -FLT_MAX;
+                smax = hi;
+            }
+        }
+    }
+
+    // candidates x >= tau into the LDS buffer: a counting pass, one scan of the wave counts,
+    // then a writing pass at exact positions (row positions first, turned into
+    // entries afterwards, so a resident-page lookup never sits inside the loop)
+    uint32_t wcount = 0;
+#pragma unroll
+    for (int u = 0; u < kRowVec; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wcount += v[u][c] >= tau ? 1u : 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wcount += __shfl_xor(wcount, o);
+    __syncthreads();                                  // the sample's reads of sh are done
+    if (ln == 0) L.sh[w] = wcount;
+    __syncthreads();
+    uint32_t base = 0, passed = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t ci = L.sh[i];
+        base += i < w ? ci : 0u;
+        passed += ci;
+    }
+    if (passed <= (uint32_t)kBuf) {
+        // a copy of tau the compiler cannot see through: the first pass's 64 compare masks
+        // are not kept alive for this one
+        float tw;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(tw) : "v"(tau));
+        uint32_t run = base;
+#pragma unroll
+        for (int u = 0; u < kRowVec; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float x = v[u][c];
+                const uint64_t m = __ballot(x >= tw);
+                if (m) {
+                    if (x >= tw) {
+                        const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        const uint32_t p = run + below;
+                        L.bval[p] = x;
+                        L.bent[p] = 4 * (u * NT + tid) + c;
+                    }
+                    run += (uint32_t)__popcll(m);
+                }
+            }
+        if (R.rp) {
+            // row positions to entries through the resident-page list, every lookup in flight
+            constexpr int EPT = kBuf / NT;
+            __syncthreads();
+            int32_t pg[EPT];
+#pragma unroll
+            for (int q = 0; q < EPT; ++q) {
+                const uint32_t i = q * NT + tid;
+                pg[q] = i < passed ? R.rp[L.bent[i] >> 6] : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < EPT; ++q) {
+                const uint32_t i = q * NT + tid;
+                if (i < passed) L.bent[i] = pg[q] * kPage + (L.bent[i] & 63);
+            }
+        }
+    }
+    __syncthreads();
+
+    int32_t *oi = A.out_idx + (int64_t)t * A.k;
+    float *ov = A.out_val ? A.out_val + (int64_t)t * A.k : nullptr;
+    if (passed <= (uint32_t)kBuf && !(tau > -FLT_MAX && passed < k)) {
+        // bins over [tau, sample max]: every buffered value is >= tau, and the binning clamps
+        // values above the sample's maximum into the top bin (monotone, so still exact)
+        select_buffer<NT>(L.bval, L.bent, (int)passed, k, L.hist, L.sh, L.misc, L.shf, L.bnd,
+                          L.sel_idx, L.sel_val, L.cnt2, oi, ov, A.k, tau > -FLT_MAX, tau, smax,
+                          !R.rp && n <= (int64_t)kOrderBits);
+    } else {
+        const Rule rule = radix_rule<NT>(R, k, L.hist, L.sh, L.misc);
+        if (tid == 0) L.s_count = 0u;
+        __syncthreads();
+        gather<NT>(R, rule, L.sel_val, L.sel_idx, &L.s_count, FM_MAX_K);
+        __syncthreads();
+        sort_and_write<NT>(L.sel_idx, L.sel_val, (int)min(L.s_count, k), A.k, oi, ov);
+    }
+}
 
 // Filter one kTopkChunk-entry chunk of row t into its workspace slot: every chunk of a long row
 // recomputes the row's cut from the same sample (identical result in every workgroup).
@@ -712,56 +978,61 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
     return __popc(x & 0x01010101u);
 }
 
-// One workgroup per request.  Thread t takes pages base + 4 t .. + 3 of a round of
-// 4 kRowThreads pages and loads all their mask bytes before using any (one round trip per
-// round); one block scan of the per-thread counts places the resident pages in ascending order.
+// One workgroup per request, rounds of 4 kRowThreads pages.  The round's mask bytes are read
+// coalesced (16-byte chunk i kRowThreads + tid of the round; four consecutive lanes share a
+// page) with every load in flight at once, the per-page counts go to LDS, and thread t then
+// takes pages 4 t .. 4 t + 3 for one block scan that places the resident pages in order.
 __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
     constexpr int PPT = 4;
+    constexpr int RP = PPT * kRowThreads;                 // pages a round
     __shared__ uint32_t sh[kRowThreads / 64 + 1];
+    __shared__ uint32_t s_d[RP];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const uint8_t *mrow = A.mask + (int64_t)b * A.mask_ld;
     const bool wide = ((uintptr_t)mrow % 16 == 0);
     uint32_t running = 0;
-    for (int64_t base = 0; base < A.n_pages; base += PPT * kRowThreads) {
-        const int64_t p0 = base + (int64_t)PPT * tid;
-        uint32_t dens[PPT];
-        if (wide && (p0 + PPT) * kPage <= A.mask_ld) {
-            uint4 v[PPT][4];
+    for (int64_t base = 0; base < A.n_pages; base += RP) {
+        const int np = (int)min((int64_t)RP, A.n_pages - base);
+        if (wide && (base + np) * kPage <= A.mask_ld) {
+            uint4 x[16];
 #pragma unroll
-            for (int i = 0; i < PPT; ++i)
+            for (int i = 0; i < 16; ++i) {
+                const int q = i * kRowThreads + tid;          // chunk of the round
+                x[i] = q < 4 * np ? ((const uint4 *)(mrow + base * kPage))[q] : uint4{0, 0, 0, 0};
+            }
 #pragma unroll
-                for (int c = 0; c < 4; ++c) v[i][c] = ((const uint4 *)(mrow + (p0 + i) * kPage))[c];
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                dens[i] = 0;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    dens[i] += nonzero_bytes(v[i][c].x) + nonzero_bytes(v[i][c].y) +
-                               nonzero_bytes(v[i][c].z) + nonzero_bytes(v[i][c].w);
+            for (int i = 0; i < 16; ++i) {
+                uint32_t d = nonzero_bytes(x[i].x) + nonzero_bytes(x[i].y) + nonzero_bytes(x[i].z) +
+                             nonzero_bytes(x[i].w);
+                d += __shfl_xor(d, 1);
+                d += __shfl_xor(d, 2);
+                if ((tid & 3) == 0) s_d[(i * kRowThreads + tid) >> 2] = d;
             }
         } else {
-#pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                dens[i] = 0;
-                const int64_t s0 = (p0 + i) * kPage, s1 = min(s0 + kPage, A.mask_ld);
-                for (int64_t s = s0; s < s1; ++s) dens[i] += mrow[s] != 0;
+            for (int p = tid; p < np; p += kRowThreads) {
+                const int64_t s0 = (base + p) * kPage, s1 = min(s0 + kPage, A.mask_ld);
+                uint32_t d = 0;
+                for (int64_t s = s0; s < s1; ++s) d += mrow[s] != 0;
+                s_d[p] = d;
             }
         }
-        uint32_t cnt = 0;
+        __syncthreads();
+        uint32_t dens[PPT], cnt = 0;
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            if (p0 + i < A.n_pages && A.page_density)
-                A.page_density[(int64_t)b * A.n_pages + p0 + i] = (int32_t)dens[i];
-            cnt += (p0 + i < A.n_pages && dens[i] > 0) ? 1u : 0u;
+            const int p = PPT * tid + i;
+            dens[i] = p < np ? s_d[p] : 0u;
+            if (p < np && A.page_density) A.page_density[(int64_t)b * A.n_pages + base + p] = (int32_t)dens[i];
+            cnt += dens[i] > 0 ? 1u : 0u;
         }
         uint32_t tot;
         uint32_t pos = running + block_excl_scan<kRowThreads>(cnt, sh, tot);
         if (A.page_list) {
 #pragma unroll
             for (int i = 0; i < PPT; ++i)
-                if (p0 + i < A.n_pages && dens[i] > 0) {
-                    if (pos < A.page_list_ld) A.page_list[(int64_t)b * A.page_list_ld + pos] = (int32_t)(p0 + i);
+                if (dens[i] > 0) {
+                    if (pos < A.page_list_ld) A.page_list[(int64_t)b * A.page_list_ld + pos] = (int32_t)(base + PPT * tid + i);
                     ++pos;
                 }
         }
@@ -776,7 +1047,9 @@ __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
 }  // namespace
 
 size_t topk_ws_bytes(int T, int64_t n) {
-    if (T <= 0 || n <= FM_TOPK_STAGE_MIN || n > (int64_t)kTopkMaxChunks * kTopkChunk) return 0;
+    if (T <= 0 || n <= FM_TOPK_STAGE_MIN || n <= (int64_t)kRowMax ||
+        n > (int64_t)kTopkMaxChunks * kTopkChunk)
+        return 0;
     const size_t slots = (size_t)T * (size_t)((n + kTopkChunk - 1) / kTopkChunk);
     return align_up(slots * kTopkCap * sizeof(float), 256) +
            align_up(slots * kTopkCap * sizeof(int32_t), 256) + align_up(slots * sizeof(int32_t), 256);
@@ -797,6 +1070,10 @@ TopkWs topk_ws_carve(void *ws, int T, int64_t n) {
 }
 
 hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s) {
+    if (a.ld <= (int64_t)kRowMax && FM_TOPK_ROW) {
+        topk_row_kernel<<<dim3((unsigned)a.T), dim3(kRowNT), 0, s>>>(a);
+        return hipGetLastError();
+    }
     if (ws) {
         topk_filter_kernel<<<dim3((unsigned)ws->n_chunks, (unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, *ws);
         const hipError_t e = hipGetLastError();
