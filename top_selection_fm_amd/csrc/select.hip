@@ -427,8 +427,9 @@ __device__ uint32_t filter_range(const RowSrc &R, int64_t j0, int64_t j1, const 
 // selected, and the few in that bin are ranked exactly by the full key.  When that bin holds
 // more than kBnd entries (many near-equal values) the radix selection takes over.
 //
-// have_range: [rlo, rhi] bounds the buffer's values (the caller knows them; skips a reduction).  When every entry is below kOrderBits (small_entries), the output order
-// comes from a bitmap of the selected entries and prefix popcounts instead of pairwise counts.
+// have_range: [rlo, rhi] bounds the buffer's values (the caller knows them; skips a reduction).
+// The output order: when every entry is below kOrderBits (small_entries), from a bitmap of the
+// selected entries and prefix popcounts; otherwise from counts of smaller entries.
 constexpr int kOrderBits = kBins * 32;
 template <int NT>
 __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uint32_t k,
@@ -757,7 +758,8 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
         asm volatile("v_mov_b32 %0, %1" : "=v"(tw) : "v"(tau));
         uint32_t run = base;
 #pragma unroll
-        for (int u = 0; u < kRowVec; ++u)
+        for (int u = 0; u < kRowVec; ++u) {
+            if (4 * u * NT >= n32) continue;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float x = v[u][c];
@@ -773,6 +775,7 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
                     run += (uint32_t)__popcll(m);
                 }
             }
+        }
         if (R.rp) {
             // row positions to entries through the resident-page list, every lookup in flight
             constexpr int EPT = kBuf / NT;
