@@ -185,6 +185,35 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
                             int64_t res_ld, int k, int32_t *out_idx, float *out_val,
                             void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Two-level scoring with the fused remap (README, "Key optimizations" table, the fused-remap
+ * row: the top-512 columns map directly to reserve cells).  Recalled pages fill a reserve in
+ * list order, so entry `offset` of the j-th listed page sits in reserve cell 64 * j + offset.
+ * Same inputs, workspace and candidates as fm_score_resident; the selection ranks candidates by
+ * logit, ties by lower cell, and out_cells[t * k + i] lists the selected cells in ascending
+ * order, padded with -1 (out_val as in fm_score_resident).  With an ascending resident list (as
+ * fm_densest_pages and fm_resident_mask produce) cells and logical entries are in the same
+ * order, so the selection is fm_score_resident's, each entry given as its cell.
+ */
+fm_status fm_score_resident_cells(const fm_query_desc *q, const fm_kv_desc *kv,
+                                  const int32_t *resident_pages, const int32_t *n_resident,
+                                  int64_t res_ld, int k, int32_t *out_cells, float *out_val,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The KMAX densest pages of each request (README, reference-performance notes: KMAX is the
+ * number of densest pages recalled per request, about 10% of the history).  density is an
+ * int32 [B, density_ld] matrix, e.g. the page_density of fm_resident_mask.  For request b,
+ * the pages p < n_pages with density[b * density_ld + p] > 0 are ranked by density, ties by
+ * lower page id; out_pages[b * kmax + i] lists the first min(kmax, count) in ascending page
+ * id, padded with -1, and out_count[b] (nullable) holds min(kmax, count).  The result is a
+ * resident list for fm_score_resident (res_ld = kmax, n_resident = out_count).
+ * 1 <= kmax <= FM_MAX_K, n_pages <= density_ld.  Device precondition: densities <= 2^24 (a
+ * page's density is at most 64).  No workspace.
+ */
+fm_status fm_densest_pages(const int32_t *density, int64_t density_ld, int B, int64_t n_pages,
+                           int kmax, int32_t *out_pages, int32_t *out_count, void *stream);
+
 /* Workspace bytes an operation needs for T rows of up to max_candidates entries each. */
 size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates);
 

@@ -77,6 +77,10 @@ def lib():
                                         C.c_int64, P, P, P, C.c_int64, P]
         L.fmo_score_resident.restype = None
         L.fmo_score_resident.argtypes = [P, P, P, P, C.c_int64, C.c_int, P, P, P]
+        L.fmo_score_resident_ex.restype = None
+        L.fmo_score_resident_ex.argtypes = [P, P, P, P, C.c_int64, C.c_int, C.c_int, P, P, P]
+        L.fmo_densest_pages.restype = None
+        L.fmo_densest_pages.argtypes = [P, C.c_int64, C.c_int, C.c_int64, C.c_int, P, P]
         L.fmo_num_threads.restype = C.c_int
         L.fmo_set_num_threads.argtypes = [C.c_int]
         _lib = L
@@ -233,7 +237,10 @@ def resident_mask(wl, mode: str = "max", threshold: float = 0.5, n_sink: int = 0
     return dict(mask=mask, union=score, page_count=cnt, page_list=plist, page_density=dens)
 
 
-def score_resident(wl, k: int = 512, resident_pages=None, n_resident=None):
+def score_resident(wl, k: int = 512, resident_pages=None, n_resident=None, cells: bool = False):
+    """Two-level top-k over the listed resident pages.  cells=False: logical entry indices;
+    cells=True: reserve cells 64 j + offset (j = the page's position in the list), ranked and
+    listed by cell."""
     b = _Bound(wl, [0])
     rp = np.ascontiguousarray(wl.resident_pages if resident_pages is None else resident_pages,
                               np.int32)
@@ -242,9 +249,21 @@ def score_resident(wl, k: int = 512, resident_pages=None, n_resident=None):
     oi = np.empty((T, k), np.int32)
     ov = np.empty((T, k), np.float64)
     cnt = np.empty(T, np.int32)
-    lib().fmo_score_resident(b.qref(), b.kvref(), rp.ctypes.data, nr.ctypes.data, rp.shape[1],
-                             k, oi.ctypes.data, ov.ctypes.data, cnt.ctypes.data)
+    lib().fmo_score_resident_ex(b.qref(), b.kvref(), rp.ctypes.data, nr.ctypes.data,
+                                rp.shape[1], k, int(cells), oi.ctypes.data, ov.ctypes.data,
+                                cnt.ctypes.data)
     return oi, ov, cnt
+
+
+def densest_pages(density, kmax: int, n_pages: int | None = None):
+    """KMAX densest pages per request (density > 0 only), ties by lower page id, ascending."""
+    d = np.ascontiguousarray(density, np.int32)
+    B, ld = d.shape
+    n_pages = ld if n_pages is None else n_pages
+    out = np.empty((B, kmax), np.int32)
+    cnt = np.empty(B, np.int32)
+    lib().fmo_densest_pages(d.ctypes.data, ld, B, n_pages, kmax, out.ctypes.data, cnt.ctypes.data)
+    return out, cnt
 
 
 def num_threads() -> int:

@@ -32,6 +32,12 @@
  *  - Two-level scoring (README, "Two-level recall" and the env table row for
  *    SGLANG_PATHP_SCORE_RESIDENT): the same top-k over the entries of the listed resident
  *    pages only.
+ *  - Densest pages (README, reference-performance notes: KMAX is the number of densest pages
+ *    recalled per request): the KMAX pages with the most resident entries, ties by lower page
+ *    id, among the pages with at least one; listed in ascending page id.
+ *  - Reserve cells (README env table, the fused-remap row: the top-512 columns map directly to
+ *    reserve cells): recalled pages fill a reserve in list order, so entry `offset` of the
+ *    j-th listed page sits in cell 64 j + offset; the fused top-k ranks and lists cells.
  */
 #include <math.h>
 #include <stdint.h>
@@ -354,9 +360,9 @@ void fmo_resident_mask(const fmo_q *qs, int n_layers, const fmo_kv *kv, int mode
  * For every row t (request b): candidates are the entries of the listed resident logical
  * pages resident_pages[b, 0..n_resident[b]) that are valid and visible; top-k as fmo_topk.
  */
-void fmo_score_resident(const fmo_q *q, const fmo_kv *kv, const int32_t *resident_pages,
-                        const int32_t *n_resident, int64_t res_ld, int k, int32_t *out_idx,
-                        double *out_val, int32_t *out_count)
+void fmo_score_resident_ex(const fmo_q *q, const fmo_kv *kv, const int32_t *resident_pages,
+                           const int32_t *n_resident, int64_t res_ld, int k, int cells,
+                           int32_t *out_idx, double *out_val, int32_t *out_count)
 {
     int H = q->n_heads, D = kv->head_dim, P = kv->page_size;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -378,13 +384,49 @@ void fmo_score_resident(const fmo_q *q, const fmo_kv *kv, const int32_t *residen
                 double L = -INFINITY;
                 if (s < nv && load_key(kv, 0, b, s, kk)) L = logit_one(qv, wv, kk, H, D);
                 vals[(int64_t)j * P + e] = L;
-                idx[(int64_t)j * P + e] = s;
+                idx[(int64_t)j * P + e] = cells ? (int64_t)j * P + e : s;   /* cell or entry */
             }
         }
         int got = fmo_topk(vals, idx, NULL, n, k, out_idx + (int64_t)t * k,
                            out_val ? out_val + (int64_t)t * k : NULL);
         if (out_count) out_count[t] = got;
         free(vals); free(idx); free(qv); free(wv); free(kk);
+    }
+}
+
+void fmo_score_resident(const fmo_q *q, const fmo_kv *kv, const int32_t *resident_pages,
+                        const int32_t *n_resident, int64_t res_ld, int k, int32_t *out_idx,
+                        double *out_val, int32_t *out_count)
+{
+    fmo_score_resident_ex(q, kv, resident_pages, n_resident, res_ld, k, 0, out_idx, out_val,
+                          out_count);
+}
+
+/* ------------------------------------------------------------------ densest pages */
+/*
+ * For every request b: the pages p < n_pages with density[b * density_ld + p] > 0 ranked by
+ * density descending, ties by lower page id; the first min(kmax, count) in ascending page
+ * id, padded with -1 (out_pages[b * kmax + i]); out_count[b] = how many.
+ */
+void fmo_densest_pages(const int32_t *density, int64_t density_ld, int B, int64_t n_pages,
+                       int kmax, int32_t *out_pages, int32_t *out_count)
+{
+    for (int b = 0; b < B; ++b) {
+        cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (n_pages > 0 ? n_pages : 1));
+        int64_t m = 0;
+        for (int64_t p = 0; p < n_pages; ++p) {
+            const int32_t d = density[(int64_t)b * density_ld + p];
+            if (d <= 0) continue;
+            c[m].v = (double)d;
+            c[m].s = p;
+            ++m;
+        }
+        qsort(c, m, sizeof(cand_t), by_score);
+        const int64_t take = m < kmax ? m : kmax;
+        qsort(c, take, sizeof(cand_t), by_index);
+        for (int i = 0; i < kmax; ++i) out_pages[(int64_t)b * kmax + i] = i < take ? (int32_t)c[i].s : -1;
+        if (out_count) out_count[b] = (int32_t)take;
+        free(c);
     }
 }
 

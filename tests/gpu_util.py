@@ -68,6 +68,28 @@ def score_resident(dw, k=512, resident_pages=None, n_resident=None, replica=0):
     return idx, val
 
 
+def score_resident_cells(dw, k=512, resident_pages=None, n_resident=None, replica=0):
+    rp = dw.resident_pages if resident_pages is None else resident_pages
+    nr = dw.n_resident if n_resident is None else n_resident
+    T = dw.wl.queries[0].T
+    res_ld = rp.shape[1]
+    nb = api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, T, res_ld * 64)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dw.device)
+    cells = torch.empty((T, k), dtype=torch.int32, device=dw.device)
+    val = torch.empty((T, k), dtype=torch.float32, device=dw.device)
+    api.fm_score_resident_cells(dw.query(0), dw.kv(replica), rp, nr, res_ld, k, cells, val, ws, nb)
+    return cells, val
+
+
+def densest_pages(density, kmax, n_pages=None):
+    B, ld = density.shape
+    n_pages = ld if n_pages is None else n_pages
+    out = torch.empty((B, kmax), dtype=torch.int32, device=density.device)
+    cnt = torch.empty(B, dtype=torch.int32, device=density.device)
+    api.fm_densest_pages(density, ld, B, n_pages, kmax, out, cnt)
+    return out, cnt
+
+
 def resident_mask(dw, mode=api.FM_UNION_MAX, threshold=0.5, n_sink=0, n_recent=0,
                   mask_ld=None, layers=None, with_union=True):
     layers = list(range(len(dw.wl.queries))) if layers is None else layers

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     L = api.lib()
     names = declared_functions()
     assert set(names) >= {"fm_index_logits", "fm_resident_mask", "fm_topk512",
-                          "fm_score_resident"}
+                          "fm_score_resident", "fm_score_resident_cells", "fm_densest_pages"}
     for n in names:
         assert hasattr(L, n), n
     assert sorted(api.EXPORTS) == names
@@ -183,6 +183,31 @@ def test_score_resident_validation():
     assert st(ws=FAKE + 16, ws_bytes=need) == api.FM_ERR_WORKSPACE   # needs 256-byte alignment
     assert st(rp=None, ws_bytes=need) == api.FM_ERR_INVALID_ARG
     assert st(res_ld=0, ws_bytes=need) == api.FM_ERR_INVALID_ARG
+    assert st(k=4096, ws_bytes=need) == api.FM_ERR_UNSUPPORTED
+
+
+def test_densest_pages_validation():
+    st = lambda **kw: status_of(api.fm_densest_pages, kw.get("d", FAKE), kw.get("ld", 100),
+                                kw.get("B", 2), kw.get("n", 100), kw.get("kmax", 96),
+                                kw.get("out", FAKE), None)[0]
+    assert st(kmax=0) == api.FM_ERR_UNSUPPORTED
+    assert st(kmax=1025) == api.FM_ERR_UNSUPPORTED
+    assert st(n=101) == api.FM_ERR_INVALID_ARG          # more pages than the row holds
+    assert st(n=-1) == api.FM_ERR_INVALID_ARG
+    assert st(B=-1) == api.FM_ERR_INVALID_ARG
+    assert st(d=None) == api.FM_ERR_INVALID_ARG
+    assert st(out=None) == api.FM_ERR_INVALID_ARG
+    api.fm_densest_pages(None, 100, 0, 100, 96, None)  # B = 0: nothing to do, nothing launched
+
+
+def test_score_resident_cells_validation():
+    q, kv = good_q(), good_kv("fp8x132")
+    need = api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 2, 10 * 64)
+    st = lambda **kw: status_of(api.fm_score_resident_cells, q, kv, kw.get("rp", FAKE),
+                                kw.get("nr", FAKE), kw.get("res_ld", 10), kw.get("k", 512),
+                                FAKE, None, kw.get("ws", FAKE), kw.get("ws_bytes", need - 4))[0]
+    assert st() == api.FM_ERR_WORKSPACE
+    assert st(rp=None, ws_bytes=need) == api.FM_ERR_INVALID_ARG
     assert st(k=4096, ws_bytes=need) == api.FM_ERR_UNSUPPORTED
 
 

@@ -253,6 +253,82 @@ def test_two_level_equals_masked_topk_and_gate_off():
     assert torch.equal(i2, ip) and torch.equal(v2, vp)
 
 
+# ----------------------------------------------------------------------------- densest pages
+@pytest.mark.parametrize("kmax", [1, 96, 384, 1024])
+def test_densest_pages_bit_exact(kmax):
+    rng = np.random.default_rng(4000 + kmax)
+    d = rng.integers(0, 65, (8, 4096)).astype(np.int32)      # page densities of 1M-entry rows
+    d[1, rng.random(4096) < 0.97] = 0                        # fewer resident pages than kmax
+    d[2] = 0                                                 # nothing resident
+    d[3] = 64                                                # all tied
+    d[4, :] = 0
+    d[4, [5, 4095]] = [1, 64]                                # two pages, far apart
+    dt = torch.from_numpy(d).cuda()
+    pages, cnt = G.densest_pages(dt, kmax, n_pages=4000)     # the last 96 columns are ignored
+    rp, rc = oracle.densest_pages(d, kmax, n_pages=4000)
+    assert np.array_equal(pages.cpu().numpy(), rp)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+
+
+def test_mask_densest_two_level_chain():
+    """Level 1 to Level 2 on the device: the GPU mask's page densities -> the KMAX densest pages
+    -> two-level top-512 over them, each step compared with the oracle on the GPU's own input."""
+    wl = W.three_layer_mask_fp8(seed=2006, B=3, seq_len=64 * 60 + 11, ragged=True)
+    dw = dev(wl)
+    m = G.resident_mask(dw)
+    dens = m["page_density"]
+    pages, cnt = G.densest_pages(dens, 12)
+    rp, rc = oracle.densest_pages(dens.cpu().numpy(), 12)
+    assert np.array_equal(pages.cpu().numpy(), rp) and np.array_equal(cnt.cpu().numpy(), rc)
+    # layer 0's query row and pool score the recalled pages
+    wl0 = W.Workload(wl.name, wl.kv, wl.queries[:1], resident_pages=rp, n_resident=rc,
+                     meta=wl.meta)
+    dw0 = dev(wl0)
+    idx, val = G.score_resident(dw0, resident_pages=pages, n_resident=cnt)
+    cells, cval = G.score_resident_cells(dw0, resident_pages=pages, n_resident=cnt)
+    ri, rv, rcnt = oracle.score_resident(wl0)
+    ig, vg = idx.cpu().numpy(), val.cpu().numpy()
+    for t in range(wl0.queries[0].T):
+        sel = ig[t][ig[t] >= 0]
+        allv = oracle.logits_at(wl0, np.full(sel.size, t), sel)
+        scale = np.max(np.abs(np.concatenate([allv, rv[t, :rcnt[t]]]))) if sel.size else 1.0
+        G.check_topk_row(ig[t], vg[t], ri[t], rcnt[t],
+                         lambda e, t=t: oracle.logits_at(wl0, np.full(len(e), t), e),
+                         scale, 512, f"chain row {t}")
+    # an ascending list: the cells are the entries remapped, the values the same
+    cg, cv = cells.cpu().numpy(), cval.cpu().numpy()
+    for t in range(wl0.queries[0].T):
+        lst = list(rp[t, :rc[t]])
+        sel = ig[t][ig[t] >= 0]
+        assert np.array_equal(cg[t][cg[t] >= 0], [lst.index(s // 64) * 64 + s % 64 for s in sel])
+        assert np.array_equal(cv[t], vg[t])
+
+
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_score_resident_cells_small(shuffled):
+    wl = W.two_level_resident_fp8(seed=2007, B=4, seq_len=64 * 60 + 21, kmax=20,
+                                  shuffled=shuffled, ragged=True)
+    dw = dev(wl)
+    cells, val = G.score_resident_cells(dw)
+    ri, rv, rc = oracle.score_resident(wl, cells=True)
+    cg, vg = cells.cpu().numpy(), val.cpu().numpy()
+
+    def logits_of_cells(t, cs):
+        lst = wl.resident_pages[t]
+        ents = np.array([int(lst[c // 64]) * 64 + c % 64 for c in cs], np.int64)
+        return oracle.logits_at(wl, np.full(len(ents), t), ents)
+
+    dis = 0
+    for t in range(wl.queries[0].T):
+        sel = cg[t][cg[t] >= 0]
+        allv = logits_of_cells(t, sel)
+        scale = np.max(np.abs(np.concatenate([allv, rv[t, :rc[t]]])))
+        d, _ = G.check_topk_row(cg[t], vg[t], ri[t], rc[t], lambda cs, t=t: logits_of_cells(t, cs),
+                                scale, 512, f"two-level cells row {t}")
+        dis += d
+    G.note(f"two-level cells shuffled={shuffled}", disagreements=dis)
+
+
 @pytest.fixture(scope="module")
 def two_level_full():
     return W.two_level_resident_fp8()

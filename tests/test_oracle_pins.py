@@ -414,6 +414,69 @@ def test_two_level_never_touches_poisoned_pages():
         assert cnt[b] == min(512, 64 * wl.n_resident[b])
 
 
+def _densest_brute(d, kmax):
+    """Pages with density > 0, by density descending then page ascending, first kmax, ascending."""
+    out = np.full((d.shape[0], kmax), -1, np.int32)
+    cnt = np.zeros(d.shape[0], np.int32)
+    for b in range(d.shape[0]):
+        cand = [p for p in range(d.shape[1]) if d[b, p] > 0]
+        cand.sort(key=lambda p: (-int(d[b, p]), p))
+        take = sorted(cand[:kmax])
+        out[b, :len(take)] = take
+        cnt[b] = len(take)
+    return out, cnt
+
+
+@pytest.mark.parametrize("kmax", [1, 7, 96, 384, 1000])
+def test_densest_pages_brute_force(kmax):
+    rng = np.random.default_rng(kmax)
+    d = rng.integers(0, 65, (4, 300)).astype(np.int32)      # many ties among 65 levels
+    d[1, rng.random(300) < 0.8] = 0                          # sparse: fewer than kmax pages
+    d[2] = 0                                                 # nothing resident
+    d[3, :] = 5                                              # all tied: lowest ids win
+    got, cnt = oracle.densest_pages(d, kmax)
+    ref, rcnt = _densest_brute(d, kmax)
+    assert np.array_equal(got, ref) and np.array_equal(cnt, rcnt)
+    assert cnt[2] == 0 and np.all(got[2] == -1)
+    assert np.array_equal(got[3, :min(kmax, 300)], np.arange(min(kmax, 300)))
+
+
+def test_densest_pages_of_the_mask_are_its_fullest_pages():
+    """From a real Level-1 mask: the selected pages are resident, and no unselected page is
+    denser than a selected one."""
+    wl = W.three_layer_mask_fp8(seed=2003, B=2, seq_len=64 * 50 + 7, ragged=True)
+    r = oracle.resident_mask(wl)
+    d = r["page_density"]
+    pages, cnt = oracle.densest_pages(d, 9)
+    for b in range(2):
+        sel = pages[b, :cnt[b]]
+        assert cnt[b] == min(9, int((d[b] > 0).sum()))
+        assert np.all(d[b, sel] > 0) and np.all(np.diff(sel) > 0)
+        rest = np.setdiff1d(np.nonzero(d[b])[0], sel)
+        if rest.size and sel.size:
+            assert d[b, rest].max() <= d[b, sel].min()
+
+
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_reserve_cells_are_the_remapped_entries(shuffled):
+    """Reserve cell of entry 64 p + o = 64 j + o, j = the page's position in the resident list.
+    With continuous random logits there are no exact ties, so the cell selection is the entry
+    selection remapped, whatever the list order."""
+    wl = W.two_level_resident_fp8(seed=33, B=3, seq_len=64 * 40 + 19, kmax=11,
+                                  shuffled=shuffled, poison=False, ragged=True)
+    ie, ve, ce = oracle.score_resident(wl)
+    ic, vc, cc = oracle.score_resident(wl, cells=True)
+    assert np.array_equal(ce, cc)
+    for t in range(wl.queries[0].T):
+        b = t
+        lst = list(wl.resident_pages[b, :wl.n_resident[b]])
+        remap = sorted(lst.index(s // 64) * 64 + s % 64 for s in ie[t, :ce[t]])
+        assert np.array_equal(ic[t, :cc[t]], remap)
+        assert np.all(ic[t, cc[t]:] == -1)
+        # the same logits, listed by cell
+        assert np.allclose(np.sort(vc[t, :cc[t]]), np.sort(ve[t, :ce[t]]), rtol=0, atol=0)
+
+
 # ----------------------------------------------------------------------------- shape
 def test_flop_table_slope_is_64_heads_by_128_dims():
     """The baseline column of the per-token FLOP table grows by 2 * 64 * 128 (+ ~1%) FLOP per

@@ -27,7 +27,8 @@ KEY_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8x132": FM_FP8_E4M3_SCALED132}
 Q_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8": FM_FP8_E4M3}
 
 EXPORTS = ["fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
-           "fm_workspace_bytes", "fm_status_string", "fm_last_error", "fm_version"]
+           "fm_score_resident_cells", "fm_densest_pages", "fm_workspace_bytes",
+           "fm_status_string", "fm_last_error", "fm_version"]
 
 
 class FmError(RuntimeError):
@@ -66,7 +67,10 @@ def lib():
                                        P, I64, P, P, I64, P, P, P]
         L.fm_topk512.argtypes = [P, I64, C.c_int, P, P, I64, P, C.c_int, P, P, P, C.c_size_t, P]
         L.fm_score_resident.argtypes = [P, P, P, P, I64, C.c_int, P, P, P, C.c_size_t, P]
-        for f in ("fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident"):
+        L.fm_score_resident_cells.argtypes = [P, P, P, P, I64, C.c_int, P, P, P, C.c_size_t, P]
+        L.fm_densest_pages.argtypes = [P, I64, C.c_int, I64, C.c_int, P, P, P]
+        for f in ("fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
+                  "fm_score_resident_cells", "fm_densest_pages"):
             getattr(L, f).restype = C.c_int
         L.fm_workspace_bytes.argtypes = [C.c_int, C.c_int, I64]
         L.fm_workspace_bytes.restype = C.c_size_t
@@ -167,6 +171,20 @@ def fm_score_resident(q: QueryDesc, kv: KvDesc, resident_pages, n_resident, res_
     _check(lib().fm_score_resident(C.byref(q), C.byref(kv), _ptr(resident_pages),
                                    _ptr(n_resident), int(res_ld), int(k), _ptr(out_idx),
                                    _ptr(out_val), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def fm_score_resident_cells(q: QueryDesc, kv: KvDesc, resident_pages, n_resident, res_ld: int,
+                            k: int, out_cells, out_val=None, ws=None, ws_bytes: int = 0,
+                            stream=None) -> None:
+    _check(lib().fm_score_resident_cells(C.byref(q), C.byref(kv), _ptr(resident_pages),
+                                         _ptr(n_resident), int(res_ld), int(k), _ptr(out_cells),
+                                         _ptr(out_val), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def fm_densest_pages(density, density_ld: int, B: int, n_pages: int, kmax: int, out_pages,
+                     out_count=None, stream=None) -> None:
+    _check(lib().fm_densest_pages(_ptr(density), int(density_ld), int(B), int(n_pages), int(kmax),
+                                  _ptr(out_pages), _ptr(out_count), _stream(stream)))
 
 
 def fm_workspace_bytes(op: int, T: int, max_candidates: int) -> int:

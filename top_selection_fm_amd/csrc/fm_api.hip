@@ -157,6 +157,50 @@ fm_status run_score(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t 
     return launched(fm::launch_score(a, key_fmt(kv->key_dtype), qf, st), "score");
 }
 
+fm_status score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
+                            const int32_t *resident_pages, const int32_t *n_resident,
+                            int64_t res_ld, int k, int32_t *out_idx, float *out_val, void *ws,
+                            size_t ws_bytes, void *stream, int cells) {
+    CHECK(check_kv(kv, 1));
+    CHECK(check_q(q, kv, "q"));
+    REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
+    REQUIRE(res_ld >= 1 && res_ld * FM_PAGE_SIZE <= (int64_t)INT32_MAX / 4, FM_ERR_INVALID_ARG,
+            "res_ld = %lld", (long long)res_ld);
+    if (q->T == 0) return ok();
+    REQUIRE(resident_pages && n_resident && out_idx, FM_ERR_INVALID_ARG,
+            "resident_pages / n_resident / out_idx NULL");
+    const size_t need = fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T, res_ld * FM_PAGE_SIZE);
+    REQUIRE(ws && ws_bytes >= need && aligned(ws, 256), FM_ERR_WORKSPACE,
+            "workspace %zu bytes at %p, need %zu (256-byte aligned)", ws_bytes, ws, need);
+    hipStream_t st = (hipStream_t)stream;
+    float *wl = (float *)ws;
+    const int64_t ld = res_ld * FM_PAGE_SIZE;
+    CHECK(run_score(q, kv, resident_pages, n_resident, res_ld, wl, ld, res_ld, st));
+    fm::TopkArgs a;
+    a.logits = wl;
+    a.ld = ld;
+    a.T = q->T;
+    a.n_valid = nullptr;
+    a.mask = nullptr;
+    a.mask_ld = 0;
+    a.row_req = q->row_req;
+    a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
+    a.res_pages = resident_pages;
+    a.n_res = n_resident;
+    a.res_ld = res_ld;
+    a.res_cells = cells;
+    a.B = kv->B;
+    a.k = k;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    const size_t logit_bytes = fm::align_up((size_t)q->T * (size_t)ld * sizeof(float), 256);
+    fm::TopkWs W;
+    const bool staged = fm::topk_ws_bytes(q->T, ld) > 0;
+    if (staged) W = fm::topk_ws_carve((uint8_t *)ws + logit_bytes, q->T, ld);
+    CHECK(launched(fm::launch_topk(a, staged ? &W : nullptr, st), "topk"));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,6 +250,7 @@ fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_va
     a.row_req = row_req;
     a.b_is_zero = 0;
     a.res_pages = nullptr;
+    a.res_cells = 0;
     a.n_res = nullptr;
     a.res_ld = 0;
     a.B = INT32_MAX;   // mask rows are the caller's: row_req[t] must index one
@@ -225,42 +270,35 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
                             const int32_t *resident_pages, const int32_t *n_resident,
                             int64_t res_ld, int k, int32_t *out_idx, float *out_val, void *ws,
                             size_t ws_bytes, void *stream) {
-    CHECK(check_kv(kv, 1));
-    CHECK(check_q(q, kv, "q"));
-    REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
-    REQUIRE(res_ld >= 1 && res_ld * FM_PAGE_SIZE <= (int64_t)INT32_MAX / 4, FM_ERR_INVALID_ARG,
-            "res_ld = %lld", (long long)res_ld);
-    if (q->T == 0) return ok();
-    REQUIRE(resident_pages && n_resident && out_idx, FM_ERR_INVALID_ARG,
-            "resident_pages / n_resident / out_idx NULL");
-    const size_t need = fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T, res_ld * FM_PAGE_SIZE);
-    REQUIRE(ws && ws_bytes >= need && aligned(ws, 256), FM_ERR_WORKSPACE,
-            "workspace %zu bytes at %p, need %zu (256-byte aligned)", ws_bytes, ws, need);
-    hipStream_t st = (hipStream_t)stream;
-    float *wl = (float *)ws;
-    const int64_t ld = res_ld * FM_PAGE_SIZE;
-    CHECK(run_score(q, kv, resident_pages, n_resident, res_ld, wl, ld, res_ld, st));
-    fm::TopkArgs a;
-    a.logits = wl;
-    a.ld = ld;
-    a.T = q->T;
-    a.n_valid = nullptr;
-    a.mask = nullptr;
-    a.mask_ld = 0;
-    a.row_req = q->row_req;
-    a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
-    a.res_pages = resident_pages;
-    a.n_res = n_resident;
-    a.res_ld = res_ld;
-    a.B = kv->B;
-    a.k = k;
-    a.out_idx = out_idx;
-    a.out_val = out_val;
-    const size_t logit_bytes = fm::align_up((size_t)q->T * (size_t)ld * sizeof(float), 256);
-    fm::TopkWs W;
-    const bool staged = fm::topk_ws_bytes(q->T, ld) > 0;
-    if (staged) W = fm::topk_ws_carve((uint8_t *)ws + logit_bytes, q->T, ld);
-    CHECK(launched(fm::launch_topk(a, staged ? &W : nullptr, st), "topk"));
+    return score_resident(q, kv, resident_pages, n_resident, res_ld, k, out_idx, out_val, ws,
+                          ws_bytes, stream, 0);
+}
+
+fm_status fm_score_resident_cells(const fm_query_desc *q, const fm_kv_desc *kv,
+                                  const int32_t *resident_pages, const int32_t *n_resident,
+                                  int64_t res_ld, int k, int32_t *out_cells, float *out_val,
+                                  void *ws, size_t ws_bytes, void *stream) {
+    return score_resident(q, kv, resident_pages, n_resident, res_ld, k, out_cells, out_val, ws,
+                          ws_bytes, stream, 1);
+}
+
+fm_status fm_densest_pages(const int32_t *density, int64_t density_ld, int B, int64_t n_pages,
+                           int kmax, int32_t *out_pages, int32_t *out_count, void *stream) {
+    REQUIRE(B >= 0, FM_ERR_INVALID_ARG, "B = %d", B);
+    REQUIRE(kmax >= 1 && kmax <= FM_MAX_K, FM_ERR_UNSUPPORTED, "kmax = %d (1..%d)", kmax, FM_MAX_K);
+    REQUIRE(n_pages >= 0 && n_pages <= density_ld && n_pages <= (int64_t)INT32_MAX,
+            FM_ERR_INVALID_ARG, "n_pages = %lld, density_ld = %lld", (long long)n_pages,
+            (long long)density_ld);
+    if (B == 0) return ok();
+    REQUIRE(density && out_pages, FM_ERR_INVALID_ARG, "density / out_pages NULL");
+    fm::DensestArgs a;
+    a.density = density;
+    a.ld = density_ld;
+    a.n_pages = n_pages;
+    a.kmax = kmax;
+    a.out_pages = out_pages;
+    a.out_count = out_count;
+    CHECK(launched(fm::launch_densest(a, B, (hipStream_t)stream), "densest_pages"));
     return ok();
 }
 

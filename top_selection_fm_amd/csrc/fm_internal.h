@@ -105,10 +105,20 @@ struct TopkArgs {
     const int32_t *res_pages;  // two-level index map (nullable)
     const int32_t *n_res;
     int64_t res_ld;
+    int res_cells;             // with res_pages: rank and emit reserve cells (row positions)
     int B;                     // requests (bounds row_req in two-level mode)
     int k;
     int32_t *out_idx;
     float *out_val;            // nullable
+};
+
+struct DensestArgs {
+    const int32_t *density;    // [B, ld]
+    int64_t ld;
+    int64_t n_pages;
+    int kmax;
+    int32_t *out_pages;        // [B, kmax]
+    int32_t *out_count;        // [B] or null
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -132,6 +142,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs &a, int key_fmt, int B, hipStream_t s);
 hipError_t launch_compact(const CompactArgs &a, int B, hipStream_t s);
+hipError_t launch_densest(const DensestArgs &a, int B, hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s);
 
 }  // namespace fm

@@ -268,10 +268,10 @@ __device__ RowSrc row_source(const TopkArgs &A, int t) {
     const bool b_ok = b >= 0 && b < A.B;
     RowSrc R;
     R.row = A.logits + (int64_t)t * A.ld;
-    R.rp = A.res_pages ? A.res_pages + (int64_t)(b_ok ? b : 0) * A.res_ld : nullptr;
+    R.rp = (A.res_pages && !A.res_cells) ? A.res_pages + (int64_t)(b_ok ? b : 0) * A.res_ld : nullptr;
     R.mrow = A.mask ? A.mask + (int64_t)(b_ok ? b : 0) * A.mask_ld : nullptr;
     int64_t n = b_ok ? A.ld : 0;
-    if (R.rp && b_ok) n = min(n, (int64_t)A.n_res[b] * kPage);
+    if (A.res_pages && b_ok) n = min(n, (int64_t)A.n_res[b] * kPage);
     if (A.n_valid) n = min(n, (int64_t)A.n_valid[t]);
     R.n = n < 0 ? 0 : n;
     return R;
@@ -1047,6 +1047,37 @@ __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
             A.page_list[(int64_t)b * A.page_list_ld + i] = -1;
 }
 
+// ---------------------------------------------------------------- densest pages
+// One request's page densities as top-k candidates: page p with density d > 0 is a candidate
+// of value d (exact in float for d <= 2^24); the radix selection ranks them by (d, lower p).
+struct DensSrc {
+    const int32_t *d;
+    int64_t n;
+    template <int NT, class F>
+    __device__ void each(F f) const {
+        for (int64_t p = threadIdx.x; p < n; p += NT) {
+            const int32_t x = d[p];
+            if (x > 0) f((float)x, p);
+        }
+    }
+};
+
+// One workgroup per request: the kmax densest pages, ascending page id, -1 padded.
+__global__ __launch_bounds__(kRowNT) void densest_kernel(DensestArgs A) {
+    constexpr int NT = kRowNT;
+    __shared__ TopkLds L;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const DensSrc src{A.density + (int64_t)b * A.ld, A.n_pages};
+    const Rule rule = radix_rule<NT>(src, (uint32_t)A.kmax, L.hist, L.sh, L.misc);
+    if (tid == 0) L.s_count = 0u;
+    __syncthreads();
+    gather<NT>(src, rule, L.sel_val, L.sel_idx, &L.s_count, FM_MAX_K);
+    __syncthreads();
+    const int cnt = (int)min(L.s_count, (uint32_t)A.kmax);
+    sort_and_write<NT>(L.sel_idx, L.sel_val, cnt, A.kmax, A.out_pages + (int64_t)b * A.kmax, nullptr);
+    if (tid == 0 && A.out_count) A.out_count[b] = cnt;
+}
+
 }  // namespace
 
 size_t topk_ws_bytes(int T, int64_t n) {
@@ -1083,6 +1114,11 @@ hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     topk_kernel<<<dim3((unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, ws ? *ws : TopkWs{}, ws ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_densest(const DensestArgs &a, int B, hipStream_t s) {
+    densest_kernel<<<dim3((unsigned)B), dim3(kRowNT), 0, s>>>(a);
     return hipGetLastError();
 }
 
