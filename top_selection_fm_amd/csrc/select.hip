@@ -429,14 +429,17 @@ __device__ uint32_t filter_range(const RowSrc &R, int64_t j0, int64_t j1, const 
 //
 // have_range: [rlo, rhi] bounds the buffer's values (the caller knows them; skips a reduction).
 // The output order: when every entry is below kOrderBits (small_entries), from a bitmap of the
-// selected entries and prefix popcounts; otherwise from counts of smaller entries.
+// selected entries and prefix popcounts; otherwise from counts of smaller entries.  out_rp
+// (small_entries only): the buffered indices are row positions of a resident-page row with an
+// ascending page list, written out as entries out_rp[j / 64] * 64 + j % 64.
 constexpr int kOrderBits = kBins * 32;
 template <int NT>
 __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uint32_t k,
                               uint32_t *hist, uint32_t *sh, uint32_t *misc, float *shf,
                               int32_t *bnd, int32_t *sel_idx, float *sel_val, uint32_t *cnt2,
                               int32_t *oi, float *ov, int k_out, bool have_range = false,
-                              float rlo = 0.f, float rhi = 0.f, bool small_entries = false) {
+                              float rlo = 0.f, float rhi = 0.f, bool small_entries = false,
+                              const int32_t *out_rp = nullptr) {
     const int tid = threadIdx.x;
     if (tid == 0) {
         cnt2[0] = 0u;
@@ -555,7 +558,7 @@ __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uin
             const int32_t e = sel_idx[i];
             const uint32_t wv = hist[e >> 5];
             const int pos = (int)pref[e >> 5] + __popc(wv & ((1u << (e & 31)) - 1u));
-            oi[pos] = e;
+            oi[pos] = out_rp ? out_rp[e >> 6] * kPage + (e & 63) : e;
             if (ov) ov[pos] = sel_val[i];
         }
     } else {
@@ -751,6 +754,8 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
         base += i < w ? ci : 0u;
         passed += ci;
     }
+    bool asc = false;
+
     if (passed <= (uint32_t)kBuf) {
         // a copy of tau the compiler cannot see through: the first pass's 64 compare masks
         // are not kept alive for this one
@@ -776,7 +781,15 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
                 }
             }
         }
+        // a resident-page row whose page list is ascending: positions and entries are in the
+        // same order, so the row is selected by position and mapped to entries when written
         if (R.rp) {
+            const int npg = (n32 + kPage - 1) / kPage;
+            int ok = 1;
+            for (int i = tid; i + 1 < npg; i += NT) ok &= R.rp[i] < R.rp[i + 1] ? 1 : 0;
+            asc = __syncthreads_and(ok) != 0;
+        }
+        if (R.rp && !asc) {
             // row positions to entries through the resident-page list, every lookup in flight
             constexpr int EPT = kBuf / NT;
             __syncthreads();
@@ -802,7 +815,7 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
         // values above the sample's maximum into the top bin (monotone, so still exact)
         select_buffer<NT>(L.bval, L.bent, (int)passed, k, L.hist, L.sh, L.misc, L.shf, L.bnd,
                           L.sel_idx, L.sel_val, L.cnt2, oi, ov, A.k, tau > -FLT_MAX, tau, smax,
-                          !R.rp && n <= (int64_t)kOrderBits);
+                          (!R.rp || asc) && n <= (int64_t)kOrderBits, asc ? R.rp : nullptr);
     } else {
         const Rule rule = radix_rule<NT>(R, k, L.hist, L.sh, L.misc);
         if (tid == 0) L.s_count = 0u;
