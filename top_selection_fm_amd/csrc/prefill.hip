@@ -16,8 +16,8 @@
 //
 // MFMA layout (v_mfma_scale_f32_16x16x128_f8f6f4, wave64).  Row i of fragment n of the A tile
 // is head 16 n + i of the wave's query row, so the accumulator lane 16 g + j holds heads
-// 16 n + 4 g + 0..3 for key entry j of a 16-entry block; the head sum is 16 in-lane terms plus
-// two row swaps across the four lane groups.  The K dimension (128 head dims) is split the same
+// 16 n + 4 g + 0..3 for key entry j of a 16-entry block; the head sum is 16 in-lane terms per
+// block, and one reduce-scatter over the four lane groups finishes a page's four blocks.  The K dimension (128 head dims) is split the same
 // way for queries and keys (32 consecutive bytes per lane), so the dot products are exact
 // whatever order the hardware walks K in.  The MFMAs of block u + 1 are issued between the
 // epilogue steps of block u, across page boundaries too.
@@ -87,18 +87,24 @@ __device__ __forceinline__ h2 relu16(float a, float b) {
     return __builtin_elementwise_min(__builtin_elementwise_max(x, h2{0, 0}), h2{1, 1});
 }
 
-// One fp8 accumulator tile of the epilogue: heads 8 n + 4 (g % 2) + 0..3 of this lane's row.
-__device__ __forceinline__ void epi_step(const f32x4 &c, h2 w01, h2 w23, float &a0, float &a1) {
-    a0 = __builtin_amdgcn_fdot2(relu16(c[0], c[1]), w01, a0, false);
-    a1 = __builtin_amdgcn_fdot2(relu16(c[2], c[3]), w23, a1, false);
+// One fp8 accumulator tile of the epilogue: heads 16 n + 4 g + 0..3 of this lane's row.
+__device__ __forceinline__ float epi_step(const f32x4 &c, h2 w01, h2 w23, float a) {
+    a = __builtin_amdgcn_fdot2(relu16(c[0], c[1]), w01, a, false);
+    return __builtin_amdgcn_fdot2(relu16(c[2], c[3]), w23, a, false);
 }
 
-// This lane's half of its row's 64-head sum plus the partner lane group's (lane xor 16), by a
-// row swap; both lanes of a pair add in the same order.
-__device__ __forceinline__ float pair_total(float p) {
-    const uint32_t u = __float_as_uint(p);
-    const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+// The four 16-entry blocks of a page as partial head sums p[u] (lane 16 g + j: heads 4 g + 0..3
+// of each fragment, entry j of block u) become totals by one reduce-scatter over the four
+// 16-lane rows: a 16-lane row swap and add leaves rows 0 + 1 and 2 + 3 of one block in the even
+// rows and of the other in the odd rows, and a 32-lane swap and add then leaves block g's total
+// (entry j) in row g.  Six instructions for the page.
+__device__ __forceinline__ float block_totals(float p0, float p1, float p2, float p3) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+    const float q01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float q23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(q01), __float_as_uint(q23), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
@@ -210,21 +216,18 @@ void prefill_fp8_kernel(PrefillArgs A) {
     auto flush = [&]() {
         if (row_ok && pend_s < A.out_ld) orow[pend_s] = pend_v;
     };
-    // the fp8 MFMAs of the next block into `nxt`, the current block's epilogue on the vector unit
+    // the fp8 MFMAs of the next block into `nxt`, the current block's epilogue on the vector
+    // unit: this lane's partial head sum of the current block
     auto phase = [&](f32x4 (&nxt)[4], const i32x8 &kn, const f32x4 (&cur)[4]) {
-        float a0 = 0.f, a1 = 0.f;
+        float a = 0.f;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             nxt[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 qf[n], kn, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, kScaleA, 0, 127);
-            epi_step(cur[n], wp[2 * n], wp[2 * n + 1], a0, a1);
+            a = epi_step(cur[n], wp[2 * n], wp[2 * n + 1], a);
             if (n & 1) __builtin_amdgcn_sched_barrier(0);
         }
-        // sum over the four lane groups (heads 4 g + 0..3 of every fragment)
-        const float p = pair_total(a0 + a1);
-        const uint32_t u = __float_as_uint(p);
-        const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        return a;
     };
 
     if (p_begin < p_vis) {
@@ -255,10 +258,10 @@ void prefill_fp8_kernel(PrefillArgs A) {
             tot[2] = phase(cb, k3, ca);
             k1 = kfrag(b1, 1);
             tot[3] = phase(ca, kn, cb);
-            // every lane holds all four block totals; lane group g stores block g
+            // lane group g holds block g's totals and stores them
             const int e = 16 * g + j;
             const int64_t s = p * kPage + e;
-            const float tt = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+            const float tt = block_totals(tot[0], tot[1], tot[2], tot[3]);
             const float v = s_phys[p - p_begin] >= 0 ? tt * row_factor * s_scale[b0][e]
                                                      : __builtin_nanf("");
             pend_s = s;
