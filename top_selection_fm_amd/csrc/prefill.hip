@@ -36,6 +36,10 @@
 
 #include "fm_internal.h"
 
+#ifndef FM_PF_WAVES
+#define FM_PF_WAVES 8   // query rows (waves) of a workgroup
+#endif
+
 namespace fm {
 namespace {
 
@@ -49,15 +53,11 @@ constexpr int kLdsRow = 144;                       // a key row's 128 codes, pad
 constexpr int kSExp = 25;                          // dot products of codes are scaled by 2^-25
 constexpr int kScaleA = 127 - kSExp;               // E8M0 block scale of the A operand
 constexpr int kMaxChunkPages = 128;                // pages of one workgroup's key chunk, at most
-constexpr int kWaves = 8;                          // one query row per wave
+constexpr int kWaves = FM_PF_WAVES;                // one query row per wave
+constexpr int kStageParts = 512 / (64 * kWaves);    // 16-byte parts of a page each thread stages
 constexpr int kThreads = 64 * kWaves;
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ u32x4 load16(const uint8_t *p) {  // 4-byte aligned
-    const uint32_t *w = (const uint32_t *)p;
-    return u32x4{w[0], w[1], w[2], w[3]};
-}
 
 __device__ __forceinline__ int row_request(const QArgs &q, const KvArgs &kv, int t) {
     const int b = q.row_req ? q.row_req[t] : (q.b_is_zero ? 0 : t);
@@ -113,7 +113,8 @@ void prefill_fp8_kernel(PrefillArgs A) {
     __shared__ float s_scale[3][kPage];
     __shared__ int s_phys[kMaxChunkPages];
 
-    const int tid = threadIdx.x, ln = __lane_id(), wave = tid >> 6;
+    const int tid = threadIdx.x, ln = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);                    // uniform
     const int j = ln & 15, g = ln >> 4;
     const int chunk = (int)(blockIdx.x % (unsigned)A.n_chunks);
     const int rblk = (int)(blockIdx.x / (unsigned)A.n_chunks);
@@ -189,20 +190,38 @@ void prefill_fp8_kernel(PrefillArgs A) {
         s_phys[i] = p_begin + i < p_end ? page_phys(A.kv, p_begin + i) : -1;
     __syncthreads();
 
-    // staging: thread tid carries entry tid / 8, code bytes 16 (tid % 8) .. + 15, and the scale
+    // staging: thread tid carries entry tid / 8, code bytes 16 (tid % 8) .. + 15, and the scale,
+    // through a buffer descriptor of the page (scalar setup, 32-bit offsets)
+    // (kStageParts parts a thread: entries se + i kThreads / 8)
     const int se = tid >> 3, sp = tid & 7;
-    u32x4 Rc = u32x4{0u, 0u, 0u, 0u};
-    float Rs = 0.f;
+    const uint32_t soff = (uint32_t)(se * kRowFp8);
+    u32x4 Rc[kStageParts];
+    float Rs[kStageParts];
+#pragma unroll
+    for (int i = 0; i < kStageParts; ++i) {
+        Rc[i] = u32x4{0u, 0u, 0u, 0u};
+        Rs[i] = 0.f;
+    }
     auto stage = [&](int64_t p) {
         const int64_t pc = min(p, p_vis - 1);
-        const int phys = max(s_phys[pc - p_begin], 0);
-        const uint8_t *row = A.kv.pool[0] + ((int64_t)phys * kPage + se) * kRowFp8;
-        Rc = load16(row + 16 * sp);
-        Rs = *(const float *)(row + kDim);
+        const int phys = __builtin_amdgcn_readfirstlane(max(s_phys[pc - p_begin], 0));   // uniform
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(A.kv.pool[0] + (int64_t)phys * (kPage * kRowFp8)), (short)0, kPage * kRowFp8,
+            0x00020000);
+#pragma unroll
+        for (int i = 0; i < kStageParts; ++i) {
+            const uint32_t o = soff + (uint32_t)(i * (kThreads / 8) * kRowFp8);
+            Rc[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 16 * sp, 0, 0);
+            Rs[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, o + kDim, 0, 0));
+        }
     };
     auto commit = [&](int buf) {
-        *(u32x4 *)&s_codes[buf][se * kLdsRow + 16 * sp] = Rc;
-        if (sp == 0) s_scale[buf][se] = Rs;
+#pragma unroll
+        for (int i = 0; i < kStageParts; ++i) {
+            const int e = se + i * (kThreads / 8);
+            *(u32x4 *)&s_codes[buf][e * kLdsRow + 16 * sp] = Rc[i];
+            if (sp == 0) s_scale[buf][e] = Rs[i];
+        }
     };
     auto kfrag = [&](int buf, int u) {
         const uint8_t *kp = s_codes[buf] + (16 * u + j) * kLdsRow + 32 * g;
@@ -211,10 +230,15 @@ void prefill_fp8_kernel(PrefillArgs A) {
         return i32x8{(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
                      (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
     };
-    int64_t pend_s = A.out_ld;
+    // the row's logits through a buffer descriptor: a store at or past out_ld is dropped
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)orow, (short)0, row_ok ? (int)(A.out_ld * 4) : 0, 0x00020000);
+    const int out_ld32 = (int)A.out_ld;                  // out_ld * 4 < 2^31 (checked on the host)
+    int pend_s = out_ld32;
     float pend_v = 0.f;
     auto flush = [&]() {
-        if (row_ok && pend_s < A.out_ld) orow[pend_s] = pend_v;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_v), orsrc,
+                                              (uint32_t)min(pend_s, out_ld32) * 4u, 0, 0);
     };
     // the fp8 MFMAs of the next block into `nxt`, the current block's epilogue on the vector
     // unit: this lane's partial head sum of the current block
@@ -260,7 +284,7 @@ void prefill_fp8_kernel(PrefillArgs A) {
             tot[3] = phase(ca, kn, cb);
             // lane group g holds block g's totals and stores them
             const int e = 16 * g + j;
-            const int64_t s = p * kPage + e;
+            const int s = (int)p * kPage + e;
             const float tt = block_totals(tot[0], tot[1], tot[2], tot[3]);
             const float v = s_phys[p - p_begin] >= 0 ? tt * row_factor * s_scale[b0][e]
                                                      : __builtin_nanf("");
