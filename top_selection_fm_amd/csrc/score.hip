@@ -76,6 +76,7 @@ constexpr int kSlotInvisible = -1;  // every entry of the page is past the visib
 constexpr int kSlotUnmapped = -2;   // the block table (or resident list) points nowhere valid
 constexpr int kSlotEmpty = -3;      // resident-list slot beyond n_resident: nothing to write
 constexpr int kMaxPpw = 16;         // page slots per wave, at most
+constexpr int kStoreNt = 2;         // buffer store cache policy: non-temporal
 constexpr int kMaskPpw = FM_MASK_MAXPPW;   // pages per wave of the fp8 mask kernel, at most
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -334,6 +335,48 @@ __device__ __forceinline__ void stream_pages(int n, Pg (&P)[NBUF], Fetch fetch, 
     }
 }
 
+// A wave's logits, staged in LDS as res[slot][entry], out to row orsrc.  Slot i of the wave is
+// output columns (slot0 + i) * 64 .. + 63 in both modes (its logical page, or its place in the
+// resident list), so the wave's logits are one contiguous run: with 16-byte aligned columns
+// (out_ld % 4 == 0) it goes out as 16-byte stores, lane ln taking entries 4 (ln % 16) .. + 3 of
+// slot 4 p + ln / 16, four slots an instruction (res must have 4 ceil(nslot / 4) rows, 16-byte
+// aligned).  Unmapped slots give NaN, invisible entries -inf, empty slots nothing.  The stores
+// are marked non-temporal: nothing reads the logits back in the kernel.
+__device__ __forceinline__ void store_wave_logits(const ScoreArgs &A, __amdgpu_buffer_rsrc_t orsrc,
+                                                  const float (*res)[64], int phys_l, int lp_l,
+                                                  int64_t slot0, int nslot, int64_t nvis, int ln) {
+    if ((A.out_ld & 3) == 0) {
+        const int c = 4 * (ln & 15);
+        for (int p = 0; 4 * p < nslot; ++p) {
+            const int i = 4 * p + (ln >> 4);          // < 16: slots past nslot are empty
+            const int phys = __shfl(phys_l, i);
+            const int lp = __shfl(lp_l, i);
+            const int64_t col = phys == kSlotEmpty ? A.out_ld : (slot0 + i) * kPage + c;
+            const f32x4 got = *(const f32x4 *)&res[i][c];
+            const float bad = phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY;
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = phys >= 0 ? got[e] : bad;
+                if ((int64_t)lp * kPage + c + e >= nvis) x = -INFINITY;
+                v[e] = __float_as_uint(x);
+            }
+            const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
+            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, voff, 0, kStoreNt);
+        }
+        return;
+    }
+    for (int i = 0; i < nslot; ++i) {
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        const int lp = __builtin_amdgcn_readlane(lp_l, i);
+        const int64_t col = phys == kSlotEmpty ? A.out_ld : (slot0 + i) * kPage + ln;
+        float v = phys >= 0 ? res[i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
+        if ((int64_t)lp * kPage + ln >= nvis) v = -INFINITY;
+        const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, kStoreNt);
+    }
+}
+
 // ---------------------------------------------------------------- row scoring kernel
 // grid (ceil(n_slots / (4 ppw)), T), 4 waves per workgroup, all on row blockIdx.y; wave w of
 // workgroup x scores slots [(4 x + w) ppw, +ppw).  The query fragments stay in registers; pages
@@ -346,7 +389,7 @@ template <int KF, int QF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_WAVES_PER_EU)))
 void score_kernel(ScoreArgs A) {
     typedef typename PageOf<KF>::T Pg;
-    __shared__ float s_res[4][kMaxPpw + 4][64];   // logits until the wave's loads are done
+    __shared__ __align__(16) float s_res[4][kMaxPpw + 4][64];   // logits until the wave's loads are done
     const int t = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int wave = threadIdx.x >> 6;
@@ -382,17 +425,7 @@ void score_kernel(ScoreArgs A) {
     };
     Pg P[PageOf<KF>::nbuf];
     stream_pages(nslot, P, fetch, emit);
-    for (int i = 0; i < nslot; ++i) {
-        const int phys = __builtin_amdgcn_readlane(phys_l, i);
-        const int lp = __builtin_amdgcn_readlane(lp_l, i);
-        const int64_t s = (int64_t)lp * kPage + ln;
-        const int64_t col = phys == kSlotEmpty ? A.out_ld
-                          : (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
-        float v = phys >= 0 ? s_res[wave][i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
-        if (s >= nvis) v = -INFINITY;
-        const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, 0);
-    }
+    store_wave_logits(A, orsrc, s_res[wave], phys_l, lp_l, slot0, nslot, nvis, ln);
 }
 
 // ---------------------------------------------------------------- bf16 decode: tile ring
@@ -409,34 +442,35 @@ template <int RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_DECODE_WAVES)))
 void score_bf16_ring_kernel(ScoreArgs A) {
     __shared__ u32x4 s_q[16][64];        // fragment (m, kk) = 4 m + kk, lane-contiguous
-    __shared__ float s_res[4][kMaxPpw][64];   // each wave's logits until its loads are done
+    __shared__ __align__(16) float s_res[4][kMaxPpw][64];   // each wave's logits until its loads are done
     const int t = blockIdx.y;
     const int ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int wave = threadIdx.x >> 6;
-    {
-        const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2;
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int fi = wave * 4 + f;
-            s_q[fi][ln] = q_frag_bf16<KEY_BF16>(qrow, fi >> 2, fi & 3, r, g);
-        }
-    }
-    __syncthreads();
+    // The page list is resolved first and the first key tiles are requested before the query
+    // fragments are staged: every wave of the grid starts at once, so the latency of these
+    // dependent reads is paid once per launch and is better overlapped than serialised.
     const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
-    if (slot0 >= A.n_slots) return;
-    const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
+    const int nslot = (int)max((int64_t)0, min((int64_t)A.ppw, A.n_slots - slot0));
     const int braw = row_request(A.q, A.kv, t);
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
     const uint8_t *pool = A.kv.pool[0];
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
-
     int lp_l = -1, phys_l = kSlotEmpty;
     if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
+    u32x4 qf[4];
+    {
+        const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int fi = wave * 4 + f;
+            qf[f] = q_frag_bf16<KEY_BF16>(qrow, fi >> 2, fi & 3, r, g);
+        }
+    }
     float wv[16];
     load_w(wv, A.q.w, A.q.w_bf16, t, g);
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
 
     const uint32_t off = (uint32_t)(r * kRowBf16 + g * 16);
     auto fetch = [&](TileBf16 &T, int x) {       // tile x: page x / 4, entry tile x % 4
@@ -476,6 +510,10 @@ void score_bf16_ring_kernel(ScoreArgs A) {
     TileBf16 T[RING];
 #pragma unroll
     for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) s_q[wave * 4 + f][ln] = qf[f];
+    __syncthreads();
+    if (nslot == 0) return;
     f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int x0 = 0; x0 < 4 * nslot; x0 += 4 * RING) {
 #pragma unroll
@@ -485,17 +523,7 @@ void score_bf16_ring_kernel(ScoreArgs A) {
             if ((u & 3) == 3) emit(tot, (x0 + u) >> 2);
         }
     }
-    for (int i = 0; i < nslot; ++i) {
-        const int phys = __builtin_amdgcn_readlane(phys_l, i);
-        const int lp = __builtin_amdgcn_readlane(lp_l, i);
-        const int64_t s = (int64_t)lp * kPage + ln;
-        const int64_t col = phys == kSlotEmpty ? A.out_ld
-                          : (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
-        float v = phys >= 0 ? s_res[wave][i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
-        if (s >= nvis) v = -INFINITY;
-        const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, 0);
-    }
+    store_wave_logits(A, orsrc, s_res[wave], phys_l, lp_l, slot0, nslot, nvis, ln);
 }
 
 // ---------------------------------------------------------------- fp8 keys x bf16 queries
@@ -709,7 +737,7 @@ __device__ __forceinline__ void stream_tiles_f8(int n, const QF &Q, Fetch fetch,
 template <int RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void score_f8_kernel(ScoreArgs A) {
-    __shared__ float s_res[4][kMaxPpw + RING][64];
+    __shared__ __align__(16) float s_res[4][kMaxPpw + RING][64];
     __shared__ u32x4 s_qa[16 * 64];
     const int t = blockIdx.y;
     const int ln = __lane_id();
@@ -735,17 +763,7 @@ void score_f8_kernel(ScoreArgs A) {
     };
     auto take = [&](float t0, float t1, int i) { s_res[wave][i][ln] = (ln >> 5) ? t1 : t0; };
     stream_tiles_f8<RING>(nslot, Q, fetch, take);
-    for (int i = 0; i < nslot; ++i) {
-        const int phys = __builtin_amdgcn_readlane(phys_l, i);
-        const int lp = __builtin_amdgcn_readlane(lp_l, i);
-        const int64_t s = (int64_t)lp * kPage + ln;
-        const int64_t col = phys == kSlotEmpty ? A.out_ld
-                          : (A.res_pages ? (slot0 + i) : (int64_t)lp) * kPage + ln;
-        float v = phys >= 0 ? s_res[wave][i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
-        if (s >= nvis) v = -INFINITY;
-        const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, 0);
-    }
+    store_wave_logits(A, orsrc, s_res[wave], phys_l, lp_l, slot0, nslot, nvis, ln);
 }
 
 // ---------------------------------------------------------------- fp32 path (VALU)
