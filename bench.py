@@ -17,7 +17,8 @@ HIP events recorded on the stream the kernels run on, in the eager timed loop.  
 roofline object reports the scoring kernel against HBM peak (8 TB/s) with its algorithmic
 bytes: keys once, q/w once, block table, logits written.  Secondary entries measure the other
 workloads (three-layer fp8 mask, two-level fp8 scoring over 384 resident pages, causal fp8
-prefill) the same way.  cpu_baseline times the fp64 oracle on a bounded sample of the
+prefill, and the Mode A selection of 21 layers x 8 requests over 262,144 masked candidates)
+the same way.  cpu_baseline times the fp64 oracle on a bounded sample of the
 headline workload on the host cores.
 
 Prints exactly one JSON line on stdout.
@@ -237,6 +238,35 @@ def run_prefill(torch, api, W, steps, warmup):
                 mfma_frac=flops / (per["score"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS)
 
 
+def run_mode_a(torch, api, W, steps, warmup, B=8, layers=21, n=262144, replicas=2):
+    """Mode A selection: full-history top-512 of every c4 layer of B requests (one row per
+    (request, layer), 262,144 candidates) under the request's resident mask, all layers in one
+    call through row_req.  The logits are synthetic (standard normal, replicas rotated); the
+    mask is page-clustered with about 12% of the pages resident."""
+    T = B * layers
+    g = torch.Generator(device="cuda:0").manual_seed(1006)
+    logits = [torch.randn((T, n), device="cuda:0", generator=g) for _ in range(replicas)]
+    pages = (torch.rand((B, n // 64), device="cuda:0", generator=g) < 0.12).to(torch.uint8)
+    mask = pages.repeat_interleave(64, dim=1).contiguous()
+    row_req = torch.arange(B, dtype=torch.int32, device="cuda:0").repeat_interleave(layers)
+    idx = torch.empty((T, 512), dtype=torch.int32, device="cuda:0")
+    nb = api.fm_workspace_bytes(api.FM_OP_TOPK, T, n)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+
+    def step(s, tm):
+        if tm: tm.mark(s, 0)
+        api.fm_topk512(logits[s % replicas], n, T, None, mask, n, row_req, 512, idx, None, ws, nb)
+        if tm: tm.mark(s, 1)
+
+    wall, per = timed(torch, ["topk"], step, steps, warmup)
+    ms = per["topk"]
+    alg = T * n * 4 + B * n + T * 4 + T * 512 * 4     # logits + each mask once + row map + out
+    return dict(workload=f"mode_a_topk512_b{B}_l{layers}_n{n}_masked", rows=T,
+                candidates=T * n, ms=ms, candidates_per_s=T * n / (ms * 1e-3),
+                hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes=alg, note="selection only; logits synthetic")
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, budget_s=12.0):
     import oracle
@@ -332,7 +362,7 @@ def main():
     if not args.headline_only:
         sec = []
         for name, fn in (("mask", run_mask), ("two_level", run_two_level),
-                         ("prefill", run_prefill)):
+                         ("prefill", run_prefill), ("mode_a", run_mode_a)):
             log(f"secondary: {name} ...")
             try:
                 sec.append(fn(torch, api, W, max(5, args.steps // 2), 2))

@@ -91,6 +91,52 @@ def test_topk_long_rows_262144_candidates(workspace):
     assert np.array_equal(ig, ri)
 
 
+def mode_a_inputs(rng, B, layers, n, resident_frac=0.12):
+    """Mode A: every layer's full-history logits of a request, one row per (request, layer),
+    sharing the request's resident mask through row_req (page-clustered residency)."""
+    L = rng.standard_normal((B * layers, n)).astype(np.float32)
+    pages = (rng.random((B, n // 64)) < resident_frac).astype(np.uint8)
+    mask = np.repeat(pages, 64, axis=1)
+    row_req = np.repeat(np.arange(B, dtype=np.int32), layers)
+    return L, mask, row_req
+
+
+@pytest.mark.parametrize("workspace", [True, False])
+def test_topk_mode_a_21_layers_shared_mask(workspace):
+    """Full-history top-512 of 21 layers over 262,144 candidates, the layers of a request
+    sharing its resident mask (rows 21 b .. 21 b + 20 -> request b).  Bit-exact."""
+    rng = np.random.default_rng(23)
+    L, mask, row_req = mode_a_inputs(rng, 2, 21, 262144)
+    L[5, np.flatnonzero(mask[0])[:3000]] = np.float32(1.75)     # a tie group among residents
+    ig, vg = gpu_topk(L, 512, mask=mask, row_req=row_req, workspace=workspace)
+    ri, rv = ref_topk(L, 512, mask=mask, row_req=row_req)
+    assert np.array_equal(ig, ri)
+    assert np.array_equal(vg[ri >= 0], rv[ri >= 0].astype(np.float32))
+    # nothing outside the request's resident pages is ever selected
+    for t in range(L.shape[0]):
+        sel = ig[t][ig[t] >= 0]
+        assert mask[row_req[t], sel].all()
+
+
+def test_topk_more_survivors_than_the_buffer():
+    """Long rows whose sampled positions run colder than the rest: the row's cut lets about
+    10% of the row through (far more than the 4,096-entry buffer, but under each chunk's
+    capacity), so the final selection runs over the stage-1 survivors.  Bit-exact."""
+    n = 262144
+    rng = np.random.default_rng(29)
+    L = rng.standard_normal((4, n)).astype(np.float32)
+    runs = (np.arange(128) * (n // 128))[:, None] + np.arange(16)[None, :]   # sampled positions
+    L[:, runs.ravel()] -= np.float32(1.0)
+    L[2, rng.choice(n, 20000, replace=False)] = np.float32(2.0)   # ties across the boundary
+    mask = (rng.random((2, n)) < 0.6).astype(np.uint8)
+    row_req = np.array([0, 1, 0, 1], np.int32)
+    for mk, rr in ((None, None), (mask, row_req)):
+        ig, vg = gpu_topk(L, 512, mask=mk, row_req=rr, workspace=True)
+        ri, rv = ref_topk(L, 512, mask=mk, row_req=rr)
+        assert np.array_equal(ig, ri)
+        assert np.array_equal(vg[ri >= 0], rv[ri >= 0].astype(np.float32))
+
+
 @pytest.mark.parametrize("workspace", [True, False])
 def test_topk_sampled_cut_and_its_fallbacks(workspace):
     """Long rows go through a sampled cut; rows where the cut cannot hold fall back to the exact

@@ -124,13 +124,17 @@ struct DensestArgs {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Top-k workspace: stage-1 survivors of every (row, kTopkChunk-entry chunk), kTopkCap each.
-constexpr int kTopkChunk = 8192;
+#ifndef FM_TOPK_CHUNK
+#define FM_TOPK_CHUNK 8192
+#endif
+constexpr int kTopkChunk = FM_TOPK_CHUNK;
 constexpr int kTopkCap = 1024;
 constexpr int kTopkMaxChunks = 256;   // staged path for rows of up to 2M entries
 struct TopkWs {
     float *val;      // [T, n_chunks, kTopkCap]
     int32_t *idx;    // [T, n_chunks, kTopkCap]
     int32_t *cnt;    // [T, n_chunks]; > kTopkCap: overflow or no cut
+    float4 *cut;     // [T]: the row's cut (bins lo, 1 / bin width, flat, cut bin as int bits)
     int n_chunks;
 };
 size_t topk_ws_bytes(int T, int64_t n);   // bytes for T rows of up to n entries (0: not used)

@@ -50,6 +50,7 @@ constexpr int kBins = 2048;
 constexpr int kRowThreads = 1024;     // page compaction
 constexpr int kTopkThreads = 512;
 constexpr int kSample = 2048;         // sampled entries of a long row
+constexpr int kLongSample = 8192;     // sampled entries of a row cut by its own kernel
 constexpr int kBnd = 1024;            // boundary-bin capacity of the final selection
 constexpr int kBuf = 4096;            // LDS candidate buffer
 constexpr int kTopkLdsThreads = 1024; // largest workgroup sharing TopkLds
@@ -300,16 +301,17 @@ struct Cut {
     int b;
 };
 
-// Sample position i of a row of n > kBuf entries: kSample / 16 runs of 16 contiguous entries
+// Sample position i (of M) of a row of n > kBuf entries: M / 16 runs of 16 contiguous entries
 // spread evenly over the row (few cache lines, many pages).
+template <int M>
 __device__ __forceinline__ int64_t sample_pos(int i, int64_t n) {
-    return (int64_t)(i >> 4) * n / (kSample / 16) + (i & 15);
+    return (int64_t)(i >> 4) * n / (M / 16) + (i & 15);
 }
 
 // Cut of row R from its sample (block-uniform).  Aims at the sample's (2 k m / n + 16)-th
 // largest value (m = sample size), i.e. about 2 k + 16 n / m candidates of the row passing:
 // comfortably more than k, far fewer than the buffer holds.
-template <int NT>
+template <int NT, int M>
 __device__ Cut row_cut(const RowSrc &R, uint32_t k, float *sval, uint32_t *hist, uint32_t *sh,
                        uint32_t *misc, float *shf) {
     const int tid = threadIdx.x;
@@ -318,11 +320,25 @@ __device__ Cut row_cut(const RowSrc &R, uint32_t k, float *sval, uint32_t *hist,
     c.b = -1;
     if (R.n <= kBuf) return c;
     float lo = INFINITY, hi = -INFINITY;
-    for (int i = tid; i < kSample; i += NT) {
-        float v;
-        int64_t s;
-        const bool ok = R.cand(sample_pos(i, R.n), v, s);
-        sval[i] = ok ? v : __builtin_nanf("");
+    static_assert(M % NT == 0, "sample layout");
+    constexpr int PER = M / NT;
+    // every sampled value in flight at once, then every mask byte (read unconditionally)
+    float sv[PER];
+    int64_t se[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int64_t j = sample_pos<M>(tid + q * NT, R.n);
+        sv[q] = R.row[j];
+        se[q] = R.entry(j);
+    }
+    uint8_t sm[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) sm[q] = R.mrow ? R.mrow[se[q]] : (uint8_t)1;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const float v = sv[q];
+        const bool ok = v > -INFINITY && sm[q] != 0;     // -inf and NaN are never candidates
+        sval[tid + q * NT] = ok ? v : __builtin_nanf("");
         if (ok) {
             lo = fminf(lo, v);
             hi = fmaxf(hi, v);
@@ -331,12 +347,12 @@ __device__ Cut row_cut(const RowSrc &R, uint32_t k, float *sval, uint32_t *hist,
     lo = block_reduce<NT>(lo, false, shf);
     hi = block_reduce<NT>(hi, true, shf);
     if (!(lo <= hi)) return c;                               // no sampled candidate
-    const uint32_t r = 2u * (uint32_t)(((uint64_t)k * kSample + R.n - 1) / R.n) + 16u;
+    const uint32_t r = 2u * (uint32_t)(((uint64_t)k * M + R.n - 1) / R.n) + 16u;
     LinBins bins{lo, 0.f, !(hi > lo)};
     bins.inv_w = bins.flat ? 0.f : (float)kBins / (hi - lo);
     for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < kSample; i += NT) {
+    for (int i = tid; i < M; i += NT) {
         const float v = sval[i];
         if (v == v) atomicAdd(&hist[bins(v)], 1u);
     }
@@ -589,7 +605,7 @@ __device__ void select_buffer(const float *bval, const int32_t *bent, int m, uin
 
 // Shared memory of a row cut and a chunk filter (the sample, the cut's histogram, reductions).
 struct CutLds {
-    float sample[kSample];
+    float sample[kLongSample];
     uint32_t hist[kBins];
     uint32_t sh[kTopkThreads / 64 + 1];
     uint32_t misc[2];
@@ -826,21 +842,22 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
     }
 }
 
-// Filter one kTopkChunk-entry chunk of row t into its workspace slot: every chunk of a long row
-// recomputes the row's cut from the same sample (identical result in every workgroup).
+// Filter one kTopkChunk-entry chunk of row t into its workspace slot with the row's cut, which
+// the cut kernel computed once for the row from its sample.
 __device__ void filter_chunk(const TopkArgs &A, const TopkWs &W, const RowSrc &R, int c, int t,
-                             CutLds &L) {
+                             uint32_t &s_count) {
     constexpr int NT = kTopkThreads;
-    static_assert(kTopkChunk == NT * 16, "one chunk = 16 values per thread");
+    constexpr int U = kTopkChunk / (4 * NT);      // float4 loads a thread
+    static_assert(U * 4 * NT == kTopkChunk, "chunk layout");
     const int tid = threadIdx.x, ln = __lane_id();
     const int64_t slot = (int64_t)t * W.n_chunks + c;
-    // the chunk's 16 values per thread are requested first and stay in flight while the cut
-    // is computed from the sample (element j = j0 + 4 (u NT + tid) + e)
+    // the chunk's values (4 U a thread) are requested first and stay in flight while the row's
+    // cut is read (element j = j0 + 4 (u NT + tid) + e)
     const int64_t j0 = (int64_t)c * kTopkChunk, j1 = min(j0 + kTopkChunk, R.n);
     const bool vec = !R.rp && ((uintptr_t)(R.row + j0) % 16 == 0);
-    float v[4][4];
+    float v[U][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
         const int64_t j = j0 + 4 * ((int64_t)u * NT + tid);
         if (vec && j + 4 <= j1) {
             const float4 x = *(const float4 *)(R.row + j);
@@ -850,14 +867,33 @@ __device__ void filter_chunk(const TopkArgs &A, const TopkWs &W, const RowSrc &R
             for (int e = 0; e < 4; ++e) v[u][e] = (j + e < j1) ? R.row[j + e] : -INFINITY;
         }
     }
-    const Cut cut = row_cut<NT>(R, (uint32_t)A.k, L.sample, L.hist, L.sh, L.misc, L.shf);
-    if (tid == 0) L.s_count = 0u;
+    // a mask row without a page map: the chunk's mask bytes come with the values (bounded by the
+    // row: bytes past n read as 0), so no hit waits on a dependent load
+    const bool pre = R.mrow && !R.rp;
+    uint8_t mb[U][4];
+    if (pre) {
+        const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)R.mrow, (short)0, (int)R.n, 0x00020000);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                mb[u][e] = __builtin_amdgcn_raw_buffer_load_b8(
+                    mr, (uint32_t)(j0 + 4 * ((int64_t)u * NT + tid) + e), 0, 0);
+    }
+    Cut cut;
+    {
+        const float4 cw = W.cut[t];
+        cut.bins = LinBins{cw.x, cw.y, cw.z != 0.f};
+        cut.b = __float_as_int(cw.w);
+    }
+    if (tid == 0) s_count = 0u;
     __syncthreads();
     float *bv = W.val + slot * kTopkCap;
     int32_t *be = W.idx + slot * kTopkCap;
     const uint64_t lt = (ln == 0) ? 0ull : (~0ull >> (64 - ln));
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int64_t j = j0 + 4 * ((int64_t)u * NT + tid) + e;
@@ -866,13 +902,13 @@ __device__ void filter_chunk(const TopkArgs &A, const TopkWs &W, const RowSrc &R
             bool hit = x > -INFINITY && cut.bins(x) >= cut.b;
             if (hit) {
                 sidx = R.entry(j);
-                hit = !(R.mrow && !R.mrow[sidx]);
+                hit = pre ? mb[u][e] != 0 : !(R.mrow && !R.mrow[sidx]);
             }
             const uint64_t mask = __ballot(hit);
             if (mask) {
                 const int leader = (int)__builtin_ctzll(mask);
                 uint32_t b0 = 0;
-                if (ln == leader) b0 = atomicAdd(&L.s_count, (uint32_t)__popcll(mask));
+                if (ln == leader) b0 = atomicAdd(&s_count, (uint32_t)__popcll(mask));
                 b0 = __shfl(b0, leader);
                 const uint32_t pos = b0 + (uint32_t)__popcll(mask & lt);
                 if (hit && pos < (uint32_t)kTopkCap) {
@@ -882,18 +918,43 @@ __device__ void filter_chunk(const TopkArgs &A, const TopkWs &W, const RowSrc &R
             }
         }
     __syncthreads();
-    if (tid == 0) W.cnt[slot] = cut.b < 0 ? (int32_t)(kTopkCap + 1) : (int32_t)L.s_count;
+    if (tid == 0) W.cnt[slot] = cut.b < 0 ? (int32_t)(kTopkCap + 1) : (int32_t)s_count;
 }
 
+// The stage-1 survivors of a row in the workspace, chunk c's at slot base + c (offs in LDS: chunk
+// c holds survivors offs[c] .. offs[c + 1] - 1 of the row).
+struct WsSrc {
+    const float *val;
+    const int32_t *idx;
+    const uint32_t *offs;
+    int n_chunks;
+    int64_t base;
+    template <int NT, class F>
+    __device__ void each(F f) const {
+        const uint32_t total = offs[n_chunks];
+        for (uint32_t g = threadIdx.x; g < total; g += NT) {
+            int lo = 0, hi = n_chunks;                      // offs[lo] <= g < offs[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (offs[mid] <= g) lo = mid; else hi = mid;
+            }
+            const int64_t at = (base + lo) * kTopkCap + (g - offs[lo]);
+            f(val[at], (int64_t)idx[at]);
+        }
+    }
+};
+
 // Final selection of row t.  With stage-1 survivors (staged) the buffer is filled from the
-// workspace; otherwise the workgroup cuts and filters the row itself.  When the cut did not hold
-// (fewer than k passed) or the buffer overflowed, the exact selection runs over the whole row.
+// workspace; otherwise the workgroup cuts and filters the row itself.  More survivors than the
+// buffer holds (but at least k, none dropped) are selected exactly from the workspace; when the
+// cut did not hold (fewer than k passed, or a chunk overflowed) the exact selection runs over the
+// whole row.
 __device__ void select_row(const TopkArgs &A, const TopkWs &W, bool staged, const RowSrc &R, int t,
                            TopkLds &L) {
     constexpr int NT = kTopkThreads;
     const int tid = threadIdx.x;
     const uint32_t k = (uint32_t)A.k;
-    bool from_buf;
+    bool from_buf, from_ws = false;
     uint32_t total = 0;
     if (staged) {
         // survivors of the row's chunks: offsets first, then one round of loads
@@ -912,6 +973,7 @@ __device__ void select_row(const TopkArgs &A, const TopkWs &W, bool staged, cons
         __syncthreads();
         total = L.offs[W.n_chunks];
         from_buf = !L.misc[0] && total >= k && total <= (uint32_t)kBuf;
+        from_ws = !L.misc[0] && total > (uint32_t)kBuf;
         __syncthreads();
         if (from_buf) {
             constexpr int U = kBuf / NT;
@@ -942,7 +1004,7 @@ __device__ void select_row(const TopkArgs &A, const TopkWs &W, bool staged, cons
         }
         __syncthreads();
     } else {
-        const Cut cut = row_cut<NT>(R, k, L.bval, L.hist, L.sh, L.misc, L.shf);
+        const Cut cut = row_cut<NT, kSample>(R, k, L.bval, L.hist, L.sh, L.misc, L.shf);
         total = filter_range<NT>(R, 0, R.n, cut, L.bval, L.bent, kBuf, &L.s_count);
         from_buf = total <= (uint32_t)kBuf && !(cut.b >= 0 && total < k);
     }
@@ -952,6 +1014,14 @@ __device__ void select_row(const TopkArgs &A, const TopkWs &W, bool staged, cons
     if (from_buf) {
         select_buffer<NT>(L.bval, L.bent, (int)total, k, L.hist, L.sh, L.misc, L.shf, L.bnd,
                           L.sel_idx, L.sel_val, L.cnt2, oi, ov, A.k);
+    } else if (from_ws) {
+        const WsSrc S{W.val, W.idx, L.offs, W.n_chunks, (int64_t)t * W.n_chunks};
+        const Rule rule = radix_rule<NT>(S, k, L.hist, L.sh, L.misc);
+        if (tid == 0) L.s_count = 0u;
+        __syncthreads();
+        gather<NT>(S, rule, L.sel_val, L.sel_idx, &L.s_count, FM_MAX_K);
+        __syncthreads();
+        sort_and_write<NT>(L.sel_idx, L.sel_val, (int)min(L.s_count, k), A.k, oi, ov);
     } else {
         const Rule rule = radix_rule<NT>(R, k, L.hist, L.sh, L.misc);
         if (tid == 0) L.s_count = 0u;
@@ -962,10 +1032,22 @@ __device__ void select_row(const TopkArgs &A, const TopkWs &W, bool staged, cons
     }
 }
 
+// Stage 0 of the workspace path: grid T, the cut of each long row from its sample, once.
+__global__ __launch_bounds__(kTopkThreads) void topk_cut_kernel(TopkArgs A, TopkWs W) {
+    __shared__ CutLds L;
+    const int t = blockIdx.x;
+    const RowSrc R = row_source(A, t);
+    if (R.n <= kBuf) return;                 // short rows: stage 2 selects them directly
+    const Cut c = row_cut<kTopkThreads, kLongSample>(R, (uint32_t)A.k, L.sample, L.hist, L.sh,
+                                                     L.misc, L.shf);
+    if (threadIdx.x == 0)
+        W.cut[t] = make_float4(c.bins.lo, c.bins.inv_w, c.bins.flat ? 1.f : 0.f, __int_as_float(c.b));
+}
+
 // Stage 1 of the workspace path: grid (n_chunks, T), one workgroup per kTopkChunk-entry chunk
 // of a long row.  A chunk past its row's end records no survivors.
 __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, TopkWs W) {
-    __shared__ CutLds L;
+    __shared__ uint32_t s_count;
     const int c = blockIdx.x, t = blockIdx.y;
     const RowSrc R = row_source(A, t);
     if (R.n <= kBuf) return;                 // short rows: stage 2 selects them directly
@@ -973,7 +1055,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_filter_kernel(TopkArgs A, T
         if (threadIdx.x == 0) W.cnt[(int64_t)t * W.n_chunks + c] = 0;
         return;
     }
-    filter_chunk(A, W, R, c, t, L);
+    filter_chunk(A, W, R, c, t, s_count);
 }
 
 // Stage 2: one workgroup per row selects from the chunks' survivors (rows longer than kBuf
@@ -1099,7 +1181,8 @@ size_t topk_ws_bytes(int T, int64_t n) {
         return 0;
     const size_t slots = (size_t)T * (size_t)((n + kTopkChunk - 1) / kTopkChunk);
     return align_up(slots * kTopkCap * sizeof(float), 256) +
-           align_up(slots * kTopkCap * sizeof(int32_t), 256) + align_up(slots * sizeof(int32_t), 256);
+           align_up(slots * kTopkCap * sizeof(int32_t), 256) + align_up(slots * sizeof(int32_t), 256) +
+           align_up((size_t)T * sizeof(float4), 256);
 }
 
 TopkWs topk_ws_carve(void *ws, int T, int64_t n) {
@@ -1113,6 +1196,8 @@ TopkWs topk_ws_carve(void *ws, int T, int64_t n) {
     W.idx = (int32_t *)p;
     p += align_up(slots * kTopkCap * sizeof(int32_t), 256);
     W.cnt = (int32_t *)p;
+    p += align_up(slots * sizeof(int32_t), 256);
+    W.cut = (float4 *)p;
     return W;
 }
 
@@ -1122,6 +1207,9 @@ hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s) {
         return hipGetLastError();
     }
     if (ws) {
+        topk_cut_kernel<<<dim3((unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, *ws);
+        const hipError_t e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
         topk_filter_kernel<<<dim3((unsigned)ws->n_chunks, (unsigned)a.T), dim3(kTopkThreads), 0, s>>>(a, *ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
