@@ -129,6 +129,9 @@ fm::KvArgs make_kv(const fm_kv_desc *kv) {
 // Page slots per wave: about one round of waves (resident = the waves the kernel keeps on the
 // chip at once), so each wave streams a run of pages instead of paying its start-up (query and
 // page-table loads) several times; at least 1, at most 16 slots each.
+#ifndef FM_F8_GENS
+#define FM_F8_GENS 1    // fp8 scoring: grid generations
+#endif
 #ifndef FM_DEC_GENS
 #define FM_DEC_GENS 1   // bf16 scoring: grid generations (resident waves x this many waves)
 #endif
@@ -153,9 +156,9 @@ fm_status run_score(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t 
     a.n_slots = n_slots;
     // waves resident at once: 256 CUs x 4 SIMDs x waves per SIMD of the kernel used
     const int64_t per_simd = kv->key_dtype == FM_BF16 ? 4 : kv->key_dtype == FM_FP8_E4M3_SCALED132 &&
-                             q->q_dtype == FM_BF16 ? 3 : 2;
+                             q->q_dtype == FM_BF16 ? FM_F8_WPE : 2;
     a.ppw = pages_per_wave((int64_t)q->T * n_slots, 1024 * per_simd *
-                           (kv->key_dtype == FM_BF16 ? FM_DEC_GENS : 1));
+                           (kv->key_dtype == FM_BF16 ? FM_DEC_GENS : FM_F8_GENS));
     if (kv->key_dtype == FM_F32) return launched(fm::launch_score_f32(a, st), "score_f32");
     const int qf = q->q_dtype == FM_FP8_E4M3 ? fm::Q_FP8 : fm::Q_BF16;
     return launched(fm::launch_score(a, key_fmt(kv->key_dtype), qf, st), "score");

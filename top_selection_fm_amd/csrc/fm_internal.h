@@ -124,6 +124,9 @@ struct DensestArgs {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Top-k workspace: stage-1 survivors of every (row, kTopkChunk-entry chunk), kTopkCap each.
+#ifndef FM_F8_WPE
+#define FM_F8_WPE 3       // fp8-key scoring with bf16 queries: waves per SIMD it is sized for
+#endif
 #ifndef FM_TOPK_CHUNK
 #define FM_TOPK_CHUNK 8192
 #endif

@@ -735,7 +735,7 @@ __device__ __forceinline__ void stream_tiles_f8(int n, const QF &Q, Fetch fetch,
 // Two-level (and any bf16-query) scoring over fp8 pages: the work split, slot states and
 // deferred stores of score_kernel, with the tile stream above.
 template <int RING>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_F8_WPE)))
 void score_f8_kernel(ScoreArgs A) {
     __shared__ __align__(16) float s_res[4][kMaxPpw + RING][64];
     __shared__ u32x4 s_qa[16 * 64];
