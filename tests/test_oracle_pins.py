@@ -488,3 +488,125 @@ def test_flop_table_slope_is_64_heads_by_128_dims():
         per.append((b1 - b0) * 1e9 / ((c1 - c0) / 4) / 21)
     for f in per:
         assert abs(f - 2 * W.HEADS * W.DIM) / (2 * W.HEADS * W.DIM) < 0.02
+
+
+# ----------------------------------------------------------------------------- query encoder
+from oracle import encoder as OE   # noqa: E402
+
+PAGE_ROPE = dict(rope_dim=64, base=160000.0, factor=16.0, orig_len=65536, beta_fast=32.0,
+                 beta_slow=1.0)   # the repository page's hyperparameter table
+
+
+def test_encoder_hadamard_is_sylvesters_normalised():
+    """Against scipy's Hadamard matrix (an independent construction), and H H = I."""
+    import scipy.linalg
+    rng = np.random.default_rng(41)
+    for n in (2, 8, 128):
+        x = rng.standard_normal((5, n))
+        H = scipy.linalg.hadamard(n).astype(np.float64)
+        assert np.allclose(OE.hadamard(x), x @ H / math.sqrt(n), rtol=0, atol=1e-12)
+        assert np.allclose(OE.hadamard(OE.hadamard(x)), x, rtol=0, atol=1e-12)
+    e0 = np.zeros(128)
+    e0[0] = 1.0
+    assert np.allclose(OE.hadamard(e0), np.full(128, 1 / math.sqrt(128)), rtol=0, atol=1e-15)
+
+
+def test_encoder_yarn_frequencies_follow_the_wavelength_rule():
+    """YaRN's definition in terms of wavelengths lambda_i = 2 pi / theta_i: a pair that turns more
+    than beta_fast times over the original context keeps theta_i, one that turns fewer than
+    beta_slow times is divided by the factor, and the pairs between are strictly between.  With
+    factor 1 the frequencies are plain RoPE's base^(-2i/d)."""
+    P = PAGE_ROPE
+    d, base = P["rope_dim"], P["base"]
+    theta = np.array([base ** (-2.0 * i / d) for i in range(d // 2)])
+    assert np.array_equal(OE.yarn_inv_freq(d, base, 1.0, P["orig_len"], P["beta_fast"],
+                                           P["beta_slow"]), theta)
+    inv = OE.yarn_inv_freq(d, base, P["factor"], P["orig_len"], P["beta_fast"], P["beta_slow"])
+    turns = P["orig_len"] / (2 * math.pi / theta)          # rotations over the original context
+    fast, slow = turns > P["beta_fast"], turns < P["beta_slow"]
+    mid = ~fast & ~slow
+    assert fast.sum() == 16 and slow.sum() == 7 and mid.sum() == 9
+    assert np.allclose(inv[fast], theta[fast], rtol=1e-15, atol=0)
+    assert np.allclose(inv[slow], theta[slow] / P["factor"], rtol=1e-15, atol=0)
+    assert np.all(inv[mid] < theta[mid]) and np.all(inv[mid] > theta[mid] / P["factor"])
+    assert np.all(np.diff(inv) < 0)                         # still strictly decreasing
+
+
+def test_encoder_rope_is_a_rotation_of_consecutive_pairs():
+    rng = np.random.default_rng(43)
+    P = PAGE_ROPE
+    inv = OE.yarn_inv_freq(P["rope_dim"], P["base"], P["factor"], P["orig_len"], P["beta_fast"],
+                           P["beta_slow"])
+    x = rng.standard_normal((3, 64))
+    assert np.array_equal(OE.rope(x, np.zeros(3), inv), x)              # position 0
+    pos = np.array([7.0, 131072.0, 999999.0])
+    y = OE.rope(x, pos, inv)
+    n0 = x[:, 0::2] ** 2 + x[:, 1::2] ** 2
+    assert np.allclose(y[:, 0::2] ** 2 + y[:, 1::2] ** 2, n0, rtol=1e-12, atol=0)
+    # a unit vector on the first coordinate of pair i turns to (cos, sin) of pos * theta_i
+    for i in (0, 17, 31):
+        e = np.zeros((1, 64))
+        e[0, 2 * i] = 1.0
+        r = OE.rope(e, np.array([12345.0]), inv)
+        assert np.allclose(r[0, 2 * i:2 * i + 2], [math.cos(12345 * inv[i]), math.sin(12345 * inv[i])],
+                           rtol=0, atol=1e-12)
+        assert np.count_nonzero(r) <= 2
+    # dot products depend on the position difference only
+    a, b = x[0:1], x[1:2]
+    d1 = np.sum(OE.rope(a, np.array([100.0]), inv) * OE.rope(b, np.array([37.0]), inv))
+    d2 = np.sum(OE.rope(a, np.array([5100.0]), inv) * OE.rope(b, np.array([5037.0]), inv))
+    assert abs(d1 - d2) < 1e-9
+
+
+def test_encoder_rms_norm_closed_forms():
+    assert np.allclose(OE.rms_norm(np.full((1, 16), 3.0), np.ones(16), 1e-6),
+                       np.full((1, 16), 3.0 / math.sqrt(9.0 + 1e-6)), rtol=1e-15, atol=0)
+    rng = np.random.default_rng(47)
+    a = rng.standard_normal((4, 256)) * 7.0
+    r = OE.rms_norm(a, np.ones(256), 0.0)
+    assert np.allclose(np.mean(r * r, axis=1), 1.0, rtol=1e-12, atol=0)
+    assert np.allclose(OE.rms_norm(5.0 * a, np.ones(256), 0.0), r, rtol=1e-12, atol=0)
+    g = rng.standard_normal(256)
+    assert np.allclose(OE.rms_norm(a, g, 0.0), r * g, rtol=1e-12, atol=0)
+
+
+def _encode_brute(h, pos, Wa, g, Wb, Wp, n_heads, head_dim, rope_dim, eps, inv):
+    """The pipeline with explicit loops and math, and the Hadamard entries from their closed form
+    (-1)^popcount(i & j), on tiny shapes."""
+    T, D = len(h), len(h[0])
+    R = len(Wa)
+    q = [[[0.0] * head_dim for _ in range(n_heads)] for _ in range(T)]
+    w = [[0.0] * n_heads for _ in range(T)]
+    for t in range(T):
+        a = [sum(h[t][k] * Wa[j][k] for k in range(D)) for j in range(R)]
+        ms = sum(v * v for v in a) / R
+        r = [a[j] / math.sqrt(ms + eps) * g[j] for j in range(R)]
+        for hh in range(n_heads):
+            x = [sum(r[k] * Wb[hh * head_dim + c][k] for k in range(R)) for c in range(head_dim)]
+            off = head_dim - rope_dim
+            for i in range(rope_dim // 2):
+                ang = pos[t] * inv[i]
+                x0, x1 = x[off + 2 * i], x[off + 2 * i + 1]
+                x[off + 2 * i] = x0 * math.cos(ang) - x1 * math.sin(ang)
+                x[off + 2 * i + 1] = x0 * math.sin(ang) + x1 * math.cos(ang)
+            for i in range(head_dim):
+                q[t][hh][i] = sum(x[j] * (-1) ** bin(i & j).count("1")
+                                  for j in range(head_dim)) / math.sqrt(head_dim)
+            w[t][hh] = sum(h[t][k] * Wp[hh][k] for k in range(D)) / math.sqrt(head_dim * n_heads)
+    return np.array(q), np.array(w)
+
+
+def test_encoder_matches_brute_force_on_tiny_shapes():
+    rng = np.random.default_rng(53)
+    T, D, R, NH, HD, RD = 3, 6, 4, 2, 8, 4
+    h, Wa, g = rng.standard_normal((T, D)), rng.standard_normal((R, D)), rng.standard_normal(R)
+    Wb, Wp = rng.standard_normal((NH * HD, R)), rng.standard_normal((NH, D))
+    pos = [0, 3, 70000]
+    inv = OE.yarn_inv_freq(RD, 100.0, 4.0, 64, 8.0, 1.0)
+    q, w = OE.encode(h, pos, Wa, g, Wb, Wp, n_heads=NH, head_dim=HD, rope_dim=RD, eps=1e-6,
+                     rope_base=100.0, rope_factor=4.0, rope_orig_len=64, beta_fast=8.0,
+                     beta_slow=1.0)
+    qb, wb = _encode_brute(h.tolist(), pos, Wa.tolist(), g.tolist(), Wb.tolist(), Wp.tolist(),
+                           NH, HD, RD, 1e-6, inv.tolist())
+    assert np.allclose(q, qb, rtol=0, atol=1e-10)
+    assert np.allclose(w, wb, rtol=0, atol=1e-12)
