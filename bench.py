@@ -17,8 +17,8 @@ HIP events recorded on the stream the kernels run on, in the eager timed loop.  
 roofline object reports the scoring kernel against HBM peak (8 TB/s) with its algorithmic
 bytes: keys once, q/w once, block table, logits written.  Secondary entries measure the other
 workloads (three-layer fp8 mask, two-level fp8 scoring over 384 resident pages, causal fp8
-prefill, and the Mode A selection of 21 layers x 8 requests over 262,144 masked candidates)
-the same way.  cpu_baseline times the fp64 oracle on a bounded sample of the
+prefill, the Mode A selection of 21 layers x 8 requests over 262,144 masked candidates, and
+the retriever's query encoder at decode and prefill batch sizes) the same way.  cpu_baseline times the fp64 oracle on a bounded sample of the
 headline workload on the host cores.
 
 Prints exactly one JSON line on stdout.
@@ -267,6 +267,44 @@ def run_mode_a(torch, api, W, steps, warmup, B=8, layers=21, n=262144, replicas=
                 alg_bytes=alg, note="selection only; logits synthetic")
 
 
+def run_encoder(torch, api, W, steps, warmup):
+    """The retriever's query encoder at the page's sizes (d_model 4096, q_rank 2048, 128 heads
+    of 128, RoPE on 64 dims): a decode batch of 32 rows (weight-bandwidth bound) and a prefill
+    batch of 4,096 rows (bf16 MFMA bound), synthetic weights and hidden states."""
+    out = {}
+    for T in (32, 4096):
+        e = W.query_encoder(T=T)
+        dev = "cuda:0"
+        t = {k: torch.from_numpy(getattr(e, k).view(np.int16)).to(dev)
+             for k in ("hidden", "wq_a", "q_norm", "wq_b", "w_proj")}
+        pos = torch.from_numpy(e.pos).to(dev)
+        desc = api.encoder_desc(t["wq_a"], t["q_norm"], t["wq_b"], t["w_proj"],
+                                n_heads=e.n_heads, d_model=e.d_model, q_rank=e.q_rank)
+        nb = api.fm_encode_workspace_bytes(desc, T)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        q = torch.empty((T, e.n_heads, 128), dtype=torch.bfloat16, device=dev)
+        w = torch.empty((T, e.n_heads), dtype=torch.float32, device=dev)
+
+        def step(s, tm):
+            if tm: tm.mark(s, 0)
+            api.fm_encode_queries(desc, t["hidden"], T, pos, q, w, ws, nb)
+            if tm: tm.mark(s, 1)
+
+        wall, per = timed(torch, ["encode"], step, steps, warmup)
+        ms = per["encode"]
+        wbytes = sum(t[k].numel() * 2 for k in ("wq_a", "q_norm", "wq_b", "w_proj"))
+        alg = wbytes + t["hidden"].numel() * 2 + T * 4 + q.numel() * 2 + w.numel() * 4
+        flops = 2 * T * (e.d_model * (e.q_rank + e.n_heads) + e.q_rank * e.n_heads * 128)
+        out[f"t{T}"] = dict(rows=T, ms=ms, rows_per_s=T / (ms * 1e-3),
+                            hbm_gbs=alg / (ms * 1e-3) / 1e9,
+                            hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                            mfma_tflops=flops / (ms * 1e-3) / 1e12,
+                            mfma_frac=flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            alg_bytes=alg, flops=flops)
+        del t, ws, q, w
+    return dict(workload="query_encoder_d4096_r2048_h128", **out)
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, budget_s=12.0):
     import oracle
@@ -362,7 +400,8 @@ def main():
     if not args.headline_only:
         sec = []
         for name, fn in (("mask", run_mask), ("two_level", run_two_level),
-                         ("prefill", run_prefill), ("mode_a", run_mode_a)):
+                         ("prefill", run_prefill), ("mode_a", run_mode_a),
+                         ("encoder", run_encoder)):
             log(f"secondary: {name} ...")
             try:
                 sec.append(fn(torch, api, W, max(5, args.steps // 2), 2))

@@ -162,9 +162,10 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
  * 1 <= k <= FM_MAX_K.  For ld <= 65,536 one workgroup per row selects in a single pass over
  * the row and no workspace is used (fm_workspace_bytes(FM_OP_TOPK, T, ld) is 0).  For longer
  * rows the workspace is optional: with ws 256-byte aligned and ws_bytes >=
- * fm_workspace_bytes(FM_OP_TOPK, T, ld), rows are first filtered by one workgroup per
- * 8,192-entry chunk, then selected by one workgroup per row; otherwise one workgroup per row
- * does everything.  Every path gives the same result.
+ * fm_workspace_bytes(FM_OP_TOPK, T, ld), each row's cut is taken from a sample by one
+ * workgroup per row, the rows are filtered by one workgroup per 8,192-entry chunk, then
+ * selected by one workgroup per row; otherwise one workgroup per row does everything.  Every
+ * path gives the same result.
  */
 fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_valid,
                      const uint8_t *mask, int64_t mask_ld, const int32_t *row_req, int k,
@@ -216,6 +217,56 @@ fm_status fm_densest_pages(const int32_t *density, int64_t density_ld, int B, in
 
 /* Workspace bytes an operation needs for T rows of up to max_candidates entries each. */
 size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates);
+
+/*
+ * The retriever's query encoder, one CSA layer (FlashMemory-DeepSeek-V4 repository page,
+ * section "Retriever architecture" and its "Hyperparameters" table).  For each row t:
+ *   a = hidden[t] . wq_a^T                       (q_rank values)
+ *   r = a / sqrt(mean(a^2) + rms_eps) * q_norm   (RMSNorm)
+ *   x = r . wq_b^T, as [n_heads, head_dim]
+ *   the last rope_dim dims of every head rotated by YaRN RoPE at position pos[t]: consecutive
+ *     pairs (2i, 2i+1) turn by pos[t] * theta_i, theta_i = rope_base^(-2i/rope_dim) blended
+ *     towards theta_i / rope_factor between the correction dims of beta_fast and beta_slow
+ *     over rope_orig_len (YaRN's per-dimension interpolation; no temperature factor)
+ *   q[t] = x . H / sqrt(head_dim), H Sylvester's Hadamard matrix (per head)
+ *   w[t] = (hidden[t] . w_proj^T) * head_dim^-0.5 * n_heads^-0.5
+ * Weights are Linear weights ([out, in] row-major bf16), all device pointers.  The products
+ * accumulate in float32, r is rounded to bf16 (the operand of the second product), q is
+ * rounded to bf16 at the end; w is float32.  q and w are the fm_query_desc inputs of the
+ * scoring calls (q_dtype FM_BF16, w_dtype FM_F32) when n_heads is 64.
+ */
+typedef struct fm_encoder_desc {
+    const void *wq_a;          /* bf16 [q_rank, d_model] */
+    const void *q_norm;        /* bf16 [q_rank] */
+    const void *wq_b;          /* bf16 [n_heads * head_dim, q_rank] */
+    const void *w_proj;        /* bf16 [n_heads, d_model] */
+    int d_model;               /* multiple of 16 (4096 on the page) */
+    int q_rank;                /* multiple of 32, q_rank + n_heads <= 4096 (2048) */
+    int n_heads;               /* multiple of 32 (128 on the page; 64 feeds the scoring calls) */
+    int head_dim;              /* must be 128 */
+    int rope_dim;              /* even, 0 .. head_dim (64) */
+    float rms_eps;             /* >= 0 (1e-6) */
+    float rope_base;           /* > 1 (160000) */
+    float rope_factor;         /* >= 1 (16) */
+    int rope_orig_len;         /* > 0 (65536) */
+    float beta_fast;           /* > beta_slow (32) */
+    float beta_slow;           /* > 0 (1) */
+} fm_encoder_desc;
+
+/* Workspace bytes fm_encode_queries needs for T rows (the two products' float32 results and r). */
+size_t fm_encode_workspace_bytes(const fm_encoder_desc *e, int T);
+
+/*
+ * Encode T rows: hidden bf16 [T, d_model] (16-byte aligned), pos int32 [T] (>= 0), q bf16
+ * [T, n_heads, head_dim] (4-byte aligned), w float32 [T, n_heads]; ws 256-byte aligned with
+ * ws_bytes >= fm_encode_workspace_bytes(e, T), its contents irrelevant.  T = 0 is a no-op.
+ * Errors: FM_ERR_INVALID_ARG (null pointer, bad size or alignment), FM_ERR_UNSUPPORTED
+ * (head_dim != 128, shapes off the multiples above), FM_ERR_WORKSPACE; nothing is launched on
+ * error.
+ */
+fm_status fm_encode_queries(const fm_encoder_desc *e, const void *hidden, int T,
+                            const int32_t *pos, void *q, float *w, void *ws, size_t ws_bytes,
+                            void *stream);
 
 /* Static description of a status code. */
 const char *fm_status_string(fm_status s);

@@ -239,3 +239,37 @@ def test_resident_mask_validation():
     assert mask_call(bad, kv) == api.FM_ERR_INVALID_ARG
     fp8 = [good_q("fp8") for _ in range(3)]
     assert mask_call(fp8, kv) == api.FM_ERR_UNSUPPORTED
+
+
+def good_enc(**kw):
+    e = api.encoder_desc(FAKE, FAKE, FAKE, FAKE, n_heads=128, d_model=4096, q_rank=2048)
+    for k, v in kw.items():
+        setattr(e, k, v)
+    return e
+
+
+def test_encode_queries_validation():
+    """Every bad encoder argument is refused on the host (nothing launched, no GPU needed)."""
+    need = api.fm_encode_workspace_bytes(good_enc(), 32)
+    assert need > 0
+    assert api.fm_encode_workspace_bytes(good_enc(), 4096) > need
+    assert api.fm_encode_workspace_bytes(good_enc(head_dim=64), 32) == 0
+    st = lambda e=None, T=32, h=FAKE, pos=FAKE, q=FAKE, w=FAKE, ws=FAKE, nb=need: status_of(
+        api.fm_encode_queries, good_enc() if e is None else e, h, T, pos, q, w, ws, nb)[0]
+    assert st(e=good_enc(head_dim=64)) == api.FM_ERR_UNSUPPORTED
+    assert st(e=good_enc(d_model=4100)) == api.FM_ERR_UNSUPPORTED
+    assert st(e=good_enc(q_rank=2050)) == api.FM_ERR_UNSUPPORTED
+    assert st(e=good_enc(n_heads=48)) == api.FM_ERR_UNSUPPORTED
+    assert st(e=good_enc(q_rank=4096, n_heads=128)) == api.FM_ERR_UNSUPPORTED   # > 4096 columns
+    assert st(e=good_enc(rope_dim=63)) == api.FM_ERR_INVALID_ARG
+    assert st(e=good_enc(rope_dim=130)) == api.FM_ERR_INVALID_ARG
+    assert st(e=good_enc(rope_factor=0.5)) == api.FM_ERR_INVALID_ARG
+    assert st(e=good_enc(beta_fast=0.5)) == api.FM_ERR_INVALID_ARG
+    assert st(e=good_enc(wq_b=None)) == api.FM_ERR_INVALID_ARG
+    assert st(T=-1) == api.FM_ERR_INVALID_ARG
+    assert st(h=None) == api.FM_ERR_INVALID_ARG
+    assert st(pos=None) == api.FM_ERR_INVALID_ARG
+    assert st(h=FAKE + 8) == api.FM_ERR_INVALID_ARG        # hidden not 16-byte aligned
+    assert st(nb=need - 1) == api.FM_ERR_WORKSPACE
+    assert st(ws=FAKE + 64) == api.FM_ERR_WORKSPACE         # workspace not 256-byte aligned
+    api.fm_encode_queries(good_enc(), None, 0, None, None, None, None, 0)   # T = 0: no-op

@@ -28,6 +28,7 @@ Q_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8": FM_FP8_E4M3}
 
 EXPORTS = ["fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
            "fm_score_resident_cells", "fm_densest_pages", "fm_workspace_bytes",
+           "fm_encode_queries", "fm_encode_workspace_bytes",
            "fm_status_string", "fm_last_error", "fm_version"]
 
 
@@ -50,6 +51,14 @@ class QueryDesc(C.Structure):
                 ("row_req", C.c_void_p), ("q_pos", C.c_void_p), ("compress_ratio", C.c_int)]
 
 
+class EncoderDesc(C.Structure):
+    _fields_ = [("wq_a", C.c_void_p), ("q_norm", C.c_void_p), ("wq_b", C.c_void_p),
+                ("w_proj", C.c_void_p), ("d_model", C.c_int), ("q_rank", C.c_int),
+                ("n_heads", C.c_int), ("head_dim", C.c_int), ("rope_dim", C.c_int),
+                ("rms_eps", C.c_float), ("rope_base", C.c_float), ("rope_factor", C.c_float),
+                ("rope_orig_len", C.c_int), ("beta_fast", C.c_float), ("beta_slow", C.c_float)]
+
+
 _lib = None
 
 
@@ -69,8 +78,11 @@ def lib():
         L.fm_score_resident.argtypes = [P, P, P, P, I64, C.c_int, P, P, P, C.c_size_t, P]
         L.fm_score_resident_cells.argtypes = [P, P, P, P, I64, C.c_int, P, P, P, C.c_size_t, P]
         L.fm_densest_pages.argtypes = [P, I64, C.c_int, I64, C.c_int, P, P, P]
+        L.fm_encode_queries.argtypes = [P, P, C.c_int, P, P, P, P, C.c_size_t, P]
+        L.fm_encode_workspace_bytes.argtypes = [P, C.c_int]
+        L.fm_encode_workspace_bytes.restype = C.c_size_t
         for f in ("fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
-                  "fm_score_resident_cells", "fm_densest_pages"):
+                  "fm_score_resident_cells", "fm_densest_pages", "fm_encode_queries"):
             getattr(L, f).restype = C.c_int
         L.fm_workspace_bytes.argtypes = [C.c_int, C.c_int, I64]
         L.fm_workspace_bytes.restype = C.c_size_t
@@ -185,6 +197,28 @@ def fm_densest_pages(density, density_ld: int, B: int, n_pages: int, kmax: int, 
                      out_count=None, stream=None) -> None:
     _check(lib().fm_densest_pages(_ptr(density), int(density_ld), int(B), int(n_pages), int(kmax),
                                   _ptr(out_pages), _ptr(out_count), _stream(stream)))
+
+
+def encoder_desc(wq_a, q_norm, wq_b, w_proj, *, n_heads: int, d_model: int, q_rank: int,
+                 head_dim: int = 128, rope_dim: int = 64, rms_eps: float = 1e-6,
+                 rope_base: float = 160000.0, rope_factor: float = 16.0,
+                 rope_orig_len: int = 65536, beta_fast: float = 32.0,
+                 beta_slow: float = 1.0) -> EncoderDesc:
+    """fm_encoder_desc over device tensors (bf16 bits); the defaults are the page's values."""
+    return EncoderDesc(_ptr(wq_a), _ptr(q_norm), _ptr(wq_b), _ptr(w_proj), int(d_model),
+                       int(q_rank), int(n_heads), int(head_dim), int(rope_dim), float(rms_eps),
+                       float(rope_base), float(rope_factor), int(rope_orig_len),
+                       float(beta_fast), float(beta_slow))
+
+
+def fm_encode_workspace_bytes(desc: EncoderDesc, T: int) -> int:
+    return int(lib().fm_encode_workspace_bytes(C.byref(desc), int(T)))
+
+
+def fm_encode_queries(desc: EncoderDesc, hidden, T: int, pos, q, w, ws, ws_bytes: int,
+                      stream=None) -> None:
+    _check(lib().fm_encode_queries(C.byref(desc), _ptr(hidden), int(T), _ptr(pos), _ptr(q),
+                                   _ptr(w), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def fm_workspace_bytes(op: int, T: int, max_candidates: int) -> int:

@@ -1,0 +1,253 @@
+// encoder.hip -- the retriever's query encoder: hidden states -> indexer queries q and weights w.
+//
+// The per-layer pipeline of the FlashMemory-DeepSeek-V4 repository page (section "Retriever
+// architecture", with its "Hyperparameters" table):
+//   a = hidden . wq_a^T,  r = RMSNorm(a) * q_norm,  x = r . wq_b^T as [n_heads, head_dim],
+//   YaRN RoPE on the last rope_dim dims of each head, normalised Walsh-Hadamard over head_dim;
+//   w = hidden . w_proj^T * head_dim^-0.5 * n_heads^-0.5.
+//
+// Four launches, all streaming their weights once from HBM:
+//   1. enc_gemm_kernel: [a | w_raw] = hidden . [wq_a ; w_proj]^T (float32, Z partial sums);
+//   2. enc_norm_kernel: RMSNorm -> r (bf16, the next product's operand), and the scaled head
+//      weights w;
+//   3. enc_gemm_kernel: x = r . wq_b^T (float32);
+//   4. enc_rope_had_kernel: per (row, head), the partials' sum, YaRN RoPE, Walsh-Hadamard.
+//
+// The products run on v_mfma_f32_32x32x16_bf16.  Weights are Linear weights ([out, in],
+// K-contiguous), so both MFMA operands are read straight from memory in their register layout:
+// lane j + 32 h of a wave holds row j's 8 values k0 + 8 h .. + 7 of a 16-wide k step, for the
+// activation (A) and the weight (B) alike, and the 32x32 accumulator register v of lane j + 32 h
+// is output row 8 (v / 4) + 4 h + v % 4, column j.  Decode-sized inputs (tens of rows) make
+// the products weight-bandwidth bound: Z workgroups of S waves share a 32 x 32 output tile, each
+// wave a K range, so that enough waves on enough CUs stream the weight matrix at once.
+#include <math.h>
+
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t bf16_rne(float x) {   // finite inputs
+    uint32_t u = __float_as_uint(x);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ f32x16 mma(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Workgroup (nt, mt, z) of S waves computes partial z of the 32 x 32 output tile (nt, mt):
+// wave w takes the K range [c ksplit, (c + 1) ksplit), c = z S + w, and the S accumulators are
+// summed through LDS into C[z].  Rows of A past M read as zeros through the buffer
+// descriptor's bounds.
+template <int S>
+__global__ __launch_bounds__(64 * S) void enc_gemm_kernel(EncGemmArgs G) {
+    const int ln = __lane_id(), j = ln & 31, h = ln >> 5;
+    const int w = threadIdx.x >> 6;
+    const int nt = blockIdx.x, mt = blockIdx.y, z = blockIdx.z;
+    const int N = G.N0 + G.N1;
+    const int n0 = nt * 32;
+    const uint16_t *W = n0 < G.N0 ? G.W0 + (int64_t)n0 * G.K : G.W1 + (int64_t)(n0 - G.N0) * G.K;
+    const int rows = min(32, G.M - mt * 32);
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(G.A + (int64_t)mt * 32 * G.lda), (short)0, rows * (int)G.lda * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)W, (short)0, 32 * G.K * 2, 0x00020000);
+    const int kb = min(G.K, (z * S + w) * G.ksplit), ke = min(G.K, kb + G.ksplit);
+    const uint32_t arow = (uint32_t)(j * G.lda * 2 + 16 * h), wrow = (uint32_t)(j * G.K * 2 + 16 * h);
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    // rounds of four 16-wide k steps; the next round's loads are issued before this round's
+    // MFMAs, so two rounds are in flight.  Only whole rounds inside [kb, ke) are fetched; the
+    // tail takes one 16-wide step at a time.
+    constexpr int RS = 4;
+    int k0 = kb;
+    const int rounds = (ke - kb) / (16 * RS);
+    if (rounds > 0) {
+        u32x4 a[2][RS], b[2][RS];
+        auto fetch = [&](u32x4 (&ra)[RS], u32x4 (&rb)[RS], int k) {
+#pragma unroll
+            for (int u = 0; u < RS; ++u) {
+                ra[u] = __builtin_amdgcn_raw_buffer_load_b128(ar, arow + (uint32_t)(k + 16 * u) * 2, 0, 0);
+                rb[u] = __builtin_amdgcn_raw_buffer_load_b128(wr, wrow + (uint32_t)(k + 16 * u) * 2, 0, 0);
+            }
+        };
+        fetch(a[0], b[0], k0);
+        for (int i = 0; i < rounds; i += 2) {
+            if (i + 1 < rounds) fetch(a[1], b[1], k0 + 16 * RS * (i + 1));
+#pragma unroll
+            for (int u = 0; u < RS; ++u) acc = mma(a[0][u], b[0][u], acc);
+            if (i + 1 < rounds) {
+                if (i + 2 < rounds) fetch(a[0], b[0], k0 + 16 * RS * (i + 2));
+#pragma unroll
+                for (int u = 0; u < RS; ++u) acc = mma(a[1][u], b[1][u], acc);
+            }
+        }
+        k0 += 16 * RS * rounds;
+    }
+    for (; k0 < ke; k0 += 16) {
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(ar, arow + (uint32_t)k0 * 2, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(wr, wrow + (uint32_t)k0 * 2, 0, 0);
+        acc = mma(a, b, acc);
+    }
+    // accumulator register v of lane l is output row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32
+    auto put = [&](int v, int l, float x) {
+        const int r = mt * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+        if (r < G.M) G.C[((int64_t)z * G.M + r) * N + n0 + (l & 31)] = x;
+    };
+    if constexpr (S == 1) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) put(v, ln, acc[v]);
+    } else {
+        __shared__ float red[S][16][64];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[w][v][ln] = acc[v];
+        __syncthreads();
+        for (int e = threadIdx.x; e < 16 * 64; e += 64 * S) {
+            const int v = e >> 6, l = e & 63;
+            float x = 0.f;
+#pragma unroll
+            for (int q = 0; q < S; ++q) x += red[q][v][l];
+            put(v, l, x);
+        }
+    }
+}
+
+template <int NT>
+__device__ float block_sum(float x, float *sh) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    if (__lane_id() == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += sh[i];
+    __syncthreads();
+    return t;
+}
+
+// One workgroup per row: a = the sum of the Z partials of hidden . wq_a^T, r = a / sqrt(mean(a^2)
+// + eps) * q_norm (bf16), w = the projected weights * weight scale.  Thread tid owns columns
+// tid + i NT of the row.
+constexpr int kNormNT = 1024;
+constexpr int kNormCols = 4;       // rank + n_heads <= kNormCols * kNormNT
+constexpr int kNormZ = 8;          // partials requested together
+__global__ __launch_bounds__(kNormNT) void enc_norm_kernel(EncNormArgs E) {
+    __shared__ float sh[kNormNT / 64];
+    const int m = blockIdx.x, tid = threadIdx.x;
+    const int N = E.rank + E.n_heads;
+    // every partial of the thread's columns requested at once (columns past N read column
+    // N - 1 and are not used), then summed
+    float a[kNormCols];
+#pragma unroll
+    for (int i = 0; i < kNormCols; ++i) a[i] = 0.f;
+    for (int z0 = 0; z0 < E.Z; z0 += kNormZ) {
+        float p[kNormZ][kNormCols];
+#pragma unroll
+        for (int dz = 0; dz < kNormZ; ++dz) {
+            const int z = min(z0 + dz, E.Z - 1);
+            const float *row = E.C + ((int64_t)z * E.M + m) * N;
+#pragma unroll
+            for (int i = 0; i < kNormCols; ++i) p[dz][i] = row[min(tid + i * kNormNT, N - 1)];
+        }
+#pragma unroll
+        for (int dz = 0; dz < kNormZ; ++dz)
+#pragma unroll
+            for (int i = 0; i < kNormCols; ++i) a[i] += z0 + dz < E.Z ? p[dz][i] : 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormCols; ++i) {
+        const int n = tid + i * kNormNT;
+        if (n < E.rank) ss = fmaf(a[i], a[i], ss);
+    }
+    const float ms = block_sum<kNormNT>(ss, sh) / (float)E.rank;
+    const float inv = 1.0f / sqrtf(ms + E.eps);
+#pragma unroll
+    for (int i = 0; i < kNormCols; ++i) {
+        const int n = tid + i * kNormNT;
+        if (n < E.rank) {
+            const float g = __uint_as_float((uint32_t)E.g[n] << 16);
+            E.r[(int64_t)m * E.rank + n] = bf16_rne(a[i] * inv * g);
+        } else if (n < N) {
+            E.w[(int64_t)m * E.n_heads + (n - E.rank)] = a[i] * E.w_scale;
+        }
+    }
+}
+
+// One wave per (row, head), four heads a workgroup: lane l holds dims 2 l, 2 l + 1.  The RoPE
+// angle pos * theta_i is formed and reduced in fp64 (positions reach millions of radians).
+__global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E) {
+    const int ln = __lane_id();
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= (int64_t)E.M * E.n_heads) return;
+    const int m = (int)(item / E.n_heads), hh = (int)(item % E.n_heads);
+    const int N = E.n_heads * kDim;
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll 4
+    for (int z = 0; z < E.Z; ++z) {
+        const float2 xv = *(const float2 *)&E.C[((int64_t)z * E.M + m) * N + hh * kDim + 2 * ln];
+        x0 += xv.x;
+        x1 += xv.y;
+    }
+    const int first = (kDim - E.rope_dim) / 2;          // the first rotated pair
+    if (ln >= first) {
+        const double ang = (double)E.pos[m] * E.inv_freq[ln - first];
+        const float c = (float)cos(ang), sn = (float)sin(ang);
+        const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+        x0 = y0;
+        x1 = y1;
+    }
+    // Walsh-Hadamard butterflies (Sylvester order): dims 2 l and 2 l + 1 in the lane, then
+    // lanes l and l ^ s for s = 1 .. 32 (dims 2 l + c and 2 (l ^ s) + c)
+    {
+        const float a = x0, b = x1;
+        x0 = a + b;
+        x1 = a - b;
+    }
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const float o0 = __shfl_xor(x0, s), o1 = __shfl_xor(x1, s);
+        const bool up = (ln & s) != 0;
+        x0 = up ? o0 - x0 : x0 + o0;
+        x1 = up ? o1 - x1 : x1 + o1;
+    }
+    const float nrm = 0.08838834764831845f;              // 1 / sqrt(128)
+    const uint32_t packed = (uint32_t)bf16_rne(x0 * nrm) | ((uint32_t)bf16_rne(x1 * nrm) << 16);
+    *(uint32_t *)&E.q[((int64_t)m * E.n_heads + hh) * kDim + 2 * ln] = packed;
+}
+
+}  // namespace
+
+hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
+    dim3 grid((unsigned)((g.N0 + g.N1) / 32), (unsigned)((g.M + 31) / 32), (unsigned)g.Z);
+    switch (g.S) {
+        case 1: enc_gemm_kernel<1><<<grid, 64, 0, s>>>(g); break;
+        case 2: enc_gemm_kernel<2><<<grid, 128, 0, s>>>(g); break;
+        case 4: enc_gemm_kernel<4><<<grid, 256, 0, s>>>(g); break;
+        case 8: enc_gemm_kernel<8><<<grid, 512, 0, s>>>(g); break;
+        case 16: enc_gemm_kernel<16><<<grid, 1024, 0, s>>>(g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_enc_norm(const EncNormArgs &a, hipStream_t s) {
+    enc_norm_kernel<<<dim3((unsigned)a.M), kNormNT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_enc_rope_had(const EncRopeArgs &a, hipStream_t s) {
+    const int64_t items = (int64_t)a.M * a.n_heads;
+    enc_rope_had_kernel<<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace fm

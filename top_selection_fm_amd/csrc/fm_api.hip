@@ -208,6 +208,102 @@ fm_status score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     return ok();
 }
 
+// ---------------------------------------------------------------- query encoder
+fm_status check_enc(const fm_encoder_desc *e) {
+    REQUIRE(e, FM_ERR_INVALID_ARG, "encoder descriptor is NULL");
+    REQUIRE(e->wq_a && e->q_norm && e->wq_b && e->w_proj, FM_ERR_INVALID_ARG,
+            "encoder weight pointer is NULL");
+    REQUIRE(e->head_dim == FM_HEAD_DIM, FM_ERR_UNSUPPORTED, "head_dim %d (only %d)", e->head_dim,
+            FM_HEAD_DIM);
+    REQUIRE(e->d_model >= 16 && e->d_model % 16 == 0 && e->d_model <= (1 << 20),
+            FM_ERR_UNSUPPORTED, "d_model %d (a multiple of 16, at most 2^20)", e->d_model);
+    REQUIRE(e->q_rank >= 32 && e->q_rank % 32 == 0, FM_ERR_UNSUPPORTED,
+            "q_rank %d (a multiple of 32)", e->q_rank);
+    REQUIRE(e->n_heads >= 32 && e->n_heads % 32 == 0 && e->n_heads <= 1024, FM_ERR_UNSUPPORTED,
+            "n_heads %d (a multiple of 32, at most 1024)", e->n_heads);
+    REQUIRE(e->q_rank + e->n_heads <= 4096, FM_ERR_UNSUPPORTED,
+            "q_rank + n_heads = %d (at most 4096)", e->q_rank + e->n_heads);
+    REQUIRE(e->rope_dim >= 0 && e->rope_dim <= FM_HEAD_DIM && e->rope_dim % 2 == 0,
+            FM_ERR_INVALID_ARG, "rope_dim %d (even, 0 .. %d)", e->rope_dim, FM_HEAD_DIM);
+    REQUIRE(e->rms_eps >= 0.f && isfinite(e->rms_eps), FM_ERR_INVALID_ARG, "rms_eps");
+    REQUIRE(e->rope_base > 1.f && isfinite(e->rope_base), FM_ERR_INVALID_ARG, "rope_base");
+    REQUIRE(e->rope_factor >= 1.f && isfinite(e->rope_factor), FM_ERR_INVALID_ARG,
+            "rope_factor");
+    REQUIRE(e->rope_orig_len > 0, FM_ERR_INVALID_ARG, "rope_orig_len");
+    REQUIRE(e->beta_slow > 0.f && e->beta_fast > e->beta_slow && isfinite(e->beta_fast),
+            FM_ERR_INVALID_ARG, "beta_fast > beta_slow > 0 required");
+    return FM_OK;
+}
+
+// Split-K plan of a product with `tiles` 32 x 32 output tiles over K: about FM_ENC_WAVES waves, each
+// split a multiple of 128 long (the kernel's unrolled round) unless K itself is shorter.
+#ifndef FM_ENC_WAVES
+#define FM_ENC_WAVES 2048   // waves a product aims at
+#endif
+// Work split of a product with `tiles` 32 x 32 output tiles over K: S waves a workgroup (at
+// most 4) and Z workgroups a tile (partial sums), about FM_ENC_WAVES waves on at least ~256
+// workgroups in all when the shape allows, each wave's K range a multiple of 64 long (at least
+// 128) unless K is shorter.
+struct EncSplit {
+    int S, Z, ksplit;
+};
+EncSplit enc_split(int64_t tiles, int K) {
+    EncSplit p{1, 1, K};
+    auto room = [&](int parts) { return K / (2 * parts) >= 128; };
+    while (p.S < 4 && tiles * p.S * p.Z < FM_ENC_WAVES && room(p.S * p.Z)) p.S *= 2;
+    while (p.Z < 16 && tiles * p.S * p.Z < FM_ENC_WAVES && room(p.S * p.Z)) p.Z *= 2;
+    int64_t ks = (K + p.S * p.Z - 1) / (p.S * p.Z);
+    ks = (ks + 63) / 64 * 64;
+    if (ks >= K) ks = K;
+    p.ksplit = (int)ks;
+    return p;
+}
+
+struct EncPlan {
+    EncSplit g1, g2;
+    size_t off_r, off_c2, bytes;
+};
+
+EncPlan enc_plan(const fm_encoder_desc *e, int T) {
+    EncPlan p;
+    const int64_t mt = (T + 31) / 32;
+    const int64_t n1 = e->q_rank + e->n_heads, n2 = (int64_t)e->n_heads * FM_HEAD_DIM;
+    p.g1 = enc_split(mt * (n1 / 32), e->d_model);
+    p.g2 = enc_split(mt * (n2 / 32), e->q_rank);
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t c1 = al((size_t)p.g1.Z * T * n1 * 4), r = al((size_t)T * e->q_rank * 2);
+    const size_t c2 = al((size_t)p.g2.Z * T * n2 * 4);
+    p.off_r = c1;
+    p.off_c2 = c1 + r;
+    p.bytes = c1 + r + c2;
+    return p;
+}
+
+// YaRN per-pair frequencies: theta_i = base^(-2i/d), divided by the factor above the slow
+// correction dim, kept below the fast one, blended linearly in between.  The correction dim of
+// beta is the pair index whose wavelength fits beta times into the original context.
+void yarn_freqs(const fm_encoder_desc *e, double *out) {
+    const int d = e->rope_dim, half = d / 2;
+    const double base = e->rope_base, f = e->rope_factor;
+    auto corr = [&](double beta) {
+        return d * log((double)e->rope_orig_len / (beta * 2.0 * M_PI)) / (2.0 * log(base));
+    };
+    double lo = floor(corr(e->beta_fast)), hi = ceil(corr(e->beta_slow));
+    if (lo < 0) lo = 0;
+    if (hi > half - 1) hi = half - 1;
+    if (hi == lo) hi = lo + 0.001;
+    for (int i = 0; i < half; ++i) {
+        const double th = pow(base, -2.0 * i / d);
+        if (f == 1.0) {
+            out[i] = th;
+            continue;
+        }
+        double ramp = (i - lo) / (hi - lo);
+        ramp = ramp < 0 ? 0 : ramp > 1 ? 1 : ramp;
+        out[i] = th / f * ramp + th * (1.0 - ramp);
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,6 +459,86 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
     c.page_list_ld = page_list_ld;
     c.page_density = page_density;
     CHECK(launched(fm::launch_compact(c, kv->B, st), "page_compact"));
+    return ok();
+}
+
+size_t fm_encode_workspace_bytes(const fm_encoder_desc *e, int T) {
+    if (T <= 0 || T > (1 << 22) || check_enc(e) != FM_OK) return 0;
+    return enc_plan(e, T).bytes;
+}
+
+fm_status fm_encode_queries(const fm_encoder_desc *e, const void *hidden, int T,
+                            const int32_t *pos, void *q, float *w, void *ws, size_t ws_bytes,
+                            void *stream) {
+    CHECK(check_enc(e));
+    REQUIRE(T >= 0 && T <= (1 << 22), FM_ERR_INVALID_ARG, "T = %d (0 .. 2^22)", T);
+    if (T == 0) return ok();
+    REQUIRE(hidden && pos && q && w, FM_ERR_INVALID_ARG, "hidden, pos, q and w must be non-NULL");
+    REQUIRE(aligned(hidden, 16), FM_ERR_INVALID_ARG, "hidden must be 16-byte aligned");
+    REQUIRE(aligned(q, 4) && aligned(w, 4), FM_ERR_INVALID_ARG, "q and w must be 4-byte aligned");
+    const EncPlan p = enc_plan(e, T);
+    REQUIRE(ws && aligned(ws, 256) && ws_bytes >= p.bytes, FM_ERR_WORKSPACE,
+            "workspace: need %zu bytes, 256-byte aligned", p.bytes);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t *base = (uint8_t *)ws;
+    float *c1 = (float *)base;
+    uint16_t *r = (uint16_t *)(base + p.off_r);
+    float *c2 = (float *)(base + p.off_c2);
+
+    fm::EncGemmArgs g1;
+    g1.A = (const uint16_t *)hidden;
+    g1.lda = e->d_model;
+    g1.M = T;
+    g1.W0 = (const uint16_t *)e->wq_a;
+    g1.N0 = e->q_rank;
+    g1.W1 = (const uint16_t *)e->w_proj;
+    g1.N1 = e->n_heads;
+    g1.K = e->d_model;
+    g1.ksplit = p.g1.ksplit;
+    g1.S = p.g1.S;
+    g1.Z = p.g1.Z;
+    g1.C = c1;
+    CHECK(launched(fm::launch_enc_gemm(g1, st), "encoder wq_a / w_proj"));
+
+    fm::EncNormArgs na;
+    na.C = c1;
+    na.Z = p.g1.Z;
+    na.M = T;
+    na.rank = e->q_rank;
+    na.n_heads = e->n_heads;
+    na.g = (const uint16_t *)e->q_norm;
+    na.eps = e->rms_eps;
+    na.w_scale = (float)(1.0 / sqrt((double)e->head_dim * (double)e->n_heads));
+    na.r = r;
+    na.w = w;
+    CHECK(launched(fm::launch_enc_norm(na, st), "encoder RMSNorm"));
+
+    fm::EncGemmArgs g2;
+    g2.A = r;
+    g2.lda = e->q_rank;
+    g2.M = T;
+    g2.W0 = (const uint16_t *)e->wq_b;
+    g2.N0 = e->n_heads * FM_HEAD_DIM;
+    g2.W1 = nullptr;
+    g2.N1 = 0;
+    g2.K = e->q_rank;
+    g2.ksplit = p.g2.ksplit;
+    g2.S = p.g2.S;
+    g2.Z = p.g2.Z;
+    g2.C = c2;
+    CHECK(launched(fm::launch_enc_gemm(g2, st), "encoder wq_b"));
+
+    fm::EncRopeArgs ra;
+    ra.C = c2;
+    ra.Z = p.g2.Z;
+    ra.M = T;
+    ra.n_heads = e->n_heads;
+    ra.rope_dim = e->rope_dim;
+    ra.pos = pos;
+    for (int i = 0; i < fm::kEncMaxPairs; ++i) ra.inv_freq[i] = 0.0;
+    yarn_freqs(e, ra.inv_freq);
+    ra.q = (uint16_t *)q;
+    CHECK(launched(fm::launch_enc_rope_had(ra, st), "encoder RoPE / Hadamard"));
     return ok();
 }
 

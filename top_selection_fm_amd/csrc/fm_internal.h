@@ -140,6 +140,41 @@ struct TopkWs {
     float4 *cut;     // [T]: the row's cut (bins lo, 1 / bin width, flat, cut bin as int bits)
     int n_chunks;
 };
+// Query encoder (encoder.hip): split-K products, RMSNorm + head weights, RoPE + Hadamard.
+constexpr int kEncMaxPairs = FM_HEAD_DIM / 2;   // rotated pairs of a head, at most
+struct EncGemmArgs {        // C[m, n] = sum over k of A[m, k] * W[n, k]
+    const uint16_t *A;      // bf16 [M, lda]
+    int64_t lda;
+    int M;
+    const uint16_t *W0;     // bf16 [N0, K]: columns 0 .. N0 - 1
+    int N0;
+    const uint16_t *W1;     // bf16 [N1, K]: columns N0 .. N0 + N1 - 1 (N1 may be 0)
+    int N1;
+    int K;
+    int ksplit;             // K per wave, a multiple of 16
+    int S;                  // waves per workgroup: 1, 2, 4, 8 or 16
+    int Z;                  // workgroups per output tile (partial sums)
+    float *C;               // [Z, M, N0 + N1]
+};
+struct EncNormArgs {
+    const float *C;         // [Z, M, rank + n_heads]: partials of hidden . [wq_a ; w_proj]^T
+    int Z, M, rank, n_heads;
+    const uint16_t *g;      // bf16 [rank] RMSNorm weight
+    float eps, w_scale;
+    uint16_t *r;            // bf16 [M, rank]
+    float *w;               // [M, n_heads]
+};
+struct EncRopeArgs {
+    const float *C;         // [Z, M, n_heads * 128]: partials of r . wq_b^T
+    int Z, M, n_heads, rope_dim;
+    const int32_t *pos;     // [M]
+    double inv_freq[kEncMaxPairs];
+    uint16_t *q;            // bf16 [M, n_heads, 128]
+};
+hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s);
+hipError_t launch_enc_norm(const EncNormArgs &a, hipStream_t s);
+hipError_t launch_enc_rope_had(const EncRopeArgs &a, hipStream_t s);
+
 size_t topk_ws_bytes(int T, int64_t n);   // bytes for T rows of up to n entries (0: not used)
 TopkWs topk_ws_carve(void *ws, int T, int64_t n);
 

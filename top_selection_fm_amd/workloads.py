@@ -340,3 +340,31 @@ def prefill_causal_fp8(seed: int = 1005, T: int = 4096, pos0: int = 131072,
                   q_pos=(pos0 + np.arange(T)).astype(np.int32), compress_ratio=ratio)
     return Workload(f"prefill_causal_fp8_t{T}_s{seq_len}", kv, [qry],
                     meta=dict(pos0=pos0))
+
+
+class EncoderInputs:
+    """Synthetic inputs of the retriever's query encoder (bf16 bit patterns, uint16)."""
+
+    def __init__(self, name, hidden, pos, wq_a, q_norm, wq_b, w_proj, n_heads):
+        self.name = name
+        self.hidden, self.pos = hidden, pos
+        self.wq_a, self.q_norm, self.wq_b, self.w_proj = wq_a, q_norm, wq_b, w_proj
+        self.n_heads = n_heads
+        self.T, self.d_model = hidden.shape
+        self.q_rank = wq_a.shape[0]
+
+
+def query_encoder(seed: int = 1007, T: int = 32, n_heads: int = 128, d_model: int = 4096,
+                  q_rank: int = 2048, max_pos: int = 1 << 20) -> EncoderInputs:
+    """The encoder at the page's sizes (d_model 4096, q_rank 2048, head_dim 128): random
+    Linear weights with 1/sqrt(fan_in) scale, an RMSNorm weight near 1, unit-normal hidden
+    states, positions uniform over a 1M-token context."""
+    rng = make_rng(seed)
+    hidden = bf16_bits(_normal(rng, (T, d_model)))
+    wq_a = bf16_bits(_normal(rng, (q_rank, d_model), std=1.0 / np.sqrt(d_model)))
+    q_norm = bf16_bits(_normal(rng, (q_rank,), mean=1.0, std=0.05))
+    wq_b = bf16_bits(_normal(rng, (n_heads * DIM, q_rank), std=1.0 / np.sqrt(q_rank)))
+    w_proj = bf16_bits(_normal(rng, (n_heads, d_model), std=1.0 / np.sqrt(d_model)))
+    pos = rng.integers(0, max_pos, size=T).astype(np.int32)
+    return EncoderInputs(f"query_encoder_t{T}_h{n_heads}_d{d_model}_r{q_rank}", hidden, pos,
+                         wq_a, q_norm, wq_b, w_proj, n_heads)
