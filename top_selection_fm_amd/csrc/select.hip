@@ -682,14 +682,16 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
 
     // The cut: candidates x >= tau pass.  -FLT_MAX (no cut) passes every candidate and no -inf
     // or NaN.  For rows > kBuf the cut comes from a sample of SPT register values a thread,
-    // v[(SPT tid + q) % kRowVec][q] (q < SPT: spread over the whole row), aiming at about
-    // 2 k + 16 n / kSample candidates passing.
+    // v[(SPT tid + q) % un][q] (q < SPT), un the number of float4 blocks a thread holds that
+    // reach into the row: the sample spreads over the row's entries only, whatever its length,
+    // aiming at about 2 k + 16 n / kSample candidates passing.
     float tau = -FLT_MAX, smax = 0.f;
     if (n > kBuf) {
         float lo = INFINITY, hi = -INFINITY;
+        const int un = min(kRowVec, (n32 + 4 * NT - 1) / (4 * NT));
+        int uq = (int)((uint32_t)(SPT * tid) % (uint32_t)un);
 #pragma unroll
-        for (int q = 0; q < SPT; ++q) {
-            const int uq = (SPT * tid + q) & (kRowVec - 1);
+        for (int q = 0; q < SPT; ++q, uq = uq + 1 == un ? 0 : uq + 1) {
             float sq = -INFINITY;
 #pragma unroll
             for (int u = 0; u < kRowVec; ++u) sq = u == uq ? v[u][q] : sq;
