@@ -76,6 +76,28 @@ def test_topk_n_valid_mask_and_row_req(workspace):
     assert np.all(ig[0] == -1)
 
 
+@pytest.mark.parametrize("n", [1, 700, 4097, 20000, 34816, 34817])
+def test_topk_many_rows(n):
+    """520 rows, two workgroups a CU: rows of up to 34,816 entries take the 512-thread row
+    kernel, 34,817 the 1,024-thread one.  Constructed rows, n_valid, a mask per request and
+    row_req, bit-exact against the oracle."""
+    rng = np.random.default_rng(n + 77)
+    T = 520
+    L = constructed_rows(rng, T, n)
+    L[8:] *= rng.uniform(0.1, 10.0, (T - 8, 1)).astype(np.float32)
+    ig, vg = gpu_topk(L, 512)
+    ri, rv = ref_topk(L, 512)
+    assert np.array_equal(ig, ri)
+    sel = ri >= 0
+    assert np.array_equal(vg[sel], rv[sel].astype(np.float32))
+    nv = rng.integers(0, n + 1, T).astype(np.int32)
+    mask = (rng.random((4, n)) < 0.6).astype(np.uint8)
+    row_req = (np.arange(T) % 4).astype(np.int32)
+    ig, _ = gpu_topk(L, 512, n_valid=nv, mask=mask, row_req=row_req)
+    ri, _ = ref_topk(L, 512, n_valid=nv, mask=mask, row_req=row_req)
+    assert np.array_equal(ig, ri)
+
+
 @pytest.mark.parametrize("workspace", [True, False])
 def test_topk_long_rows_262144_candidates(workspace):
     """Mode-A sized rows: 262,144 candidates, with planted duplicates of the 512th value."""

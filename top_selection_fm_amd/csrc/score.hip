@@ -76,7 +76,7 @@ constexpr int kSlotInvisible = -1;  // every entry of the page is past the visib
 constexpr int kSlotUnmapped = -2;   // the block table (or resident list) points nowhere valid
 constexpr int kSlotEmpty = -3;      // resident-list slot beyond n_resident: nothing to write
 constexpr int kMaxPpw = 16;         // page slots per wave, at most
-constexpr int kStoreNt = 2;         // buffer store cache policy: non-temporal
+constexpr int kStorePolicy = 0;     // logit stores: default cache policy (see store_wave_logits)
 constexpr int kMaskPpw = FM_MASK_MAXPPW;   // pages per wave of the fp8 mask kernel, at most
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -341,7 +341,8 @@ __device__ __forceinline__ void stream_pages(int n, Pg (&P)[NBUF], Fetch fetch, 
 // (out_ld % 4 == 0) it goes out as 16-byte stores, lane ln taking entries 4 (ln % 16) .. + 3 of
 // slot 4 p + ln / 16, four slots an instruction (res must have 4 ceil(nslot / 4) rows, 16-byte
 // aligned).  Unmapped slots give NaN, invisible entries -inf, empty slots nothing.  The stores
-// are marked non-temporal: nothing reads the logits back in the kernel.
+// keep the default cache policy: the top-k that follows reads the logits, and finds part of
+// them still in the caches (a decode step measured ~2 us faster than with non-temporal stores).
 __device__ __forceinline__ void store_wave_logits(const ScoreArgs &A, __amdgpu_buffer_rsrc_t orsrc,
                                                   const float (*res)[64], int phys_l, int lp_l,
                                                   int64_t slot0, int nslot, int64_t nvis, int ln) {
@@ -362,7 +363,7 @@ __device__ __forceinline__ void store_wave_logits(const ScoreArgs &A, __amdgpu_b
                 v[e] = __float_as_uint(x);
             }
             const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
-            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, voff, 0, kStoreNt);
+            __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, voff, 0, kStorePolicy);
         }
         return;
     }
@@ -373,7 +374,7 @@ __device__ __forceinline__ void store_wave_logits(const ScoreArgs &A, __amdgpu_b
         float v = phys >= 0 ? res[i][ln] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
         if ((int64_t)lp * kPage + ln >= nvis) v = -INFINITY;
         const uint32_t voff = (uint32_t)(min(col, A.out_ld) * 4);   // out_ld * 4: dropped
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, kStoreNt);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), orsrc, voff, 0, kStorePolicy);
     }
 }
 

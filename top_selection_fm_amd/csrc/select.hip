@@ -37,6 +37,9 @@
 #ifndef FM_TOPK_NT
 #define FM_TOPK_NT 1024  // threads of the single-pass row kernel
 #endif
+#ifndef FM_TOPK_SHORT_VEC
+#define FM_TOPK_SHORT_VEC 17   // float4 blocks a thread of the 512-thread row kernel
+#endif
 #ifndef FM_TOPK_STAGE_MIN
 #define FM_TOPK_STAGE_MIN 4096
 #endif
@@ -632,20 +635,30 @@ struct TopkLds {
 static_assert(kSample <= kBuf, "the sample fits the candidate buffer");
 
 // ---------------------------------------------------------------- single-pass row top-k
-// Rows of up to kRowMax entries: one workgroup of kRowNT threads per row loads the whole row
+// Rows of up to 4 NT VEC entries: one workgroup of NT threads per row loads the whole row
 // into registers at once (every load in flight together), takes the cut's sample from those
 // registers (a few values a thread, spread over the row), keeps the candidates
 // at or above the cut in the LDS buffer and selects exactly from it (select_buffer).  One read
 // of the row, no workspace, no second launch.  When the cut does not hold (fewer than k pass,
 // or more than the buffer holds) the exact radix selection runs over the row instead.
+// Two shapes: 512 threads for rows of up to 34,816 entries, two rows a CU, so that one row's
+// loads overlap the other's selection (4,096 rows of 33,792: 300 -> 181 us against one row a
+// CU); 1,024 threads for rows of up to 65,536 entries.
 constexpr int kRowNT = FM_TOPK_NT;
 constexpr int kRowMax = 65536;
 constexpr int kRowVec = kRowMax / (4 * kRowNT);
+constexpr int kShortNT = 512;
+constexpr int kShortVec = FM_TOPK_SHORT_VEC;
+constexpr int kShortMax = 4 * kShortNT * kShortVec;
 
-__global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
-    constexpr int NT = kRowNT, NW = NT / 64;
+// WPE: waves a SIMD the registers are sized for (4: at most 128 VGPRs)
+template <int NT, int VEC, int WPE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE)))
+void topk_row_kernel(TopkArgs A) {
+    constexpr int NW = NT / 64;
     constexpr int SPT = kSample / NT;               // sampled values a thread
     static_assert(SPT * NT == kSample && SPT <= 4, "sample layout");
+    static_assert(NT <= kTopkLdsThreads, "TopkLds sized for the workgroup");
     __shared__ TopkLds L;
     __shared__ float s_max[NW];
     const int t = blockIdx.x, tid = threadIdx.x, ln = __lane_id(), w = tid >> 6;
@@ -656,12 +669,12 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
 
     // the row, every non-candidate (-inf, NaN, masked, past n) as -inf.  Buffer loads bounded
     // by the row (4-byte alignment suffices; dwords past n read as 0 and are replaced)
-    float v[kRowVec][4];
+    float v[VEC][4];
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)R.row, (short)0, (int)(n * 4), 0x00020000);
-    const int n32 = (int)n;                           // n <= kRowMax here
+    const int n32 = (int)n;                           // n <= 4 NT VEC here
 #pragma unroll
-    for (int u = 0; u < kRowVec; ++u) {
+    for (int u = 0; u < VEC; ++u) {
         const int j = 4 * (u * NT + tid);
         const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 4u, 0, 0));
 #pragma unroll
@@ -672,7 +685,7 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
         const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
             (void *)R.mrow, (short)0, n32, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < kRowVec; ++u)
+        for (int u = 0; u < VEC; ++u)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t j = (uint32_t)(4 * (u * NT + tid) + c);
@@ -688,13 +701,13 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
     float tau = -FLT_MAX, smax = 0.f;
     if (n > kBuf) {
         float lo = INFINITY, hi = -INFINITY;
-        const int un = min(kRowVec, (n32 + 4 * NT - 1) / (4 * NT));
+        const int un = min(VEC, (n32 + 4 * NT - 1) / (4 * NT));
         int uq = (int)((uint32_t)(SPT * tid) % (uint32_t)un);
 #pragma unroll
         for (int q = 0; q < SPT; ++q, uq = uq + 1 == un ? 0 : uq + 1) {
             float sq = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < kRowVec; ++u) sq = u == uq ? v[u][q] : sq;
+            for (int u = 0; u < VEC; ++u) sq = u == uq ? v[u][q] : sq;
             L.bval[q * NT + tid] = sq > -INFINITY ? sq : __builtin_nanf("");
             lo = sq > -INFINITY ? fminf(lo, sq) : lo;
             hi = fmaxf(hi, sq);
@@ -757,7 +770,7 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
     // entries afterwards, so a resident-page lookup never sits inside the loop)
     uint32_t wcount = 0;
 #pragma unroll
-    for (int u = 0; u < kRowVec; ++u)
+    for (int u = 0; u < VEC; ++u)
 #pragma unroll
         for (int c = 0; c < 4; ++c) wcount += v[u][c] >= tau ? 1u : 0u;
 #pragma unroll
@@ -781,7 +794,7 @@ __global__ __launch_bounds__(kRowNT) void topk_row_kernel(TopkArgs A) {
         asm volatile("v_mov_b32 %0, %1" : "=v"(tw) : "v"(tau));
         uint32_t run = base;
 #pragma unroll
-        for (int u = 0; u < kRowVec; ++u) {
+        for (int u = 0; u < VEC; ++u) {
             if (4 * u * NT >= n32) continue;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -1204,8 +1217,12 @@ TopkWs topk_ws_carve(void *ws, int T, int64_t n) {
 }
 
 hipError_t launch_topk(const TopkArgs &a, const TopkWs *ws, hipStream_t s) {
+    if (a.ld <= (int64_t)kShortMax && FM_TOPK_ROW) {
+        topk_row_kernel<kShortNT, kShortVec, 4><<<dim3((unsigned)a.T), dim3(kShortNT), 0, s>>>(a);
+        return hipGetLastError();
+    }
     if (a.ld <= (int64_t)kRowMax && FM_TOPK_ROW) {
-        topk_row_kernel<<<dim3((unsigned)a.T), dim3(kRowNT), 0, s>>>(a);
+        topk_row_kernel<kRowNT, kRowVec, 4><<<dim3((unsigned)a.T), dim3(kRowNT), 0, s>>>(a);
         return hipGetLastError();
     }
     if (ws) {
