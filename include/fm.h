@@ -49,7 +49,8 @@ extern "C" {
 #define FM_MAX_LAYERS 4
 #define FM_PAGE_SIZE 64         /* compressed entries per page */
 #define FM_HEAD_DIM 128
-#define FM_N_HEADS 64
+#define FM_N_HEADS 64           /* indexer heads of every (q, key) dtype pair */
+#define FM_N_HEADS_WIDE 128     /* the retriever's heads (FlashMemory README, "Hyperparameters") */
 #define FM_MAX_K 1024
 
 typedef enum {
@@ -108,6 +109,10 @@ typedef struct {
  * floor(pos / ratio)); without it, every s < seq_len is visible.
  * Supported (q_dtype, key_dtype): (F32, F32), (BF16, BF16), (BF16, SCALED132),
  * (FP8_E4M3 with q_scale[T], SCALED132).  w_dtype: F32 or BF16.
+ * n_heads: 64 for every pair; 128 (the retriever's head count, as fm_encode_queries produces
+ * it) for (BF16, SCALED132) and (F32, F32); anything else is FM_ERR_UNSUPPORTED.  The score
+ * is the same sum over all n_heads heads.  All layers of one fm_resident_mask call have the
+ * same n_heads.
  */
 typedef struct {
     const void *q;
@@ -116,7 +121,7 @@ typedef struct {
     const void *w;
     fm_dtype w_dtype;
     int T;
-    int n_heads;                /* must be 64 */
+    int n_heads;                /* 64, or 128 (see above) */
     const int32_t *row_req;     /* [T] or NULL */
     const int32_t *q_pos;       /* [T] or NULL */
     int compress_ratio;         /* > 0; used only with q_pos (4 for CSA) */

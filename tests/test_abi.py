@@ -104,7 +104,11 @@ def logits_call(q, kv, ld=1000):
 
 
 @pytest.mark.parametrize("mutate,status", [
-    (lambda q, kv: setattr(q, "n_heads", 128), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: setattr(q, "n_heads", 128), api.FM_ERR_UNSUPPORTED),   # bf16 keys: 64 only
+    (lambda q, kv: setattr(q, "n_heads", 96), api.FM_ERR_UNSUPPORTED),
+    (lambda q, kv: (setattr(q, "n_heads", 128), setattr(kv, "key_dtype", api.FM_FP8_E4M3_SCALED132),
+                    setattr(q, "q_dtype", api.FM_FP8_E4M3), setattr(q, "q_scale", FAKE)),
+     api.FM_ERR_UNSUPPORTED),                                                 # fp8 q: 64 only
     (lambda q, kv: setattr(kv, "page_size", 32), api.FM_ERR_UNSUPPORTED),
     (lambda q, kv: setattr(kv, "head_dim", 64), api.FM_ERR_UNSUPPORTED),
     (lambda q, kv: setattr(kv, "key_dtype", api.FM_FP8_E4M3), api.FM_ERR_UNSUPPORTED),
@@ -239,6 +243,13 @@ def test_resident_mask_validation():
     assert mask_call(bad, kv) == api.FM_ERR_INVALID_ARG
     fp8 = [good_q("fp8") for _ in range(3)]
     assert mask_call(fp8, kv) == api.FM_ERR_UNSUPPORTED
+    mixed = [good_q() for _ in range(3)]
+    mixed[1].n_heads = 128
+    assert mask_call(mixed, kv) == api.FM_ERR_UNSUPPORTED
+    wide_bf16 = [good_q() for _ in range(3)]
+    for q in wide_bf16:
+        q.n_heads = 128
+    assert mask_call(wide_bf16, good_kv("bf16", n_pools=3)) == api.FM_ERR_UNSUPPORTED
 
 
 def good_enc(**kw):

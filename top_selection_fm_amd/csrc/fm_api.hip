@@ -78,8 +78,8 @@ fm_status check_kv(const fm_kv_desc *kv, int n_pools_needed) {
 fm_status check_q(const fm_query_desc *q, const fm_kv_desc *kv, const char *name) {
     REQUIRE(q, FM_ERR_INVALID_ARG, "%s: query descriptor is NULL", name);
     REQUIRE(q->T >= 0, FM_ERR_INVALID_ARG, "%s: T = %d", name, q->T);
-    REQUIRE(q->n_heads == FM_N_HEADS, FM_ERR_UNSUPPORTED, "%s: n_heads %d (only %d)", name,
-            q->n_heads, FM_N_HEADS);
+    REQUIRE(q->n_heads == FM_N_HEADS || q->n_heads == FM_N_HEADS_WIDE, FM_ERR_UNSUPPORTED,
+            "%s: n_heads %d (%d, or %d)", name, q->n_heads, FM_N_HEADS, FM_N_HEADS_WIDE);
     REQUIRE(q->w_dtype == FM_F32 || q->w_dtype == FM_BF16, FM_ERR_UNSUPPORTED,
             "%s: w dtype %d", name, (int)q->w_dtype);
     const fm_dtype k = kv->key_dtype;
@@ -88,6 +88,10 @@ fm_status check_q(const fm_query_desc *q, const fm_kv_desc *kv, const char *name
                        (q->q_dtype == FM_FP8_E4M3 && k == FM_FP8_E4M3_SCALED132);
     REQUIRE(combo, FM_ERR_UNSUPPORTED, "%s: q dtype %d with key dtype %d", name, (int)q->q_dtype,
             (int)k);
+    REQUIRE(q->n_heads == FM_N_HEADS || (q->q_dtype == FM_BF16 && k == FM_FP8_E4M3_SCALED132) ||
+                (q->q_dtype == FM_F32 && k == FM_F32),
+            FM_ERR_UNSUPPORTED, "%s: %d heads need bf16 q with fp8 keys, or fp32 q and keys", name,
+            q->n_heads);
     if (q->T == 0) return FM_OK;
     REQUIRE(q->q && q->w, FM_ERR_INVALID_ARG, "%s: q / w NULL", name);
     REQUIRE(aligned(q->q, 16), FM_ERR_INVALID_ARG, "%s: q not 16-byte aligned", name);
@@ -106,6 +110,7 @@ fm::QArgs make_q(const fm_query_desc *q, const fm_kv_desc *kv) {
     a.q_scale = q->q_scale;
     a.w = q->w;
     a.w_bf16 = q->w_dtype == FM_BF16;
+    a.n_heads = q->n_heads;
     a.T = q->T;
     a.row_req = q->row_req;
     a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
@@ -156,7 +161,7 @@ fm_status run_score(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t 
     a.n_slots = n_slots;
     // waves resident at once: 256 CUs x 4 SIMDs x waves per SIMD of the kernel used
     const int64_t per_simd = kv->key_dtype == FM_BF16 ? 4 : kv->key_dtype == FM_FP8_E4M3_SCALED132 &&
-                             q->q_dtype == FM_BF16 ? FM_F8_WPE : 2;
+                             q->q_dtype == FM_BF16 ? (q->n_heads == FM_N_HEADS ? FM_F8_WPE : 2) : 2;
     a.ppw = pages_per_wave((int64_t)q->T * n_slots, 1024 * per_simd *
                            (kv->key_dtype == FM_BF16 ? FM_DEC_GENS : FM_F8_GENS));
     if (kv->key_dtype == FM_F32) return launched(fm::launch_score_f32(a, st), "score_f32");
@@ -421,6 +426,8 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
                 q_layers[l].T, kv->B);
         REQUIRE(q_layers[l].q_dtype == q_layers[0].q_dtype, FM_ERR_UNSUPPORTED,
                 "layers mix q dtypes");
+        REQUIRE(q_layers[l].n_heads == q_layers[0].n_heads, FM_ERR_UNSUPPORTED,
+                "layers mix head counts");
         REQUIRE(q_layers[l].q_dtype != FM_FP8_E4M3, FM_ERR_UNSUPPORTED,
                 "fp8 queries are not supported for the resident mask");
     }

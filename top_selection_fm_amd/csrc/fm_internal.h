@@ -22,10 +22,11 @@ enum QFmt { Q_F32 = 0, Q_BF16 = 1, Q_FP8 = 2 };
 
 // One query layer as the kernels see it.
 struct QArgs {
-    const void *q;          // [T, 64, 128]
+    const void *q;          // [T, n_heads, 128]
     const float *q_scale;   // [T] (fp8 q)
-    const void *w;          // [T, 64]
+    const void *w;          // [T, n_heads]
     int w_bf16;             // 1: w is bf16, 0: float32
+    int n_heads;            // 64, or 128 (fp8 keys with bf16 q; fp32 keys)
     int T;
     const int32_t *row_req; // [T] or null
     int b_is_zero;          // row_req null and B == 1: every row is request 0

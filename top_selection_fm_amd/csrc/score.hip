@@ -587,6 +587,7 @@ struct QF8Lds {
     }
     __device__ __forceinline__ u32x4 get(const u32x4 *f, int m, int st) const { return f[(8 * m + st) * 64]; }
     __device__ __forceinline__ const f32x4 *weights() const { return (const f32x4 *)&w[0][0]; }
+    static constexpr int kMT = 2;
     static constexpr bool kLds = true;
     static constexpr int kAhead = FM_QLDS_AHEAD;
 };
@@ -605,14 +606,33 @@ struct QF8Reg {
     __device__ __forceinline__ const u32x4 *frags() const { return nullptr; }
     __device__ __forceinline__ u32x4 get(const u32x4 *, int m, int st) const { return a[m][st]; }
     __device__ __forceinline__ const f32x4 *weights() const { return (const f32x4 *)&w[0][0]; }
+    static constexpr int kMT = 2;
     static constexpr bool kLds = false;
     static constexpr int kAhead = 4;
 };
 
-// One layer's A operands and head weights, both in LDS (weights as [h][16 m + v] per lane half).
-struct QLayerLds {
-    const u32x4 *a;                 // [8 m + s][lane]
-    const f32x4 *w;                 // [2][8]
+// One query row's A operands and head weights for 32 MT heads, both in LDS, staged by the whole
+// workgroup (its waves all score that row): fragment (m, s) at a[(8 m + s) * 64 + lane] as
+// qa_frag lays it out, weights as [lane half h][16 m + v] = head 32 m + 8 (v / 4) + 4 h + v % 4,
+// the accumulator layout of tile_logit_f8.  The wide-head (128) kernels use it.
+template <int MT>
+struct QWideLds {
+    const u32x4 *a;
+    const f32x4 *w;
+    // every thread of the workgroup calls this; the caller synchronises before the first use
+    __device__ void stage(u32x4 *lds_a, float *lds_w, const uint8_t *qrow, const void *wp, int w_bf16,
+                          int64_t wrow) {
+        const int ln = __lane_id(), nw = (int)(blockDim.x >> 6);
+        for (int fi = (int)(threadIdx.x >> 6); fi < 8 * MT; fi += nw)
+            lds_a[fi * 64 + ln] = qa_frag(qrow, fi >> 3, fi & 7, ln);
+        for (int i = (int)threadIdx.x; i < 32 * MT; i += (int)blockDim.x) {
+            const int h = i / (16 * MT), m = (i % (16 * MT)) >> 4, v = i & 15;
+            const int64_t head = wrow * 32 * MT + 32 * m + 8 * (v >> 2) + 4 * h + (v & 3);
+            lds_w[i] = w_bf16 ? bf16f(((const uint16_t *)wp)[head]) : ((const float *)wp)[head];
+        }
+        a = lds_a;
+        w = (const f32x4 *)lds_w;
+    }
     __device__ __forceinline__ const u32x4 *frags() const {
         int z;
         asm volatile("s_mov_b32 %0, 0" : "=s"(z));
@@ -622,8 +642,9 @@ struct QLayerLds {
     __device__ __forceinline__ const f32x4 *weights() const {
         int z;
         asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-        return w + 8 * (__lane_id() >> 5) + z;
+        return w + 4 * MT * (__lane_id() >> 5) + z;
     }
+    static constexpr int kMT = MT;
     static constexpr bool kLds = true;
     static constexpr int kAhead = FM_MASK_AHEAD;
 };
@@ -670,16 +691,17 @@ __device__ __forceinline__ void tile_to_mma_layout(TileF8 &T, uint8_t *buf, int 
 template <class QF>
 __device__ __forceinline__ float tile_logit_f8(const QF &Q, const TileF8 &T) {
     typedef float f32x16 __attribute__((ext_vector_type(16)));
+    constexpr int MT = QF::kMT;                   // head tiles of 32
     const u32x4 *qf = Q.frags();
-    f32x16 acc[2];
+    f32x16 acc[MT];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
-    constexpr int D = QF::kAhead;                 // fragments in flight
+    constexpr int D = QF::kAhead;                 // fragments in flight (fragment k = MT st + m)
     u32x4 a[D];
 #pragma unroll
-    for (int k = 0; k < D; ++k) a[k] = Q.get(qf, k & 1, k >> 1);
+    for (int k = 0; k < D; ++k) a[k] = Q.get(qf, k % MT, k / MT);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
         const uint32_t d0 = T.c[st >> 1][(st & 1) * 2], d1 = T.c[st >> 1][(st & 1) * 2 + 1];
@@ -690,17 +712,17 @@ __device__ __forceinline__ float tile_logit_f8(const QF &Q, const TileF8 &T) {
         bw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
         const bf16x8 b = __builtin_bit_cast(bf16x8, bw);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int k = 2 * st + m;
+        for (int m = 0; m < MT; ++m) {
+            const int k = MT * st + m;
             acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[k % D]), b, acc[m], 0, 0, 0);
-            if (k + D < 16) a[k % D] = Q.get(qf, (k + D) & 1, (k + D) >> 1);
+            if (k + D < 8 * MT) a[k % D] = Q.get(qf, (k + D) % MT, (k + D) / MT);
             if (QF::kLds) __builtin_amdgcn_sched_barrier(0);
         }
     }
     const f32x4 *wt = Q.weights();
     float p = 0.f;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
             const f32x4 w4 = wt[4 * m + v4];
@@ -734,18 +756,11 @@ __device__ __forceinline__ void stream_tiles_f8(int n, const QF &Q, Fetch fetch,
 }
 
 // Two-level (and any bf16-query) scoring over fp8 pages: the work split, slot states and
-// deferred stores of score_kernel, with the tile stream above.
-template <int RING>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_F8_WPE)))
-void score_f8_kernel(ScoreArgs A) {
-    __shared__ __align__(16) float s_res[4][kMaxPpw + RING][64];
-    __shared__ u32x4 s_qa[16 * 64];
-    const int t = blockIdx.y;
-    const int ln = __lane_id();
-    const int wave = threadIdx.x >> 6;
-    QF8Lds Q;
-    Q.init(s_qa, (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2, A.q.w, A.q.w_bf16, t, ln);
-    __syncthreads();
+// deferred stores of score_kernel, with the tile stream above.  One wave's page slots of row
+// blockIdx.y, with the row's query source Q already staged.
+template <int RING, class QF>
+__device__ __forceinline__ void score_f8_slots(const ScoreArgs &A, const QF &Q, float (*res)[64], int t,
+                                               int ln, int wave) {
     const int64_t slot0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
     if (slot0 >= A.n_slots) return;
     const int nslot = (int)min((int64_t)A.ppw, A.n_slots - slot0);
@@ -762,22 +777,48 @@ void score_f8_kernel(ScoreArgs A) {
     auto fetch = [&](TileF8 &T, int x) {
         load_tile_f8(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);
     };
-    auto take = [&](float t0, float t1, int i) { s_res[wave][i][ln] = (ln >> 5) ? t1 : t0; };
+    auto take = [&](float t0, float t1, int i) { res[i][ln] = (ln >> 5) ? t1 : t0; };
     stream_tiles_f8<RING>(nslot, Q, fetch, take);
-    store_wave_logits(A, orsrc, s_res[wave], phys_l, lp_l, slot0, nslot, nvis, ln);
+    store_wave_logits(A, orsrc, res, phys_l, lp_l, slot0, nslot, nvis, ln);
+}
+
+// 32 MT heads: MT = 2 keeps the query fragments in LDS and the head weights in registers
+// (QF8Lds); MT = 4 (128 heads) keeps both in LDS (QWideLds), at two waves a SIMD.
+template <int RING, int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 2 ? FM_F8_WPE : 2)))
+void score_f8_kernel(ScoreArgs A) {
+    __shared__ __align__(16) float s_res[4][kMaxPpw + RING][64];
+    __shared__ u32x4 s_qa[8 * MT * 64];
+    const int t = blockIdx.y;
+    const int ln = __lane_id();
+    const int wave = threadIdx.x >> 6;
+    const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * (32 * MT) * kDim * 2;
+    if constexpr (MT == 2) {
+        QF8Lds Q;
+        Q.init(s_qa, qrow, A.q.w, A.q.w_bf16, t, ln);
+        __syncthreads();
+        score_f8_slots<RING>(A, Q, s_res[wave], t, ln, wave);
+    } else {
+        __shared__ __align__(16) float s_w[32 * MT];
+        QWideLds<MT> Q;
+        Q.stage(s_qa, s_w, qrow, A.q.w, A.q.w_bf16, t);
+        __syncthreads();
+        score_f8_slots<RING>(A, Q, s_res[wave], t, ln, wave);
+    }
 }
 
 // ---------------------------------------------------------------- fp32 path (VALU)
-// One thread per output column; fp32 products and sums.  For fp32 inputs only.
+// One thread per output column; fp32 products and sums.  For fp32 inputs only; NH heads.
+template <int NH>
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
-    __shared__ float qs[kHeads * kDim];
-    __shared__ float wsm[kHeads];
+    __shared__ float qs[NH * kDim];
+    __shared__ float wsm[NH];
     const int t = blockIdx.y;
-    const float *qrow = (const float *)A.q.q + (int64_t)t * kHeads * kDim;
-    for (int i = threadIdx.x; i < kHeads * kDim; i += blockDim.x) qs[i] = qrow[i];
-    for (int i = threadIdx.x; i < kHeads; i += blockDim.x)
-        wsm[i] = A.q.w_bf16 ? bf16f(((const uint16_t *)A.q.w)[(int64_t)t * kHeads + i])
-                            : ((const float *)A.q.w)[(int64_t)t * kHeads + i];
+    const float *qrow = (const float *)A.q.q + (int64_t)t * NH * kDim;
+    for (int i = threadIdx.x; i < NH * kDim; i += blockDim.x) qs[i] = qrow[i];
+    for (int i = threadIdx.x; i < NH; i += blockDim.x)
+        wsm[i] = A.q.w_bf16 ? bf16f(((const uint16_t *)A.q.w)[(int64_t)t * NH + i])
+                            : ((const float *)A.q.w)[(int64_t)t * NH + i];
     __syncthreads();
     const int64_t col = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (col >= A.n_slots * kPage || col >= A.out_ld) return;
@@ -796,7 +837,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
 #pragma unroll
         for (int d = 0; d < kDim; ++d) kr[d] = k[d];
         v = 0.f;
-        for (int h = 0; h < kHeads; ++h) {
+        for (int h = 0; h < NH; ++h) {
             float x = 0.f;
 #pragma unroll
             for (int d = 0; d < kDim; ++d) x = fmaf(qs[h * kDim + d], kr[d], x);
@@ -924,8 +965,11 @@ __device__ __forceinline__ void stream_tiles_rows(int n, const QF &Q, uint8_t *b
 // ppw pages of request blockIdx.y for all NL layers in turn: layer l's query operands and head
 // weights sit in the wave's registers while it streams its pages of pool l, and the running
 // union of each entry waits in LDS.  After the last layer the wave forms the decisions and
-// writes its pages' mask bytes.
-template <int NL>
+// writes its pages' mask bytes.  32 MT heads: with MT = 4 (128 heads) a layer's query would not
+// fit the registers, so the workgroup stages each layer's fragments and weights in LDS
+// (QWideLds) in turn, and every wave stays to the last barrier (one without pages streams
+// nothing).
+template <int NL, int MT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FM_MASK_WPE)))
 void mask_f8_kernel(MaskArgs A) {
     constexpr int RING = FM_MASK_RING;
@@ -934,8 +978,8 @@ void mask_f8_kernel(MaskArgs A) {
     const int b = blockIdx.y;
     const int ln = __lane_id(), wave = threadIdx.x >> 6;
     const int64_t page0 = ((int64_t)blockIdx.x * 4 + wave) * A.ppw;
-    if (page0 >= A.n_pages) return;
-    const int np = (int)min((int64_t)A.ppw, A.n_pages - page0);
+    if (MT == 2 && page0 >= A.n_pages) return;
+    const int np = (int)max((int64_t)0, min((int64_t)A.ppw, A.n_pages - page0));
     const int64_t seq = A.kv.seq_lens[b];
 
     // lane i describes page page0 + i (i < np): physical page or state; past np: invisible
@@ -952,8 +996,7 @@ void mask_f8_kernel(MaskArgs A) {
     const float inv_n = 1.0f / (float)NL;
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-        QF8Reg Q;
-        Q.init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, A.q[l].w, A.q[l].w_bf16, b, ln);
+        const uint8_t *qrow = (const uint8_t *)A.q[l].q + (int64_t)b * (32 * MT) * kDim * 2;
         const uint8_t *pool = A.kv.pool[l];
         auto fetch = [&](TileF8 &T, int x) {
             load_tile_rows(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);
@@ -971,7 +1014,19 @@ void mask_f8_kernel(MaskArgs A) {
                 u = l == 0 ? L : ((L != L || u != u) ? __builtin_nanf("") : fmaxf(u, L));
             }
         };
-        stream_tiles_rows<RING>(np, Q, s_tile[wave], fetch, take);
+        if constexpr (MT == 2) {
+            QF8Reg Q;
+            Q.init(qrow, A.q[l].w, A.q[l].w_bf16, b, ln);
+            stream_tiles_rows<RING>(np, Q, s_tile[wave], fetch, take);
+        } else {
+            __shared__ u32x4 s_qa[8 * MT * 64];
+            __shared__ __align__(16) float s_w[32 * MT];
+            if (l > 0) __syncthreads();     // every wave is done with the previous layer
+            QWideLds<MT> Q;
+            Q.stage(s_qa, s_w, qrow, A.q[l].w, A.q[l].w_bf16, b);
+            __syncthreads();
+            stream_tiles_rows<RING>(np, Q, s_tile[wave], fetch, take);
+        }
     }
 
     // decisions and mask bytes (0 / 1): 16-byte chunks when the span is whole and aligned, else
@@ -1002,10 +1057,11 @@ void mask_f8_kernel(MaskArgs A) {
     }
 }
 
-// fp32 keys: one thread per entry, fp32 VALU arithmetic.
+// fp32 keys: one thread per entry, fp32 VALU arithmetic; NH heads.
+template <int NH>
 __global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
-    __shared__ float qs[kHeads * kDim];
-    __shared__ float wsm[kHeads];
+    __shared__ float qs[NH * kDim];
+    __shared__ float wsm[NH];
     const int b = blockIdx.y;
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t seq = A.kv.seq_lens[b];
@@ -1013,11 +1069,11 @@ __global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
     float u = A.mean_mode ? 0.f : -INFINITY;
     for (int l = 0; l < A.n_layers; ++l) {
         __syncthreads();
-        const float *qrow = (const float *)A.q[l].q + (int64_t)b * kHeads * kDim;
-        for (int i = threadIdx.x; i < kHeads * kDim; i += blockDim.x) qs[i] = qrow[i];
-        for (int i = threadIdx.x; i < kHeads; i += blockDim.x)
-            wsm[i] = A.q[l].w_bf16 ? bf16f(((const uint16_t *)A.q[l].w)[(int64_t)b * kHeads + i])
-                                   : ((const float *)A.q[l].w)[(int64_t)b * kHeads + i];
+        const float *qrow = (const float *)A.q[l].q + (int64_t)b * NH * kDim;
+        for (int i = threadIdx.x; i < NH * kDim; i += blockDim.x) qs[i] = qrow[i];
+        for (int i = threadIdx.x; i < NH; i += blockDim.x)
+            wsm[i] = A.q[l].w_bf16 ? bf16f(((const uint16_t *)A.q[l].w)[(int64_t)b * NH + i])
+                                   : ((const float *)A.q[l].w)[(int64_t)b * NH + i];
         __syncthreads();
         if (s >= seq || s >= A.mask_ld) continue;
         int64_t lp = s / kPage;
@@ -1031,7 +1087,7 @@ __global__ __launch_bounds__(256) void mask_f32_kernel(MaskArgs A) {
 #pragma unroll
             for (int d = 0; d < kDim; ++d) kr[d] = k[d];
             L = 0.f;
-            for (int h = 0; h < kHeads; ++h) {
+            for (int h = 0; h < NH; ++h) {
                 float x = 0.f;
 #pragma unroll
                 for (int d = 0; d < kDim; ++d) x = fmaf(qs[h * kDim + d], kr[d], x);
@@ -1059,8 +1115,10 @@ hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t 
         else
             score_kernel<KEY_BF16, Q_BF16><<<grid, 256, 0, s>>>(a);
     }
+    else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16 && a.q.n_heads == 128)
+        score_f8_kernel<FM_F8_RING, 4><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16)
-        score_f8_kernel<FM_F8_RING><<<grid, 256, 0, s>>>(a);
+        score_f8_kernel<FM_F8_RING, 2><<<grid, 256, 0, s>>>(a);
     else if (key_fmt == KEY_FP8 && q_fmt == Q_FP8)
         score_kernel<KEY_FP8, Q_FP8><<<grid, 256, 0, s>>>(a);
     else
@@ -1070,7 +1128,10 @@ hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t 
 
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s) {
     dim3 grid((unsigned)((a.n_slots * kPage + 255) / 256), (unsigned)a.q.T);
-    score_f32_kernel<<<grid, 256, 0, s>>>(a);
+    if (a.q.n_heads == 128)
+        score_f32_kernel<128><<<grid, 256, 0, s>>>(a);
+    else
+        score_f32_kernel<kHeads><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -1083,12 +1144,22 @@ hipError_t launch_mask(const MaskArgs &a0, int key_fmt, int B, hipStream_t s) {
     a.ppw = (int)std::min<int64_t>(kMaskPpw, std::max<int64_t>(1, (total + FM_MASK_RESIDENT - 1) / FM_MASK_RESIDENT));
     if (key_fmt == KEY_F32) {
         dim3 grid((unsigned)((a.mask_ld + 255) / 256), (unsigned)B);
-        mask_f32_kernel<<<grid, 256, 0, s>>>(a);
+        if (a.q[0].n_heads == 128)
+            mask_f32_kernel<128><<<grid, 256, 0, s>>>(a);
+        else
+            mask_f32_kernel<kHeads><<<grid, 256, 0, s>>>(a);
+    } else if (key_fmt == KEY_FP8 && a.q[0].n_heads == 128) {
+        dim3 grid((unsigned)((a.n_pages + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)B);
+        if (a.n_layers == 1) mask_f8_kernel<1, 4><<<grid, 256, 0, s>>>(a);
+        else if (a.n_layers == 2) mask_f8_kernel<2, 4><<<grid, 256, 0, s>>>(a);
+        else if (a.n_layers == 3) mask_f8_kernel<3, 4><<<grid, 256, 0, s>>>(a);
+        else mask_f8_kernel<4, 4><<<grid, 256, 0, s>>>(a);
     } else if (key_fmt == KEY_FP8 && FM_MASK_F8) {
         dim3 grid((unsigned)((a.n_pages + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)B);
-        if (a.n_layers == 1) mask_f8_kernel<1><<<grid, 256, 0, s>>>(a);
-        else if (a.n_layers == 2) mask_f8_kernel<2><<<grid, 256, 0, s>>>(a);
-        else mask_f8_kernel<3><<<grid, 256, 0, s>>>(a);
+        if (a.n_layers == 1) mask_f8_kernel<1, 2><<<grid, 256, 0, s>>>(a);
+        else if (a.n_layers == 2) mask_f8_kernel<2, 2><<<grid, 256, 0, s>>>(a);
+        else if (a.n_layers == 3) mask_f8_kernel<3, 2><<<grid, 256, 0, s>>>(a);
+        else mask_f8_kernel<4, 2><<<grid, 256, 0, s>>>(a);
     } else {
         dim3 grid((unsigned)((a.n_pages + PPW - 1) / PPW), (unsigned)B);
         const unsigned threads = 64u * (unsigned)a.n_layers;

@@ -174,11 +174,11 @@ def _clear_tail(pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray)
 
 
 # ----------------------------------------------------------------------------- workloads
-def tiny_single_query(seed: int = 1001, n_entries: int = 4096) -> Workload:
+def tiny_single_query(seed: int = 1001, n_entries: int = 4096, heads: int = HEADS) -> Workload:
     """One fp32 query row over n_entries fp32 keys; w ~ N(-0.05, 0.125)."""
     rng = make_rng(seed)
-    q = _normal(rng, (1, HEADS, DIM), std=1.0 / np.sqrt(DIM))
-    w = _normal(rng, (1, HEADS), mean=-0.05, std=0.125)
+    q = _normal(rng, (1, heads, DIM), std=1.0 / np.sqrt(DIM))
+    w = _normal(rng, (1, heads), mean=-0.05, std=0.125)
     n_pages = -(-n_entries // PAGE)
     keys = _keys_f32(rng, n_pages)
     kv = KeyPool([keys], "f32", np.arange(n_pages, dtype=np.int32)[None, :],
@@ -221,13 +221,14 @@ def decode_bf16(seed: int = 1002, B: int = 32, seq_len: int = 65536, hot_frac: f
 def three_layer_mask_fp8(seed: int = 1003, B: int = 8, seq_len: int = 262144,
                          n_layers: int = 3, hot_frac: float = 0.12, cluster: int = 8,
                          hot_offset: float = 0.75, w_bias: float = -0.085,
-                         shared_keys: bool = False, ragged: bool = False) -> Workload:
+                         shared_keys: bool = False, ragged: bool = False,
+                         heads: int = HEADS) -> Workload:
     """Level-1 residency workload: n_layers query encoders over per-layer fp8 key pools.
 
     The pools share one permuted block table.  Each request has the same set of hot pages in
     every layer, grouped in runs of `cluster` contiguous logical pages.  Layer l's head
     weights are w0 - mean(w0) + w_bias with w0 ~ N(0, 0.125), so every row's weights sum to
-    64*w_bias; hot keys are shifted by hot_offset along the unit direction of sum_h w_h q_h
+    heads*w_bias; hot keys are shifted by hot_offset along the unit direction of sum_h w_h q_h
     of that layer and request.  With the defaults about 12% of entries end up resident.
     """
     rng = make_rng(seed)
@@ -244,8 +245,8 @@ def three_layer_mask_fp8(seed: int = 1003, B: int = 8, seq_len: int = 262144,
     hot = np.stack(hot).astype(np.int32)
     queries, dirs = [], []
     for _ in range(n_layers):
-        q32 = _normal(rng, (B, HEADS, DIM), std=1.0 / np.sqrt(DIM))
-        w0 = _normal(rng, (B, HEADS), std=0.125)
+        q32 = _normal(rng, (B, heads, DIM), std=1.0 / np.sqrt(DIM))
+        w0 = _normal(rng, (B, heads), std=0.125)
         w32 = (w0 - w0.mean(axis=1, keepdims=True) + np.float32(w_bias)).astype(np.float32)
         qb, wb = bf16_bits(q32), bf16_bits(w32)
         queries.append(Queries(qb, "bf16", wb, "bf16"))
@@ -271,7 +272,7 @@ def three_layer_mask_fp8(seed: int = 1003, B: int = 8, seq_len: int = 262144,
 
 def two_level_resident_fp8(seed: int = 1004, B: int = 30, seq_len: int = 262144,
                            kmax: int = 384, shuffled: bool = False, poison: bool = True,
-                           ragged: bool = False) -> Workload:
+                           ragged: bool = False, heads: int = HEADS) -> Workload:
     """Level-2 scoring restricted to kmax resident pages per request (fp8 keys).
 
     The pool holds every logical page of every request (permuted).  With poison=True the
@@ -279,8 +280,8 @@ def two_level_resident_fp8(seed: int = 1004, B: int = 30, seq_len: int = 262144,
     entries are -1, so a result that touched one of them would show it.
     """
     rng = make_rng(seed)
-    q32 = _normal(rng, (B, HEADS, DIM), std=1.0 / np.sqrt(DIM))
-    w32 = _normal(rng, (B, HEADS), mean=0.05, std=0.125)
+    q32 = _normal(rng, (B, heads, DIM), std=1.0 / np.sqrt(DIM))
+    w32 = _normal(rng, (B, heads), mean=0.05, std=0.125)
     qb, wb = bf16_bits(q32), bf16_bits(w32)
     seq_lens = _ragged_lens(rng, B, seq_len, ragged)
     ppr = -(-seq_len // PAGE)
