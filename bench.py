@@ -16,10 +16,11 @@ step; the eager rate of the same calls is reported beside it.  Per-kernel durati
 HIP events recorded on the stream the kernels run on, in the eager timed loop.  The
 roofline object reports the scoring kernel against HBM peak (8 TB/s) with its algorithmic
 bytes: keys once, q/w once, block table, logits written.  Secondary entries measure the other
-workloads (three-layer fp8 mask, two-level fp8 scoring over 384 resident pages, causal fp8
-prefill, the Mode A selection of 21 layers x 8 requests over 262,144 masked candidates, and
-the retriever's query encoder at decode and prefill batch sizes) the same way.  cpu_baseline times the fp64 oracle on a bounded sample of the
-headline workload on the host cores.
+workloads the same way: the three-layer fp8 mask with 64 heads and with the retriever's 128,
+two-level fp8 scoring over 384 resident pages, causal fp8 prefill, the Mode A selection of
+21 layers x 8 requests over 262,144 masked candidates, and the retriever's query encoder at
+decode and prefill batch sizes.  cpu_baseline times the fp64 oracle on a bounded sample of
+the headline workload on the host cores.
 
 Prints exactly one JSON line on stdout.
 """
@@ -155,8 +156,8 @@ def run_decode(torch, api, W, steps, warmup, replicas=3):
                     flops=entries * FLOP_PER_PAIR, graph_wall_s=graph_wall, graph_ms=graph_ms)
 
 
-def run_mask(torch, api, W, steps, warmup, replicas=2):
-    wl = W.three_layer_mask_fp8()
+def run_mask(torch, api, W, steps, warmup, replicas=2, heads=64):
+    wl = W.three_layer_mask_fp8(heads=heads)
     dw = api.DeviceWorkload(wl, "cuda:0", pool_copies=replicas)
     B = wl.kv.B
     ld = wl.kv.block_table.shape[1] * 64
@@ -175,13 +176,15 @@ def run_mask(torch, api, W, steps, warmup, replicas=2):
 
     wall, per = timed(torch, ["mask+compact"], step, steps, warmup)
     entries = int(wl.kv.seq_lens.sum())
-    alg = 3 * entries * 132 + 3 * B * (64 * 128 * 2 + 64 * 2) + wl.kv.block_table.nbytes + \
+    alg = 3 * entries * 132 + 3 * B * (heads * 128 * 2 + heads * 2) + wl.kv.block_table.nbytes + \
         B * ld + B * n_pages * 4
-    return dict(workload=wl.name, entries=entries, layers=3, ms=per["mask+compact"],
-                entries_per_s=entries / (per["mask+compact"] * 1e-3),
-                hbm_gbs=alg / (per["mask+compact"] * 1e-3) / 1e9,
-                hbm_frac=alg / (per["mask+compact"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                alg_bytes=alg, resident_pages_mean=None)
+    flops = 3 * entries * 2 * heads * 128
+    sec = per["mask+compact"] * 1e-3
+    return dict(workload=wl.name + ("" if heads == 64 else f"_h{heads}"), entries=entries,
+                layers=3, heads=heads, ms=per["mask+compact"], entries_per_s=entries / sec,
+                hbm_gbs=alg / sec / 1e9, hbm_frac=alg / sec / 1e9 / HBM_PEAK_GBS,
+                alg_bytes=alg, mfma_tflops=flops / sec / 1e12,
+                bf16_mfma_frac=flops / sec / 1e12 / BF16_PEAK_TFLOPS, resident_pages_mean=None)
 
 
 def run_two_level(torch, api, W, steps, warmup, replicas=12):
@@ -392,14 +395,15 @@ def main():
         "graph_event_ms_per_step": h["graph_ms"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "score_kernel<bf16 keys, bf16 q>",
+                     "kernel": "score_bf16_ring_kernel<4> (bf16 keys, bf16 q)",
                      "alg_bytes_per_launch": h["alg_bytes"], "avg_kernel_ms": score_ms},
         "kernels_ms": h["per"],
         "kernel_sources": digest,
     }
     if not args.headline_only:
         sec = []
-        for name, fn in (("mask", run_mask), ("two_level", run_two_level),
+        run_mask_h128 = lambda *a: run_mask(*a, heads=128)   # the retriever's head count
+        for name, fn in (("mask", run_mask), ("mask_h128", run_mask_h128), ("two_level", run_two_level),
                          ("prefill", run_prefill), ("mode_a", run_mode_a),
                          ("encoder", run_encoder)):
             log(f"secondary: {name} ...")

@@ -190,6 +190,22 @@ def test_mask_two_layers(mask_small, mode):
         assert np.array_equal(m["page_list"].cpu().numpy(), r["page_list"])
 
 
+def test_mask_four_layers():
+    """FM_MAX_LAYERS = 4 fp8 layers in one call: every layer takes part in the union."""
+    wl = W.three_layer_mask_fp8(seed=2013, B=2, seq_len=64 * 60 + 30, n_layers=4, ragged=True,
+                                cluster=2, w_bias=-0.04)
+    dw = dev(wl)
+    m = G.resident_mask(dw, layers=[0, 1, 2, 3])
+    r = oracle.resident_mask(wl, layers=[0, 1, 2, 3])
+    r3 = oracle.resident_mask(wl, layers=[0, 1, 2])
+    assert not np.array_equal(r["mask"], r3["mask"]), "the fourth layer must matter here"
+    dis, band = G.check_mask(m["mask"].cpu().numpy(), r["mask"], r["union"], 0.0,
+                             wl.kv.seq_lens, "mask four layers")
+    if dis == 0:
+        assert np.array_equal(m["page_count"].cpu().numpy(), r["page_count"])
+    G.note("mask four layers", disagreements=dis, band_entries=band)
+
+
 @pytest.fixture(scope="module")
 def mask_full():
     return W.three_layer_mask_fp8()
