@@ -18,8 +18,9 @@ roofline object reports the scoring kernel against HBM peak (8 TB/s) with its al
 bytes: keys once, q/w once, block table, logits written.  Secondary entries measure the other
 workloads the same way: the three-layer fp8 mask with 64 heads and with the retriever's 128,
 two-level fp8 scoring over 384 resident pages, causal fp8 prefill, the Mode A selection of
-21 layers x 8 requests over 262,144 masked candidates, and the retriever's query encoder at
-decode and prefill batch sizes.  cpu_baseline times the fp64 oracle on a bounded sample of
+21 layers x 8 requests over 262,144 masked candidates, the retriever's query encoder at
+decode and prefill batch sizes, and golden-label construction from 128 tokens x 21 layers x
+65,536 selector scores.  cpu_baseline times the fp64 oracle on a bounded sample of
 the headline workload on the host cores.
 
 Prints exactly one JSON line on stdout.
@@ -270,6 +271,37 @@ def run_mode_a(torch, api, W, steps, warmup, B=8, layers=21, n=262144, replicas=
                 alg_bytes=alg, note="selection only; logits synthetic")
 
 
+def run_labels(torch, api, W, steps, warmup):
+    """Golden labels for retriever training: 128 future tokens x 21 CSA layers x 65,536
+    compressed entries (256K context at 4:1) of synthetic selector scores, nucleus p = 0.6,
+    3 votes, lookahead tau = 64 (65 windows).  The pass reads every score once."""
+    g = W.selector_scores()
+    dev = "cuda:0"
+    S = torch.from_numpy(g.scores).to(dev)
+    nv = torch.from_numpy(g.n_valid).to(dev)
+    T, L, ld, tau = g.T, g.n_layers, g.ld, 64
+    nb = api.fm_golden_workspace_bytes(T, L, ld, tau)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ptr = torch.empty(T - tau + 2, dtype=torch.int32, device=dev)
+    cap = (T - tau + 1) * 4096
+    idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    sc = torch.empty(cap, dtype=torch.float32, device=dev)
+
+    def step(s, tm):
+        if tm: tm.mark(s, 0)
+        api.fm_golden_labels(S, ld, T, L, nv, 0.6, 3, tau, ptr, idx, sc, cap, ws, nb)
+        if tm: tm.mark(s, 1)
+
+    wall, per = timed(torch, ["labels"], step, steps, warmup)
+    ms = per["labels"]
+    n_labels = int(ptr[-1].item())
+    alg = S.numel() * 4 + nv.numel() * 4 + ptr.numel() * 4 + n_labels * 8
+    return dict(workload=g.name + f"_tau{tau}", rows=T * L, scores=S.numel(), ms=ms,
+                scores_per_s=S.numel() / (ms * 1e-3), hbm_gbs=alg / (ms * 1e-3) / 1e9,
+                hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, alg_bytes=alg,
+                labels=n_labels, windows=T - tau + 1)
+
+
 def run_encoder(torch, api, W, steps, warmup):
     """The retriever's query encoder at the page's sizes (d_model 4096, q_rank 2048, 128 heads
     of 128, RoPE on 64 dims): a decode batch of 32 rows (weight-bandwidth bound) and a prefill
@@ -405,7 +437,7 @@ def main():
         run_mask_h128 = lambda *a: run_mask(*a, heads=128)   # the retriever's head count
         for name, fn in (("mask", run_mask), ("mask_h128", run_mask_h128), ("two_level", run_two_level),
                          ("prefill", run_prefill), ("mode_a", run_mode_a),
-                         ("encoder", run_encoder)):
+                         ("encoder", run_encoder), ("labels", run_labels)):
             log(f"secondary: {name} ...")
             try:
                 sec.append(fn(torch, api, W, max(5, args.steps // 2), 2))

@@ -273,6 +273,37 @@ fm_status fm_encode_queries(const fm_encoder_desc *e, const void *hidden, int T,
                             const int32_t *pos, void *q, float *w, void *ws, size_t ws_bytes,
                             void *stream);
 
+/*
+ * Golden labels for training the retriever from the future native selector's scores
+ * (FlashMemory-DeepSeek-V4 paper summary, section 4, label construction; README "Data": CSR
+ * labels).  scores: float32 [T, n_layers, ld], 4-byte aligned: the selector score of future
+ * token i, CSA layer l and compressed entry s.  The candidates of token i are the entries
+ * s < n_valid[i] (n_valid NULL: ld) whose score is not -inf or NaN; scores are finite or -inf.
+ *   P[i,l,s] = softmax over the candidates;
+ *   M[i,l]   = the candidates sorted by score (descending; equal scores by lower s) up to the
+ *              last whose cumulative P is at most p (inclusive; a token whose largest P
+ *              exceeds p has an empty M);
+ *   V[i,s]   = the number of layers l with s in M[i,l];  A[i] = {s : V[i,s] >= min_votes};
+ *   Y[t]     = union of A[i] for i = t .. t + tau - 1, for the windows t = 0 .. T - tau.
+ * Output, CSR: label_ptr int32 [T - tau + 2] (always written in full); window t's labels are
+ * label_idx[label_ptr[t] .. label_ptr[t + 1]) in ascending s, and label_score (nullable) holds
+ * for each the fraction of the window's tau tokens whose A holds it (the page defines no
+ * score).  Positions at or past cap are not written: a caller sizes the arrays from
+ * label_ptr[T - tau + 1] (a first call with cap 0 may count only).
+ * The membership decisions use softmax masses in 2^-31 fixed point with integer sums: they
+ * agree with exact arithmetic except where a cumulative mass lies within about 1e-6 of p.
+ * Limits: 1 <= ld <= 65,536, 1 <= n_layers <= 64, 1 <= tau <= T, (T - tau + 1) * ld < 2^31,
+ * 1 <= min_votes, 0 < p <= 1.  ws 256-byte aligned, ws_bytes >=
+ * fm_golden_workspace_bytes(T, n_layers, ld, tau), its contents irrelevant.
+ * Errors: FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED (ld or n_layers past the limits),
+ * FM_ERR_WORKSPACE; nothing is launched on error.
+ */
+size_t fm_golden_workspace_bytes(int T, int n_layers, int64_t ld, int tau);
+fm_status fm_golden_labels(const float *scores, int64_t ld, int T, int n_layers,
+                           const int32_t *n_valid, float p, int min_votes, int tau,
+                           int32_t *label_ptr, int32_t *label_idx, float *label_score,
+                           int64_t cap, void *ws, size_t ws_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *fm_status_string(fm_status s);
 

@@ -284,3 +284,33 @@ def test_encode_queries_validation():
     assert st(nb=need - 1) == api.FM_ERR_WORKSPACE
     assert st(ws=FAKE + 64) == api.FM_ERR_WORKSPACE         # workspace not 256-byte aligned
     api.fm_encode_queries(good_enc(), None, 0, None, None, None, None, 0)   # T = 0: no-op
+
+
+def test_golden_labels_validation():
+    L = api.lib()
+    need = api.fm_golden_workspace_bytes(10, 4, 1000, 3)
+    assert need > 0 and api.fm_golden_workspace_bytes(10, 4, 1000, 11) == 0
+
+    def st(**kw):
+        a = dict(scores=FAKE, ld=1000, T=10, n_layers=4, n_valid=None, p=0.6, min_votes=3, tau=3,
+                 ptr=FAKE, idx=FAKE, score=None, cap=100, ws=FAKE, ws_bytes=need)
+        a.update(kw)
+        return L.fm_golden_labels(a["scores"], a["ld"], a["T"], a["n_layers"], a["n_valid"],
+                                  a["p"], a["min_votes"], a["tau"], a["ptr"], a["idx"],
+                                  a["score"], a["cap"], a["ws"], a["ws_bytes"], None)
+    assert st(tau=0) == api.FM_ERR_INVALID_ARG
+    assert st(tau=11) == api.FM_ERR_INVALID_ARG
+    assert st(ld=0) == api.FM_ERR_INVALID_ARG
+    assert st(ld=65537, ws_bytes=1 << 30) == api.FM_ERR_UNSUPPORTED
+    assert st(n_layers=0) == api.FM_ERR_INVALID_ARG
+    assert st(n_layers=65) == api.FM_ERR_UNSUPPORTED
+    assert st(min_votes=0) == api.FM_ERR_INVALID_ARG
+    assert st(p=0.0) == api.FM_ERR_INVALID_ARG
+    assert st(p=1.5) == api.FM_ERR_INVALID_ARG
+    assert st(scores=None) == api.FM_ERR_INVALID_ARG
+    assert st(scores=FAKE + 2) == api.FM_ERR_INVALID_ARG
+    assert st(ptr=None) == api.FM_ERR_INVALID_ARG
+    assert st(idx=None) == api.FM_ERR_INVALID_ARG
+    assert st(ws_bytes=need - 1) == api.FM_ERR_WORKSPACE
+    assert st(ws=FAKE + 16) == api.FM_ERR_WORKSPACE
+    assert st(T=40000, tau=1, ld=65536, ws_bytes=1 << 40) == api.FM_ERR_UNSUPPORTED

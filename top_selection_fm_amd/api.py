@@ -28,8 +28,8 @@ Q_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8": FM_FP8_E4M3}
 
 EXPORTS = ["fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
            "fm_score_resident_cells", "fm_densest_pages", "fm_workspace_bytes",
-           "fm_encode_queries", "fm_encode_workspace_bytes",
-           "fm_status_string", "fm_last_error", "fm_version"]
+           "fm_encode_queries", "fm_encode_workspace_bytes", "fm_golden_labels",
+           "fm_golden_workspace_bytes", "fm_status_string", "fm_last_error", "fm_version"]
 
 
 class FmError(RuntimeError):
@@ -81,8 +81,13 @@ def lib():
         L.fm_encode_queries.argtypes = [P, P, C.c_int, P, P, P, P, C.c_size_t, P]
         L.fm_encode_workspace_bytes.argtypes = [P, C.c_int]
         L.fm_encode_workspace_bytes.restype = C.c_size_t
+        L.fm_golden_labels.argtypes = [P, I64, C.c_int, C.c_int, P, C.c_float, C.c_int, C.c_int,
+                                       P, P, P, I64, P, C.c_size_t, P]
+        L.fm_golden_workspace_bytes.argtypes = [C.c_int, C.c_int, I64, C.c_int]
+        L.fm_golden_workspace_bytes.restype = C.c_size_t
         for f in ("fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
-                  "fm_score_resident_cells", "fm_densest_pages", "fm_encode_queries"):
+                  "fm_score_resident_cells", "fm_densest_pages", "fm_encode_queries",
+                  "fm_golden_labels"):
             getattr(L, f).restype = C.c_int
         L.fm_workspace_bytes.argtypes = [C.c_int, C.c_int, I64]
         L.fm_workspace_bytes.restype = C.c_size_t
@@ -219,6 +224,19 @@ def fm_encode_queries(desc: EncoderDesc, hidden, T: int, pos, q, w, ws, ws_bytes
                       stream=None) -> None:
     _check(lib().fm_encode_queries(C.byref(desc), _ptr(hidden), int(T), _ptr(pos), _ptr(q),
                                    _ptr(w), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def fm_golden_workspace_bytes(T: int, n_layers: int, ld: int, tau: int) -> int:
+    return int(lib().fm_golden_workspace_bytes(int(T), int(n_layers), int(ld), int(tau)))
+
+
+def fm_golden_labels(scores, ld: int, T: int, n_layers: int, n_valid, p: float, min_votes: int,
+                     tau: int, label_ptr, label_idx, label_score, cap: int, ws, ws_bytes: int,
+                     stream=None) -> None:
+    _check(lib().fm_golden_labels(_ptr(scores), int(ld), int(T), int(n_layers), _ptr(n_valid),
+                                  float(p), int(min_votes), int(tau), _ptr(label_ptr),
+                                  _ptr(label_idx), _ptr(label_score), int(cap), _ptr(ws),
+                                  int(ws_bytes), _stream(stream)))
 
 
 def fm_workspace_bytes(op: int, T: int, max_candidates: int) -> int:

@@ -549,6 +549,53 @@ fm_status fm_encode_queries(const fm_encoder_desc *e, const void *hidden, int T,
     return ok();
 }
 
+size_t fm_golden_workspace_bytes(int T, int n_layers, int64_t ld, int tau) {
+    if (T <= 0 || n_layers <= 0 || ld <= 0 || tau <= 0 || tau > T) return 0;
+    return fm::labels_ws_bytes(T, n_layers, ld, tau);
+}
+
+fm_status fm_golden_labels(const float *scores, int64_t ld, int T, int n_layers,
+                           const int32_t *n_valid, float p, int min_votes, int tau,
+                           int32_t *label_ptr, int32_t *label_idx, float *label_score,
+                           int64_t cap, void *ws, size_t ws_bytes, void *stream) {
+    REQUIRE(T >= 1 && tau >= 1 && tau <= T, FM_ERR_INVALID_ARG, "T = %d, tau = %d (1 <= tau <= T)",
+            T, tau);
+    REQUIRE(ld >= 1, FM_ERR_INVALID_ARG, "ld = %lld", (long long)ld);
+    REQUIRE(ld <= fm::kLabelMaxLd, FM_ERR_UNSUPPORTED, "ld = %lld (at most %d)", (long long)ld,
+            fm::kLabelMaxLd);
+    REQUIRE(n_layers >= 1, FM_ERR_INVALID_ARG, "n_layers = %d", n_layers);
+    REQUIRE(n_layers <= 64, FM_ERR_UNSUPPORTED, "n_layers = %d (at most 64)", n_layers);
+    REQUIRE((int64_t)(T - tau + 1) * ld < (int64_t)INT32_MAX, FM_ERR_UNSUPPORTED,
+            "(T - tau + 1) * ld = %lld labels could overflow int32 pointers",
+            (long long)((int64_t)(T - tau + 1) * ld));
+    REQUIRE(min_votes >= 1, FM_ERR_INVALID_ARG, "min_votes = %d", min_votes);
+    REQUIRE(p > 0.f && p <= 1.f, FM_ERR_INVALID_ARG, "p = %g outside (0, 1]", (double)p);
+    REQUIRE(scores && aligned(scores, 4), FM_ERR_INVALID_ARG, "scores NULL or not 4-byte aligned");
+    REQUIRE(label_ptr, FM_ERR_INVALID_ARG, "label_ptr is NULL");
+    REQUIRE(cap >= 0 && (cap == 0 || label_idx), FM_ERR_INVALID_ARG,
+            "cap = %lld needs label_idx", (long long)cap);
+    const size_t need = fm::labels_ws_bytes(T, n_layers, ld, tau);
+    REQUIRE(ws && aligned(ws, 256) && ws_bytes >= need, FM_ERR_WORKSPACE,
+            "workspace %zu bytes at %p, need %zu (256-byte aligned)", ws_bytes, ws, need);
+    fm::LabelArgs a;
+    a.scores = scores;
+    a.ld = ld;
+    a.T = T;
+    a.n_layers = n_layers;
+    a.n_valid = n_valid;
+    a.p = p;
+    a.min_votes = min_votes;
+    a.tau = tau;
+    a.words = (int)((ld + 31) / 32);
+    a.label_ptr = label_ptr;
+    a.label_idx = label_idx;
+    a.label_score = cap ? label_score : nullptr;
+    a.cap = cap;
+    fm::labels_ws_carve(a, ws);
+    CHECK(launched(fm::launch_labels(a, (hipStream_t)stream), "golden labels"));
+    return ok();
+}
+
 size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates) {
     if (T <= 0 || max_candidates <= 0) return 0;
     if (op == FM_OP_TOPK) return fm::topk_ws_bytes(T, max_candidates);

@@ -176,6 +176,28 @@ hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s);
 hipError_t launch_enc_norm(const EncNormArgs &a, hipStream_t s);
 hipError_t launch_enc_rope_had(const EncRopeArgs &a, hipStream_t s);
 
+// Golden labels (labels.hip).
+constexpr int kLabelMaxLd = 65536;      // entries of one token's row, at most
+struct LabelArgs {
+    const float *scores;      // [T, n_layers, ld]
+    int64_t ld;
+    int T, n_layers;
+    const int32_t *n_valid;   // [T] or null
+    float p;
+    int min_votes, tau;
+    int words;                // ceil(ld / 32)
+    uint32_t *mbits;          // workspace [T, n_layers, words]: nucleus membership
+    uint32_t *gbits;          // workspace [T, words]: golden sets
+    int32_t *counts;          // workspace [T - tau + 1]: labels per window
+    int32_t *label_ptr;       // [T - tau + 2]
+    int32_t *label_idx;       // [cap]
+    float *label_score;       // [cap] or null
+    int64_t cap;
+};
+size_t labels_ws_bytes(int T, int n_layers, int64_t ld, int tau);
+void labels_ws_carve(LabelArgs &a, void *ws);
+hipError_t launch_labels(const LabelArgs &a, hipStream_t s);
+
 size_t topk_ws_bytes(int T, int64_t n);   // bytes for T rows of up to n entries (0: not used)
 TopkWs topk_ws_carve(void *ws, int T, int64_t n);
 

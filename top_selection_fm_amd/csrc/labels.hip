@@ -1,0 +1,448 @@
+// labels.hip -- golden labels for training the retriever, built from the future native
+// selector's scores (FlashMemory-DeepSeek-V4 paper summary, section 4, label construction):
+//   P[i,l,:] = softmax of S[i,l,:] over token i's candidates;
+//   M[i,l]   = the candidates sorted by score (descending, lower entry first) up to the last one
+//              whose cumulative mass is at most p;
+//   V[i,s]   = the number of layers whose nucleus holds s;  A[i] = {s : V[i,s] >= min_votes};
+//   Y[t]     = the union of A[i] over the lookahead window i = t .. t + tau - 1, as CSR.
+//
+// Four steps, each a kernel:
+//   nucleus_kernel  one workgroup per (token, layer) row holds the row in registers and finds
+//                   the nucleus boundary exactly: softmax masses in 2^-31 fixed point summed
+//                   as integers (so the sums, and with them every decision, are independent of
+//                   the summation order), a mass histogram over linear score bins to find the
+//                   boundary bin, then a 32-bit radix search over the scores of that bin
+//                   (gathered in LDS)
+//                   for the boundary score; equal scores at the boundary are taken by lower
+//                   entry.  Membership goes out as one bit per entry.
+//   golden_kernel   votes across layers, one thread per 32-entry word: the golden bits A[i].
+//   window kernels  per window t: OR of tau golden words (count, then an exclusive scan of
+//                   the counts into label_ptr, then the ascending indices with their scores,
+//                   the fraction of the window's tokens whose golden set holds the entry).
+#include <math.h>
+
+#include "fm_internal.h"
+
+namespace fm {
+namespace {
+
+constexpr int kNucNT = 1024;                 // threads of a nucleus row
+constexpr int kNucVec = kLabelMaxLd / (4 * kNucNT);   // float4 blocks a thread
+constexpr int kNucBins = 2048;
+constexpr float kNucSpan = 32.0f;            // linear bins over scores in [max - 32, max]
+constexpr int kWinNT = 256;                  // threads of a window kernel
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64;
+
+template <class U>
+__device__ __forceinline__ U wave_incl_scan_t(U x) {
+    const int ln = __lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const U y = __shfl_up(x, o);
+        if (ln >= o) x += y;
+    }
+    return x;
+}
+
+// exclusive prefix sum over the NT threads of the block; sh holds NT / 64 + 1 values
+template <class U, int NT>
+__device__ U block_excl_scan_t(U x, U *sh, U &total) {
+    constexpr int NW = NT / 64;
+    const int w = threadIdx.x >> 6, ln = __lane_id();
+    const U inc = wave_incl_scan_t<U>(x);
+    if (ln == 63) sh[w] = inc;
+    __syncthreads();
+    if (w == 0) {
+        const U v = ln < NW ? sh[ln] : (U)0;
+        const U vi = wave_incl_scan_t<U>(v);
+        if (ln < NW) sh[ln] = vi - v;
+        if (ln == NW - 1) sh[NW] = vi;
+    }
+    __syncthreads();
+    const U res = sh[w] + inc - x;
+    total = sh[NW];
+    __syncthreads();
+    return res;
+}
+
+// order-preserving key of a score: a larger score has a larger key; -0 and +0 are one key
+__device__ __forceinline__ uint32_t score_key(float x) {
+    const uint32_t u = __float_as_uint(x == 0.f ? 0.f : x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kBinsPerUnit = (float)kNucBins / kNucSpan;
+constexpr int kNucList = 4096;               // boundary-bin entries gathered in LDS, at most
+
+// Per-row constants: with c31 = 31 - mx log2(e), exp(x - mx) 2^31 = exp2(fma(x, log2 e, c31))
+// (the fixed-point scale rides in the exponent); cb places x = mx - kNucSpan at bin 0.
+struct RowConst {
+    float c31, cb;
+};
+
+// exp(x - mx) in units of 2^-31 (at most about 2^31: mx is the row maximum)
+__device__ __forceinline__ uint32_t mass_fx(float x, const RowConst &k) {
+    return (uint32_t)__builtin_amdgcn_exp2f(fmaf(x, kLog2e, k.c31));
+}
+
+// linear bin of a score over [mx - kNucSpan, mx]: monotone in x, so every score of a higher
+// bin is larger than every score of a lower one
+__device__ __forceinline__ int score_bin(float x, const RowConst &k) {
+    const int b = (int)fmaf(x, kBinsPerUnit, k.cb);
+    return b < 0 ? 0 : (b > kNucBins - 1 ? kNucBins - 1 : b);
+}
+
+// the score of an order-preserving key (score_key's inverse)
+__device__ __forceinline__ float key_score(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// The row's registers pass through an empty asm statement before each sweep over them, so the
+// compiler cannot keep per-entry results (keys, bins, masses) of one sweep alive for the next:
+// 64 values a thread already fill half the registers.
+template <int VEC>
+__device__ __forceinline__ void opaque_row(float (&v)[VEC][4]) {
+#pragma unroll
+    for (int u = 0; u < VEC; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(v[u][c]));
+}
+
+struct NucLds {
+    u64 hm[kNucBins];                   // mass per bin
+    uint32_t hc[kNucBins];              // entries per bin (radix passes)
+    float lx[kNucList];                 // scores of the boundary bin
+    u64 sh64[kNucNT / 64 + 1];
+    uint32_t sh32[kNucNT / 64 + 1];
+    float shf[kNucNT / 64];
+    u64 m64[2];
+    uint32_t m32[2];
+    uint32_t list_n;
+};
+
+// Bins [0, nb) are walked from the top (largest scores first): find the bin where the running
+// mass, starting at 0, first exceeds `room`; its index goes to m32[0] and the mass of the bins
+// above it to m64[0].  The caller guarantees that the bins' total exceeds room.
+template <int NT>
+__device__ void find_boundary_bin(NucLds &L, int nb, u64 room) {
+    const int tid = threadIdx.x;
+    constexpr int BPT = kNucBins / NT;
+    const int top = nb - 1 - BPT * tid;
+    u64 h[BPT], sum = 0;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        h[k] = top - k >= 0 ? L.hm[top - k] : 0ull;
+        sum += h[k];
+    }
+    u64 total;
+    u64 above = block_excl_scan_t<u64, NT>(sum, L.sh64, total);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+        if (above <= room && room < above + h[k]) {
+            L.m32[0] = (uint32_t)(top - k);
+            L.m64[0] = above;
+        }
+        above += h[k];
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
+    constexpr int NT = kNucNT, NW = NT / 64, VEC = kNucVec;
+    __shared__ NucLds L;
+    const int l = blockIdx.x, i = blockIdx.y, tid = threadIdx.x, ln = __lane_id(), w = tid >> 6;
+    const float *row = A.scores + ((int64_t)i * A.n_layers + l) * A.ld;
+    uint32_t *mout = A.mbits + ((int64_t)i * A.n_layers + l) * A.words;
+    int n = A.n_valid ? A.n_valid[i] : (int)A.ld;
+    n = n < 0 ? 0 : (n > (int)A.ld ? (int)A.ld : n);
+    for (int b = tid; b < kNucBins; b += NT) L.hm[b] = 0ull;
+    if (tid == 0) L.list_n = 0u;
+
+    // the row; entries past n, -inf and NaN are not candidates (-inf here)
+    float v[VEC][4];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, n * 4, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+        const int j = 4 * (u * NT + tid);
+        const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 4u, 0, 0));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[u][c] = (j + c < n && x[c] == x[c]) ? x[c] : -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < VEC; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, v[u][c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if (ln == 0) L.shf[w] = mx;
+    __syncthreads();
+    mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) mx = fmaxf(mx, L.shf[k]);
+    if (mx == -INFINITY) {                      // no candidate: an empty nucleus
+        for (int wd = tid; wd < A.words; wd += NT) mout[wd] = 0u;
+        return;
+    }
+    const RowConst K{31.0f - mx * kLog2e, (kNucSpan - mx) * kBinsPerUnit};
+
+    // masses, their total and the mass histogram over linear score bins
+    u64 zt = 0;
+#pragma unroll
+    for (int u = 0; u < VEC; ++u)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float x = v[u][c];
+            if (x > -INFINITY) {
+                const uint32_t q = mass_fx(x, K);
+                zt += q;
+                if (q) atomicAdd(&L.hm[score_bin(x, K)], (u64)q);
+            }
+        }
+    u64 Z;
+    (void)block_excl_scan_t<u64, NT>(zt, L.sh64, Z);   // also orders the histogram's atomics
+    // room for the members: cumulative mass <= p Z, in the same fixed point
+    const u64 room = (u64)((double)A.p * (double)Z);
+    const bool all = room >= Z;                 // p = 1 (or above): every candidate
+    float xstar = INFINITY;
+    uint32_t r = 0u, g = 0u;
+    if (!all) {
+        find_boundary_bin<NT>(L, kNucBins, room);
+        const int b1 = (int)L.m32[0];
+        u64 above = L.m64[0];
+        // the boundary bin's scores, gathered in LDS (few: the bins are narrow)
+        opaque_row<VEC>(v);
+#pragma unroll
+        for (int u = 0; u < VEC; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float x = v[u][c];
+                if (x > -INFINITY && score_bin(x, K) == b1) {
+                    const uint32_t e = atomicAdd(&L.list_n, 1u);
+                    if (e < (uint32_t)kNucList) L.lx[e] = x;
+                }
+            }
+        __syncthreads();
+        const uint32_t nlist = L.list_n;
+        // the exact boundary score inside bin b1: radix over the 32-bit key, 11 + 11 + 10 bits,
+        // over the gathered scores (or, if the bin overflowed the list, over the row in memory)
+        uint32_t prefix = 0u, pmask = 0u, dig = 0u;
+        auto radix_pass = [&](int pass, auto &&sweep) {
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const int nb = pass == 2 ? 1024 : 2048;
+            for (int b = tid; b < kNucBins; b += NT) {
+                L.hm[b] = 0ull;
+                L.hc[b] = 0u;
+            }
+            __syncthreads();
+            sweep([&](float x) {
+                const uint32_t key = score_key(x);
+                if ((key & pmask) == prefix) {
+                    const uint32_t d = (key >> shift) & (uint32_t)(nb - 1);
+                    atomicAdd(&L.hm[d], (u64)mass_fx(x, K));
+                    atomicAdd(&L.hc[d], 1u);
+                }
+            });
+            __syncthreads();
+            find_boundary_bin<NT>(L, nb, room - above);
+            dig = L.m32[0];
+            above += L.m64[0];
+            prefix |= dig << shift;
+            pmask |= (uint32_t)(nb - 1) << shift;
+        };
+        if (nlist <= (uint32_t)kNucList) {
+#pragma unroll 1
+            for (int pass = 0; pass < 3; ++pass)
+                radix_pass(pass, [&](auto &&add) {
+                    for (uint32_t e = tid; e < nlist; e += NT) add(L.lx[e]);
+                });
+        } else {
+#pragma unroll 1
+            for (int pass = 0; pass < 3; ++pass)
+                radix_pass(pass, [&](auto &&add) {
+                    // the row again from memory (the bin overflowed the list: many equal or
+                    // nearly equal scores), so the registers stay as they are
+                    for (int j = 4 * tid; j < n; j += 4 * NT) {
+                        const f32x4 x4 = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 4u, 0, 0));
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const float x = x4[c];
+                            if (j + c < n && x == x && x > -INFINITY && score_bin(x, K) == b1) add(x);
+                        }
+                    }
+                });
+        }
+        // every entry of the boundary score has the same mass wq; r of its g entries are members
+        xstar = key_score(prefix);
+        g = L.hc[dig];
+        const u64 wq = g ? L.hm[dig] / g : 1ull;   // g > 0 and wq > 0: the bin holds the boundary
+        const u64 rr = (room - above) / (wq ? wq : 1ull);
+        r = (uint32_t)(rr < (u64)g ? rr : (u64)g);
+        __syncthreads();                        // L.hc / L.hm are read before anything reuses them
+    }
+
+    // membership bits: score > xstar, or score == xstar among the first r of those by entry
+    // index (lower entries first).  Entry 4 (u NT + tid) + c is bit 4 (tid % 8) + c of word
+    // (u NT + tid) / 8: eight neighbouring lanes assemble a word.
+    const bool split = !all && r > 0u && r < g;  // workgroup-uniform
+    const bool take_eq = all || r == g;
+    uint32_t run = 0u;                          // boundary entries in earlier slabs
+    opaque_row<VEC>(v);
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+        uint32_t nib = 0u, eq_mask = 0u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float x = v[u][c];
+            const bool cand = x > -INFINITY;
+            const bool in = cand && (all || x > xstar || (x == xstar && take_eq));
+            nib |= (in ? 1u : 0u) << c;
+            eq_mask |= (cand && x == xstar ? 1u : 0u) << c;
+        }
+        if (split) {
+            uint32_t tot;
+            const uint32_t before = run + block_excl_scan_t<uint32_t, NT>((uint32_t)__popc(eq_mask), L.sh32, tot);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if ((eq_mask >> c) & 1u) {
+                    const uint32_t rank = before + (uint32_t)__popc(eq_mask & ((1u << c) - 1u));
+                    nib |= (rank < r ? 1u : 0u) << c;
+                }
+            run += tot;
+        }
+        uint32_t word = nib << (4 * (tid & 7));
+        word |= __shfl_xor(word, 1);
+        word |= __shfl_xor(word, 2);
+        word |= __shfl_xor(word, 4);
+        const int wd = (u * NT + tid) >> 3;
+        if ((tid & 7) == 0 && wd < A.words) mout[wd] = word;
+    }
+}
+
+// votes of token blockIdx.y across layers, one thread per 32-entry word
+__global__ __launch_bounds__(256) void golden_kernel(LabelArgs A) {
+    const int wd = blockIdx.x * 256 + threadIdx.x, i = blockIdx.y;
+    if (wd >= A.words) return;
+    uint32_t cnt[32];
+#pragma unroll
+    for (int b = 0; b < 32; ++b) cnt[b] = 0u;
+    const uint32_t *m = A.mbits + (int64_t)i * A.n_layers * A.words + wd;
+    for (int l = 0; l < A.n_layers; ++l) {
+        const uint32_t x = m[(int64_t)l * A.words];
+#pragma unroll
+        for (int b = 0; b < 32; ++b) cnt[b] += (x >> b) & 1u;
+    }
+    uint32_t gw = 0u;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) gw |= (cnt[b] >= (uint32_t)A.min_votes ? 1u : 0u) << b;
+    A.gbits[(int64_t)i * A.words + wd] = gw;
+}
+
+// labels of window t = blockIdx.x: their number
+__global__ __launch_bounds__(kWinNT) void window_count_kernel(LabelArgs A) {
+    __shared__ uint32_t sh[kWinNT / 64 + 1];
+    const int t = blockIdx.x;
+    uint32_t c = 0u;
+    for (int wd = threadIdx.x; wd < A.words; wd += kWinNT) {
+        uint32_t y = 0u;
+        for (int k = 0; k < A.tau; ++k) y |= A.gbits[(int64_t)(t + k) * A.words + wd];
+        c += (uint32_t)__popc(y);
+    }
+    uint32_t tot;
+    (void)block_excl_scan_t<uint32_t, kWinNT>(c, sh, tot);
+    if (threadIdx.x == 0) A.counts[t] = (int32_t)tot;
+}
+
+// label_ptr = exclusive prefix sum of the window counts (one workgroup)
+__global__ __launch_bounds__(1024) void window_scan_kernel(LabelArgs A) {
+    __shared__ uint32_t sh[1024 / 64 + 1];
+    const int n = A.T - A.tau + 1;
+    uint32_t carry = 0u;
+    for (int b = 0; b < n; b += 1024) {
+        const int t = b + (int)threadIdx.x;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan_t<uint32_t, 1024>(t < n ? (uint32_t)A.counts[t] : 0u, sh, tot);
+        if (t < n) A.label_ptr[t] = (int32_t)(carry + ex);
+        carry += tot;
+    }
+    if (threadIdx.x == 0) A.label_ptr[n] = (int32_t)carry;
+}
+
+// labels of window t = blockIdx.x: ascending entries, each with the fraction of the window's
+// tokens whose golden set holds it.  Thread k owns a contiguous run of words, so the order of
+// the threads is the order of the entries.  Positions at or past cap are not written.
+__global__ __launch_bounds__(kWinNT) void window_write_kernel(LabelArgs A) {
+    __shared__ uint32_t sh[kWinNT / 64 + 1];
+    constexpr int kMaxWpt = kLabelMaxLd / 32 / kWinNT;
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int wpt = (A.words + kWinNT - 1) / kWinNT;
+    const int w0 = tid * wpt;
+    const uint32_t *gb = A.gbits + (int64_t)t * A.words;
+    uint32_t y[kMaxWpt];
+    uint32_t c = 0u;
+#pragma unroll
+    for (int k = 0; k < kMaxWpt; ++k) {
+        y[k] = 0u;
+        if (k < wpt && w0 + k < A.words)
+            for (int i = 0; i < A.tau; ++i) y[k] |= gb[(int64_t)i * A.words + w0 + k];
+        c += (uint32_t)__popc(y[k]);
+    }
+    uint32_t tot;
+    int64_t pos = (int64_t)A.label_ptr[t] + block_excl_scan_t<uint32_t, kWinNT>(c, sh, tot);
+#pragma unroll
+    for (int k = 0; k < kMaxWpt; ++k) {
+        uint32_t bits = y[k];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            if (pos < A.cap) {
+                A.label_idx[pos] = 32 * (w0 + k) + b;
+                if (A.label_score) {
+                    int hits = 0;
+                    for (int i = 0; i < A.tau; ++i) hits += (gb[(int64_t)i * A.words + w0 + k] >> b) & 1u;
+                    A.label_score[pos] = (float)hits / (float)A.tau;
+                }
+            }
+            ++pos;
+        }
+    }
+}
+
+}  // namespace
+
+size_t labels_ws_bytes(int T, int n_layers, int64_t ld, int tau) {
+    const size_t words = (size_t)((ld + 31) / 32);
+    return align_up((size_t)T * n_layers * words * 4, 256) + align_up((size_t)T * words * 4, 256) +
+           align_up((size_t)(T - tau + 1) * 4, 256);
+}
+
+void labels_ws_carve(LabelArgs &a, void *ws) {
+    uint8_t *p = (uint8_t *)ws;
+    const size_t words = (size_t)a.words;
+    a.mbits = (uint32_t *)p;
+    p += align_up((size_t)a.T * a.n_layers * words * 4, 256);
+    a.gbits = (uint32_t *)p;
+    p += align_up((size_t)a.T * words * 4, 256);
+    a.counts = (int32_t *)p;
+}
+
+hipError_t launch_labels(const LabelArgs &a, hipStream_t s) {
+    nucleus_kernel<<<dim3((unsigned)a.n_layers, (unsigned)a.T), dim3(kNucNT), 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    golden_kernel<<<dim3((unsigned)((a.words + 255) / 256), (unsigned)a.T), dim3(256), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const unsigned windows = (unsigned)(a.T - a.tau + 1);
+    window_count_kernel<<<dim3(windows), dim3(kWinNT), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    window_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    window_write_kernel<<<dim3(windows), dim3(kWinNT), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace fm

@@ -369,3 +369,53 @@ def query_encoder(seed: int = 1007, T: int = 32, n_heads: int = 128, d_model: in
     pos = rng.integers(0, max_pos, size=T).astype(np.int32)
     return EncoderInputs(f"query_encoder_t{T}_h{n_heads}_d{d_model}_r{q_rank}", hidden, pos,
                          wq_a, q_norm, wq_b, w_proj, n_heads)
+
+
+class SelectorScores:
+    """Future native-selector scores for golden-label construction: S [T, n_layers, ld] float32
+    and n_valid [T] (token i sees the compressed entries below n_valid[i])."""
+
+    def __init__(self, name, scores, n_valid):
+        self.name = name
+        self.scores = scores
+        self.n_valid = n_valid
+
+    @property
+    def T(self) -> int:
+        return int(self.scores.shape[0])
+
+    @property
+    def n_layers(self) -> int:
+        return int(self.scores.shape[1])
+
+    @property
+    def ld(self) -> int:
+        return int(self.scores.shape[2])
+
+
+def selector_scores(seed: int = 1008, T: int = 128, n_layers: int = 21, ld: int = 65536,
+                    pool: int = 256, per_token: int = 48, layer_frac: float = 0.7,
+                    boost=(7.0, 11.0), causal: bool = True) -> SelectorScores:
+    """Synthetic selector scores of T consecutive future tokens over ld compressed entries.
+
+    Every score is N(0, 1); each token attends to per_token entries drawn from a persistent pool
+    of `pool` entries, and each layer boosts a random layer_frac of those by U(boost) -- so a few
+    dozen entries carry most of each token's softmax mass, the layers mostly agree, and the
+    window's union stays in the hundreds.  With causal=True token i sees
+    ld - (T - 1 - i) // 4 entries (one more compressed entry every 4 tokens); the scores past
+    that stay in the array and are not candidates.
+    """
+    rng = make_rng(seed)
+    S = rng.standard_normal((T, n_layers, ld), dtype=np.float32)
+    hot_pool = rng.choice(ld, size=min(pool, ld), replace=False)
+    for i in range(T):
+        hot = rng.choice(hot_pool, size=min(per_token, hot_pool.size), replace=False)
+        for l in range(n_layers):
+            sel = hot[rng.random(hot.size) < layer_frac]
+            S[i, l, sel] += rng.uniform(boost[0], boost[1], sel.size).astype(np.float32)
+    if causal:
+        n_valid = (ld - (T - 1 - np.arange(T)) // 4).astype(np.int32)
+    else:
+        n_valid = np.full(T, ld, np.int32)
+    n_valid = np.maximum(n_valid, 0)
+    return SelectorScores(f"selector_scores_t{T}_l{n_layers}_n{ld}", S, n_valid)
