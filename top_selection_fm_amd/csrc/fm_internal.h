@@ -188,7 +188,9 @@ struct LabelArgs {
     int words;                // ceil(ld / 32)
     uint32_t *mbits;          // workspace [T, n_layers, words]: nucleus membership
     uint32_t *gbits;          // workspace [T, words]: golden sets
-    int32_t *counts;          // workspace [T - tau + 1]: labels per window
+    uint32_t *ybits;          // workspace [T - tau + 1, words]: label sets of the windows
+    int32_t *counts;          // workspace [T - tau + 1, chunks]: labels, then first positions
+    int chunks;               // 256-word chunks of a row
     int32_t *label_ptr;       // [T - tau + 2]
     int32_t *label_idx;       // [cap]
     float *label_score;       // [cap] or null

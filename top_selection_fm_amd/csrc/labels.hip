@@ -16,9 +16,10 @@
 //                   for the boundary score; equal scores at the boundary are taken by lower
 //                   entry.  Membership goes out as one bit per entry.
 //   golden_kernel   votes across layers, one thread per 32-entry word: the golden bits A[i].
-//   window kernels  per window t: OR of tau golden words (count, then an exclusive scan of
-//                   the counts into label_ptr, then the ascending indices with their scores,
-//                   the fraction of the window's tokens whose golden set holds the entry).
+//   window kernels  per (window t, 256-word chunk): the OR of tau golden words and its count,
+//                   an exclusive scan of the counts into label_ptr and chunk positions, then
+//                   the ascending indices with their scores, the fraction of the window's
+//                   tokens whose golden set holds the entry.
 #include <math.h>
 
 #include "fm_internal.h"
@@ -342,91 +343,88 @@ __global__ __launch_bounds__(256) void golden_kernel(LabelArgs A) {
     A.gbits[(int64_t)i * A.words + wd] = gw;
 }
 
-// labels of window t = blockIdx.x: their number
-__global__ __launch_bounds__(kWinNT) void window_count_kernel(LabelArgs A) {
+// Window t = blockIdx.x, words [256 c, 256 c + 256) with c = blockIdx.y: the label words
+// (OR of the window's tau golden words) to the workspace, and their label count.
+__global__ __launch_bounds__(kWinNT) void window_or_kernel(LabelArgs A) {
     __shared__ uint32_t sh[kWinNT / 64 + 1];
-    const int t = blockIdx.x;
-    uint32_t c = 0u;
-    for (int wd = threadIdx.x; wd < A.words; wd += kWinNT) {
-        uint32_t y = 0u;
-        for (int k = 0; k < A.tau; ++k) y |= A.gbits[(int64_t)(t + k) * A.words + wd];
-        c += (uint32_t)__popc(y);
+    const int t = blockIdx.x, c = blockIdx.y, wd = c * kWinNT + (int)threadIdx.x;
+    uint32_t y = 0u;
+    if (wd < A.words) {
+        const uint32_t *gb = A.gbits + (int64_t)t * A.words + wd;
+        for (int k = 0; k < A.tau; ++k) y |= gb[(int64_t)k * A.words];
+        A.ybits[(int64_t)t * A.words + wd] = y;
     }
     uint32_t tot;
-    (void)block_excl_scan_t<uint32_t, kWinNT>(c, sh, tot);
-    if (threadIdx.x == 0) A.counts[t] = (int32_t)tot;
+    (void)block_excl_scan_t<uint32_t, kWinNT>((uint32_t)__popc(y), sh, tot);
+    if (threadIdx.x == 0) A.counts[(int64_t)t * A.chunks + c] = (int32_t)tot;
 }
 
-// label_ptr = exclusive prefix sum of the window counts (one workgroup)
+// exclusive prefix sum of the (window, chunk) counts in window-major order (one workgroup):
+// the chunks' first positions, and label_ptr
 __global__ __launch_bounds__(1024) void window_scan_kernel(LabelArgs A) {
     __shared__ uint32_t sh[1024 / 64 + 1];
-    const int n = A.T - A.tau + 1;
+    const int windows = A.T - A.tau + 1;
+    const int64_t n = (int64_t)windows * A.chunks;
     uint32_t carry = 0u;
-    for (int b = 0; b < n; b += 1024) {
-        const int t = b + (int)threadIdx.x;
+    for (int64_t b = 0; b < n; b += 1024) {
+        const int64_t e = b + threadIdx.x;
         uint32_t tot;
-        const uint32_t ex = block_excl_scan_t<uint32_t, 1024>(t < n ? (uint32_t)A.counts[t] : 0u, sh, tot);
-        if (t < n) A.label_ptr[t] = (int32_t)(carry + ex);
+        const uint32_t ex = block_excl_scan_t<uint32_t, 1024>(e < n ? (uint32_t)A.counts[e] : 0u, sh, tot);
+        if (e < n) {
+            A.counts[e] = (int32_t)(carry + ex);
+            if (e % A.chunks == 0) A.label_ptr[e / A.chunks] = (int32_t)(carry + ex);
+        }
         carry += tot;
     }
-    if (threadIdx.x == 0) A.label_ptr[n] = (int32_t)carry;
+    if (threadIdx.x == 0) A.label_ptr[windows] = (int32_t)carry;
 }
 
-// labels of window t = blockIdx.x: ascending entries, each with the fraction of the window's
-// tokens whose golden set holds it.  Thread k owns a contiguous run of words, so the order of
-// the threads is the order of the entries.  Positions at or past cap are not written.
+// window t = blockIdx.x, chunk c = blockIdx.y: the chunk's labels in ascending entry order
+// (thread order is word order), each with the fraction of the window's tokens whose golden set
+// holds it.  Positions at or past cap are not written.
 __global__ __launch_bounds__(kWinNT) void window_write_kernel(LabelArgs A) {
     __shared__ uint32_t sh[kWinNT / 64 + 1];
-    constexpr int kMaxWpt = kLabelMaxLd / 32 / kWinNT;
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const int wpt = (A.words + kWinNT - 1) / kWinNT;
-    const int w0 = tid * wpt;
-    const uint32_t *gb = A.gbits + (int64_t)t * A.words;
-    uint32_t y[kMaxWpt];
-    uint32_t c = 0u;
-#pragma unroll
-    for (int k = 0; k < kMaxWpt; ++k) {
-        y[k] = 0u;
-        if (k < wpt && w0 + k < A.words)
-            for (int i = 0; i < A.tau; ++i) y[k] |= gb[(int64_t)i * A.words + w0 + k];
-        c += (uint32_t)__popc(y[k]);
-    }
+    const int t = blockIdx.x, c = blockIdx.y, wd = c * kWinNT + (int)threadIdx.x;
+    const uint32_t y = wd < A.words ? A.ybits[(int64_t)t * A.words + wd] : 0u;
     uint32_t tot;
-    int64_t pos = (int64_t)A.label_ptr[t] + block_excl_scan_t<uint32_t, kWinNT>(c, sh, tot);
-#pragma unroll
-    for (int k = 0; k < kMaxWpt; ++k) {
-        uint32_t bits = y[k];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1u;
-            if (pos < A.cap) {
-                A.label_idx[pos] = 32 * (w0 + k) + b;
-                if (A.label_score) {
-                    int hits = 0;
-                    for (int i = 0; i < A.tau; ++i) hits += (gb[(int64_t)i * A.words + w0 + k] >> b) & 1u;
-                    A.label_score[pos] = (float)hits / (float)A.tau;
-                }
+    int64_t pos = (int64_t)A.counts[(int64_t)t * A.chunks + c] +
+                  block_excl_scan_t<uint32_t, kWinNT>((uint32_t)__popc(y), sh, tot);
+    const uint32_t *gb = A.gbits + (int64_t)t * A.words + wd;
+    uint32_t bits = y;
+    while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (pos < A.cap) {
+            A.label_idx[pos] = 32 * wd + b;
+            if (A.label_score) {
+                int hits = 0;
+                for (int k = 0; k < A.tau; ++k) hits += (gb[(int64_t)k * A.words] >> b) & 1u;
+                A.label_score[pos] = (float)hits / (float)A.tau;
             }
-            ++pos;
         }
+        ++pos;
     }
 }
 
 }  // namespace
 
 size_t labels_ws_bytes(int T, int n_layers, int64_t ld, int tau) {
-    const size_t words = (size_t)((ld + 31) / 32);
+    const size_t words = (size_t)((ld + 31) / 32), windows = (size_t)(T - tau + 1);
+    const size_t chunks = (words + kWinNT - 1) / kWinNT;
     return align_up((size_t)T * n_layers * words * 4, 256) + align_up((size_t)T * words * 4, 256) +
-           align_up((size_t)(T - tau + 1) * 4, 256);
+           align_up(windows * words * 4, 256) + align_up(windows * chunks * 4, 256);
 }
 
 void labels_ws_carve(LabelArgs &a, void *ws) {
     uint8_t *p = (uint8_t *)ws;
-    const size_t words = (size_t)a.words;
+    const size_t words = (size_t)a.words, windows = (size_t)(a.T - a.tau + 1);
+    a.chunks = (int)((words + kWinNT - 1) / kWinNT);
     a.mbits = (uint32_t *)p;
     p += align_up((size_t)a.T * a.n_layers * words * 4, 256);
     a.gbits = (uint32_t *)p;
     p += align_up((size_t)a.T * words * 4, 256);
+    a.ybits = (uint32_t *)p;
+    p += align_up(windows * words * 4, 256);
     a.counts = (int32_t *)p;
 }
 
@@ -436,12 +434,12 @@ hipError_t launch_labels(const LabelArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     golden_kernel<<<dim3((unsigned)((a.words + 255) / 256), (unsigned)a.T), dim3(256), 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const unsigned windows = (unsigned)(a.T - a.tau + 1);
-    window_count_kernel<<<dim3(windows), dim3(kWinNT), 0, s>>>(a);
+    const dim3 wgrid((unsigned)(a.T - a.tau + 1), (unsigned)a.chunks);
+    window_or_kernel<<<wgrid, dim3(kWinNT), 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     window_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    window_write_kernel<<<dim3(windows), dim3(kWinNT), 0, s>>>(a);
+    window_write_kernel<<<wgrid, dim3(kWinNT), 0, s>>>(a);
     return hipGetLastError();
 }
 
