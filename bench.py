@@ -15,7 +15,9 @@ replayed (the pages run this step inside a CUDA graph), so host launch latency s
 step; the eager rate of the same calls is reported beside it.  Per-kernel durations come from
 HIP events recorded on the stream the kernels run on, in the eager timed loop.  The
 roofline object reports the scoring kernel against HBM peak (8 TB/s) with its algorithmic
-bytes: keys once, q/w once, block table, logits written.  Secondary entries measure the other
+bytes (keys once, q/w once, block table, logits written) over its average launch duration:
+HIP events around the same scoring calls launched back to back (events around each single
+launch, which add a few microseconds, are reported beside it as bracketed_ms).  Secondary entries measure the other
 workloads the same way: the three-layer fp8 mask with 64 heads and with the retriever's 128,
 two-level fp8 scoring over 384 resident pages, causal fp8 prefill, the Mode A selection of
 21 layers x 8 requests over 262,144 masked candidates, the retriever's query encoder at
@@ -149,12 +151,22 @@ def run_decode(torch, api, W, steps, warmup, replicas=3):
     torch.cuda.synchronize()
     graph_wall = time.perf_counter() - t0
     graph_ms = g0.elapsed_time(g1) / steps
+    # the scoring kernel's average launch duration: the same launches back to back on the
+    # stream, between two events (per-launch events around each call add their own few us)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for s in range(steps):
+        api.fm_index_logits(q, kvs[s % replicas], logits, ld)
+    s1.record()
+    torch.cuda.synchronize()
+    score_b2b_ms = s0.elapsed_time(s1) / steps
     entries = int(wl.kv.seq_lens.sum())
     key_bytes = entries * 256
     alg_bytes = key_bytes + B * 64 * 128 * 2 + B * 64 * 2 + wl.kv.block_table.nbytes + \
         wl.kv.seq_lens.nbytes + B * ld * 4
     return wl, dict(entries=entries, wall_s=wall, per=per, alg_bytes=alg_bytes,
-                    flops=entries * FLOP_PER_PAIR, graph_wall_s=graph_wall, graph_ms=graph_ms)
+                    flops=entries * FLOP_PER_PAIR, graph_wall_s=graph_wall, graph_ms=graph_ms,
+                    score_b2b_ms=score_b2b_ms)
 
 
 def run_mask(torch, api, W, steps, warmup, replicas=2, heads=64):
@@ -402,7 +414,7 @@ def main():
     log("headline: decode bf16 B=32 x 65536 ...")
     wl, h = run_decode(torch, api, W, args.steps, args.warmup)
     ms_step = h["graph_wall_s"] / args.steps * 1e3
-    score_ms = h["per"]["score"]
+    score_ms = h["score_b2b_ms"]
     digest = kernel_source_digest()
     achieved = h["alg_bytes"] / (score_ms * 1e-3) / 1e9
     traffic = read_traffic("score_decode_bf16_b32_s65536_counters.txt", digest)
@@ -428,7 +440,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "score_bf16_ring_kernel<4> (bf16 keys, bf16 q)",
-                     "alg_bytes_per_launch": h["alg_bytes"], "avg_kernel_ms": score_ms},
+                     "alg_bytes_per_launch": h["alg_bytes"], "avg_kernel_ms": score_ms,
+                     "timing": "events around back-to-back launches of the scoring call",
+                     "bracketed_ms": h["per"]["score"]},
         "kernels_ms": h["per"],
         "kernel_sources": digest,
     }
