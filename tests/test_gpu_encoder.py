@@ -92,6 +92,17 @@ def test_encoder_many_rows_sampled():
     assert np.array_equal(qg, qg2) and np.array_equal(wg, wg2)
 
 
+def test_encoder_prefill_tiled_products():
+    """1,000 rows: both products take the LDS-tiled kernel (128 x 128 tiles, the last row tile
+    and, with 2,112 columns, the last column tile partial; d_model 528 leaves a 16-wide K tail;
+    the first product's columns straddle the wq_a / w_proj boundary inside a tile)."""
+    e = W.query_encoder(seed=3106, T=1000, n_heads=64, d_model=528, q_rank=2048)
+    qg, wg = run_encoder(e)
+    rows = np.array([0, 1, 127, 128, 255, 500, 896, 999])
+    qr, wr = oracle_encoder(e, rows=rows)
+    check("encoder 1000 rows tiled (sampled)", qg[rows], wg[rows], qr, wr)
+
+
 def test_encoder_feeds_scoring():
     """Encoder (64 heads) -> fm_index_logits on a small bf16 pool, against the oracle encoder's
     q and w (rounded to float32) scored by the oracle: the whole per-layer path."""

@@ -24,8 +24,14 @@
 
 #include "fm_internal.h"
 
+#ifndef FM_ENC_TILED_MIN_ROWS
+#define FM_ENC_TILED_MIN_ROWS 256   // rows from which a product (without split K) is LDS-tiled
+#endif
+
 namespace fm {
 namespace {
+
+constexpr int kTiledMinRows = FM_ENC_TILED_MIN_ROWS;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -224,9 +230,102 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E) {
     *(uint32_t *)&E.q[((int64_t)m * E.n_heads + hh) * kDim + 2 * ln] = packed;
 }
 
+// Prefill-sized products (hundreds of rows and more): a 128 x 128 output tile a workgroup,
+// staged through LDS 32 k-values at a time, so each A row and each weight row is read from
+// memory once per tile instead of once per 32 x 32 tile.  Four waves, each a 64 x 64 quarter
+// as 2 x 2 MFMA tiles; the next k-slab's global loads are in flight while the current one is
+// multiplied from the other LDS buffer.  LDS rows are padded to 40 bf16 (80 B), which keeps
+// the 16-byte operand reads of a wave conflict-free.  Z = 1 (no partial sums).
+#ifndef FM_ENC_TK
+#define FM_ENC_TK 32
+#endif
+constexpr int kTM = 128, kTN = 128, kTK = FM_ENC_TK, kTLd = kTK + 8, kTPieces = kTK / 16;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void enc_gemm_tiled_kernel(EncGemmArgs G) {
+    __shared__ __align__(16) uint16_t sA[2][kTM * kTLd];
+    __shared__ __align__(16) uint16_t sW[2][kTN * kTLd];
+    const int tid = threadIdx.x, ln = __lane_id(), j = ln & 31, h = ln >> 5, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int N = G.N0 + G.N1;
+    const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
+    // this thread's slab loads: row lr of the tile, k values kTK/2 lh .. + kTK/2 - 1
+    const int lr = tid >> 1, lh = tid & 1;
+    const int am = min(m0 + lr, G.M - 1), wnr = min(n0 + lr, N - 1);
+    const uint16_t *ap = G.A + (int64_t)am * G.lda + (kTK / 2) * lh;
+    const uint16_t *wp = (wnr < G.N0 ? G.W0 + (int64_t)wnr * G.K : G.W1 + (int64_t)(wnr - G.N0) * G.K) +
+                         (kTK / 2) * lh;
+    const int lofs = lr * kTLd + (kTK / 2) * lh;
+    u32x4 ra[kTPieces], rw[kTPieces];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int e = 0; e < kTPieces; ++e) {
+            const bool in = k0 + (kTK / 2) * lh + 8 * e < G.K;   // K is a multiple of 16
+            ra[e] = in ? *(const u32x4 *)(ap + k0 + 8 * e) : u32x4{0u, 0u, 0u, 0u};
+            rw[e] = in ? *(const u32x4 *)(wp + k0 + 8 * e) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < kTPieces; ++e) {
+            *(u32x4 *)&sA[buf][lofs + 8 * e] = ra[e];
+            *(u32x4 *)&sW[buf][lofs + 8 * e] = rw[e];
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+
+    const int nk = (G.K + kTK - 1) / kTK;
+    load(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) load((kt + 1) * kTK);
+#pragma unroll
+        for (int ks = 0; ks < kTK / 16; ++ks) {
+            u32x4 a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *(const u32x4 *)&sA[buf][(wm * 64 + 32 * i + j) * kTLd + 16 * ks + 8 * h];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                b[jj] = *(const u32x4 *)&sW[buf][(wn * 64 + 32 * jj + j) * kTLd + 16 * ks + 8 * h];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma(a[i], b[jj], acc[i][jj]);
+        }
+        if (kt + 1 < nk) stash(buf ^ 1);
+        __syncthreads();
+    }
+    // accumulator v of lane j + 32 h: row 8 (v / 4) + 4 h + v % 4, column j of its MFMA tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int col = n0 + wn * 64 + 32 * jj + j;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (row < G.M && col < N) G.C[(int64_t)row * N + col] = acc[i][jj][v];
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
+    if (g.S == 1 && g.Z == 1 && g.M >= kTiledMinRows) {
+        enc_gemm_tiled_kernel<<<dim3((unsigned)((g.N0 + g.N1 + kTN - 1) / kTN),
+                                     (unsigned)((g.M + kTM - 1) / kTM)), 256, 0, s>>>(g);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((g.N0 + g.N1) / 32), (unsigned)((g.M + 31) / 32), (unsigned)g.Z);
     switch (g.S) {
         case 1: enc_gemm_kernel<1><<<grid, 64, 0, s>>>(g); break;
