@@ -32,6 +32,8 @@ namespace fm {
 namespace {
 
 constexpr int kTiledMinRows = FM_ENC_TILED_MIN_ROWS;
+constexpr int kRopeHeadsPerWave = 16;   // heads of one row a RoPE / Hadamard wave takes, from
+                                        // 256 rows (n_heads % 32 == 0); one below
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -188,46 +190,55 @@ __global__ __launch_bounds__(kNormNT) void enc_norm_kernel(EncNormArgs E) {
     }
 }
 
-// One wave per (row, head), four heads a workgroup: lane l holds dims 2 l, 2 l + 1.  The RoPE
-// angle pos * theta_i is formed and reduced in fp64 (positions reach millions of radians).
-__global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E) {
+// One wave per (row, hpw heads), four waves a workgroup: lane l holds dims 2 l, 2 l + 1 of each
+// head in turn.  The RoPE angle pos * theta_i is formed and reduced in fp64 (positions reach
+// millions of radians), once per row and pair: every head of the row turns by the same angles.
+__global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E, int hpw) {
     const int ln = __lane_id();
+    const int groups = E.n_heads / hpw;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= (int64_t)E.M * E.n_heads) return;
-    const int m = (int)(item / E.n_heads), hh = (int)(item % E.n_heads);
+    if (item >= (int64_t)E.M * groups) return;
+    const int m = (int)(item / groups), h0 = (int)(item % groups) * hpw;
     const int N = E.n_heads * kDim;
-    float x0 = 0.f, x1 = 0.f;
-#pragma unroll 4
-    for (int z = 0; z < E.Z; ++z) {
-        const float2 xv = *(const float2 *)&E.C[((int64_t)z * E.M + m) * N + hh * kDim + 2 * ln];
-        x0 += xv.x;
-        x1 += xv.y;
-    }
+    // the rotation of pair ln at this row's position: the same for every head of the row
     const int first = (kDim - E.rope_dim) / 2;          // the first rotated pair
+    float c = 1.f, sn = 0.f;
     if (ln >= first) {
         const double ang = (double)E.pos[m] * E.inv_freq[ln - first];
-        const float c = (float)cos(ang), sn = (float)sin(ang);
-        const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
-        x0 = y0;
-        x1 = y1;
+        c = (float)cos(ang);
+        sn = (float)sin(ang);
     }
-    // Walsh-Hadamard butterflies (Sylvester order): dims 2 l and 2 l + 1 in the lane, then
-    // lanes l and l ^ s for s = 1 .. 32 (dims 2 l + c and 2 (l ^ s) + c)
-    {
-        const float a = x0, b = x1;
-        x0 = a + b;
-        x1 = a - b;
-    }
+    for (int hh = h0; hh < h0 + hpw; ++hh) {
+        float x0 = 0.f, x1 = 0.f;
+#pragma unroll 4
+        for (int z = 0; z < E.Z; ++z) {
+            const float2 xv = *(const float2 *)&E.C[((int64_t)z * E.M + m) * N + hh * kDim + 2 * ln];
+            x0 += xv.x;
+            x1 += xv.y;
+        }
+        if (ln >= first) {
+            const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+            x0 = y0;
+            x1 = y1;
+        }
+        // Walsh-Hadamard butterflies (Sylvester order): dims 2 l and 2 l + 1 in the lane, then
+        // lanes l and l ^ s for s = 1 .. 32 (dims 2 l + c and 2 (l ^ s) + c)
+        {
+            const float a = x0, b = x1;
+            x0 = a + b;
+            x1 = a - b;
+        }
 #pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        const float o0 = __shfl_xor(x0, s), o1 = __shfl_xor(x1, s);
-        const bool up = (ln & s) != 0;
-        x0 = up ? o0 - x0 : x0 + o0;
-        x1 = up ? o1 - x1 : x1 + o1;
+        for (int s = 1; s < 64; s <<= 1) {
+            const float o0 = __shfl_xor(x0, s), o1 = __shfl_xor(x1, s);
+            const bool up = (ln & s) != 0;
+            x0 = up ? o0 - x0 : x0 + o0;
+            x1 = up ? o1 - x1 : x1 + o1;
+        }
+        const float nrm = 0.08838834764831845f;              // 1 / sqrt(128)
+        const uint32_t packed = (uint32_t)bf16_rne(x0 * nrm) | ((uint32_t)bf16_rne(x1 * nrm) << 16);
+        *(uint32_t *)&E.q[((int64_t)m * E.n_heads + hh) * kDim + 2 * ln] = packed;
     }
-    const float nrm = 0.08838834764831845f;              // 1 / sqrt(128)
-    const uint32_t packed = (uint32_t)bf16_rne(x0 * nrm) | ((uint32_t)bf16_rne(x1 * nrm) << 16);
-    *(uint32_t *)&E.q[((int64_t)m * E.n_heads + hh) * kDim + 2 * ln] = packed;
 }
 
 // Prefill-sized products (hundreds of rows and more): a 128 x 128 output tile a workgroup,
@@ -344,8 +355,9 @@ hipError_t launch_enc_norm(const EncNormArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_enc_rope_had(const EncRopeArgs &a, hipStream_t s) {
-    const int64_t items = (int64_t)a.M * a.n_heads;
-    enc_rope_had_kernel<<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a);
+    const int hpw = a.M >= 256 ? kRopeHeadsPerWave : 1;
+    const int64_t items = (int64_t)a.M * (a.n_heads / hpw);
+    enc_rope_had_kernel<<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a, hpw);
     return hipGetLastError();
 }
 
