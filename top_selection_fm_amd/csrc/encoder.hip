@@ -251,6 +251,10 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E, int hp
 #define FM_ENC_TK 32
 #endif
 constexpr int kTM = 128, kTN = 128, kTK = FM_ENC_TK, kTLd = kTK + 8, kTPieces = kTK / 16;
+#ifndef FM_ENC_GROUP_M
+#define FM_ENC_GROUP_M 4
+#endif
+constexpr int kTGroupM = FM_ENC_GROUP_M;
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void enc_gemm_tiled_kernel(EncGemmArgs G) {
@@ -259,7 +263,16 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
     const int tid = threadIdx.x, ln = __lane_id(), j = ln & 31, h = ln >> 5, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int N = G.N0 + G.N1;
-    const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
+    // Tile order: the chip's 8 XCDs (each with its own L2) take consecutive workgroup ids in
+    // turn, so workgroup b runs on XCD b % 8; each XCD is given a contiguous run of tiles, and
+    // within it tiles go in groups of kTGroupM row tiles by every column tile, so the
+    // workgroups an L2 serves at once share their activation rows and weight rows.
+    const int mT = (G.M + kTM - 1) / kTM, nTl = (N + kTN - 1) / kTN, total = mT * nTl;
+    const int b = blockIdx.x, x = b % 8, per = total / 8, rem = total % 8;
+    const int t = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + b / 8;
+    const int grp = t / (kTGroupM * nTl), fm = grp * kTGroupM, gs = min(kTGroupM, mT - fm);
+    const int within = t - grp * kTGroupM * nTl;
+    const int m0 = (fm + within % gs) * kTM, n0 = (within / gs) * kTN;
     // this thread's slab loads: row lr of the tile, k values kTK/2 lh .. + kTK/2 - 1
     const int lr = tid >> 1, lh = tid & 1;
     const int am = min(m0 + lr, G.M - 1), wnr = min(n0 + lr, N - 1);
@@ -333,8 +346,8 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
 
 hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
     if (g.S == 1 && g.Z == 1 && g.M >= kTiledMinRows) {
-        enc_gemm_tiled_kernel<<<dim3((unsigned)((g.N0 + g.N1 + kTN - 1) / kTN),
-                                     (unsigned)((g.M + kTM - 1) / kTM)), 256, 0, s>>>(g);
+        const int tiles = ((g.N0 + g.N1 + kTN - 1) / kTN) * ((g.M + kTM - 1) / kTM);
+        enc_gemm_tiled_kernel<<<dim3((unsigned)tiles), 256, 0, s>>>(g);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((g.N0 + g.N1) / 32), (unsigned)((g.M + 31) / 32), (unsigned)g.Z);
