@@ -192,6 +192,23 @@ def test_head_permutation_and_positive_rescaling():
     assert np.array_equal(i0, i4)
 
 
+def test_head_sum_splits_into_head_groups():
+    """The score is a sum over heads, so a 128-head row's logits are the sum of its two 64-head
+    halves' (each scored alone); a dropped or double-counted head group fails it."""
+    wl = tiny_wl(seed=9, T=2, H=128, D=128, n_entries=70, page=64, key_dtype="fp8",
+                 q_dtype="bf16", w_dtype="f32")
+    L = oracle.logits(wl)
+    q, w = wl.queries[0].q, wl.queries[0].w
+    halves = []
+    for h0 in (0, 64):
+        part = W.Workload("half", wl.kv, [W.Queries(np.ascontiguousarray(q[:, h0:h0 + 64]), "bf16",
+                                                    np.ascontiguousarray(w[:, h0:h0 + 64]), "f32")])
+        halves.append(oracle.logits(part))
+    fin = np.isfinite(L)
+    assert np.array_equal(fin, np.isfinite(halves[0]))
+    assert np.allclose(L[fin], (halves[0] + halves[1])[fin], rtol=1e-12, atol=1e-14)
+
+
 def test_fp8_scale_factors_out():
     """Doubling every per-entry scale doubles every logit (scales are positive)."""
     wl = tiny_wl(seed=6, T=2, H=4, D=8, n_entries=32, page=8, key_dtype="fp8", q_dtype="bf16",
