@@ -237,12 +237,15 @@ def run_prefill(torch, api, W, steps, warmup):
     nb = api.fm_workspace_bytes(api.FM_OP_TOPK, T, ld)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
     q, kv = dw.query(), dw.kv()
+    # each row's visible length (its causal cut): the top-k reads no further
+    n_vis = np.minimum(wl.queries[0].q_pos.astype(np.int64) // 4, ld).astype(np.int32)
+    n_valid = torch.from_numpy(n_vis).to("cuda:0")
 
     def step(s, tm):
         if tm: tm.mark(s, 0)
         api.fm_index_logits(q, kv, logits, ld)
         if tm: tm.mark(s, 1)
-        api.fm_topk512(logits, ld, T, None, None, 0, None, 512, idx, None, ws, nb)
+        api.fm_topk512(logits, ld, T, n_valid, None, 0, None, 512, idx, None, ws, nb)
         if tm: tm.mark(s, 2)
 
     wall, per = timed(torch, ["score", "topk"], step, steps, warmup)

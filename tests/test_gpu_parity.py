@@ -422,6 +422,19 @@ def test_prefill_full_sampled_rows(prefill_full):
     G.note("prefill full sampled", rows=rows.tolist(), logit_err=err, topk_dis=dis)
 
 
+def test_prefill_topk_with_causal_lengths(prefill_full):
+    """Giving the top-k each row's causal length (as a prefill caller can) selects exactly what
+    the full rows select: every entry past the cut is -inf in the logits."""
+    wl = prefill_full
+    dw = dev(wl)
+    L = G.index_logits(dw)
+    ld = L.shape[1]
+    nv = np.minimum(wl.queries[0].q_pos.astype(np.int64) // 4, ld).astype(np.int32)
+    i_full, v_full = G.topk(L)
+    i_cut, v_cut = G.topk(L, n_valid=torch.from_numpy(nv).cuda())
+    assert torch.equal(i_full, i_cut) and torch.equal(v_full, v_cut)
+
+
 @pytest.mark.parametrize("T,pos0,seq_len,extra_ld", [
     (16, 4 * 700, 64 * 12 + 3, 0),       # exactly one 16-row tile
     (17, 4 * 700, 64 * 12 + 3, 70),      # a ragged second tile; columns past seq_len
