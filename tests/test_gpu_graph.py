@@ -1,7 +1,7 @@
 """The entry points inside a captured HIP graph.
 
-A serving loop launches the decode step (scoring + top-512), two-level scoring and the Level-1
-mask as graphs.  Each graph here is captured once, then replayed several times with eager work
+A serving loop launches the decode step (scoring + top-512), two-level scoring, the Level-1
+mask and the query encoder as graphs (label construction is captured alike).  Each graph here is captured once, then replayed several times with eager work
 of the library and of torch in between; every replay must reproduce the eager result bit for
 bit (the kernels are deterministic).  Nothing in these calls allocates or clears memory with a
 memset, so they are safe to capture.
@@ -99,3 +99,55 @@ def test_mask_graph():
 
     keys = ["mask", "page_count", "page_list", "page_density", "union"]
     _replays(g, [out[k] for k in keys], [ref[k] for k in keys], disturb)
+
+
+def test_encoder_graph():
+    """The query encoder (four launches) captured at a decode batch and at a tiled batch."""
+    for T, kw in ((32, dict(n_heads=128, d_model=512, q_rank=256)),
+                  (300, dict(n_heads=64, d_model=256, q_rank=1024))):
+        e = W.query_encoder(seed=3010 + T, T=T, **kw)
+        t = {k: torch.from_numpy(getattr(e, k).view(np.int16)).cuda()
+             for k in ("hidden", "wq_a", "q_norm", "wq_b", "w_proj")}
+        pos = torch.from_numpy(e.pos).cuda()
+        desc = api.encoder_desc(t["wq_a"], t["q_norm"], t["wq_b"], t["w_proj"],
+                                n_heads=e.n_heads, d_model=e.d_model, q_rank=e.q_rank)
+        nb = api.fm_encode_workspace_bytes(desc, T)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        q = torch.empty((T, e.n_heads, 128), dtype=torch.bfloat16, device="cuda")
+        w = torch.empty((T, e.n_heads), dtype=torch.float32, device="cuda")
+        api.fm_encode_queries(desc, t["hidden"], T, pos, q, w, ws, nb)
+        torch.cuda.synchronize()
+        ref_q, ref_w = q.clone(), w.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            api.fm_encode_queries(desc, t["hidden"], T, pos, q, w, ws, nb)
+        _replays(g, [q, w], [ref_q, ref_w], lambda: ws.fill_(0))
+
+
+def test_golden_labels_graph():
+    g0 = W.selector_scores(seed=3020, T=12, n_layers=5, ld=3000, pool=64, per_token=16)
+    T, L, ld, tau = g0.T, g0.n_layers, g0.ld, 4
+    S = torch.from_numpy(g0.scores).cuda()
+    nv = torch.from_numpy(g0.n_valid).cuda()
+    nb = api.fm_golden_workspace_bytes(T, L, ld, tau)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ptr = torch.empty(T - tau + 2, dtype=torch.int32, device="cuda")
+    cap = (T - tau + 1) * ld
+    idx = torch.empty(cap, dtype=torch.int32, device="cuda")
+    sc = torch.empty(cap, dtype=torch.float32, device="cuda")
+    api.fm_golden_labels(S, ld, T, L, nv, 0.6, 3, tau, ptr, idx, sc, cap, ws, nb)
+    torch.cuda.synchronize()
+    n = int(ptr[-1].item())
+    ref = (ptr.clone(), idx[:n].clone(), sc[:n].clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.fm_golden_labels(S, ld, T, L, nv, 0.6, 3, tau, ptr, idx, sc, cap, ws, nb)
+    for i in range(4):
+        ptr.fill_(-1)
+        idx.fill_(-1)
+        sc.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ptr, ref[0]) and torch.equal(idx[:n], ref[1]) and torch.equal(sc[:n], ref[2]), f"replay {i}"
