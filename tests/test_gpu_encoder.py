@@ -103,6 +103,16 @@ def test_encoder_prefill_tiled_products():
     check("encoder 1000 rows tiled (sampled)", qg[rows], wg[rows], qr, wr)
 
 
+def test_encoder_prefill_wide_tiles():
+    """600 rows x 256 heads: the second product (32,768 columns) takes the 128 x 256 tiles
+    (a partial last row tile)."""
+    e = W.query_encoder(seed=3107, T=600, n_heads=256, d_model=256, q_rank=512)
+    qg, wg = run_encoder(e)
+    rows = np.array([0, 63, 64, 127, 128, 300, 511, 512, 599])
+    qr, wr = oracle_encoder(e, rows=rows)
+    check("encoder 600 rows x 256 heads, wide tiles (sampled)", qg[rows], wg[rows], qr, wr)
+
+
 def test_encoder_feeds_scoring():
     """Encoder (64 heads) -> fm_index_logits on a small bf16 pool, against the oracle encoder's
     q and w (rounded to float32) scored by the oracle: the whole per-layer path."""

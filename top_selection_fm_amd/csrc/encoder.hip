@@ -250,16 +250,25 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E, int hp
 #ifndef FM_ENC_TK
 #define FM_ENC_TK 32
 #endif
-constexpr int kTM = 128, kTN = 128, kTK = FM_ENC_TK, kTLd = kTK + 8, kTPieces = kTK / 16;
+constexpr int kTM = 128, kTK = FM_ENC_TK, kTLd = kTK + 8;
+#ifndef FM_ENC_WIDE_TILES
+#define FM_ENC_WIDE_TILES 512
+#endif
+constexpr int kWideTiles = FM_ENC_WIDE_TILES;
 #ifndef FM_ENC_GROUP_M
 #define FM_ENC_GROUP_M 4
 #endif
 constexpr int kTGroupM = FM_ENC_GROUP_M;
 
+template <int BN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void enc_gemm_tiled_kernel(EncGemmArgs G) {
+    // PR 16-byte pieces a row of a k-slab; PA / PW pieces a thread loads of A / W; WJ MFMA
+    // column tiles a wave (its quarter is 64 x BN / 2)
+    constexpr int PR = kTK / 8, PA = kTM * PR / 256, PW = BN * PR / 256, WJ = BN / 64;
+    static_assert(PA >= 1 && PW >= 1 && kTM * PR % 256 == 0 && BN * PR % 256 == 0, "slab layout");
     __shared__ __align__(16) uint16_t sA[2][kTM * kTLd];
-    __shared__ __align__(16) uint16_t sW[2][kTN * kTLd];
+    __shared__ __align__(16) uint16_t sW[2][BN * kTLd];
     const int tid = threadIdx.x, ln = __lane_id(), j = ln & 31, h = ln >> 5, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int N = G.N0 + G.N1;
@@ -267,40 +276,51 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
     // turn, so workgroup b runs on XCD b % 8; each XCD is given a contiguous run of tiles, and
     // within it tiles go in groups of kTGroupM row tiles by every column tile, so the
     // workgroups an L2 serves at once share their activation rows and weight rows.
-    const int mT = (G.M + kTM - 1) / kTM, nTl = (N + kTN - 1) / kTN, total = mT * nTl;
+    const int mT = (G.M + kTM - 1) / kTM, nTl = (N + BN - 1) / BN, total = mT * nTl;
     const int b = blockIdx.x, x = b % 8, per = total / 8, rem = total % 8;
     const int t = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + b / 8;
     const int grp = t / (kTGroupM * nTl), fm = grp * kTGroupM, gs = min(kTGroupM, mT - fm);
     const int within = t - grp * kTGroupM * nTl;
-    const int m0 = (fm + within % gs) * kTM, n0 = (within / gs) * kTN;
-    // this thread's slab loads: row lr of the tile, k values kTK/2 lh .. + kTK/2 - 1
-    const int lr = tid >> 1, lh = tid & 1;
-    const int am = min(m0 + lr, G.M - 1), wnr = min(n0 + lr, N - 1);
-    const uint16_t *ap = G.A + (int64_t)am * G.lda + (kTK / 2) * lh;
-    const uint16_t *wp = (wnr < G.N0 ? G.W0 + (int64_t)wnr * G.K : G.W1 + (int64_t)(wnr - G.N0) * G.K) +
-                         (kTK / 2) * lh;
-    const int lofs = lr * kTLd + (kTK / 2) * lh;
-    u32x4 ra[kTPieces], rw[kTPieces];
-    auto load = [&](int k0) {
+    const int m0 = (fm + within % gs) * kTM, n0 = (within / gs) * BN;
+    // this thread's slab pieces: piece p = tid P + e is row p / PR, k values 8 (p % PR) .. + 7
+    const uint16_t *ap[PA];
+    const uint16_t *wp[PW];
+    int aofs[PA], wofs[PW], akp[PA], wkp[PW];
 #pragma unroll
-        for (int e = 0; e < kTPieces; ++e) {
-            const bool in = k0 + (kTK / 2) * lh + 8 * e < G.K;   // K is a multiple of 16
-            ra[e] = in ? *(const u32x4 *)(ap + k0 + 8 * e) : u32x4{0u, 0u, 0u, 0u};
-            rw[e] = in ? *(const u32x4 *)(wp + k0 + 8 * e) : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int e = 0; e < PA; ++e) {
+        const int p = tid * PA + e, r = p / PR, kp = 8 * (p % PR);
+        ap[e] = G.A + (int64_t)min(m0 + r, G.M - 1) * G.lda + kp;
+        aofs[e] = r * kTLd + kp;
+        akp[e] = kp;
+    }
+#pragma unroll
+    for (int e = 0; e < PW; ++e) {
+        const int p = tid * PW + e, r = p / PR, kp = 8 * (p % PR);
+        const int n = min(n0 + r, N - 1);
+        wp[e] = (n < G.N0 ? G.W0 + (int64_t)n * G.K : G.W1 + (int64_t)(n - G.N0) * G.K) + kp;
+        wofs[e] = r * kTLd + kp;
+        wkp[e] = kp;
+    }
+    u32x4 ra[PA], rw[PW];
+    auto load = [&](int k0) {   // K is a multiple of 16, so a piece is wholly in or out
+#pragma unroll
+        for (int e = 0; e < PA; ++e)
+            ra[e] = k0 + akp[e] < G.K ? *(const u32x4 *)(ap[e] + k0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < PW; ++e)
+            rw[e] = k0 + wkp[e] < G.K ? *(const u32x4 *)(wp[e] + k0) : u32x4{0u, 0u, 0u, 0u};
     };
     auto stash = [&](int buf) {
 #pragma unroll
-        for (int e = 0; e < kTPieces; ++e) {
-            *(u32x4 *)&sA[buf][lofs + 8 * e] = ra[e];
-            *(u32x4 *)&sW[buf][lofs + 8 * e] = rw[e];
-        }
+        for (int e = 0; e < PA; ++e) *(u32x4 *)&sA[buf][aofs[e]] = ra[e];
+#pragma unroll
+        for (int e = 0; e < PW; ++e) *(u32x4 *)&sW[buf][wofs[e]] = rw[e];
     };
-    f32x16 acc[2][2];
+    f32x16 acc[2][WJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < WJ; ++jj)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
 
@@ -313,17 +333,17 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
         if (kt + 1 < nk) load((kt + 1) * kTK);
 #pragma unroll
         for (int ks = 0; ks < kTK / 16; ++ks) {
-            u32x4 a[2], b[2];
+            u32x4 a[2], bw[WJ];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 a[i] = *(const u32x4 *)&sA[buf][(wm * 64 + 32 * i + j) * kTLd + 16 * ks + 8 * h];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                b[jj] = *(const u32x4 *)&sW[buf][(wn * 64 + 32 * jj + j) * kTLd + 16 * ks + 8 * h];
+            for (int jj = 0; jj < WJ; ++jj)
+                bw[jj] = *(const u32x4 *)&sW[buf][(wn * (BN / 2) + 32 * jj + j) * kTLd + 16 * ks + 8 * h];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mma(a[i], b[jj], acc[i][jj]);
+                for (int jj = 0; jj < WJ; ++jj) acc[i][jj] = mma(a[i], bw[jj], acc[i][jj]);
         }
         if (kt + 1 < nk) stash(buf ^ 1);
         __syncthreads();
@@ -332,8 +352,8 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int col = n0 + wn * 64 + 32 * jj + j;
+        for (int jj = 0; jj < WJ; ++jj) {
+            const int col = n0 + wn * (BN / 2) + 32 * jj + j;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -346,8 +366,14 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
 
 hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
     if (g.S == 1 && g.Z == 1 && g.M >= kTiledMinRows) {
-        const int tiles = ((g.N0 + g.N1 + kTN - 1) / kTN) * ((g.M + kTM - 1) / kTM);
-        enc_gemm_tiled_kernel<<<dim3((unsigned)tiles), 256, 0, s>>>(g);
+        // 128 x 256 tiles (a wave 64 x 128: fewer LDS reads per MFMA) when they still give
+        // at least kWideTiles workgroups, else 128 x 128
+        const int mt = (g.M + kTM - 1) / kTM, n = g.N0 + g.N1;
+        const int wide = mt * ((n + 255) / 256);
+        if (wide >= kWideTiles)
+            enc_gemm_tiled_kernel<256><<<dim3((unsigned)wide), 256, 0, s>>>(g);
+        else
+            enc_gemm_tiled_kernel<128><<<dim3((unsigned)(mt * ((n + 127) / 128))), 256, 0, s>>>(g);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((g.N0 + g.N1) / 32), (unsigned)((g.M + 31) / 32), (unsigned)g.Z);
