@@ -113,6 +113,17 @@ def test_encoder_prefill_wide_tiles():
     check("encoder 600 rows x 256 heads, wide tiles (sampled)", qg[rows], wg[rows], qr, wr)
 
 
+@pytest.mark.parametrize("T", [255, 256, 257])
+def test_encoder_around_the_tiled_threshold(T):
+    """The second product: 255 rows take the per-32x32-tile kernel, 256 and 257 the LDS-tiled
+    one; RoPE/Hadamard takes one head a wave, then 16."""
+    e = W.query_encoder(seed=3108 + T, T=T, n_heads=64, d_model=256, q_rank=2048)
+    qg, wg = run_encoder(e)
+    rows = np.array([0, 127, 128, T - 2, T - 1])
+    qr, wr = oracle_encoder(e, rows=rows)
+    check(f"encoder {T} rows (sampled)", qg[rows], wg[rows], qr, wr)
+
+
 def test_encoder_feeds_scoring():
     """Encoder (64 heads) -> fm_index_logits on a small bf16 pool, against the oracle encoder's
     q and w (rounded to float32) scored by the oracle: the whole per-layer path."""

@@ -171,3 +171,13 @@ def test_labels_cap_and_count_only():
     assert np.array_equal(idx, full[1][:cap]) and np.array_equal(sc, full[2][:cap])
     ptr2, idx2, sc2 = gpu_labels(S, None, p=0.6, min_votes=2, tau=3, cap=total, with_score=False)
     assert np.array_equal(idx2, full[1]) and sc2 is None
+
+
+@pytest.mark.parametrize("T,L,ld,tau,min_votes", [(1, 1, 1, 1, 1), (3, 2, 31, 3, 1), (5, 4, 33, 2, 2),
+                                                  (6, 3, 257, 6, 3), (4, 64, 100, 2, 40)])
+def test_labels_small_shapes(T, L, ld, tau, min_votes):
+    """Word and chunk edges (ld 1, 31, 33, 257), one window (tau = T), 64 layers."""
+    rng = np.random.default_rng(T * 1000 + ld)
+    S = (rng.standard_normal((T, L, ld)) * 2).astype(np.float32)
+    got = gpu_labels(S, None, p=0.6, min_votes=min_votes, tau=tau)
+    check_labels(f"labels T={T} L={L} ld={ld}", S, None, 0.6, min_votes, tau, got)
