@@ -18,7 +18,7 @@ roofline object reports the scoring kernel against HBM peak (8 TB/s) with its al
 bytes (keys once, q/w once, block table, logits written) over its average launch duration:
 HIP events around the same scoring calls launched back to back (events around each single
 launch, which add a few microseconds, are reported beside it as bracketed_ms).  Secondary entries measure the other
-workloads the same way: the three-layer fp8 mask with 64 heads and with the retriever's 128,
+workloads (one call a step, timed over the calls back to back): the three-layer fp8 mask with 64 heads and with the retriever's 128,
 two-level fp8 scoring over 384 resident pages, causal fp8 prefill, the Mode A selection of
 21 layers x 8 requests over 262,144 masked candidates, the retriever's query encoder at
 decode and prefill batch sizes, and golden-label construction from 128 tokens x 21 layers x
@@ -79,18 +79,29 @@ def read_traffic(name: str, digest: str):
 
 
 class Timer:
-    """Events around each kernel launch, on the current (launch) stream."""
+    """HIP events on the current (launch) stream.  With several names, events around each
+    call of each step (per-call brackets); with one name, one event before the first call and
+    one after the last, so the average covers the calls back to back (brackets around every
+    single call add a few microseconds of their own)."""
 
     def __init__(self, torch, names, steps):
         self.torch = torch
         self.names = names
+        self.steps = steps
+        self.b2b = len(names) == 1
+        n_ev = 1 if self.b2b else steps
         self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-                   for _ in range(steps)]
+                   for _ in range(n_ev)]
 
     def mark(self, step, i):
-        self.ev[step][i].record()
+        if not self.b2b:
+            self.ev[step][i].record()
+        elif (step == 0 and i == 0) or (step == self.steps - 1 and i == 1):
+            self.ev[0][i].record()
 
     def per_kernel_ms(self):
+        if self.b2b:
+            return {self.names[0]: self.ev[0][0].elapsed_time(self.ev[0][1]) / self.steps}
         out = {}
         for i, n in enumerate(self.names):
             out[n] = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in self.ev]))
