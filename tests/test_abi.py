@@ -314,3 +314,13 @@ def test_golden_labels_validation():
     assert st(ws_bytes=need - 1) == api.FM_ERR_WORKSPACE
     assert st(ws=FAKE + 16) == api.FM_ERR_WORKSPACE
     assert st(T=40000, tau=1, ld=65536, ws_bytes=1 << 40) == api.FM_ERR_UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """With no built library the binding raises; there is no fallback path to compute on."""
+    monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "libfm.so"))
+    monkeypatch.setattr(api, "_lib", None)
+    with pytest.raises(FileNotFoundError):
+        api.lib()
+    with pytest.raises(FileNotFoundError):
+        api.fm_workspace_bytes(api.FM_OP_TOPK, 1, 100000)
