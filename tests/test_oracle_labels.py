@@ -57,6 +57,35 @@ def test_exact_rationals():
     assert checked > 250
 
 
+
+def test_cumulative_mass_matches_exact_rationals():
+    """cumulative_mass (which sets the decision band of the GPU label checks) against exact
+    fractions: scores log(a_j) with integer a_j give P_j = a_j / sum(a), so the order is
+    (a descending, index ascending) and the k-th inclusive mass is sum of the first k a over
+    sum(a).  Entries at or past n_valid and -inf / NaN scores are not candidates."""
+    rng = random.Random(5)
+    for trial in range(200):
+        n = rng.randint(1, 60)
+        a = [rng.randint(1, 30) for _ in range(n)]
+        x = np.log(np.asarray(a, np.float64))
+        n_valid = rng.randint(1, n)
+        excl = set(rng.sample(range(n_valid), rng.randint(0, n_valid - 1)))
+        for j in excl:
+            x[j] = -np.inf if j % 2 else np.nan
+        cand = [j for j in range(n_valid) if j not in excl]
+        tot = sum(a[j] for j in cand)
+        order = sorted(cand, key=lambda j: (-a[j], j))
+        got_order, got_c = OL.cumulative_mass(x, n_valid)
+        assert got_order.tolist() == order
+        c = Fraction(0)
+        for j, g in zip(order, got_c):
+            c += Fraction(a[j], tot)
+            assert abs(g - float(c)) <= 1e-14, (a, j)
+        assert got_c[-1] == 1.0
+    o, c = OL.cumulative_mass(np.full(4, -np.inf))
+    assert o.size == 0 and c.size == 0
+
+
 def test_uniform_scores_closed_form():
     # equal scores: equal masses 1/n, ties to the lower index, so the nucleus is the first
     # floor(p n) entries (cases with p n an integer are left out: rounding decides those)

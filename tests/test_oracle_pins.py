@@ -130,6 +130,47 @@ def test_logits_match_exact_rationals_full_width_sample():
         assert rel_err(L[0, s], float(ex[0][s])) <= 1e-12
 
 
+
+@pytest.mark.parametrize("key_dtype,q_dtype", [("f32", "f32"), ("fp8", "bf16"), ("fp8", "fp8")])
+def test_logits_at_points_match_exact_rationals(key_dtype, q_dtype):
+    """logits_at (the point-wise oracle the sampled GPU checks use) against exact rationals at
+    shuffled (row, entry) points: two requests shared by five rows through row_req, causal
+    positions, an unmapped page (block table -1), a page past the block table, and entries that
+    are negative, past seq_len or past the causal limit all give -inf; every other point is the
+    exact logit.  A wrong row-to-request map, visibility test or entry-to-page mapping fails."""
+    P, N = 8, 43                                    # 6 pages a request, the last one partial
+    wl = tiny_wl(seed=21, T=5, B=2, H=4, D=8, n_entries=N, page=P, key_dtype=key_dtype,
+                 q_dtype=q_dtype, q_pos=[9, 400, 120, 77, 173], ratio=4)
+    rr = np.array([1, 0, 1, 0, 1], np.int32)
+    wl.queries[0].row_req = rr
+    wl.kv.block_table[0, 2] = -1                    # request 0, entries 16..23: unmapped
+    wl.kv.seq_lens[1] = 40                          # request 1 is shorter than its pages
+    ex = exact_ref.logits_logical(wl)               # None where the page is unmapped
+    rng = np.random.default_rng(3)
+    rows, ents, want = [], [], []
+    for t in range(5):
+        b = int(rr[t])
+        n_vis = min(int(wl.kv.seq_lens[b]), int(wl.queries[0].q_pos[t]) // 4)
+        for s in list(range(-2, 52)) + [P * wl.kv.block_table.shape[1] + 5, 10 ** 6]:
+            rows.append(t)
+            ents.append(s)
+            ok = 0 <= s < n_vis and ex[t][s] is not None
+            want.append(float(ex[t][s]) if ok else -np.inf)
+    perm = rng.permutation(len(rows))
+    rows, ents, want = (np.asarray(rows)[perm], np.asarray(ents)[perm], np.asarray(want)[perm])
+    got = oracle.logits_at(wl, rows, ents)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.all(np.isneginf(got[~fin]))
+    assert fin.sum() > 60 and (~fin).sum() > 60
+    for g, x in zip(got[fin], want[fin]):
+        assert rel_err(g, x) <= 1e-12 or abs(g - x) < 1e-300
+    # and the same points read out of the full logit matrix
+    L = oracle.logits(wl)
+    inside = (ents >= 0) & (ents < L.shape[1])
+    assert np.array_equal(got[inside], L[rows[inside], ents[inside]])
+
+
 def test_rank_one_closed_form():
     """k_s = a_s u and q_h = b_h u with |u| = 1 give L_s = a_s * sum_{h: a_s b_h > 0} w_h b_h."""
     H, D, N = 6, 16, 24
