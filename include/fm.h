@@ -132,6 +132,13 @@ typedef struct {
  *   logits[t * ld + s] = L[t,s] (float32) if s < n_vis(t), else -inf,
  * where n_vis(t) = seq_len[b] (cut to floor(q_pos / ratio) with positions).  Entries of an
  * unmapped page score NaN.  Key layer 0 of `kv` is used.
+ * Accuracy: bf16 / fp8 inputs are decoded exactly and products accumulate in float32.  With
+ * FP8_E4M3 q over SCALED132 keys, one request and T >= 16 (prefill), each ReLU(q_h . k) term
+ * is rounded to f16 on a per-row power-of-two scale set by the row's largest query code: the
+ * term's error is at most 2^-11 relative, or 2^(E-15) code-product units absolute with E the
+ * largest E4M3 exponent field among the row's codes (one unit for codes that fill the E4M3
+ * range, 2^-10 units for codes below 1, as with q_scale = 1).  Key codes are assumed to use
+ * the E4M3 range (scale = absmax / 448, as the compressed_k quantiser produces them).
  */
 fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *logits,
                           int64_t ld, void *stream);
@@ -161,6 +168,9 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
  * Top-k per row of a logit matrix logits[T, ld].  Candidates of row t are the entries
  * s < n_valid[t] (n_valid NULL: s < ld) whose logit is finite (not -inf, not NaN) and, when
  * mask is given, with mask[row_req[t] * mask_ld + s] != 0 (row_req NULL: mask row t).
+ * Precondition (not checked on the device): every row_req[t] >= 0 indexes a row of the mask
+ * buffer; the library does not know the mask's row count, so a larger value reads past it.
+ * A negative row_req[t] gives row t no candidates.
  * Selects the k candidates of largest logit, ties broken by lower s (-0.0 == +0.0); with
  * fewer than k candidates, all of them.  out_idx[t * k + i] lists the selected s in
  * ascending order, padded with -1; out_val (nullable) holds their logits, padded with -inf.
@@ -290,8 +300,11 @@ fm_status fm_encode_queries(const fm_encoder_desc *e, const void *hidden, int T,
  * for each the fraction of the window's tau tokens whose A holds it (the page defines no
  * score).  Positions at or past cap are not written: a caller sizes the arrays from
  * label_ptr[T - tau + 1] (a first call with cap 0 may count only).
- * The membership decisions use softmax masses in 2^-31 fixed point with integer sums: they
- * agree with exact arithmetic except where a cumulative mass lies within about 1e-6 of p.
+ * The membership decisions use float32 exponentials exp(x - max) rounded to 2^-44 fixed point,
+ * with exact integer sums: a cumulative mass ratio is within 3e-6 of exact in the worst case
+ * (each mass carries about (|x - max| + 1) 2^-23 relative error, the heavy ones the least,
+ * plus 2^-45 of the largest per entry), so decisions agree with exact arithmetic except where
+ * a cumulative mass lies that close to p.
  * Limits: 1 <= ld <= 65,536, 1 <= n_layers <= 64, 1 <= tau <= T, (T - tau + 1) * ld < 2^31,
  * 1 <= min_votes, 0 < p <= 1.  ws 256-byte aligned, ws_bytes >=
  * fm_golden_workspace_bytes(T, n_layers, ld, tau), its contents irrelevant.

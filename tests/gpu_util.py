@@ -172,3 +172,48 @@ def check_mask(mask_gpu, mask_ref, union_ref, cut, seq_lens, tag):
         dis += int(d.sum())
         band_n += int(inband.sum())
     return dis, band_n
+
+
+def check_pages(m, ref, cut, seq_lens, tag, page=64):
+    """Page outputs of fm_resident_mask (count, ascending -1-padded list, density), always:
+      * as a pure function of the GPU's own mask bytes (any / popcount of each 64-entry page);
+      * against the oracle on every page that holds no band entry (|u_ref - cut| within
+        1e-3 * max|u_ref| of the request): the same residency and the same density; the page
+        count may differ from the oracle's by at most the number of pages holding band entries.
+    m: the GPU outputs (torch tensors), ref: the oracle's resident_mask dict."""
+    mg = m["mask"].cpu().numpy().astype(bool)
+    B, ld = mg.shape
+    n_pages = -(-ld // page)
+    padded = np.zeros((B, n_pages * page), bool)
+    padded[:, :ld] = mg
+    dens = padded.reshape(B, n_pages, page).sum(-1)
+    got_d = m["page_density"].cpu().numpy()
+    got_l = m["page_list"].cpu().numpy()
+    got_c = m["page_count"].cpu().numpy()
+    assert np.array_equal(got_d[:, :n_pages], dens), f"{tag}: density is not the mask's"
+    for b in range(B):
+        nz = np.nonzero(dens[b])[0]
+        assert got_c[b] == nz.size, f"{tag}: request {b}: page count is not the mask's"
+        assert np.array_equal(got_l[b, :nz.size], nz), f"{tag}: request {b}: page list"
+        assert np.all(got_l[b, nz.size:n_pages] == -1), f"{tag}: request {b}: list padding"
+    u = np.asarray(ref["union"], np.float64)
+    banded = 0
+    for b in range(B):
+        n = min(int(seq_lens[b]), ld)
+        ub = u[b, :n]
+        fin = np.isfinite(ub)
+        scale = np.max(np.abs(ub[fin])) if fin.any() else 1.0
+        inband = np.zeros(n_pages * page, bool)
+        inband[:n] = np.abs(ub - cut) <= BAND * scale
+        pb = inband.reshape(n_pages, page).any(-1)
+        clean = ~pb
+        rd = ref["page_density"][b, :n_pages]
+        assert np.array_equal(dens[b, clean], rd[clean]), (
+            f"{tag}: request {b}: density differs from the oracle on band-free pages")
+        assert abs(int(got_c[b]) - int(ref["page_count"][b])) <= int(pb.sum()), (
+            f"{tag}: request {b}: page count {got_c[b]} vs oracle {ref['page_count'][b]}")
+        rl = ref["page_list"][b, :ref["page_count"][b]]
+        assert np.array_equal(got_l[b, :got_c[b]][clean[got_l[b, :got_c[b]]]],
+                              rl[clean[rl]]), f"{tag}: request {b}: list on band-free pages"
+        banded += int(pb.sum())
+    return banded

@@ -1,9 +1,9 @@
 """GPU parity of the golden-label construction (fm_golden_labels) against the fp64 oracle.
 
 The membership decision compares a cumulative softmax mass with p.  The GPU sums masses in
-2^-31 fixed point (exact integer sums of float32 exponentials), so its cumulative masses agree
-with the oracle's to about 1e-6; entries whose oracle cumulative mass lies within BAND = 1e-5
-of p are "band" entries and may go either way.  Everything downstream is compared exactly
+2^-44 fixed point (exact integer sums of rounded float32 exponentials), so its cumulative mass
+ratios agree with the oracle's to within 3e-6 in the worst case; entries whose oracle
+cumulative mass lies within BAND = 1e-5 of p are "band" entries and may go either way.  Everything downstream is compared exactly
 where no band entry can change it: a golden decision is certain when the certain votes alone
 reach min_votes or cannot reach it with every band vote; a label (and its score) is certain
 when every token of its window is certain for it.  With equal scores (no rounding in the

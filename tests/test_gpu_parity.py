@@ -62,7 +62,7 @@ def test_tiny_fp32_logits_mask_topk(n_entries):
     mr = oracle.resident_mask(wl)
     md, mb = G.check_mask(m["mask"].cpu().numpy(), mr["mask"], mr["union"], 0.0,
                           wl.kv.seq_lens, "tiny f32 mask")
-    assert np.array_equal(m["page_count"].cpu().numpy(), mr["page_count"]) or md > 0
+    G.check_pages(m, mr, 0.0, wl.kv.seq_lens, "tiny f32 pages")
     G.note("tiny f32", n=n_entries, ld=ld, logit_err=err, topk_dis=dis, mask_dis=md,
            mask_band=mb, mask_true=int(mr["mask"].sum()))
 
@@ -135,6 +135,7 @@ def test_mask_fp8_small(mask_small, mode, p, sink, recent):
     mg = m["mask"].cpu().numpy()
     dis, band = G.check_mask(mg, r["mask"], r["union"], cut, wl.kv.seq_lens,
                              f"mask {mode} p={p}")
+    G.check_pages(m, r, cut, wl.kv.seq_lens, f"mask {mode} p={p} pages")
     if dis == 0:
         assert np.array_equal(m["page_count"].cpu().numpy(), r["page_count"])
         assert np.array_equal(m["page_list"].cpu().numpy(), r["page_list"])
@@ -172,8 +173,10 @@ def test_mask_single_layer_and_short_mask_ld(mask_small):
     r = oracle.resident_mask(wl, layers=[1], mask_ld=ld)
     dis, _ = G.check_mask(m["mask"].cpu().numpy(), r["mask"], r["union"], 0.0,
                           np.minimum(wl.kv.seq_lens, ld), "mask layer 1, mask_ld 1289")
+    G.check_pages(m, r, 0.0, np.minimum(wl.kv.seq_lens, ld), "mask_ld 1289 pages")
     if dis == 0:
         assert np.array_equal(m["page_count"].cpu().numpy(), r["page_count"])
+        assert np.array_equal(m["page_list"].cpu().numpy(), r["page_list"])
 
 
 @pytest.mark.parametrize("mode", ["max", "mean"])
@@ -185,6 +188,7 @@ def test_mask_two_layers(mask_small, mode):
     r = oracle.resident_mask(wl, mode=mode, layers=[2, 0])
     dis, _ = G.check_mask(m["mask"].cpu().numpy(), r["mask"], r["union"],
                           0.0 if mode == "max" else 0.5, wl.kv.seq_lens, f"mask layers 2,0 {mode}")
+    G.check_pages(m, r, 0.0 if mode == "max" else 0.5, wl.kv.seq_lens, f"layers 2,0 {mode} pages")
     if dis == 0:
         assert np.array_equal(m["page_count"].cpu().numpy(), r["page_count"])
         assert np.array_equal(m["page_list"].cpu().numpy(), r["page_list"])
@@ -201,6 +205,7 @@ def test_mask_four_layers():
     assert not np.array_equal(r["mask"], r3["mask"]), "the fourth layer must matter here"
     dis, band = G.check_mask(m["mask"].cpu().numpy(), r["mask"], r["union"], 0.0,
                              wl.kv.seq_lens, "mask four layers")
+    G.check_pages(m, r, 0.0, wl.kv.seq_lens, "mask four layers pages")
     if dis == 0:
         assert np.array_equal(m["page_count"].cpu().numpy(), r["page_count"])
     G.note("mask four layers", disagreements=dis, band_entries=band)
@@ -220,7 +225,8 @@ def test_mask_fp8_full(mask_full):
     dis, band = G.check_mask(m["mask"].cpu().numpy(), r["mask"], r["union"], 0.0,
                              wl.kv.seq_lens, "mask B8x262144 x3")
     pc = m["page_count"].cpu().numpy()
-    G.note("mask full", disagreements=dis, band_entries=band,
+    banded_pages = G.check_pages(m, r, 0.0, wl.kv.seq_lens, "mask B8x262144 x3 pages")
+    G.note("mask full", disagreements=dis, band_entries=band, banded_pages=banded_pages,
            resident_fraction=float(r["mask"].mean()), page_count=pc.tolist(),
            page_count_ref=r["page_count"].tolist())
     if dis == 0:
@@ -413,13 +419,51 @@ def prefill_full():
 
 
 def test_prefill_full_sampled_rows(prefill_full):
+    """One row of every 8-row block (each block is scored by one workgroup per key chunk, and
+    the chunks are dealt to the 8 XCDs), its wave position rotating with the block, plus the
+    first and last rows: every workgroup of the launch is checked on every chunk it scores."""
     wl = prefill_full
-    rows = np.array([0, 1, 2, 3, 511, 1024, 2047, 2048, 3001, 4092, 4093, 4094, 4095])
+    T = wl.queries[0].T
+    rows = np.unique(np.concatenate([8 * np.arange(T // 8) + np.arange(T // 8) % 8,
+                                     [0, 1, 2, 3, T - 4, T - 3, T - 2, T - 1]]))
     err, dis, idx = _prefill_rows_parity(wl, dev(wl), rows, "prefill 4096x33792")
     ig = idx.cpu().numpy()
     assert not np.any(ig == 33791), "entry 33,791 is visible to no row"
     assert np.all(ig < 33791)
     G.note("prefill full sampled", rows=rows.tolist(), logit_err=err, topk_dis=dis)
+
+
+@pytest.mark.parametrize("code_max", [None, 1.0 / 16])
+def test_prefill_small_query_codes(code_max):
+    """Queries whose E4M3 codes do not fill the range: q passed unscaled (q_scale = 1, codes
+    about 0.1) or with codes below 1/16.  The prefill kernel's per-row block scale keeps these
+    rows as accurate as full-range ones; 15 rows (the exact float32 path) and 16 rows (the
+    prefill kernel) of the same input agree."""
+    wl = W.prefill_causal_fp8(seed=2040, T=16, pos0=4 * 1500, seq_len=64 * 24 + 9)
+    q = wl.queries[0]
+    vals = (torch.from_numpy(q.q.copy()).view(torch.float8_e4m3fn).float().numpy()
+            * q.q_scale[:, None, None])
+    if code_max is None:
+        sc = np.ones(q.T, np.float32)
+    else:
+        sc = (np.abs(vals.reshape(q.T, -1)).max(1) / code_max).astype(np.float32)
+    q.q[:] = W.e4m3_codes(vals / sc[:, None, None])
+    q.q_scale[:] = sc
+    ld = wl.kv.max_seq_len
+    L16 = G.index_logits(dev(wl), ld=ld).cpu().numpy()
+    q15 = W.Queries(np.ascontiguousarray(q.q[:15]), q.q_dtype, np.ascontiguousarray(q.w[:15]),
+                    q.w_dtype, q_scale=np.ascontiguousarray(q.q_scale[:15]),
+                    row_req=np.ascontiguousarray(q.row_req[:15]),
+                    q_pos=np.ascontiguousarray(q.q_pos[:15]), compress_ratio=q.compress_ratio)
+    wl15 = W.Workload(wl.name, wl.kv, [q15])
+    L15 = G.index_logits(dev(wl15), ld=ld).cpu().numpy()
+    Lr = oracle.logits(wl, s_end=ld)
+    err16 = G.check_logits(L16, Lr, TOL_LOW, f"prefill small codes {code_max} T=16")
+    err15 = G.check_logits(L15, Lr[:15], TOL_LOW, f"prefill small codes {code_max} T=15")
+    fin = np.isfinite(Lr[:15])
+    scale = np.max(np.abs(Lr[:15][fin]))
+    assert np.max(np.abs(L16[:15][fin] - L15[fin])) <= TOL_LOW * scale
+    G.note(f"prefill small codes {code_max}", err16=err16, err15=err15)
 
 
 def test_prefill_topk_with_causal_lengths(prefill_full):

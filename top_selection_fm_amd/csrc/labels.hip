@@ -8,7 +8,7 @@
 //
 // Four steps, each a kernel:
 //   nucleus_kernel  one workgroup per (token, layer) row holds the row in registers and finds
-//                   the nucleus boundary exactly: softmax masses in 2^-31 fixed point summed
+//                   the nucleus boundary exactly: softmax masses in 2^-44 fixed point summed
 //                   as integers (so the sums, and with them every decision, are independent of
 //                   the summation order), a mass histogram over linear score bins to find the
 //                   boundary bin, then a 32-bit radix search over the scores of that bin
@@ -78,15 +78,21 @@ constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kBinsPerUnit = (float)kNucBins / kNucSpan;
 constexpr int kNucList = 4096;               // boundary-bin entries gathered in LDS, at most
 
-// Per-row constants: with c31 = 31 - mx log2(e), exp(x - mx) 2^31 = exp2(fma(x, log2 e, c31))
-// (the fixed-point scale rides in the exponent); cb places x = mx - kNucSpan at bin 0.
+// Per-row constants: the row maximum mx, and cb placing x = mx - kNucSpan at bin 0.
 struct RowConst {
-    float c31, cb;
+    float mx, cb;
 };
 
-// exp(x - mx) in units of 2^-31 (at most about 2^31: mx is the row maximum)
-__device__ __forceinline__ uint32_t mass_fx(float x, const RowConst &k) {
-    return (uint32_t)__builtin_amdgcn_exp2f(fmaf(x, kLog2e, k.c31));
+// Softmax masses in fixed point: exp(x - mx) in units of 2^-44, rounded to nearest.  The
+// exponential's argument (x - mx) log2(e) is small for the heavy entries, so its rounding
+// costs them about 2^-23 |x - mx| relative; the fixed-point rounding adds at most 2^-45 of the
+// largest mass per entry.  A mass is at most 2^44 and a row at most 2^16 entries, so the
+// 64-bit sums cannot overflow.
+constexpr int kMassBits = 44;
+
+__device__ __forceinline__ u64 mass_fx(float x, const RowConst &k) {
+    const float m = __builtin_amdgcn_exp2f((x - k.mx) * kLog2e);
+    return (u64)__builtin_rintf(__builtin_ldexpf(m, kMassBits));
 }
 
 // linear bin of a score over [mx - kNucSpan, mx]: monotone in x, so every score of a higher
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
         for (int wd = tid; wd < A.words; wd += NT) mout[wd] = 0u;
         return;
     }
-    const RowConst K{31.0f - mx * kLog2e, (kNucSpan - mx) * kBinsPerUnit};
+    const RowConst K{mx, (kNucSpan - mx) * kBinsPerUnit};
 
     // masses, their total and the mass histogram over linear score bins
     u64 zt = 0;
@@ -198,9 +204,9 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
         for (int c = 0; c < 4; ++c) {
             const float x = v[u][c];
             if (x > -INFINITY) {
-                const uint32_t q = mass_fx(x, K);
+                const u64 q = mass_fx(x, K);
                 zt += q;
-                if (q) atomicAdd(&L.hm[score_bin(x, K)], (u64)q);
+                if (q) atomicAdd(&L.hm[score_bin(x, K)], q);
             }
         }
     u64 Z;
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
                 const uint32_t key = score_key(x);
                 if ((key & pmask) == prefix) {
                     const uint32_t d = (key >> shift) & (uint32_t)(nb - 1);
-                    atomicAdd(&L.hm[d], (u64)mass_fx(x, K));
+                    atomicAdd(&L.hm[d], mass_fx(x, K));
                     atomicAdd(&L.hc[d], 1u);
                 }
             });

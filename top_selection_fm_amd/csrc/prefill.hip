@@ -23,15 +23,19 @@
 // epilogue steps of block u, across page boundaries too.
 //
 // Epilogue.  The MFMA's power-of-two block scale multiplies every dot product of E4M3 codes by
-// 2^-25, which puts any possible value (|S| <= 448^2 * 128 < 2^25) strictly inside (-1, 1).
-// Each pair of head results is rounded to f16 with the conversion's clamp to [0, 1] (packed),
-// which on that range is exactly ReLU, and multiplied by the head weights with v_dot2c_f32_f16
-// into float accumulators: two VALU instructions per four head results.  The weights are
-// scaled per row by a power of two into [2^14, 2^15) first, so a bf16 weight converts to f16
-// exactly.  The only rounding beyond float accumulation is the f16 rounding of each ReLU(S)
-// term (relative 2^-11 for terms >= 2^-14, absolute 2^-25 of the largest possible S below).
-// The per-token query scale, the per-entry key scale and the powers of two are applied to the
-// sum, which is valid because the scales are positive.
+// 2^-e, with e chosen per query row from the largest exponent field E of the row's codes: a
+// code is below 2^(E-6) in magnitude (2^-6 for E = 0), a key code at most 448 < 2^9, so
+// |S| < 128 * 2^(E-6) * 2^9 = 2^(E+10) and e = max(E, 1) + 10 puts every dot product strictly
+// inside (-1, 1) (e = 25 for codes that fill the E4M3 range).  Each pair of head results is
+// rounded to f16 with the conversion's clamp to [0, 1] (packed), which on that range is exactly
+// ReLU, and multiplied by the head weights with v_dot2c_f32_f16 into float accumulators: two
+// VALU instructions per four head results.  The weights are scaled per row by a power of two
+// into [2^14, 2^15) first, so a bf16 weight converts to f16 exactly.  The only rounding beyond
+// float accumulation is the f16 rounding of each ReLU(S) term: relative 2^-11 for terms of at
+// least 2^(e-14) code-product units, else absolute 2^(e-25) units (one unit for full-range
+// query codes, 2^-10 units for codes below 1, as when q is passed unscaled).  The per-token
+// query scale, the per-entry key scale and the powers of two are applied to the sum, which is
+// valid because the scales are positive.
 #include <math.h>
 
 #include "fm_internal.h"
@@ -50,8 +54,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int kLdsRow = 144;                       // a key row's 128 codes, padded (bank spread)
-constexpr int kSExp = 25;                          // dot products of codes are scaled by 2^-25
-constexpr int kScaleA = 127 - kSExp;               // E8M0 block scale of the A operand
 constexpr int kMaxChunkPages = 128;                // pages of one workgroup's key chunk, at most
 constexpr int kWaves = FM_PF_WAVES;                // one query row per wave
 constexpr int kStageParts = 512 / (64 * kWaves);    // 16-byte parts of a page each thread stages
@@ -145,6 +147,23 @@ void prefill_fp8_kernel(PrefillArgs A) {
                           (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
         }
     }
+    // the row's largest exponent field sets the block scale 2^-sexp of its dot products
+    int sexp;
+    {
+        uint32_t em = 0;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const uint32_t x = (uint32_t)qf[n][v];
+#pragma unroll
+                for (int by = 0; by < 4; ++by) em = max(em, (x >> (8 * by + 3)) & 15u);
+            }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) em = max(em, (uint32_t)__shfl_xor((int)em, o));
+        sexp = __builtin_amdgcn_readfirstlane((int)max(em, 1u) + 10);
+    }
+    const int scale_a = 127 - sexp;                    // E8M0 block scale of the A operand
     // this lane's 16 head weights (heads 16 n + 4 g + 0..3) as f16 pairs scaled by 2^ew
     h2 wp[8];
     float row_factor;
@@ -180,7 +199,7 @@ void prefill_fp8_kernel(PrefillArgs A) {
             wp[2 * n + 1] = __builtin_convertvector(f32x2{ldexpf(wl[n][2], ew), ldexpf(wl[n][3], ew)}, h2);
         }
         const float qs = row_ok ? A.q.q_scale[t] : 0.f;
-        row_factor = ldexpf(qs, kSExp - ew);
+        row_factor = ldexpf(qs, sexp - ew);
     }
 
     const int64_t p_begin = (int64_t)chunk * A.chunk_pages;
@@ -247,7 +266,7 @@ void prefill_fp8_kernel(PrefillArgs A) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             nxt[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                qf[n], kn, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, kScaleA, 0, 127);
+                qf[n], kn, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, scale_a, 0, 127);
             a = epi_step(cur[n], wp[2 * n], wp[2 * n + 1], a);
             if (n & 1) __builtin_amdgcn_sched_barrier(0);
         }
@@ -265,7 +284,7 @@ void prefill_fp8_kernel(PrefillArgs A) {
 #pragma unroll
         for (int n = 0; n < 4; ++n)
             ca[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                qf[n], kfrag(0, 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, kScaleA, 0, 127);
+                qf[n], kfrag(0, 0), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, scale_a, 0, 127);
         i32x8 k1 = kfrag(0, 1);
         int b0 = 0;
         for (int64_t p = p_begin; p < p_vis; ++p) {
