@@ -217,6 +217,25 @@ fm_status fm_score_resident_cells(const fm_query_desc *q, const fm_kv_desc *kv,
                                   void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * fm_score_resident for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments and results
+ * as fm_score_resident (same kernels), but the workspace is the library's own static device
+ * array of FM_STATIC_SCRATCH_BYTES (64 MiB) per GPU, held from the first call on that GPU
+ * until the process ends; nothing is allocated or freed by the call.  The stream must belong
+ * to the current device.  Calls whose fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T,
+ * res_ld * 64) exceeds FM_STATIC_SCRATCH_BYTES return FM_ERR_WORKSPACE before any launch
+ * (e.g. 30 rows x 384 pages need 2.9 MB; 630 rows x 384 pages 62 MB).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (on different streams, or
+ * from different threads without ordering) race and give undefined results.
+ */
+#define FM_STATIC_SCRATCH_BYTES (64ull << 20)
+
+fm_status fm_score_resident_noalloc(const fm_query_desc *q, const fm_kv_desc *kv,
+                                    const int32_t *resident_pages, const int32_t *n_resident,
+                                    int64_t res_ld, int k, int32_t *out_idx, float *out_val,
+                                    void *stream);
+
+/*
  * The KMAX densest pages of each request (README, reference-performance notes: KMAX is the
  * number of densest pages recalled per request, about 10% of the history).  density is an
  * int32 [B, density_ld] matrix, e.g. the page_density of fm_resident_mask.  For request b,

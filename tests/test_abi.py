@@ -190,6 +190,25 @@ def test_score_resident_validation():
     assert st(k=4096, ws_bytes=need) == api.FM_ERR_UNSUPPORTED
 
 
+def test_score_resident_noalloc_validation():
+    """The allocation-free variant validates like fm_score_resident, and refuses (before any
+    HIP call) a shape whose workspace would not fit its static array."""
+    q, kv = good_q(), good_kv("fp8x132")
+    st = lambda **kw: status_of(api.fm_score_resident_noalloc, q, kv, kw.get("rp", FAKE),
+                                kw.get("nr", FAKE), kw.get("res_ld", 10), kw.get("k", 512),
+                                FAKE, None)[0]
+    assert st(rp=None) == api.FM_ERR_INVALID_ARG
+    assert st(res_ld=0) == api.FM_ERR_INVALID_ARG
+    assert st(k=4096) == api.FM_ERR_UNSUPPORTED
+    too_big = api.STATIC_SCRATCH_BYTES // (2 * 64 * 4) + 1          # 2 rows
+    assert api.fm_workspace_bytes(api.FM_OP_SCORE_RESIDENT, 2, too_big * 64) > \
+        api.STATIC_SCRATCH_BYTES
+    assert st(res_ld=too_big) == api.FM_ERR_WORKSPACE
+    assert "static scratch" in api.fm_last_error()
+    m = re.search(r"#define FM_STATIC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", open(HEADER).read())
+    assert api.STATIC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+
 def test_densest_pages_validation():
     st = lambda **kw: status_of(api.fm_densest_pages, kw.get("d", FAKE), kw.get("ld", 100),
                                 kw.get("B", 2), kw.get("n", 100), kw.get("kmax", 96),

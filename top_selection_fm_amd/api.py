@@ -27,7 +27,7 @@ KEY_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8x132": FM_FP8_E4M3_SCALED132}
 Q_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8": FM_FP8_E4M3}
 
 EXPORTS = ["fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
-           "fm_score_resident_cells", "fm_densest_pages", "fm_workspace_bytes",
+           "fm_score_resident_noalloc", "fm_score_resident_cells", "fm_densest_pages", "fm_workspace_bytes",
            "fm_encode_queries", "fm_encode_workspace_bytes", "fm_golden_labels",
            "fm_golden_workspace_bytes", "fm_status_string", "fm_last_error", "fm_version"]
 
@@ -77,6 +77,7 @@ def lib():
         L.fm_topk512.argtypes = [P, I64, C.c_int, P, P, I64, P, C.c_int, P, P, P, C.c_size_t, P]
         L.fm_score_resident.argtypes = [P, P, P, P, I64, C.c_int, P, P, P, C.c_size_t, P]
         L.fm_score_resident_cells.argtypes = [P, P, P, P, I64, C.c_int, P, P, P, C.c_size_t, P]
+        L.fm_score_resident_noalloc.argtypes = [P, P, P, P, I64, C.c_int, P, P, P]
         L.fm_densest_pages.argtypes = [P, I64, C.c_int, I64, C.c_int, P, P, P]
         L.fm_encode_queries.argtypes = [P, P, C.c_int, P, P, P, P, C.c_size_t, P]
         L.fm_encode_workspace_bytes.argtypes = [P, C.c_int]
@@ -86,7 +87,7 @@ def lib():
         L.fm_golden_workspace_bytes.argtypes = [C.c_int, C.c_int, I64, C.c_int]
         L.fm_golden_workspace_bytes.restype = C.c_size_t
         for f in ("fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
-                  "fm_score_resident_cells", "fm_densest_pages", "fm_encode_queries",
+                  "fm_score_resident_noalloc", "fm_score_resident_cells", "fm_densest_pages", "fm_encode_queries",
                   "fm_golden_labels"):
             getattr(L, f).restype = C.c_int
         L.fm_workspace_bytes.argtypes = [C.c_int, C.c_int, I64]
@@ -188,6 +189,16 @@ def fm_score_resident(q: QueryDesc, kv: KvDesc, resident_pages, n_resident, res_
     _check(lib().fm_score_resident(C.byref(q), C.byref(kv), _ptr(resident_pages),
                                    _ptr(n_resident), int(res_ld), int(k), _ptr(out_idx),
                                    _ptr(out_val), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def fm_score_resident_noalloc(q: QueryDesc, kv: KvDesc, resident_pages, n_resident, res_ld: int,
+                              k: int, out_idx, out_val=None, stream=None) -> None:
+    _check(lib().fm_score_resident_noalloc(C.byref(q), C.byref(kv), _ptr(resident_pages),
+                                           _ptr(n_resident), int(res_ld), int(k), _ptr(out_idx),
+                                           _ptr(out_val), _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 def fm_score_resident_cells(q: QueryDesc, kv: KvDesc, resident_pages, n_resident, res_ld: int,

@@ -8,7 +8,14 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fm_internal.h"
+
+// The static workspace of fm_score_resident_noalloc: each GPU holds its own copy of this array
+// (at its own address) from the library's first use on that GPU.  In host code the name is
+// only a stand-in: the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) uint8_t scratch[FM_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -169,18 +176,27 @@ fm_status run_score(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t 
     return launched(fm::launch_score(a, key_fmt(kv->key_dtype), qf, st), "score");
 }
 
-fm_status score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
-                            const int32_t *resident_pages, const int32_t *n_resident,
-                            int64_t res_ld, int k, int32_t *out_idx, float *out_val, void *ws,
-                            size_t ws_bytes, void *stream, int cells) {
+// Arguments of two-level scoring other than the workspace.
+fm_status check_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
+                               const int32_t *resident_pages, const int32_t *n_resident,
+                               int64_t res_ld, int k, const int32_t *out_idx) {
     CHECK(check_kv(kv, 1));
     CHECK(check_q(q, kv, "q"));
     REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
     REQUIRE(res_ld >= 1 && res_ld * FM_PAGE_SIZE <= (int64_t)INT32_MAX / 4, FM_ERR_INVALID_ARG,
             "res_ld = %lld", (long long)res_ld);
-    if (q->T == 0) return ok();
+    if (q->T == 0) return FM_OK;
     REQUIRE(resident_pages && n_resident && out_idx, FM_ERR_INVALID_ARG,
             "resident_pages / n_resident / out_idx NULL");
+    return FM_OK;
+}
+
+fm_status score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
+                            const int32_t *resident_pages, const int32_t *n_resident,
+                            int64_t res_ld, int k, int32_t *out_idx, float *out_val, void *ws,
+                            size_t ws_bytes, void *stream, int cells) {
+    CHECK(check_score_resident(q, kv, resident_pages, n_resident, res_ld, k, out_idx));
+    if (q->T == 0) return ok();
     const size_t need = fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T, res_ld * FM_PAGE_SIZE);
     REQUIRE(ws && ws_bytes >= need && aligned(ws, 256), FM_ERR_WORKSPACE,
             "workspace %zu bytes at %p, need %zu (256-byte aligned)", ws_bytes, ws, need);
@@ -211,6 +227,38 @@ fm_status score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     if (staged) W = fm::topk_ws_carve((uint8_t *)ws + logit_bytes, q->T, ld);
     CHECK(launched(fm::launch_topk(a, staged ? &W : nullptr, st), "topk"));
     return ok();
+}
+
+// Device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+fm_status scratch_address(hipStream_t st, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    REQUIRE(e == hipSuccess, FM_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    REQUIRE(dev >= 0 && dev < kMaxDevices, FM_ERR_UNSUPPORTED, "device %d (at most %d devices)",
+            dev, kMaxDevices);
+    if (st) {
+        int sdev = -1;
+        e = hipStreamGetDevice(st, &sdev);
+        REQUIRE(e == hipSuccess, FM_ERR_INVALID_ARG, "hipStreamGetDevice: %s",
+                hipGetErrorString(e));
+        REQUIRE(sdev == dev, FM_ERR_INVALID_ARG,
+                "the stream belongs to device %d, the current device is %d", sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        REQUIRE(e == hipSuccess && p, FM_ERR_LAUNCH, "hipGetSymbolAddress(scratch): %s",
+                hipGetErrorString(e));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return FM_OK;
 }
 
 // ---------------------------------------------------------------- query encoder
@@ -380,6 +428,23 @@ fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
                             size_t ws_bytes, void *stream) {
     return score_resident(q, kv, resident_pages, n_resident, res_ld, k, out_idx, out_val, ws,
                           ws_bytes, stream, 0);
+}
+
+fm_status fm_score_resident_noalloc(const fm_query_desc *q, const fm_kv_desc *kv,
+                                    const int32_t *resident_pages, const int32_t *n_resident,
+                                    int64_t res_ld, int k, int32_t *out_idx, float *out_val,
+                                    void *stream) {
+    CHECK(check_score_resident(q, kv, resident_pages, n_resident, res_ld, k, out_idx));
+    if (q->T == 0) return ok();
+    const size_t need = fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T, res_ld * FM_PAGE_SIZE);
+    REQUIRE(need <= FM_STATIC_SCRATCH_BYTES, FM_ERR_WORKSPACE,
+            "T = %d rows x res_ld = %lld pages need %zu bytes of workspace; the static scratch "
+            "holds %llu",
+            q->T, (long long)res_ld, need, (unsigned long long)FM_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    CHECK(scratch_address((hipStream_t)stream, &ws));
+    return score_resident(q, kv, resident_pages, n_resident, res_ld, k, out_idx, out_val, ws,
+                          FM_STATIC_SCRATCH_BYTES, stream, 0);
 }
 
 fm_status fm_score_resident_cells(const fm_query_desc *q, const fm_kv_desc *kv,
