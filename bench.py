@@ -122,62 +122,92 @@ def timed(torch, names, fn, steps, warmup):
 
 
 # ----------------------------------------------------------------------------- workloads
-def run_decode(torch, api, W, steps, warmup, replicas=3):
-    wl = W.decode_bf16()
-    dw = api.DeviceWorkload(wl, "cuda:0", pool_copies=replicas)
-    B = wl.kv.B
-    ld = wl.kv.block_table.shape[1] * 64
-    logits = torch.empty((B, ld), dtype=torch.float32, device="cuda:0")
-    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda:0")
-    nb = api.fm_workspace_bytes(api.FM_OP_TOPK, B, ld)
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
-    q = dw.query()
-    kvs = [dw.kv(r) for r in range(replicas)]
-
-    def step(s, tm):
-        if tm: tm.mark(s, 0)
-        api.fm_index_logits(q, kvs[s % replicas], logits, ld)
-        if tm: tm.mark(s, 1)
-        api.fm_topk512(logits, ld, B, None, None, 0, None, 512, idx, None, ws, nb)
-        if tm: tm.mark(s, 2)
-
-    wall, per = timed(torch, ["score", "topk"], step, steps, warmup)
-    # the same step launched as a HIP graph (one per replica), as a serving loop runs it
+def graph_time(torch, calls, steps, warmup):
+    """Each of `calls` (one per pool replica) captured once into a HIP graph; the graphs are
+    replayed in turn.  Returns (wall seconds, event ms per step)."""
     graphs = []
-    for r in range(replicas):
+    for c in calls:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            api.fm_index_logits(q, kvs[r], logits, ld)
-            api.fm_topk512(logits, ld, B, None, None, 0, None, 512, idx, None, ws, nb)
+            c()
         graphs.append(g)
     for s in range(warmup):
-        graphs[s % replicas].replay()
+        graphs[s % len(graphs)].replay()
     torch.cuda.synchronize()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     g0.record()
     for s in range(steps):
-        graphs[s % replicas].replay()
+        graphs[s % len(graphs)].replay()
     g1.record()
     torch.cuda.synchronize()
-    graph_wall = time.perf_counter() - t0
-    graph_ms = g0.elapsed_time(g1) / steps
-    # the scoring kernel's average launch duration: the same launches back to back on the
-    # stream, between two events (per-launch events around each call add their own few us)
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for s in range(steps):
-        api.fm_index_logits(q, kvs[s % replicas], logits, ld)
-    s1.record()
+    return time.perf_counter() - t0, g0.elapsed_time(g1) / steps
+
+
+def b2b_ms(torch, call, steps, warmup):
+    """Average duration of `call(step)` launched back to back, between two events on the
+    launch stream (events around every single call would add their own few us)."""
+    for s in range(warmup):
+        call(s)
     torch.cuda.synchronize()
-    score_b2b_ms = s0.elapsed_time(s1) / steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(steps):
+        call(s)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def run_decode(torch, api, W, steps, warmup, replicas=3):
+    """The decode step: one fm_index_topk call (scoring and top-512 fused) over 32 requests x
+    65,536 bf16 entries; the two-call path (fm_index_logits + fm_topk512) is timed beside it."""
+    wl = W.decode_bf16()
+    dw = api.DeviceWorkload(wl, "cuda:0", pool_copies=replicas)
+    B = wl.kv.B
+    ld = wl.kv.block_table.shape[1] * 64
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda:0")
+    nb = api.fm_workspace_bytes(api.FM_OP_INDEX_TOPK, B, ld)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+    q = dw.query()
+    kvs = [dw.kv(r) for r in range(replicas)]
+
+    def fused(s):
+        api.fm_index_topk(q, kvs[s % replicas], None, 0, 512, idx, None, None, 0, ws, nb)
+
+    def step(s, tm):
+        if tm: tm.mark(s, 0)
+        fused(s)
+        if tm: tm.mark(s, 1)
+
+    wall, per = timed(torch, ["index_topk"], step, steps, warmup)
+    graph_wall, graph_ms = graph_time(torch, [lambda r=r: fused(r) for r in range(replicas)],
+                                      steps, warmup)
+    fused_ms = b2b_ms(torch, fused, steps, warmup)
+    # the two-call path: logits to memory, then the top-k kernel
+    logits = torch.empty((B, ld), dtype=torch.float32, device="cuda:0")
+    nbt = api.fm_workspace_bytes(api.FM_OP_TOPK, B, ld)
+    wst = torch.empty(max(nbt, 16), dtype=torch.uint8, device="cuda:0")
+
+    def two(s):
+        api.fm_index_logits(q, kvs[s % replicas], logits, ld)
+        api.fm_topk512(logits, ld, B, None, None, 0, None, 512, idx, None, wst, nbt)
+
+    two_wall, two_graph_ms = graph_time(torch, [lambda r=r: two(r) for r in range(replicas)],
+                                        steps, warmup)
+    score_ms = b2b_ms(torch, lambda s: api.fm_index_logits(q, kvs[s % replicas], logits, ld),
+                      steps, warmup)
     entries = int(wl.kv.seq_lens.sum())
     key_bytes = entries * 256
     alg_bytes = key_bytes + B * 64 * 128 * 2 + B * 64 * 2 + wl.kv.block_table.nbytes + \
-        wl.kv.seq_lens.nbytes + B * ld * 4
+        wl.kv.seq_lens.nbytes + B * 512 * 4
     return wl, dict(entries=entries, wall_s=wall, per=per, alg_bytes=alg_bytes,
                     flops=entries * FLOP_PER_PAIR, graph_wall_s=graph_wall, graph_ms=graph_ms,
-                    score_b2b_ms=score_b2b_ms)
+                    fused_b2b_ms=fused_ms, two_call=dict(
+                        ms_per_step=two_wall / steps * 1e3, graph_event_ms=two_graph_ms,
+                        score_kernel_ms=score_ms,
+                        score_hbm_frac=(alg_bytes + B * ld * 4 - B * 512 * 4) / (score_ms * 1e-3)
+                        / 1e9 / HBM_PEAK_GBS))
 
 
 def run_mask(torch, api, W, steps, warmup, replicas=2, heads=64):
@@ -398,6 +428,15 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
+def stream_copy_gbs(torch, nbytes=1 << 30, reps=10):
+    """Measured HBM rate of a plain 1 GiB device-to-device copy (bytes read + written)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    b = torch.empty_like(a)
+    ms = b2b_ms(torch, lambda s: b.copy_(a), reps, 2)
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -428,10 +467,11 @@ def main():
     log("headline: decode bf16 B=32 x 65536 ...")
     wl, h = run_decode(torch, api, W, args.steps, args.warmup)
     ms_step = h["graph_wall_s"] / args.steps * 1e3
-    score_ms = h["score_b2b_ms"]
+    kern_ms = h["fused_b2b_ms"]
     digest = kernel_source_digest()
-    achieved = h["alg_bytes"] / (score_ms * 1e-3) / 1e9
-    traffic = read_traffic("score_decode_bf16_b32_s65536_counters.txt", digest)
+    achieved = h["alg_bytes"] / (kern_ms * 1e-3) / 1e9
+    traffic = read_traffic("score_topk_decode_bf16_b32_s65536_counters.txt", digest)
+    copy_gbs = stream_copy_gbs(torch)
     line = {
         "metric": "compressed-key entries scored+selected/sec (decode, bf16 keys)",
         "value": h["entries"] * args.steps / h["graph_wall_s"],
@@ -447,16 +487,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode_bf16_b32_s65536_top512", "requests": 32,
                    "entries_per_request": 65536, "page": 64, "heads": 64, "head_dim": 128,
-                   "k": 512, "pool_replicas_rotated": 3, "launch": "hip_graph"},
+                   "k": 512, "pool_replicas_rotated": 3, "launch": "hip_graph",
+                   "call": "fm_index_topk (scoring and top-512 fused)"},
         "eager": {"ms_per_step": h["wall_s"] / args.steps * 1e3,
                   "value": h["entries"] * args.steps / h["wall_s"]},
         "graph_event_ms_per_step": h["graph_ms"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "score_bf16_ring_kernel<4> (bf16 keys, bf16 q)",
-                     "alg_bytes_per_launch": h["alg_bytes"], "avg_kernel_ms": score_ms,
-                     "timing": "events around back-to-back launches of the scoring call",
-                     "bracketed_ms": h["per"]["score"]},
+                     "kernel": "score_topk_bf16_kernel<4,16> (bf16 keys, bf16 q, fused top-512)",
+                     "alg_bytes_per_launch": h["alg_bytes"], "avg_kernel_ms": kern_ms,
+                     "timing": "events around back-to-back launches of the fused call",
+                     "bracketed_ms": h["per"]["index_topk"],
+                     "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": achieved / copy_gbs},
+        "two_call_path": h["two_call"],
         "kernels_ms": h["per"],
         "kernel_sources": digest,
     }

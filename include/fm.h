@@ -74,7 +74,8 @@ typedef enum {
     FM_OP_INDEX_LOGITS = 0,
     FM_OP_TOPK = 1,
     FM_OP_RESIDENT_MASK = 2,
-    FM_OP_SCORE_RESIDENT = 3
+    FM_OP_SCORE_RESIDENT = 3,
+    FM_OP_INDEX_TOPK = 4
 } fm_op;
 
 /*
@@ -144,6 +145,31 @@ fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *l
                           int64_t ld, void *stream);
 
 /*
+ * Scoring and top-k in one call: fm_index_logits followed by fm_topk512 over every row's
+ * visible entries (and, with a mask, its resident ones), with the same result as those two
+ * calls (paper summary, section 3: the native top-k inside the resident set C^CoreComp;
+ * README "Two-level recall": non-resident logits are -inf before the native top-512; CSA
+ * page, section 3: index_topk = 512, all entries kept when fewer exist).
+ *   Candidates of row t (request b = row_req[t], or t, or 0 when B == 1): the entries
+ *   s < n_vis(t) whose logit is finite and, when mask is given, mask[b * mask_ld + s] != 0.
+ *   out_idx[t * k + i]: the k of largest logit, ties to the lower s, ascending, padded -1;
+ *   out_val (nullable): their logits, padded -inf.  logits (nullable): also receives the
+ *   logits exactly as fm_index_logits writes them (columns s < logits_ld).
+ * Shapes whose rows split into at most 16 chunks run fused: a workgroup scores each chunk of a
+ * row into LDS and keeps a superset of the chunk's top-k in the workspace, then one workgroup
+ * per row selects from those; no logit reaches memory unless asked for.  Other shapes score
+ * into the workspace and select with the top-k kernels.  Both give the same result.
+ * Requirements: 1 <= k <= FM_MAX_K; 1 <= max_seq_len <= 2^29; mask_ld >= 64 ceil(max_seq_len
+ * / 64) and >= logits_ld (mask rows are requests, as for fm_resident_mask's output);
+ * ws 256-byte aligned, ws_bytes >= fm_workspace_bytes(FM_OP_INDEX_TOPK, T, n) with
+ * n = max(64 ceil(max_seq_len / 64), logits_ld rounded up to 64), its contents irrelevant.
+ * Calls sharing a workspace must not overlap in time.
+ */
+fm_status fm_index_topk(const fm_query_desc *q, const fm_kv_desc *kv, const uint8_t *mask,
+                        int64_t mask_ld, int k, int32_t *out_idx, float *out_val, float *logits,
+                        int64_t logits_ld, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Level-1 resident mask over n_layers encoders (1..FM_MAX_LAYERS), one query row per request
  * per encoder (q_layers[l].T == kv->B, row b = request b), encoder l scoring pool[l].
  *   FM_UNION_MAX : u[b,s] = max_l L_l[b,s]; resident iff u >= ln(p / (1 - p)), i.e.
@@ -194,7 +220,9 @@ fm_status fm_topk512(const float *logits, int64_t ld, int T, const int32_t *n_va
  * those candidates (ties by lower logical index).  Indices are logical entry positions
  * 64 * page + slot, ascending, -1 padded.  Pages outside the list are never dereferenced.
  * Needs ws 256-byte aligned with ws_bytes >= fm_workspace_bytes(FM_OP_SCORE_RESIDENT, T,
- * res_ld * 64) (the logits of the listed pages, then the top-k workspace).
+ * res_ld * 64), its contents irrelevant.  Shapes that fit run fused as fm_index_topk does (the
+ * chunks' candidates in the workspace); others score the listed pages into the workspace,
+ * then select.
  */
 fm_status fm_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
                             const int32_t *resident_pages, const int32_t *n_resident,

@@ -81,6 +81,27 @@ def score_resident_cells(dw, k=512, resident_pages=None, n_resident=None, replic
     return cells, val
 
 
+def index_topk_ws(dw, layer=0, logits_ld=0):
+    """A workspace sized for fm_index_topk over the workload's rows."""
+    T = dw.wl.queries[layer].T
+    n = max(-(-dw.wl.kv.max_seq_len // 64) * 64, -(-logits_ld // 64) * 64)
+    nb = api.fm_workspace_bytes(api.FM_OP_INDEX_TOPK, T, n)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device=dw.device)
+
+
+def index_topk(dw, k=512, layer=0, mask=None, logits_ld=0, ws=None, replica=0):
+    """fm_index_topk: (idx, val, logits or None)."""
+    T = dw.wl.queries[layer].T
+    ws = index_topk_ws(dw, layer, logits_ld) if ws is None else ws
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=dw.device)
+    val = torch.full((T, k), -7.0, dtype=torch.float32, device=dw.device)
+    L = torch.empty((T, logits_ld), dtype=torch.float32, device=dw.device) if logits_ld else None
+    api.fm_index_topk(dw.query(layer), dw.kv(replica, [layer]), mask,
+                      0 if mask is None else mask.shape[1], k, idx, val, L, logits_ld, ws,
+                      ws.numel())
+    return idx, val, L
+
+
 def densest_pages(density, kmax, n_pages=None):
     B, ld = density.shape
     n_pages = ld if n_pages is None else n_pages

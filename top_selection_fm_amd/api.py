@@ -19,14 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libfm.so")
 FM_OK, FM_ERR_INVALID_ARG, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_LAUNCH = range(5)
 FM_F32, FM_BF16, FM_FP8_E4M3, FM_FP8_E4M3_SCALED132 = range(4)
 FM_UNION_MAX, FM_UNION_MEAN = 0, 1
-FM_OP_INDEX_LOGITS, FM_OP_TOPK, FM_OP_RESIDENT_MASK, FM_OP_SCORE_RESIDENT = range(4)
+FM_OP_INDEX_LOGITS, FM_OP_TOPK, FM_OP_RESIDENT_MASK, FM_OP_SCORE_RESIDENT, FM_OP_INDEX_TOPK = range(5)
 FM_MAX_LAYERS = 4
 PAGE = 64
 
 KEY_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8x132": FM_FP8_E4M3_SCALED132}
 Q_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8": FM_FP8_E4M3}
 
-EXPORTS = ["fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
+EXPORTS = ["fm_index_logits", "fm_index_topk", "fm_resident_mask", "fm_topk512", "fm_score_resident",
            "fm_score_resident_noalloc", "fm_score_resident_cells", "fm_densest_pages", "fm_workspace_bytes",
            "fm_encode_queries", "fm_encode_workspace_bytes", "fm_golden_labels",
            "fm_golden_workspace_bytes", "fm_status_string", "fm_last_error", "fm_version"]
@@ -72,6 +72,7 @@ def lib():
         L = C.CDLL(LIB_PATH)
         P, I64 = C.c_void_p, C.c_int64
         L.fm_index_logits.argtypes = [P, P, P, I64, P]
+        L.fm_index_topk.argtypes = [P, P, P, I64, C.c_int, P, P, P, I64, P, C.c_size_t, P]
         L.fm_resident_mask.argtypes = [P, C.c_int, P, C.c_int, C.c_float, C.c_int32, C.c_int32,
                                        P, I64, P, P, I64, P, P, P]
         L.fm_topk512.argtypes = [P, I64, C.c_int, P, P, I64, P, C.c_int, P, P, P, C.c_size_t, P]
@@ -86,7 +87,7 @@ def lib():
                                        P, P, P, I64, P, C.c_size_t, P]
         L.fm_golden_workspace_bytes.argtypes = [C.c_int, C.c_int, I64, C.c_int]
         L.fm_golden_workspace_bytes.restype = C.c_size_t
-        for f in ("fm_index_logits", "fm_resident_mask", "fm_topk512", "fm_score_resident",
+        for f in ("fm_index_logits", "fm_index_topk", "fm_resident_mask", "fm_topk512", "fm_score_resident",
                   "fm_score_resident_noalloc", "fm_score_resident_cells", "fm_densest_pages", "fm_encode_queries",
                   "fm_golden_labels"):
             getattr(L, f).restype = C.c_int
@@ -175,6 +176,13 @@ def fm_resident_mask(q_layers, kv: KvDesc, mode: int, threshold: float, n_sink: 
                                   int(n_sink), int(n_recent), _ptr(mask), int(mask_ld),
                                   _ptr(page_count), _ptr(page_list), int(page_list_ld),
                                   _ptr(page_density), _ptr(union_score), _stream(stream)))
+
+
+def fm_index_topk(q: QueryDesc, kv: KvDesc, mask, mask_ld: int, k: int, out_idx, out_val=None,
+                  logits=None, logits_ld: int = 0, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(lib().fm_index_topk(C.byref(q), C.byref(kv), _ptr(mask), int(mask_ld), int(k),
+                               _ptr(out_idx), _ptr(out_val), _ptr(logits), int(logits_ld),
+                               _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def fm_topk512(logits, ld: int, T: int, n_valid, mask, mask_ld: int, row_req, k: int, out_idx,

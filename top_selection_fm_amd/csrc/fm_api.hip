@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "fm_internal.h"
@@ -176,6 +177,133 @@ fm_status run_score(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t 
     return launched(fm::launch_score(a, key_fmt(kv->key_dtype), qf, st), "score");
 }
 
+// ---------------------------------------------------------------- fused scoring + top-k
+// Workspace of the calls that score and select: either the fused path's chunk candidates or the
+// unfused path's logits and top-k workspace.
+size_t fused_region_bytes(int T) {
+    return fm::align_up((size_t)T * fm::kFuseMaxChunks * 4, 256) +
+           fm::align_up((size_t)T * fm::kFuseMaxChunks * 8, 256) +
+           2 * fm::align_up((size_t)T * fm::kFuseMaxCand * 4, 256);
+}
+size_t unfused_region_bytes(int T, int64_t n) {
+    return fm::align_up((size_t)T * (size_t)n * sizeof(float), 256) + fm::topk_ws_bytes(T, n);
+}
+size_t select_ws_bytes(int T, int64_t n) {
+    return std::max(fused_region_bytes(T), unfused_region_bytes(T, n));
+}
+
+// The fused path's work split: W waves a workgroup, ppw page slots a wave, n_chunks workgroups
+// a row.  It aims at one workgroup per CU (256), and gives way to the unfused path (scoring
+// kernel + top-k kernel) when a row would need more than kFuseMaxChunks chunks, or when few
+// workgroups would each stream long runs of pages while most of the chip idles.
+struct FusePlan {
+    bool fused;
+    int ppw, n_chunks, ppw_pad;
+};
+FusePlan fuse_plan(int T, int64_t n_slots, int k, int nw, int ring) {
+    FusePlan p{false, 0, 0, 0};
+    if (nw <= 0 || T <= 0 || n_slots <= 0) return p;
+    constexpr int64_t kWgTarget = 256;
+    auto clamp_ppw = [](int64_t x) { return x < 1 ? (int64_t)1 : (x > 16 ? (int64_t)16 : x); };
+    auto chunks_of = [&](int64_t ppw) { return (n_slots + nw * ppw - 1) / (nw * ppw); };
+    int64_t ppw = clamp_ppw(((int64_t)T * n_slots + kWgTarget * nw - 1) / (kWgTarget * nw));
+    int64_t ch = chunks_of(ppw);
+    if (ch > fm::kFuseMaxChunks) {
+        ppw = clamp_ppw((n_slots + (int64_t)nw * fm::kFuseMaxChunks - 1) / ((int64_t)nw * fm::kFuseMaxChunks));
+        ch = chunks_of(ppw);
+    }
+    if (ch > fm::kFuseMaxChunks || ch * k > fm::kFuseMaxCand) return p;
+    if ((int64_t)T * ch < kWgTarget / 2 && ppw > 2) return p;
+    p.fused = true;
+    p.ppw = (int)ppw;
+    p.n_chunks = (int)ch;
+    p.ppw_pad = (int)((ppw + ring - 1) / ring * ring);
+    return p;
+}
+
+// Score and select: rows of q over n_slots page slots each (the listed resident pages when
+// res_pages is given, else logical pages 0 .. n_slots - 1), top-k of the visible (and, with a
+// mask, resident) entries.  logits (nullable) also receives the logits.  Arguments validated.
+fm_status score_select(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t *res_pages,
+                       const int32_t *n_res, int64_t res_ld, int64_t n_slots, const uint8_t *mask,
+                       int64_t mask_ld, int k, int cells, int32_t *out_idx, float *out_val,
+                       float *logits, int64_t logits_ld, void *ws, hipStream_t st) {
+    const int kf = key_fmt(kv->key_dtype);
+    const int qf = q->q_dtype == FM_FP8_E4M3 ? fm::Q_FP8 : q->q_dtype == FM_BF16 ? fm::Q_BF16 : fm::Q_F32;
+    const fm::FuseShape fs = fm::fuse_shape(kf, qf, q->n_heads);
+    const bool prefill = q->q_dtype == FM_FP8_E4M3 && kv->B == 1 && q->T >= 16 && !res_pages;
+    const FusePlan p = prefill ? FusePlan{false, 0, 0, 0} : fuse_plan(q->T, n_slots, k, fs.waves, fs.round);
+    if (p.fused) {
+        fm::ScoreArgs a;
+        a.q = make_q(q, kv);
+        a.kv = make_kv(kv);
+        a.res_pages = res_pages;
+        a.n_res = n_res;
+        a.res_ld = res_ld;
+        a.out = logits;
+        a.out_ld = logits ? logits_ld : 0;
+        a.n_slots = n_slots;
+        a.ppw = p.ppw;
+        fm::FuseArgs f;
+        f.k = k;
+        f.n_chunks = p.n_chunks;
+        f.cap = std::max(k, fm::kFuseMaxCand / p.n_chunks);
+        f.ppw_pad = p.ppw_pad;
+        f.mask = mask;
+        f.mask_ld = mask ? mask_ld : 0;
+        f.cells = cells;
+        f.small_entries = (!res_pages || cells) && n_slots * FM_PAGE_SIZE <= 65536 ? 1 : 0;
+        uint8_t *w8 = (uint8_t *)ws;
+        f.cnt = (int32_t *)w8;
+        w8 += fm::align_up((size_t)q->T * fm::kFuseMaxChunks * 4, 256);
+        f.cstat = (float2 *)w8;
+        w8 += fm::align_up((size_t)q->T * fm::kFuseMaxChunks * 8, 256);
+        f.cval = (float *)w8;
+        w8 += fm::align_up((size_t)q->T * fm::kFuseMaxCand * 4, 256);
+        f.cidx = (int32_t *)w8;
+        f.out_idx = out_idx;
+        f.out_val = out_val;
+        return launched(fm::launch_score_topk(a, f, kf, qf, st), "score_topk");
+    }
+    // unfused: the logits (into the caller's buffer, or the workspace), then the top-k
+    const int64_t ld = logits ? logits_ld : n_slots * FM_PAGE_SIZE;
+    uint8_t *after = (uint8_t *)ws;
+    float *wl = logits ? logits : (float *)after;
+    if (!logits) after += fm::align_up((size_t)q->T * (size_t)ld * sizeof(float), 256);
+    if (prefill) {
+        fm::PrefillArgs a;
+        a.q = make_q(q, kv);
+        a.kv = make_kv(kv);
+        a.out = wl;
+        a.out_ld = ld;
+        fm::prefill_plan(a, q->T, (ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE);
+        CHECK(launched(fm::launch_prefill(a, st), "prefill"));
+    } else {
+        CHECK(run_score(q, kv, res_pages, n_res, res_ld, wl, ld, n_slots, st));
+    }
+    fm::TopkArgs a;
+    a.logits = wl;
+    a.ld = ld;
+    a.T = q->T;
+    a.n_valid = nullptr;
+    a.mask = mask;
+    a.mask_ld = mask ? mask_ld : 0;
+    a.row_req = q->row_req;
+    a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
+    a.res_pages = res_pages;
+    a.n_res = n_res;
+    a.res_ld = res_ld;
+    a.res_cells = cells;
+    a.B = kv->B;
+    a.k = k;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    fm::TopkWs W;
+    const bool staged = fm::topk_ws_bytes(q->T, ld) > 0;
+    if (staged) W = fm::topk_ws_carve(after, q->T, ld);
+    return launched(fm::launch_topk(a, staged ? &W : nullptr, st), "topk");
+}
+
 // Arguments of two-level scoring other than the workspace.
 fm_status check_score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
                                const int32_t *resident_pages, const int32_t *n_resident,
@@ -200,32 +328,8 @@ fm_status score_resident(const fm_query_desc *q, const fm_kv_desc *kv,
     const size_t need = fm_workspace_bytes(FM_OP_SCORE_RESIDENT, q->T, res_ld * FM_PAGE_SIZE);
     REQUIRE(ws && ws_bytes >= need && aligned(ws, 256), FM_ERR_WORKSPACE,
             "workspace %zu bytes at %p, need %zu (256-byte aligned)", ws_bytes, ws, need);
-    hipStream_t st = (hipStream_t)stream;
-    float *wl = (float *)ws;
-    const int64_t ld = res_ld * FM_PAGE_SIZE;
-    CHECK(run_score(q, kv, resident_pages, n_resident, res_ld, wl, ld, res_ld, st));
-    fm::TopkArgs a;
-    a.logits = wl;
-    a.ld = ld;
-    a.T = q->T;
-    a.n_valid = nullptr;
-    a.mask = nullptr;
-    a.mask_ld = 0;
-    a.row_req = q->row_req;
-    a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
-    a.res_pages = resident_pages;
-    a.n_res = n_resident;
-    a.res_ld = res_ld;
-    a.res_cells = cells;
-    a.B = kv->B;
-    a.k = k;
-    a.out_idx = out_idx;
-    a.out_val = out_val;
-    const size_t logit_bytes = fm::align_up((size_t)q->T * (size_t)ld * sizeof(float), 256);
-    fm::TopkWs W;
-    const bool staged = fm::topk_ws_bytes(q->T, ld) > 0;
-    if (staged) W = fm::topk_ws_carve((uint8_t *)ws + logit_bytes, q->T, ld);
-    CHECK(launched(fm::launch_topk(a, staged ? &W : nullptr, st), "topk"));
+    CHECK(score_select(q, kv, resident_pages, n_resident, res_ld, res_ld, nullptr, 0, k, cells,
+                       out_idx, out_val, nullptr, 0, ws, (hipStream_t)stream));
     return ok();
 }
 
@@ -383,6 +487,37 @@ fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *l
         return ok();
     }
     CHECK(run_score(q, kv, nullptr, nullptr, 0, logits, ld, n_pages, (hipStream_t)stream));
+    return ok();
+}
+
+fm_status fm_index_topk(const fm_query_desc *q, const fm_kv_desc *kv, const uint8_t *mask,
+                        int64_t mask_ld, int k, int32_t *out_idx, float *out_val, float *logits,
+                        int64_t logits_ld, void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_kv(kv, 1));
+    CHECK(check_q(q, kv, "q"));
+    REQUIRE(k >= 1 && k <= FM_MAX_K, FM_ERR_UNSUPPORTED, "k = %d (1..%d)", k, FM_MAX_K);
+    REQUIRE(!logits || (logits_ld >= 1 && logits_ld <= (int64_t)INT32_MAX / 4 && aligned(logits, 4)),
+            FM_ERR_INVALID_ARG, "logits_ld = %lld (1 .. 2^29, 4-byte aligned logits)",
+            (long long)logits_ld);
+    const int64_t n_slots = (kv->max_seq_len + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE;
+    REQUIRE(n_slots >= 1, FM_ERR_INVALID_ARG, "max_seq_len = 0: nothing to score");
+    REQUIRE(n_slots * FM_PAGE_SIZE <= (int64_t)INT32_MAX / 4, FM_ERR_UNSUPPORTED,
+            "max_seq_len = %lld (at most 2^29)", (long long)kv->max_seq_len);
+    const int64_t mask_need = std::max(n_slots * FM_PAGE_SIZE, logits ? logits_ld : (int64_t)0);
+    REQUIRE(!mask || (mask_ld >= mask_need && mask_ld <= (int64_t)INT32_MAX),
+            FM_ERR_INVALID_ARG, "mask_ld = %lld (%lld .. 2^31 - 1)", (long long)mask_ld,
+            (long long)mask_need);
+    if (q->T == 0) return ok();
+    REQUIRE(out_idx, FM_ERR_INVALID_ARG, "out_idx is NULL");
+    // with logits wanted, the pages up to logits_ld are covered too (past max_seq_len they are
+    // invisible: -inf written, nothing read)
+    const int64_t n_cover = logits ? std::max(n_slots, (logits_ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE)
+                                   : n_slots;
+    const size_t need = fm_workspace_bytes(FM_OP_INDEX_TOPK, q->T, n_cover * FM_PAGE_SIZE);
+    REQUIRE(ws && ws_bytes >= need && aligned(ws, 256), FM_ERR_WORKSPACE,
+            "workspace %zu bytes at %p, need %zu (256-byte aligned)", ws_bytes, ws, need);
+    CHECK(score_select(q, kv, nullptr, nullptr, 0, n_cover, mask, mask_ld, k, 0, out_idx, out_val,
+                       logits, logits_ld, ws, (hipStream_t)stream));
     return ok();
 }
 
@@ -664,9 +799,7 @@ fm_status fm_golden_labels(const float *scores, int64_t ld, int T, int n_layers,
 size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates) {
     if (T <= 0 || max_candidates <= 0) return 0;
     if (op == FM_OP_TOPK) return fm::topk_ws_bytes(T, max_candidates);
-    if (op == FM_OP_SCORE_RESIDENT)
-        return fm::align_up((size_t)T * (size_t)max_candidates * sizeof(float), 256) +
-               fm::topk_ws_bytes(T, max_candidates);
+    if (op == FM_OP_SCORE_RESIDENT || op == FM_OP_INDEX_TOPK) return select_ws_bytes(T, max_candidates);
     return 0;
 }
 

@@ -124,6 +124,29 @@ struct DensestArgs {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Fused scoring + top-k.  Scoring grid (n_chunks, T): workgroup (c, t) scores page slots
+// [c W ppw, (c + 1) W ppw) of row t into LDS (W waves, ppw slots each) and keeps at most cap
+// candidates (a superset of the chunk's top-k) in the workspace; then one workgroup per row
+// selects the row's top-k from its chunks' candidates.
+constexpr int kFuseMaxChunks = 16;         // chunks of one row, at most
+constexpr int kFuseMaxCand = 8192;         // chunks x cap, at most (the merge buffer in LDS)
+struct FuseArgs {
+    int k;
+    int n_chunks;
+    int cap;                     // candidates a chunk may keep: k <= cap, n_chunks cap <= 8192
+    int ppw_pad;                 // slots a wave's LDS rows hold (ppw rounded up to the ring)
+    const uint8_t *mask;         // Mode A: [rows of requests, mask_ld] by logical entry, or null
+    int64_t mask_ld;
+    int cells;                   // two-level: rank and emit reserve cells (list positions)
+    int small_entries;           // every emitted entry < 65,536 (bitmap ordering of the output)
+    int32_t *cnt;                // [T, n_chunks]: candidates each chunk kept
+    float2 *cstat;               // [T, n_chunks]: (smallest kept value, chunk maximum)
+    float *cval;                 // [T, n_chunks, cap]
+    int32_t *cidx;               // [T, n_chunks, cap]
+    int32_t *out_idx;            // [T, k]
+    float *out_val;              // [T, k] or null
+};
+
 // Top-k workspace: stage-1 survivors of every (row, kTopkChunk-entry chunk), kTopkCap each.
 #ifndef FM_F8_WPE
 #define FM_F8_WPE 3       // fp8-key scoring with bf16 queries: waves per SIMD it is sized for
@@ -204,6 +227,14 @@ size_t topk_ws_bytes(int T, int64_t n);   // bytes for T rows of up to n entries
 TopkWs topk_ws_carve(void *ws, int T, int64_t n);
 
 hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t s);
+// Fused scoring + top-k (ScoreArgs.out: the logits too, or null).  fuse_shape: W waves a
+// workgroup (0: no fused kernel for the format) and the page count a wave's slots are padded to.
+struct FuseShape {
+    int waves, round;
+};
+FuseShape fuse_shape(int key_fmt, int q_fmt, int n_heads);
+hipError_t launch_score_topk(const ScoreArgs &a, const FuseArgs &f, int key_fmt, int q_fmt,
+                             hipStream_t s);
 void prefill_plan(PrefillArgs &a, int T, int64_t n_pages);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_score_f32(const ScoreArgs &a, hipStream_t s);

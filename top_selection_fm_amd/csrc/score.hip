@@ -27,7 +27,10 @@
 // wait before a page covers that page's loads only.
 #include <math.h>
 
+#include <type_traits>
+
 #include "fm_internal.h"
+#include "select_dev.h"
 
 #ifndef FM_BF16_RING
 #define FM_BF16_RING 4
@@ -525,6 +528,564 @@ void score_bf16_ring_kernel(ScoreArgs A) {
         }
     }
     store_wave_logits(A, orsrc, s_res[wave], phys_l, lp_l, slot0, nslot, nvis, ln);
+}
+
+// ---------------------------------------------------------------- fused scoring + top-k
+// The top-k of a row (paper summary, section 3: the native selector keeps the top-k inside the
+// resident set; CSA page, section 3: index_topk = 512) without the row's logits reaching
+// memory.  Two kernels:
+//   1. workgroup (c, t) scores its chunk of row t into LDS and keeps a superset of the chunk's
+//      top-k (the entries of the chunk's highest value bins, at most `cap` of them; exactly the
+//      chunk's top-k when that superset would not fit).  Every member of the row's top-k is in
+//      its own chunk's top-k, because the order (value descending, entry ascending) is total.
+//      The candidates, their number and two bounds (the smallest candidate value, the chunk's
+//      largest value) go to the workspace.
+//   2. one workgroup per row selects the row's top-k exactly from its chunks' candidates and
+//      writes it in ascending entry order.  A chunk that kept at least k candidates proves
+//      that the row's k-th value is at least its smallest candidate, so candidates below the
+//      largest such bound are dropped on loading and the value bins span only what is left.
+
+template <int NT>
+struct FuseLds {
+    uint32_t hist[kBins];
+    uint32_t sh[NT / 64 + 1];
+    uint32_t misc[2];
+    float shf[NT / 64];
+    float shf2[NT / 64];
+    uint32_t shc[NT / 64];
+    uint32_t wsum[NT / 64];
+    int32_t bnd[kBnd];
+    uint32_t n_out, n_bnd;
+};
+
+// the candidates of a chunk in LDS (value j and its entry entry_of(j)), as a radix_rule source
+template <class EntryOf>
+struct ChunkSrc {
+    const float *v;
+    int n;
+    EntryOf entry_of;
+    template <int NT, class F>
+    __device__ void each(F f) const {
+        for (int j = (int)threadIdx.x; j < n; j += NT) {
+            const float x = v[j];
+            if (x > -INFINITY) f(x, (int64_t)entry_of(j));   // -inf and NaN are not candidates
+        }
+    }
+};
+
+// The bin holding the r-th largest of hist (r >= 1, r <= total): S.misc[0] = the bin,
+// S.misc[1] = the count in higher bins.  Wave w owns kBins / NW bins from the top, lane l
+// BPL of them; two barriers.
+template <int NT, class Lds>
+__device__ void top_bin(uint32_t r, Lds &S) {
+    constexpr int NWv = NT / 64, BPW = kBins / NWv, BPL = BPW / 64;
+    static_assert(BPW % 64 == 0, "bins a lane");
+    const int w = threadIdx.x >> 6, ln = __lane_id();
+    const int top = kBins - 1 - BPW * w - BPL * ln;      // this lane's bins: top, top - 1, ...
+    uint32_t h[BPL], sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+        h[i] = S.hist[top - i];
+        sum += h[i];
+    }
+    const uint32_t incl = wave_incl_scan<NT>(sum);
+    if (ln == 63) S.wsum[w] = incl;
+    __syncthreads();
+    uint32_t above = 0;
+    for (int v = 0; v < w; ++v) above += S.wsum[v];
+    above += incl - sum;                                  // count in bins above this lane's
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+        if (above < r && r <= above + h[i]) {
+            S.misc[0] = (uint32_t)(top - i);
+            S.misc[1] = above;
+        }
+        above += h[i];
+    }
+    __syncthreads();
+}
+
+// Keep the candidates of the chunk's n values in LDS (-inf and NaN are not candidates) that
+// can be in the top-k: all of them when they fit in cap; else those of the value bins from
+// the top down to the bin holding the chunk's k-th largest, when they fit; else exactly the
+// chunk's top-k (boundary bin ranked by the full key, or the radix selection).  Writes them to
+// cval / cidx (any order), their number to *cnt_out and (a value at or below every kept one,
+// the chunk maximum) to *stat_out.  On entry: the per-wave candidate counts, minima and maxima
+// in S.shc / shf / shf2, S.hist zero, S.n_out = S.n_bnd = 0, followed by a barrier.
+// NV = n / NT values a thread (n a multiple of NT).
+template <int NT, int NV, class EntryOf>
+__device__ void chunk_select(const float *vals, uint32_t k, uint32_t cap, EntryOf entry_of,
+                             float *cval, int32_t *cidx, int32_t *cnt_out, float2 *stat_out,
+                             FuseLds<NT> &S) {
+    constexpr int NWv = NT / 64;
+    constexpr int n = NV * NT;
+    const int tid = threadIdx.x, ln = __lane_id();
+    const uint64_t lt = ln == 0 ? 0ull : (~0ull >> (64 - ln));
+    uint32_t total = 0;
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NWv; ++i) {
+        total += S.shc[i];
+        lo = fminf(lo, S.shf[i]);
+        hi = fmaxf(hi, S.shf2[i]);
+    }
+    float v[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) v[u] = vals[u * NT + tid];
+    // keep the values whose flag is set: per group of four values a thread, one slot
+    // reservation for the wave, then the stores
+    static_assert(NV % 4 == 0, "groups of four");
+    auto emit_all = [&](auto &&flag) {
+#pragma unroll
+        for (int u0 = 0; u0 < NV; u0 += 4) {
+            uint64_t ms[4];
+            uint32_t wtot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                ms[q] = __ballot(flag(u0 + q));
+                wtot += (uint32_t)__popcll(ms[q]);
+            }
+            if (wtot == 0) continue;
+            uint32_t base = 0;
+            if (ln == 0) base = atomicAdd(&S.n_out, wtot);
+            base = __shfl(base, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if ((ms[q] >> ln) & 1ull) {
+                    const uint32_t p = base + (uint32_t)__popcll(ms[q] & lt);
+                    if (p < cap) {
+                        cval[p] = v[u0 + q];
+                        cidx[p] = (int32_t)entry_of((u0 + q) * NT + tid);
+                    }
+                }
+                base += (uint32_t)__popcll(ms[q]);
+            }
+        }
+    };
+    const float width = hi - lo;
+    uint32_t kept;
+    float bound = lo;
+    if (total <= cap) {
+        kept = total;
+        emit_all([&](int u) { return v[u] > -INFINITY; });
+    } else {
+        bool radix = !(width < INFINITY);
+        LinBins bins{lo, 0.f, !(hi > lo)};
+        bins.inv_w = bins.flat || radix ? 0.f : (float)kBins / width;
+        kept = k;
+        if (!radix) {
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+                if (v[u] > -INFINITY) atomicAdd(&S.hist[bins(v[u])], 1u);
+            __syncthreads();
+            top_bin<NT>(k, S);
+            const int bstar = (int)S.misc[0];
+            const uint32_t above = S.misc[1], nb = S.hist[bstar];
+            // a value at or below every member of bins >= bstar: the lower edge of the bin below
+            if (!bins.flat && bstar > 0) bound = lo + (float)(bstar - 1) * (width / (float)kBins);
+            if (above + nb <= cap) {
+                kept = above + nb;              // the bins from the top down to bstar, whole
+                emit_all([&](int u) { return v[u] > -INFINITY && bins(v[u]) >= bstar; });
+            } else if (nb <= (uint32_t)kBnd) {
+                // higher bins whole, the boundary bin ranked by the full key
+                const uint32_t need = k - above;
+                emit_all([&](int u) { return v[u] > -INFINITY && bins(v[u]) > bstar; });
+#pragma unroll
+                for (int u = 0; u < NV; ++u)
+                    if (v[u] > -INFINITY && bins(v[u]) == bstar) S.bnd[atomicAdd(&S.n_bnd, 1u)] = u * NT + tid;
+                __syncthreads();
+                for (uint32_t a0 = 0; a0 < nb; a0 += NT) {
+                    const uint32_t a = a0 + tid;
+                    bool keep = false;
+                    int ja = 0;
+                    if (a < nb) {
+                        ja = S.bnd[a];
+                        const uint64_t ka = full_key(vals[ja], entry_of(ja));
+                        uint32_t rank = 0;
+                        for (uint32_t cc = 0; cc < nb; ++cc) {
+                            const int jc = S.bnd[cc];
+                            rank += full_key(vals[jc], entry_of(jc)) > ka;
+                        }
+                        keep = rank < need;
+                    }
+                    const uint64_t mk = __ballot(keep);
+                    if (mk) {
+                        uint32_t b0 = 0;
+                        if (ln == 0) b0 = atomicAdd(&S.n_out, (uint32_t)__popcll(mk));
+                        b0 = __shfl(b0, 0);
+                        if (keep) {
+                            const uint32_t p = b0 + (uint32_t)__popcll(mk & lt);
+                            cval[p] = vals[ja];
+                            cidx[p] = (int32_t)entry_of(ja);
+                        }
+                    }
+                }
+            } else {
+                radix = true;
+                bound = lo;
+                __syncthreads();                   // hist is read before the radix clears it
+            }
+        }
+        if (radix) {
+            const ChunkSrc<EntryOf> src{vals, n, entry_of};
+            const Rule rule = radix_rule<NT>(src, k, S.hist, S.sh, S.misc);
+            __syncthreads();
+            emit_all([&](int u) {
+                return v[u] > -INFINITY && (full_key(v[u], entry_of(u * NT + tid)) & rule.M) >= rule.P;
+            });
+        }
+    }
+    if (tid == 0) {
+        *cnt_out = (int32_t)min(kept, cap);
+        *stat_out = make_float2(bound, hi);
+    }
+}
+
+// The candidates of a wave's page slots: entries of empty slots, of unmapped pages, past the
+// visible length or (Mode A) outside the resident mask become -inf in LDS; the wave's candidate
+// count, minimum and maximum go to S (lane 0).
+template <int NT>
+__device__ __forceinline__ void mark_candidates(const FuseArgs &F, float (*res)[64], int ppw_pad,
+                                                int phys_l, int lp_l, int nslot, int64_t nvis,
+                                                int b, int ln, int wave, FuseLds<NT> &S) {
+    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(F.mask ? F.mask + (int64_t)b * F.mask_ld : nullptr), (short)0,
+        F.mask ? (int)F.mask_ld : 0, 0x00020000);
+    uint32_t c = 0;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int i = 0; i < ppw_pad; ++i) {
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        const int lp = __builtin_amdgcn_readlane(lp_l, i);
+        const int64_t s = (int64_t)lp * kPage + ln;
+        bool ok = i < nslot && phys >= 0 && s < nvis;
+        if (F.mask && ok) ok = __builtin_amdgcn_raw_buffer_load_b8(mr, (uint32_t)s, 0, 0) != 0;
+        const float v = res[i][ln];
+        if (!ok) {
+            res[i][ln] = -INFINITY;
+        } else if (v > -INFINITY) {
+            ++c;
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        c += __shfl_xor(c, o);
+        lo = fminf(lo, __shfl_xor(lo, o));
+        hi = fmaxf(hi, __shfl_xor(hi, o));
+    }
+    if (ln == 0) {
+        S.shc[wave] = c;
+        S.shf[wave] = lo;
+        S.shf2[wave] = hi;
+    }
+}
+
+// LDS of the row merge
+template <int NT>
+struct MergeLds {
+    uint32_t hist[kBins];
+    uint32_t bits[kBins];                 // selected entries < 65,536, one bit each
+    uint32_t pref[kBins];                 // selected entries in lower words
+    uint32_t sh[NT / 64 + 1];
+    uint32_t wsum[NT / 64];
+    uint32_t misc[2];
+    float bnd_v[kBnd];                    // the boundary bin's candidates
+    int32_t bnd_e[kBnd];
+    int32_t sel_e[FM_MAX_K];              // selected (entry, value), unordered
+    float sel_v[FM_MAX_K];
+    int32_t ccnt[kFuseMaxChunks];         // the chunks' kept counts and bounds
+    float2 cst[kFuseMaxChunks];
+    uint32_t m, n_sel, n_bnd;
+};
+
+// the merge's candidates in registers (SPT a thread), as a radix_rule source
+template <int SPT>
+struct RegSrc {
+    const float *v;
+    const int32_t *e;
+    const bool *ok;
+    template <int NT, class F>
+    __device__ void each(F f) const {
+#pragma unroll
+        for (int u = 0; u < SPT; ++u)
+            if (ok[u]) f(v[u], (int64_t)e[u]);
+    }
+};
+
+// One workgroup per row: the row's top-k from its chunks' candidates, in ascending entry order.
+// Every thread reads its share of all candidate slots (and one chunk's count and bounds) in one
+// round of loads and keeps them in registers; candidates below the row's proven bound are
+// dropped, the rest binned over [bound, row maximum].  Then the boundary bin, the exact rank of
+// its entries, and the output order from a bitmap of the selected entries (entries below
+// 65,536) or from counts of smaller selected entries.
+template <int NT, int SPT>
+__global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
+    __shared__ MergeLds<NT> S;
+    const int t = blockIdx.x, tid = threadIdx.x, ln = __lane_id();
+    const int nc = F.n_chunks, cap = F.cap;
+    const uint32_t k = (uint32_t)F.k;
+    const int64_t row_c = (int64_t)t * nc;
+    const int cand = nc * cap;
+    for (int i = tid; i < kBins; i += NT) {
+        S.hist[i] = 0u;
+        S.bits[i] = 0u;
+    }
+    if (tid == 0) {
+        S.m = 0u;
+        S.n_sel = 0u;
+        S.n_bnd = 0u;
+    }
+    if (tid < nc) {
+        S.ccnt[tid] = min(F.cnt[row_c + tid], cap);
+        S.cst[tid] = F.cstat[row_c + tid];
+    }
+    float v[SPT];
+    int32_t e[SPT];
+    bool ok[SPT];
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int i = u * NT + tid;
+        v[u] = -INFINITY;
+        e[u] = 0;
+        if (i < cand) {
+            v[u] = F.cval[row_c * cap + i];
+            e[u] = F.cidx[row_c * cap + i];
+        }
+    }
+    __syncthreads();                                         // LDS cleared, counts staged
+    float lo = -INFINITY, hi = -INFINITY, lo_any = INFINITY;
+    for (int c = 0; c < nc; ++c) {
+        const int cnt = S.ccnt[c];
+        const float2 st = S.cst[c];
+        if (cnt >= F.k) lo = fmaxf(lo, st.x);      // k candidates at or above st.x: a bound
+        if (cnt > 0) {
+            hi = fmaxf(hi, st.y);
+            lo_any = fminf(lo_any, st.x);
+        }
+    }
+    const float blo = lo > -INFINITY ? lo : lo_any;         // the bins' lower end
+    const float width = hi - blo;
+    bool radix = !(width < INFINITY) || !(hi >= blo);
+    LinBins bins{blo, 0.f, !(hi > blo)};
+    bins.inv_w = bins.flat || radix ? 0.f : (float)kBins / width;
+    int bn[SPT];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int i = u * NT + tid;
+        const int c = i / cap;
+        ok[u] = i < cand && (i - c * cap) < S.ccnt[c] && v[u] >= lo;
+        mine += ok[u] ? 1u : 0u;
+        bn[u] = ok[u] && !radix ? bins(v[u]) : -1;
+        if (bn[u] >= 0) atomicAdd(&S.hist[bn[u]], 1u);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o);
+    if (ln == 0 && mine) atomicAdd(&S.m, mine);
+    __syncthreads();
+    const uint32_t m = S.m;
+    auto select = [&](float x, int32_t en) {
+        const uint32_t p = atomicAdd(&S.n_sel, 1u);
+        if (p < (uint32_t)FM_MAX_K) {
+            S.sel_e[p] = en;
+            S.sel_v[p] = x;
+        }
+        if (F.small_entries && (uint32_t)en < 65536u) atomicOr(&S.bits[en >> 5], 1u << (en & 31));
+    };
+    if (m <= k) {
+#pragma unroll
+        for (int u = 0; u < SPT; ++u)
+            if (ok[u]) select(v[u], e[u]);
+    } else {
+        if (!radix) {
+            top_bin<NT>(k, S);
+            const int bstar = (int)S.misc[0];
+            const uint32_t need = k - S.misc[1], nb = S.hist[bstar];
+            if (nb <= (uint32_t)kBnd) {
+#pragma unroll
+                for (int u = 0; u < SPT; ++u) {
+                    if (bn[u] > bstar) {
+                        select(v[u], e[u]);
+                    } else if (bn[u] == bstar) {
+                        const uint32_t p = atomicAdd(&S.n_bnd, 1u);
+                        S.bnd_v[p] = v[u];
+                        S.bnd_e[p] = e[u];
+                    }
+                }
+                __syncthreads();
+                for (uint32_t a = tid; a < nb; a += NT) {
+                    const uint64_t ka = full_key(S.bnd_v[a], S.bnd_e[a]);
+                    uint32_t rank = 0;
+                    for (uint32_t c = 0; c < nb; ++c) rank += full_key(S.bnd_v[c], S.bnd_e[c]) > ka;
+                    if (rank < need) select(S.bnd_v[a], S.bnd_e[a]);
+                }
+            } else {
+                radix = true;
+                __syncthreads();                   // hist is read before the radix clears it
+            }
+        }
+        if (radix) {
+            const RegSrc<SPT> src{v, e, ok};
+            const Rule rule = radix_rule<NT>(src, k, S.hist, S.sh, S.misc);
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < SPT; ++u)
+                if (ok[u] && (full_key(v[u], e[u]) & rule.M) >= rule.P) select(v[u], e[u]);
+        }
+    }
+    __syncthreads();
+    const uint32_t cnt = min(S.n_sel, k);
+    int32_t *oi = F.out_idx + (int64_t)t * F.k;
+    float *ov = F.out_val ? F.out_val + (int64_t)t * F.k : nullptr;
+    if (F.small_entries) {
+        // positions from the bitmap: prefix popcounts of the words, then within the word
+        constexpr int WPT = kBins / NT;
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) c += (uint32_t)__popc(S.bits[WPT * tid + i]);
+        const uint32_t incl = wave_incl_scan<NT>(c);
+        if (ln == 63) S.wsum[tid >> 6] = incl;
+        __syncthreads();
+        uint32_t pre = incl - c;
+        for (int w = 0; w < (tid >> 6); ++w) pre += S.wsum[w];
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            S.pref[WPT * tid + i] = pre;
+            pre += (uint32_t)__popc(S.bits[WPT * tid + i]);
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i < cnt; i += NT) {
+            const int32_t en = S.sel_e[i];
+            const uint32_t w = ((uint32_t)en >> 5) & (kBins - 1);
+            const uint32_t pos = S.pref[w] + (uint32_t)__popc(S.bits[w] & ((1u << (en & 31)) - 1u));
+            oi[pos] = en;
+            if (ov) ov[pos] = S.sel_v[i];
+        }
+    } else {
+        for (uint32_t i = tid; i < cnt; i += NT) {
+            const int32_t en = S.sel_e[i];
+            uint32_t pos = 0;
+            for (uint32_t c = 0; c < cnt; ++c) pos += S.sel_e[c] < en;
+            oi[pos] = en;
+            if (ov) ov[pos] = S.sel_v[i];
+        }
+    }
+    for (int i = (int)cnt + tid; i < F.k; i += NT) {
+        oi[i] = -1;
+        if (ov) ov[i] = -INFINITY;
+    }
+}
+
+// bf16 keys x bf16 queries (the decode shape), NW waves a workgroup scoring one row's chunk:
+// the tile ring of score_bf16_ring_kernel, logits into LDS, then the fused selection.
+template <int RING, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FM_DECODE_WAVES)))
+void score_topk_bf16_kernel(ScoreArgs A, FuseArgs F) {
+    constexpr int NT = 64 * NW;
+    static_assert(16 % NW == 0 || NW % 16 == 0, "query fragments a wave");
+    extern __shared__ __align__(16) float s_dyn[];          // [NW][ppw_pad][64] logits
+    __shared__ u32x4 s_q[16][64];
+    __shared__ int32_t s_base[NW * kMaxPpw];                // entry of a slot's first column
+    __shared__ FuseLds<NT> S;
+    const int t = blockIdx.y, chunk = blockIdx.x;
+    const int tid = threadIdx.x, ln = __lane_id(), r = ln & 15, g = ln >> 4;
+    const int wave = tid >> 6;
+    const int ppw_pad = F.ppw_pad;
+    const int64_t slot0 = ((int64_t)chunk * NW + wave) * A.ppw;
+    const int nslot = (int)max((int64_t)0, min((int64_t)A.ppw, A.n_slots - slot0));
+    const int braw = row_request(A.q, A.kv, t);
+    const int64_t nvis = n_visible(A.q, A.kv, t, braw);
+    const int b = braw < 0 ? 0 : braw;
+    const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
+    const uint8_t *pool = A.kv.pool[0];
+    int lp_l = -1, phys_l = kSlotEmpty;
+    if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
+    constexpr int QPW = NW >= 16 ? 1 : 16 / NW;             // query fragments a wave stages
+    u32x4 qf[QPW];
+    {
+        const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2;
+#pragma unroll
+        for (int f = 0; f < QPW; ++f) {
+            const int fi = wave * QPW + f;
+            if (fi < 16) qf[f] = q_frag_bf16<KEY_BF16>(qrow, fi >> 2, fi & 3, r, g);
+        }
+    }
+    float wv[16];
+    load_w(wv, A.q.w, A.q.w_bf16, t, g);
+    float (*res)[64] = (float (*)[64])(s_dyn + (int64_t)wave * ppw_pad * 64);
+
+    const uint32_t off = (uint32_t)(r * kRowBf16 + g * 16);
+    auto fetch = [&](TileBf16 &T, int x) {       // tile x: page x / 4, entry tile x % 4
+        const __amdgpu_buffer_rsrc_t rs =
+            page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 2), kPage * kRowBf16);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            T.b[kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + kk * 64, (x & 3) * 16 * kRowBf16, 0);
+    };
+    auto tile_logit = [&](const TileBf16 &T) {
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        const u32x4 *qs = &s_q[0][ln + z];
+        f32x4 acc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 bk = __builtin_bit_cast(bf16x8, T.b[kk]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, qs[(4 * m + kk) * 64]), bk, acc[m], 0, 0, 0);
+        }
+        return head_sum(acc, wv);
+    };
+
+    TileBf16 T[RING];
+#pragma unroll
+    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+#pragma unroll
+    for (int f = 0; f < QPW; ++f) {
+        const int fi = wave * QPW + f;
+        if (fi < 16) s_q[fi][ln] = qf[f];
+    }
+    for (int i = tid; i < kBins; i += NT) S.hist[i] = 0u;
+    if (tid == 0) {
+        S.n_out = 0u;
+        S.n_bnd = 0u;
+    }
+    if (ln < ppw_pad)
+        s_base[wave * ppw_pad + ln] = (int32_t)((F.cells ? slot0 + ln : (int64_t)lp_l) * kPage);
+    __syncthreads();
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x0 = 0; x0 < 4 * nslot; x0 += 4 * RING) {
+#pragma unroll
+        for (int u = 0; u < 4 * RING; ++u) {
+            fetch(T[(u + RING - 1) % RING], x0 + u + RING - 1);
+            tot[u & 3] = tile_logit(T[u % RING]);
+            if ((u & 3) == 3)
+                res[(x0 + u) >> 2][ln] = g == 0 ? tot[0] : g == 1 ? tot[1] : g == 2 ? tot[2] : tot[3];
+        }
+    }
+    if (A.out) {
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
+        store_wave_logits(A, orsrc, res, phys_l, lp_l, slot0, nslot, nvis, ln);
+    }
+    mark_candidates<NT>(F, res, ppw_pad, phys_l, lp_l, nslot, nvis, b, ln, wave, S);
+    __syncthreads();
+    const int64_t slot = (int64_t)t * F.n_chunks + chunk;
+    auto entry_of = [&](int j) { return s_base[j >> 6] + (j & 63); };
+    auto sel = [&](auto nv) {
+        chunk_select<NT, decltype(nv)::value>(s_dyn, (uint32_t)F.k, (uint32_t)F.cap, entry_of,
+                                              F.cval + slot * F.cap, F.cidx + slot * F.cap,
+                                              F.cnt + slot, F.cstat + slot, S);
+    };
+    // values a thread: NW ppw_pad 64 / NT = ppw_pad (a multiple of the ring, at most 16)
+    if (ppw_pad <= 4) sel(std::integral_constant<int, 4>());
+    else if (ppw_pad <= 8) sel(std::integral_constant<int, 8>());
+    else if (ppw_pad <= 12) sel(std::integral_constant<int, 12>());
+    else sel(std::integral_constant<int, 16>());
 }
 
 // ---------------------------------------------------------------- fp8 keys x bf16 queries
@@ -1123,6 +1684,28 @@ hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t 
         score_kernel<KEY_FP8, Q_FP8><<<grid, 256, 0, s>>>(a);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+FuseShape fuse_shape(int key_fmt, int q_fmt, int n_heads) {
+    if (key_fmt == KEY_BF16 && q_fmt == Q_BF16 && n_heads == kHeads)
+        return FuseShape{16, FM_BF16_RING ? FM_BF16_RING : 4};
+    return FuseShape{0, 1};                          // no fused kernel for this format
+}
+
+hipError_t launch_score_topk(const ScoreArgs &a, const FuseArgs &f, int key_fmt, int q_fmt,
+                             hipStream_t s) {
+    const dim3 grid((unsigned)f.n_chunks, (unsigned)a.q.T);
+    if (key_fmt == KEY_BF16 && q_fmt == Q_BF16 && a.q.n_heads == kHeads) {
+        constexpr int NW = 16;
+        score_topk_bf16_kernel<FM_BF16_RING ? FM_BF16_RING : 4, NW>
+            <<<grid, 64 * NW, (size_t)NW * f.ppw_pad * 64 * 4, s>>>(a, f);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    merge_chunks_kernel<1024, kFuseMaxCand / 1024><<<(unsigned)a.q.T, 1024, 0, s>>>(f);
     return hipGetLastError();
 }
 
