@@ -165,6 +165,32 @@ def test_mask_page_compaction_matches_gpu_mask(mask_small):
         assert np.array_equal(pl[b, :nz.size], nz) and np.all(pl[b, nz.size:] == -1)
 
 
+def test_mask_page_list_without_density(mask_small):
+    """Without page_density the fp8 kernel stages each page's count in page_list (when it is as
+    wide as the pages) and compaction turns it into the list in place; with a narrower list the
+    counts come from the mask bytes.  Both equal the outputs of a call with page_density."""
+    wl = mask_small
+    dw = dev(wl)
+    ref = G.resident_mask(dw)
+    B = wl.kv.B
+    ld = wl.kv.block_table.shape[1] * 64
+    n_pages = ld // 64
+    for width in (n_pages, n_pages + 3, 5):
+        mask = torch.empty((B, ld), dtype=torch.uint8, device="cuda")
+        cnt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        plist = torch.full((B, width), -7, dtype=torch.int32, device="cuda")
+        api.fm_resident_mask([dw.query(l) for l in range(3)], dw.kv(0, [0, 1, 2]),
+                             api.FM_UNION_MAX, 0.5, 0, 0, mask, ld, cnt, plist, width, None, None)
+        torch.cuda.synchronize()
+        assert torch.equal(mask, ref["mask"]), width
+        assert torch.equal(cnt, ref["page_count"]), width
+        want = ref["page_list"].cpu().numpy()
+        got = plist.cpu().numpy()
+        w = min(width, n_pages)
+        assert np.array_equal(got[:, :w], want[:, :w]), width
+        assert np.all(got[:, w:] == -1), width
+
+
 def test_mask_single_layer_and_short_mask_ld(mask_small):
     wl = mask_small
     dw = dev(wl)

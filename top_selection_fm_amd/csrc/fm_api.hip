@@ -656,10 +656,25 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
     a.mask_ld = mask_ld;
     a.union_score = union_score;
     a.n_pages = (mask_ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE;
+    // fp8 pools: the scoring kernel leaves each page's resident count in page_density (or, as
+    // scratch, in page_list when that is wide enough), so compaction reads one word a page
+    a.dens_out = nullptr;
+    a.dens_ld = 0;
+    if (kv->key_dtype == FM_FP8_E4M3_SCALED132) {
+        if (page_density) {
+            a.dens_out = page_density;
+            a.dens_ld = a.n_pages;
+        } else if (page_list && page_list_ld >= a.n_pages) {
+            a.dens_out = page_list;
+            a.dens_ld = page_list_ld;
+        }
+    }
     CHECK(launched(fm::launch_mask(a, key_fmt(kv->key_dtype), kv->B, st), "resident_mask"));
     fm::CompactArgs c;
     c.mask = mask;
     c.mask_ld = mask_ld;
+    c.dens_in = a.dens_out;
+    c.dens_ld = a.dens_ld;
     c.n_pages = a.n_pages;
     c.page_count = page_count;
     c.page_list = page_list;

@@ -82,11 +82,15 @@ struct MaskArgs {
     float *union_score;  // nullable
     int64_t n_pages;     // ceil(mask_ld / 64)
     int ppw;             // pages per wave (set by the launcher)
+    int32_t *dens_out;   // nullable: resident entries of every page, [B, dens_ld] (fp8 kernel)
+    int64_t dens_ld;
 };
 
 struct CompactArgs {
     const uint8_t *mask;
     int64_t mask_ld;
+    const int32_t *dens_in;  // nullable: page densities [B, dens_ld] instead of the mask bytes
+    int64_t dens_ld;
     int64_t n_pages;
     int32_t *page_count;
     int32_t *page_list;  // nullable

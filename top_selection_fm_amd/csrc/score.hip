@@ -1601,6 +1601,17 @@ void mask_f8_kernel(MaskArgs A) {
         if (A.union_score) A.union_score[(int64_t)b * A.mask_ld + s] = s < seq ? u : -INFINITY;
         return s < seq && (u >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
     };
+    if (A.dens_out) {
+        // the page flags of compaction: resident entries of each page, one ballot a page
+        for (int i = 0; i < np; ++i) {
+            const int e = i * kPage + ln;
+            const int64_t s = s0 + e;
+            const float u = s_u[wave][i][ln];
+            const bool d = e < nb && s < seq && (u >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
+            const uint64_t m = __ballot(d);
+            if (ln == 0) A.dens_out[(int64_t)b * A.dens_ld + page0 + i] = (int32_t)__popcll(m);
+        }
+    }
     if (nb % 16 == 0 && ((uintptr_t)(mrow + s0) % 16) == 0) {
         for (int c = ln; 16 * c < nb; c += 64) {
             u32x4 v;

@@ -780,7 +780,13 @@ __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
     uint32_t running = 0;
     for (int64_t base = 0; base < A.n_pages; base += RP) {
         const int np = (int)min((int64_t)RP, A.n_pages - base);
-        if (wide && (base + np) * kPage <= A.mask_ld) {
+        if (A.dens_in) {
+            // the scoring kernel's page densities (the list may be this same array: every
+            // density of the round is read before the barriers of the scan below, and list
+            // positions never pass the page they come from)
+            for (int p = tid; p < np; p += kRowThreads)
+                s_d[p] = (uint32_t)A.dens_in[(int64_t)b * A.dens_ld + base + p];
+        } else if (wide && (base + np) * kPage <= A.mask_ld) {
             uint4 x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -809,7 +815,8 @@ __global__ __launch_bounds__(kRowThreads) void compact_kernel(CompactArgs A) {
         for (int i = 0; i < PPT; ++i) {
             const int p = PPT * tid + i;
             dens[i] = p < np ? s_d[p] : 0u;
-            if (p < np && A.page_density) A.page_density[(int64_t)b * A.n_pages + base + p] = (int32_t)dens[i];
+            if (p < np && A.page_density && A.page_density != A.dens_in)
+                A.page_density[(int64_t)b * A.n_pages + base + p] = (int32_t)dens[i];
             cnt += dens[i] > 0 ? 1u : 0u;
         }
         uint32_t tot;
