@@ -203,3 +203,33 @@ def test_two_level_bf16_fused(shuffled):
             assert np.array_equal(got, want)
         else:   # ranked by cell, so ties may resolve differently; the cells map to valid entries
             assert got.size == sel.size
+
+
+@pytest.fixture(scope="module")
+def fp8_small():
+    return W.three_layer_mask_fp8(seed=3110, B=4, seq_len=64 * 70 + 29, ragged=True)
+
+
+@pytest.mark.parametrize("k", [512, 33, 1024])
+def test_fused_fp8_keys_equals_two_calls(fp8_small, k):
+    """fp8 keys with bf16 queries (the fp8 fused kernel), full rows: equal to the two calls."""
+    wl = W.Workload(fp8_small.name, fp8_small.kv, fp8_small.queries[:1])
+    dw = dev(wl)
+    i2, v2, _ = two_call(dw, k=k)
+    i1, v1, _ = G.index_topk(dw, k=k)
+    assert_same((i1, v1), (i2, v2), f"fp8 fused k={k}")
+    if k == 512:
+        oracle_parity(wl, i1, v1, "fp8 fused vs oracle")
+
+
+def test_fused_fp8_mode_a_mask(fp8_small):
+    """Mode A over fp8 keys: the union mask of three encoders as the resident set of a layer's
+    top-512, straight from fm_resident_mask's output."""
+    wl = W.Workload(fp8_small.name, fp8_small.kv, fp8_small.queries[:1])
+    dw3 = dev(fp8_small)
+    m = G.resident_mask(dw3)["mask"]
+    dw = dev(wl)
+    i2, v2, _ = two_call(dw, mask=m)
+    i1, v1, _ = G.index_topk(dw, mask=m)
+    assert_same((i1, v1), (i2, v2), "fp8 fused Mode A")
+    oracle_parity(wl, i1, v1, "fp8 fused Mode A vs oracle", mask=m.cpu().numpy())

@@ -182,7 +182,7 @@ fm_status run_score(const fm_query_desc *q, const fm_kv_desc *kv, const int32_t 
 // unfused path's logits and top-k workspace.
 size_t fused_region_bytes(int T) {
     return fm::align_up((size_t)T * fm::kFuseMaxChunks * 4, 256) +
-           fm::align_up((size_t)T * fm::kFuseMaxChunks * 8, 256) +
+           fm::align_up((size_t)T * fm::kFuseMaxChunks * 16, 256) +
            2 * fm::align_up((size_t)T * fm::kFuseMaxCand * 4, 256);
 }
 size_t unfused_region_bytes(int T, int64_t n) {
@@ -212,7 +212,9 @@ FusePlan fuse_plan(int T, int64_t n_slots, int k, int nw, int ring) {
         ppw = clamp_ppw((n_slots + (int64_t)nw * fm::kFuseMaxChunks - 1) / ((int64_t)nw * fm::kFuseMaxChunks));
         ch = chunks_of(ppw);
     }
-    if (ch > fm::kFuseMaxChunks || ch * k > fm::kFuseMaxCand) return p;
+    int k2 = 1;
+    while (k2 < k) k2 *= 2;                          // the chunk slots hold a power of two >= k
+    if (ch > fm::kFuseMaxChunks || ch * k2 > fm::kFuseMaxCand) return p;
     if ((int64_t)T * ch < kWgTarget / 2 && ppw > 2) return p;
     p.fused = true;
     p.ppw = (int)ppw;
@@ -247,17 +249,24 @@ fm_status score_select(const fm_query_desc *q, const fm_kv_desc *kv, const int32
         fm::FuseArgs f;
         f.k = k;
         f.n_chunks = p.n_chunks;
-        f.cap = std::max(k, fm::kFuseMaxCand / p.n_chunks);
+        // a chunk's candidate slots: a power of two (the merge finds a slot's chunk by a
+        // shift), at least k, together at most kFuseMaxCand
+        auto pow2_floor = [](int x) { int p = 1; while (2 * p <= x) p *= 2; return p; };
+        auto pow2_ceil = [](int x) { int p = 1; while (p < x) p *= 2; return p; };
+        f.cap = std::max(pow2_ceil(k), pow2_floor(fm::kFuseMaxCand / p.n_chunks));
         f.ppw_pad = p.ppw_pad;
         f.mask = mask;
         f.mask_ld = mask ? mask_ld : 0;
         f.cells = cells;
-        f.small_entries = (!res_pages || cells) && n_slots * FM_PAGE_SIZE <= 65536 ? 1 : 0;
+        // entries below 2^18 are ordered through the merge's bitmap: list positions (cells),
+        // or logical entries below the block table's width
+        const int64_t max_entry = (!res_pages || cells) ? n_slots * FM_PAGE_SIZE : kv->bt_ld * FM_PAGE_SIZE;
+        f.bit_words = max_entry <= (int64_t)1 << 18 ? (int)((max_entry + 2047) / 2048 * 64) : 0;
         uint8_t *w8 = (uint8_t *)ws;
         f.cnt = (int32_t *)w8;
         w8 += fm::align_up((size_t)q->T * fm::kFuseMaxChunks * 4, 256);
-        f.cstat = (float2 *)w8;
-        w8 += fm::align_up((size_t)q->T * fm::kFuseMaxChunks * 8, 256);
+        f.cstat = (float4 *)w8;
+        w8 += fm::align_up((size_t)q->T * fm::kFuseMaxChunks * 16, 256);
         f.cval = (float *)w8;
         w8 += fm::align_up((size_t)q->T * fm::kFuseMaxCand * 4, 256);
         f.cidx = (int32_t *)w8;

@@ -142,9 +142,11 @@ struct FuseArgs {
     const uint8_t *mask;         // Mode A: [rows of requests, mask_ld] by logical entry, or null
     int64_t mask_ld;
     int cells;                   // two-level: rank and emit reserve cells (list positions)
-    int small_entries;           // every emitted entry < 65,536 (bitmap ordering of the output)
+    int bit_words;               // entries below 32 bit_words (<= 8192 words, a multiple of 64)
+                                 // are ordered through a bitmap; 0: by counting
     int32_t *cnt;                // [T, n_chunks]: candidates each chunk kept
-    float2 *cstat;               // [T, n_chunks]: (smallest kept value, chunk maximum)
+    float4 *cstat;               // [T, n_chunks]: (bound of the kept values, chunk maximum,
+                                 //  bound of the chunk's ceil(k / n_chunks) largest, -)
     float *cval;                 // [T, n_chunks, cap]
     int32_t *cidx;               // [T, n_chunks, cap]
     int32_t *out_idx;            // [T, k]

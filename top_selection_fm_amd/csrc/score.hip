@@ -549,7 +549,7 @@ template <int NT>
 struct FuseLds {
     uint32_t hist[kBins];
     uint32_t sh[NT / 64 + 1];
-    uint32_t misc[2];
+    uint32_t misc[4];
     float shf[NT / 64];
     float shf2[NT / 64];
     uint32_t shc[NT / 64];
@@ -574,18 +574,19 @@ struct ChunkSrc {
 };
 
 // The bin holding the r-th largest of hist (r >= 1, r <= total): S.misc[0] = the bin,
-// S.misc[1] = the count in higher bins.  Wave w owns kBins / NW bins from the top, lane l
-// BPL of them; two barriers.
+// S.misc[1] = the count in higher bins; with r2 > 0 also the bin of the r2-th largest in
+// S.misc[2] (0 when r2 exceeds the total).  Wave w owns BPW bins from the top, lane l BPL of
+// them (bins below 0 hold nothing); two barriers.
 template <int NT, class Lds>
-__device__ void top_bin(uint32_t r, Lds &S) {
-    constexpr int NWv = NT / 64, BPW = kBins / NWv, BPL = BPW / 64;
-    static_assert(BPW % 64 == 0, "bins a lane");
+__device__ void top_bin(uint32_t r, Lds &S, uint32_t r2 = 0) {
+    constexpr int NWv = NT / 64;
+    constexpr int BPL = (kBins + NT - 1) / NT, BPW = 64 * BPL;
     const int w = threadIdx.x >> 6, ln = __lane_id();
     const int top = kBins - 1 - BPW * w - BPL * ln;      // this lane's bins: top, top - 1, ...
     uint32_t h[BPL], sum = 0;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
-        h[i] = S.hist[top - i];
+        h[i] = top - i >= 0 ? S.hist[top - i] : 0u;
         sum += h[i];
     }
     const uint32_t incl = wave_incl_scan<NT>(sum);
@@ -594,12 +595,14 @@ __device__ void top_bin(uint32_t r, Lds &S) {
     uint32_t above = 0;
     for (int v = 0; v < w; ++v) above += S.wsum[v];
     above += incl - sum;                                  // count in bins above this lane's
+    if (w == 0 && ln == 0 && r2) S.misc[2] = 0u;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
         if (above < r && r <= above + h[i]) {
             S.misc[0] = (uint32_t)(top - i);
             S.misc[1] = above;
         }
+        if (r2 && above < r2 && r2 <= above + h[i]) S.misc[2] = (uint32_t)(top - i);
         above += h[i];
     }
     __syncthreads();
@@ -609,14 +612,15 @@ __device__ void top_bin(uint32_t r, Lds &S) {
 // can be in the top-k: all of them when they fit in cap; else those of the value bins from
 // the top down to the bin holding the chunk's k-th largest, when they fit; else exactly the
 // chunk's top-k (boundary bin ranked by the full key, or the radix selection).  Writes them to
-// cval / cidx (any order), their number to *cnt_out and (a value at or below every kept one,
-// the chunk maximum) to *stat_out.  On entry: the per-wave candidate counts, minima and maxima
-// in S.shc / shf / shf2, S.hist zero, S.n_out = S.n_bnd = 0, followed by a barrier.
-// NV = n / NT values a thread (n a multiple of NT).
+// cval / cidx (any order), their number to *cnt_out and to *stat_out: x = a value at or below
+// every kept one, y = the chunk maximum, z = a value with at least `share` candidates at or
+// above it (-inf when unknown or fewer exist).  On entry: the per-wave candidate counts,
+// minima and maxima in S.shc / shf / shf2, S.hist zero, S.n_out = S.n_bnd = 0, followed by a
+// barrier.  NV = n / NT values a thread (n a multiple of NT).
 template <int NT, int NV, class EntryOf>
-__device__ void chunk_select(const float *vals, uint32_t k, uint32_t cap, EntryOf entry_of,
-                             float *cval, int32_t *cidx, int32_t *cnt_out, float2 *stat_out,
-                             FuseLds<NT> &S) {
+__device__ void chunk_select(const float *vals, uint32_t k, uint32_t cap, uint32_t share,
+                             EntryOf entry_of, float *cval, int32_t *cidx, int32_t *cnt_out,
+                             float4 *stat_out, FuseLds<NT> &S) {
     constexpr int NWv = NT / 64;
     constexpr int n = NV * NT;
     const int tid = threadIdx.x, ln = __lane_id();
@@ -664,7 +668,7 @@ __device__ void chunk_select(const float *vals, uint32_t k, uint32_t cap, EntryO
     };
     const float width = hi - lo;
     uint32_t kept;
-    float bound = lo;
+    float bound = lo, zshare = -INFINITY;
     if (total <= cap) {
         kept = total;
         emit_all([&](int u) { return v[u] > -INFINITY; });
@@ -678,11 +682,15 @@ __device__ void chunk_select(const float *vals, uint32_t k, uint32_t cap, EntryO
             for (int u = 0; u < NV; ++u)
                 if (v[u] > -INFINITY) atomicAdd(&S.hist[bins(v[u])], 1u);
             __syncthreads();
-            top_bin<NT>(k, S);
+            top_bin<NT>(k, S, share <= total ? share : 0u);
             const int bstar = (int)S.misc[0];
             const uint32_t above = S.misc[1], nb = S.hist[bstar];
-            // a value at or below every member of bins >= bstar: the lower edge of the bin below
-            if (!bins.flat && bstar > 0) bound = lo + (float)(bstar - 1) * (width / (float)kBins);
+            // a value at or below every member of bins >= b: the lower edge of the bin below
+            auto edge = [&](int b) {
+                return !bins.flat && b > 0 ? lo + (float)(b - 1) * (width / (float)kBins) : lo;
+            };
+            bound = edge(bstar);
+            if (share <= total) zshare = edge((int)S.misc[2]);
             if (above + nb <= cap) {
                 kept = above + nb;              // the bins from the top down to bstar, whole
                 emit_all([&](int u) { return v[u] > -INFINITY && bins(v[u]) >= bstar; });
@@ -737,7 +745,7 @@ __device__ void chunk_select(const float *vals, uint32_t k, uint32_t cap, EntryO
     }
     if (tid == 0) {
         *cnt_out = (int32_t)min(kept, cap);
-        *stat_out = make_float2(bound, hi);
+        *stat_out = make_float4(bound, hi, zshare, 0.f);
     }
 }
 
@@ -782,20 +790,21 @@ __device__ __forceinline__ void mark_candidates(const FuseArgs &F, float (*res)[
 }
 
 // LDS of the row merge
+constexpr int kMergeWords = 8192;         // output-order bitmap: entries below 2^18
 template <int NT>
 struct MergeLds {
     uint32_t hist[kBins];
-    uint32_t bits[kBins];                 // selected entries < 65,536, one bit each
-    uint32_t pref[kBins];                 // selected entries in lower words
+    uint32_t bits[kMergeWords];           // selected entries below 2^18, one bit each
+    uint32_t pref[kMergeWords];           // selected entries in lower words
     uint32_t sh[NT / 64 + 1];
     uint32_t wsum[NT / 64];
-    uint32_t misc[2];
+    uint32_t misc[4];
     float bnd_v[kBnd];                    // the boundary bin's candidates
     int32_t bnd_e[kBnd];
-    int32_t sel_e[FM_MAX_K];              // selected (entry, value), unordered
+    alignas(16) int32_t sel_e[FM_MAX_K];  // selected (entry, value), unordered
     float sel_v[FM_MAX_K];
     int32_t ccnt[kFuseMaxChunks];         // the chunks' kept counts and bounds
-    float2 cst[kFuseMaxChunks];
+    float4 cst[kFuseMaxChunks];
     uint32_t m, n_sel, n_bnd;
 };
 
@@ -815,22 +824,21 @@ struct RegSrc {
 
 // One workgroup per row: the row's top-k from its chunks' candidates, in ascending entry order.
 // Every thread reads its share of all candidate slots (and one chunk's count and bounds) in one
-// round of loads and keeps them in registers; candidates below the row's proven bound are
-// dropped, the rest binned over [bound, row maximum].  Then the boundary bin, the exact rank of
-// its entries, and the output order from a bitmap of the selected entries (entries below
-// 65,536) or from counts of smaller selected entries.
+// round of loads and keeps them in registers; candidates below the row's proven lower bound on
+// its k-th value are dropped, the rest binned over [bound, row maximum].  Then the boundary
+// bin, the exact rank of its entries, and the output order from a bitmap of the selected
+// entries (entries below 32 bit_words) or from counts of smaller selected entries.
 template <int NT, int SPT>
 __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
     __shared__ MergeLds<NT> S;
     const int t = blockIdx.x, tid = threadIdx.x, ln = __lane_id();
-    const int nc = F.n_chunks, cap = F.cap;
+    const int nc = F.n_chunks, cap = F.cap, cap_log2 = __builtin_ctz((unsigned)F.cap);
     const uint32_t k = (uint32_t)F.k;
     const int64_t row_c = (int64_t)t * nc;
     const int cand = nc * cap;
-    for (int i = tid; i < kBins; i += NT) {
-        S.hist[i] = 0u;
-        S.bits[i] = 0u;
-    }
+    const uint64_t lt = ln == 0 ? 0ull : (~0ull >> (64 - ln));
+    for (int i = tid; i < kBins; i += NT) S.hist[i] = 0u;
+    for (int i = tid; i < F.bit_words; i += NT) S.bits[i] = 0u;
     if (tid == 0) {
         S.m = 0u;
         S.n_sel = 0u;
@@ -854,16 +862,21 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
         }
     }
     __syncthreads();                                         // LDS cleared, counts staged
-    float lo = -INFINITY, hi = -INFINITY, lo_any = INFINITY;
+    // Lower bounds on the row's k-th value: a chunk that kept k candidates has k values at or
+    // above its x; and every chunk has ceil(k / chunks) values at or above its z, so together k
+    // at or above the smallest z.  Candidates below the larger bound cannot be selected.
+    float lo = -INFINITY, hi = -INFINITY, lo_any = INFINITY, zmin = INFINITY;
     for (int c = 0; c < nc; ++c) {
         const int cnt = S.ccnt[c];
-        const float2 st = S.cst[c];
-        if (cnt >= F.k) lo = fmaxf(lo, st.x);      // k candidates at or above st.x: a bound
+        const float4 st = S.cst[c];
+        if (cnt >= F.k) lo = fmaxf(lo, st.x);
+        zmin = fminf(zmin, st.z);
         if (cnt > 0) {
             hi = fmaxf(hi, st.y);
             lo_any = fminf(lo_any, st.x);
         }
     }
+    if (zmin < INFINITY) lo = fmaxf(lo, zmin);
     const float blo = lo > -INFINITY ? lo : lo_any;         // the bins' lower end
     const float width = hi - blo;
     bool radix = !(width < INFINITY) || !(hi >= blo);
@@ -874,8 +887,8 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
         const int i = u * NT + tid;
-        const int c = i / cap;
-        ok[u] = i < cand && (i - c * cap) < S.ccnt[c] && v[u] >= lo;
+        const int c = i >> cap_log2;                         // cap is a power of two
+        ok[u] = i < cand && (i & (cap - 1)) < S.ccnt[c] && v[u] >= lo;
         mine += ok[u] ? 1u : 0u;
         bn[u] = ok[u] && !radix ? bins(v[u]) : -1;
         if (bn[u] >= 0) atomicAdd(&S.hist[bn[u]], 1u);
@@ -885,18 +898,30 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
     if (ln == 0 && mine) atomicAdd(&S.m, mine);
     __syncthreads();
     const uint32_t m = S.m;
-    auto select = [&](float x, int32_t en) {
-        const uint32_t p = atomicAdd(&S.n_sel, 1u);
-        if (p < (uint32_t)FM_MAX_K) {
-            S.sel_e[p] = en;
-            S.sel_v[p] = x;
+    // append (x, en) where `take` holds, one slot reservation per wave (every lane calls it)
+    auto append = [&](bool take, float x, int32_t en, uint32_t *counter, float *xs, int32_t *es,
+                      uint32_t cap_n, bool sel) {
+        const uint64_t mk = __ballot(take);
+        if (!mk) return;
+        uint32_t b0 = 0;
+        if (ln == 0) b0 = atomicAdd(counter, (uint32_t)__popcll(mk));
+        b0 = __shfl(b0, 0);
+        if (take) {
+            const uint32_t p = b0 + (uint32_t)__popcll(mk & lt);
+            if (p < cap_n) {
+                es[p] = en;
+                xs[p] = x;
+            }
+            if (sel && (uint32_t)en < 32u * (uint32_t)F.bit_words)
+                atomicOr(&S.bits[en >> 5], 1u << (en & 31));
         }
-        if (F.small_entries && (uint32_t)en < 65536u) atomicOr(&S.bits[en >> 5], 1u << (en & 31));
+    };
+    auto select = [&](bool take, float x, int32_t en) {
+        append(take, x, en, &S.n_sel, S.sel_v, S.sel_e, (uint32_t)FM_MAX_K, true);
     };
     if (m <= k) {
 #pragma unroll
-        for (int u = 0; u < SPT; ++u)
-            if (ok[u]) select(v[u], e[u]);
+        for (int u = 0; u < SPT; ++u) select(ok[u], v[u], e[u]);
     } else {
         if (!radix) {
             top_bin<NT>(k, S);
@@ -905,20 +930,24 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
             if (nb <= (uint32_t)kBnd) {
 #pragma unroll
                 for (int u = 0; u < SPT; ++u) {
-                    if (bn[u] > bstar) {
-                        select(v[u], e[u]);
-                    } else if (bn[u] == bstar) {
-                        const uint32_t p = atomicAdd(&S.n_bnd, 1u);
-                        S.bnd_v[p] = v[u];
-                        S.bnd_e[p] = e[u];
-                    }
+                    select(bn[u] > bstar, v[u], e[u]);
+                    append(bn[u] == bstar, v[u], e[u], &S.n_bnd, S.bnd_v, S.bnd_e, (uint32_t)kBnd, false);
                 }
                 __syncthreads();
-                for (uint32_t a = tid; a < nb; a += NT) {
-                    const uint64_t ka = full_key(S.bnd_v[a], S.bnd_e[a]);
-                    uint32_t rank = 0;
-                    for (uint32_t c = 0; c < nb; ++c) rank += full_key(S.bnd_v[c], S.bnd_e[c]) > ka;
-                    if (rank < need) select(S.bnd_v[a], S.bnd_e[a]);
+                for (uint32_t a0 = 0; a0 < nb; a0 += NT) {
+                    const uint32_t a = a0 + tid;
+                    bool take = false;
+                    float x = 0.f;
+                    int32_t en = 0;
+                    if (a < nb) {
+                        x = S.bnd_v[a];
+                        en = S.bnd_e[a];
+                        const uint64_t ka = full_key(x, en);
+                        uint32_t rank = 0;
+                        for (uint32_t c = 0; c < nb; ++c) rank += full_key(S.bnd_v[c], S.bnd_e[c]) > ka;
+                        take = rank < need;
+                    }
+                    select(take, x, en);
                 }
             } else {
                 radix = true;
@@ -931,19 +960,24 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
             __syncthreads();
 #pragma unroll
             for (int u = 0; u < SPT; ++u)
-                if (ok[u] && (full_key(v[u], e[u]) & rule.M) >= rule.P) select(v[u], e[u]);
+                select(ok[u] && (full_key(v[u], e[u]) & rule.M) >= rule.P, v[u], e[u]);
         }
     }
     __syncthreads();
     const uint32_t cnt = min(S.n_sel, k);
     int32_t *oi = F.out_idx + (int64_t)t * F.k;
     float *ov = F.out_val ? F.out_val + (int64_t)t * F.k : nullptr;
-    if (F.small_entries) {
+    if (F.bit_words > 0) {
         // positions from the bitmap: prefix popcounts of the words, then within the word
-        constexpr int WPT = kBins / NT;
-        uint32_t c = 0;
+        constexpr int WPT = kMergeWords / NT;                // words a thread, at most
+        const int nw = F.bit_words;
+        uint32_t wd[WPT], c = 0;
 #pragma unroll
-        for (int i = 0; i < WPT; ++i) c += (uint32_t)__popc(S.bits[WPT * tid + i]);
+        for (int i = 0; i < WPT; ++i) {
+            const int w = WPT * tid + i;
+            wd[i] = w < nw ? S.bits[w] : 0u;
+            c += (uint32_t)__popc(wd[i]);
+        }
         const uint32_t incl = wave_incl_scan<NT>(c);
         if (ln == 63) S.wsum[tid >> 6] = incl;
         __syncthreads();
@@ -951,22 +985,34 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
         for (int w = 0; w < (tid >> 6); ++w) pre += S.wsum[w];
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
-            S.pref[WPT * tid + i] = pre;
-            pre += (uint32_t)__popc(S.bits[WPT * tid + i]);
+            const int w = WPT * tid + i;
+            if (w < nw) S.pref[w] = pre;
+            pre += (uint32_t)__popc(wd[i]);
         }
         __syncthreads();
         for (uint32_t i = tid; i < cnt; i += NT) {
             const int32_t en = S.sel_e[i];
-            const uint32_t w = ((uint32_t)en >> 5) & (kBins - 1);
+            const uint32_t w = ((uint32_t)en >> 5) & (kMergeWords - 1);
             const uint32_t pos = S.pref[w] + (uint32_t)__popc(S.bits[w] & ((1u << (en & 31)) - 1u));
             oi[pos] = en;
             if (ov) ov[pos] = S.sel_v[i];
         }
     } else {
+        // positions from counts of smaller selected entries (the list padded to a multiple of
+        // 16 with INT32_MAX, read four at a time)
+        const uint32_t cnt16 = (cnt + 15u) & ~15u;
+        for (uint32_t i = cnt + tid; i < cnt16; i += NT) S.sel_e[i] = 0x7fffffff;
+        __syncthreads();
         for (uint32_t i = tid; i < cnt; i += NT) {
             const int32_t en = S.sel_e[i];
             uint32_t pos = 0;
-            for (uint32_t c = 0; c < cnt; ++c) pos += S.sel_e[c] < en;
+            for (uint32_t c = 0; c < cnt16; c += 16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int4 x = *(const int4 *)&S.sel_e[c + 4 * q];
+                    pos += (x.x < en) + (x.y < en) + (x.z < en) + (x.w < en);
+                }
+            }
             oi[pos] = en;
             if (ov) ov[pos] = S.sel_v[i];
         }
@@ -988,7 +1034,11 @@ void score_topk_bf16_kernel(ScoreArgs A, FuseArgs F) {
     __shared__ u32x4 s_q[16][64];
     __shared__ int32_t s_base[NW * kMaxPpw];                // entry of a slot's first column
     __shared__ FuseLds<NT> S;
-    const int t = blockIdx.y, chunk = blockIdx.x;
+    // workgroup (chunk, row) = (id / T8, id % T8), T8 = T rounded up to 8: the workgroups go to
+    // the 8 XCDs in turn, so every chunk of row t runs on the XCD of the merge workgroup t
+    const int t8 = (int)(gridDim.x / (unsigned)F.n_chunks);
+    const int t = (int)(blockIdx.x % (unsigned)t8), chunk = (int)(blockIdx.x / (unsigned)t8);
+    if (t >= A.q.T) return;
     const int tid = threadIdx.x, ln = __lane_id(), r = ln & 15, g = ln >> 4;
     const int wave = tid >> 6;
     const int ppw_pad = F.ppw_pad;
@@ -1077,9 +1127,11 @@ void score_topk_bf16_kernel(ScoreArgs A, FuseArgs F) {
     const int64_t slot = (int64_t)t * F.n_chunks + chunk;
     auto entry_of = [&](int j) { return s_base[j >> 6] + (j & 63); };
     auto sel = [&](auto nv) {
-        chunk_select<NT, decltype(nv)::value>(s_dyn, (uint32_t)F.k, (uint32_t)F.cap, entry_of,
-                                              F.cval + slot * F.cap, F.cidx + slot * F.cap,
-                                              F.cnt + slot, F.cstat + slot, S);
+        chunk_select<NT, decltype(nv)::value>(s_dyn, (uint32_t)F.k, (uint32_t)F.cap,
+                                              (uint32_t)((F.k + F.n_chunks - 1) / F.n_chunks),
+                                              entry_of, F.cval + slot * F.cap,
+                                              F.cidx + slot * F.cap, F.cnt + slot,
+                                              F.cstat + slot, S);
     };
     // values a thread: NW ppw_pad 64 / NT = ppw_pad (a multiple of the ring, at most 16)
     if (ppw_pad <= 4) sel(std::integral_constant<int, 4>());
@@ -1366,6 +1418,75 @@ void score_f8_kernel(ScoreArgs A) {
         __syncthreads();
         score_f8_slots<RING>(A, Q, s_res[wave], t, ln, wave);
     }
+}
+
+// fp8 keys x bf16 queries, 64 heads (two-level scoring, Mode A over fp8 pools), NW waves a
+// workgroup scoring one row's chunk: the 32-entry tile stream of score_f8_kernel with the
+// query fragments staged in LDS for the workgroup, logits into LDS, then the fused selection.
+template <int RING, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FM_F8_WPE)))
+void score_topk_f8_kernel(ScoreArgs A, FuseArgs F) {
+    constexpr int NT = 64 * NW;
+    extern __shared__ __align__(16) float s_dyn[];          // [NW][ppw_pad][64] logits
+    __shared__ u32x4 s_qa[16 * 64];                          // fragment (m, s) at (8 m + s) 64
+    __shared__ int32_t s_base[NW * kMaxPpw];
+    __shared__ FuseLds<NT> S;
+    // workgroup (chunk, row) = (id / T8, id % T8), T8 = T rounded up to 8: the workgroups go to
+    // the 8 XCDs in turn, so every chunk of row t runs on the XCD of the merge workgroup t
+    const int t8 = (int)(gridDim.x / (unsigned)F.n_chunks);
+    const int t = (int)(blockIdx.x % (unsigned)t8), chunk = (int)(blockIdx.x / (unsigned)t8);
+    if (t >= A.q.T) return;
+    const int tid = threadIdx.x, ln = __lane_id();
+    const int wave = tid >> 6;
+    const int ppw_pad = F.ppw_pad;
+    const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * 2;
+    for (int fi = wave; fi < 16; fi += NW) s_qa[fi * 64 + ln] = qa_frag(qrow, fi >> 3, fi & 7, ln);
+    QF8Lds Q;
+    Q.a = s_qa;
+    load_w32(Q.w, A.q.w, A.q.w_bf16, t, ln);
+    const int64_t slot0 = ((int64_t)chunk * NW + wave) * A.ppw;
+    const int nslot = (int)max((int64_t)0, min((int64_t)A.ppw, A.n_slots - slot0));
+    const int braw = row_request(A.q, A.kv, t);
+    const int64_t nvis = n_visible(A.q, A.kv, t, braw);
+    const int b = braw < 0 ? 0 : braw;
+    const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
+    const uint8_t *pool = A.kv.pool[0];
+    int lp_l = -1, phys_l = kSlotEmpty;
+    if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
+    for (int i = tid; i < kBins; i += NT) S.hist[i] = 0u;
+    if (tid == 0) {
+        S.n_out = 0u;
+        S.n_bnd = 0u;
+    }
+    if (ln < ppw_pad)
+        s_base[wave * ppw_pad + ln] = (int32_t)((F.cells ? slot0 + ln : (int64_t)lp_l) * kPage);
+    __syncthreads();
+    float (*res)[64] = (float (*)[64])(s_dyn + (int64_t)wave * ppw_pad * 64);
+    auto fetch = [&](TileF8 &T, int x) {
+        load_tile_f8(T, page_rsrc(pool, __builtin_amdgcn_readlane(phys_l, x >> 1), kPage * kRowFp8), x & 1, ln);
+    };
+    auto take = [&](float t0, float t1, int i) { res[i][ln] = (ln >> 5) ? t1 : t0; };
+    stream_tiles_f8<RING>(nslot, Q, fetch, take);
+    if (A.out) {
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
+        store_wave_logits(A, orsrc, res, phys_l, lp_l, slot0, nslot, nvis, ln);
+    }
+    mark_candidates<NT>(F, res, ppw_pad, phys_l, lp_l, nslot, nvis, b, ln, wave, S);
+    __syncthreads();
+    const int64_t slot = (int64_t)t * F.n_chunks + chunk;
+    auto entry_of = [&](int j) { return s_base[j >> 6] + (j & 63); };
+    auto sel = [&](auto nv) {
+        chunk_select<NT, decltype(nv)::value>(s_dyn, (uint32_t)F.k, (uint32_t)F.cap,
+                                              (uint32_t)((F.k + F.n_chunks - 1) / F.n_chunks),
+                                              entry_of, F.cval + slot * F.cap,
+                                              F.cidx + slot * F.cap, F.cnt + slot,
+                                              F.cstat + slot, S);
+    };
+    if (ppw_pad <= 4) sel(std::integral_constant<int, 4>());
+    else if (ppw_pad <= 8) sel(std::integral_constant<int, 8>());
+    else if (ppw_pad <= 12) sel(std::integral_constant<int, 12>());
+    else sel(std::integral_constant<int, 16>());
 }
 
 // ---------------------------------------------------------------- fp32 path (VALU)
@@ -1698,19 +1819,26 @@ hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t 
     return hipGetLastError();
 }
 
+#ifndef FM_FUSE_F8_WAVES
+#define FM_FUSE_F8_WAVES 12   // fp8 fused scoring: waves a workgroup (3 a SIMD)
+#endif
 FuseShape fuse_shape(int key_fmt, int q_fmt, int n_heads) {
     if (key_fmt == KEY_BF16 && q_fmt == Q_BF16 && n_heads == kHeads)
         return FuseShape{16, FM_BF16_RING ? FM_BF16_RING : 4};
+    if (key_fmt == KEY_FP8 && q_fmt == Q_BF16 && n_heads == kHeads) return FuseShape{FM_FUSE_F8_WAVES, 4};
     return FuseShape{0, 1};                          // no fused kernel for this format
 }
 
 hipError_t launch_score_topk(const ScoreArgs &a, const FuseArgs &f, int key_fmt, int q_fmt,
                              hipStream_t s) {
-    const dim3 grid((unsigned)f.n_chunks, (unsigned)a.q.T);
+    const unsigned grid = (unsigned)(f.n_chunks * ((a.q.T + 7) / 8 * 8));
     if (key_fmt == KEY_BF16 && q_fmt == Q_BF16 && a.q.n_heads == kHeads) {
         constexpr int NW = 16;
         score_topk_bf16_kernel<FM_BF16_RING ? FM_BF16_RING : 4, NW>
             <<<grid, 64 * NW, (size_t)NW * f.ppw_pad * 64 * 4, s>>>(a, f);
+    } else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16 && a.q.n_heads == kHeads) {
+        constexpr int NW = FM_FUSE_F8_WAVES;
+        score_topk_f8_kernel<FM_F8_RING, NW><<<grid, 64 * NW, (size_t)NW * f.ppw_pad * 64 * 4, s>>>(a, f);
     } else {
         return hipErrorInvalidValue;
     }
