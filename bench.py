@@ -4,23 +4,25 @@
 
 Headline step: decode scoring of 32 requests x 65,536 bf16 compressed entries (256K-token
 context at 4:1 compression, 1,024 pages of 64 per request, pages scattered by a permuted block
-table, 10% planted hot pages), i.e. fm_index_logits followed by fm_topk512 (k = 512) on the
-same stream.  The pool is replicated on the device and the replicas rotate from step to step
+table, 10% planted hot pages) with their top-512, in one fm_index_topk call (scoring and
+selection fused); the two-call path (fm_index_logits, then fm_topk512) is timed beside it.
+The pool is replicated on the device and the replicas rotate from step to step
 so that no step finds its keys in the 256 MB Infinity Cache.  The metric is compressed entries
 scored and selected per second over the whole call; every input is resident in HBM before the
 timed region starts.
 
-The timed step is that pair of calls captured once into a HIP graph per pool replica and
+The timed step is that call captured once into a HIP graph per pool replica and
 replayed (the pages run this step inside a CUDA graph), so host launch latency stays out of the
 step; the eager rate of the same calls is reported beside it.  Per-kernel durations come from
 HIP events recorded on the stream the kernels run on, in the eager timed loop.  The
-roofline object reports the scoring kernel against HBM peak (8 TB/s) with its algorithmic
-bytes (keys once, q/w once, block table, logits written) over its average launch duration:
-HIP events around the same scoring calls launched back to back (events around each single
-launch, which add a few microseconds, are reported beside it as bracketed_ms).  Secondary entries measure the other
+roofline object reports the fused call against HBM peak (8 TB/s) with its algorithmic bytes
+(keys once, q/w once, block table, indices written) over its average duration: HIP events
+around the same calls launched back to back (events around each single call, which add a
+few microseconds, are reported beside it as bracketed_ms).  Secondary entries measure the other
 workloads (one call a step, timed over the calls back to back): the three-layer fp8 mask with 64 heads and with the retriever's 128,
-two-level fp8 scoring over 384 resident pages, causal fp8 prefill, the Mode A selection of
-21 layers x 8 requests over 262,144 masked candidates, the retriever's query encoder at
+two-level fp8 scoring over 384 resident pages, causal fp8 prefill, Mode A end to end (the
+three-encoder mask, then the masked top-512 of 21 layers x 8 requests over 262,144 entries,
+every layer scoring its own fp8 pool), the retriever's query encoder at
 decode and prefill batch sizes, and golden-label construction from 128 tokens x 21 layers x
 65,536 selector scores.  cpu_baseline times the fp64 oracle on a bounded sample of
 the headline workload on the host cores.
@@ -298,33 +300,72 @@ def run_prefill(torch, api, W, steps, warmup):
                 mfma_frac=flops / (per["score"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS)
 
 
-def run_mode_a(torch, api, W, steps, warmup, B=8, layers=21, n=262144, replicas=2):
-    """Mode A selection: full-history top-512 of every c4 layer of B requests (one row per
-    (request, layer), 262,144 candidates) under the request's resident mask, all layers in one
-    call through row_req.  The logits are synthetic (standard normal, replicas rotated); the
-    mask is page-clustered with about 12% of the pages resident."""
-    T = B * layers
-    g = torch.Generator(device="cuda:0").manual_seed(1006)
-    logits = [torch.randn((T, n), device="cuda:0", generator=g) for _ in range(replicas)]
-    pages = (torch.rand((B, n // 64), device="cuda:0", generator=g) < 0.12).to(torch.uint8)
-    mask = pages.repeat_interleave(64, dim=1).contiguous()
-    row_req = torch.arange(B, dtype=torch.int32, device="cuda:0").repeat_interleave(layers)
-    idx = torch.empty((T, 512), dtype=torch.int32, device="cuda:0")
-    nb = api.fm_workspace_bytes(api.FM_OP_TOPK, T, n)
-    ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+def run_mode_a(torch, api, W, steps, warmup):
+    """Mode A end to end over 8 requests x 262,144 entries: the Level-1 mask of three fp8
+    encoders (fm_resident_mask), then one fm_index_topk call over the 21 layers x 8 requests
+    rows, each layer scoring its own fp8 pool (row_pool) under its request's mask (row_req).
+    The scoring alone (fm_index_logits over the same rows) is timed beside it, so the
+    selection's share is level2 - scoring."""
+    wl = W.mode_a_fp8()
+    dw = api.DeviceWorkload(wl, "cuda:0")
+    B, n_enc = wl.kv.B, 3
+    q2w = wl.queries[n_enc]
+    T = q2w.T
+    ld = wl.kv.block_table.shape[1] * 64
+    n_pages = ld // 64
+    dev = "cuda:0"
+    mask = torch.empty((B, ld), dtype=torch.uint8, device=dev)
+    cnt = torch.empty(B, dtype=torch.int32, device=dev)
+    dens = torch.empty((B, n_pages), dtype=torch.int32, device=dev)
+    idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
+    nb = api.fm_workspace_bytes(api.FM_OP_INDEX_TOPK, T, ld)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    q_enc = [dw.query(l) for l in range(n_enc)]
+    kv_enc, kv_all = dw.kv(0, list(range(n_enc))), dw.kv()
+    q2 = dw.query(n_enc)
+
+    def level1(s):
+        api.fm_resident_mask(q_enc, kv_enc, api.FM_UNION_MAX, 0.5, 0, 0, mask, ld, cnt, None, 0,
+                             dens)
+
+    def level2(s):
+        api.fm_index_topk(q2, kv_all, mask, ld, 512, idx, None, None, 0, ws, nb)
 
     def step(s, tm):
         if tm: tm.mark(s, 0)
-        api.fm_topk512(logits[s % replicas], n, T, None, mask, n, row_req, 512, idx, None, ws, nb)
+        level1(s)
         if tm: tm.mark(s, 1)
+        level2(s)
+        if tm: tm.mark(s, 2)
 
-    wall, per = timed(torch, ["topk"], step, steps, warmup)
-    ms = per["topk"]
-    alg = T * n * 4 + B * n + T * 4 + T * 512 * 4     # logits + each mask once + row map + out
-    return dict(workload=f"mode_a_topk512_b{B}_l{layers}_n{n}_masked", rows=T,
-                candidates=T * n, ms=ms, candidates_per_s=T * n / (ms * 1e-3),
-                hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                alg_bytes=alg, note="selection only; logits synthetic")
+    wall, per = timed(torch, ["level1", "level2"], step, steps, warmup)
+    l1_ms = b2b_ms(torch, level1, steps, warmup)
+    l2_ms = b2b_ms(torch, level2, steps, warmup)
+    del ws
+    logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
+    score_ms = b2b_ms(torch, lambda s: api.fm_index_logits(q2, kv_all, logits, ld), steps, warmup)
+    del logits
+    n_vis = int(wl.kv.seq_lens.sum())                  # per layer
+    resident = int(mask.sum().item())
+    l1_alg = n_enc * n_vis * 132 + n_enc * B * (64 * 128 * 2 + 64 * 2) + \
+        wl.kv.block_table.nbytes + B * ld + B * n_pages * 4
+    # Level 2: every layer's keys once, queries and weights, the block table and the mask once
+    # per row, the output
+    l2_alg = (T // B) * n_vis * 132 + T * (64 * 128 * 2 + 64 * 2) + (T // B) * (
+        wl.kv.block_table.nbytes + B * ld) + T * 512 * 4
+    step_ms = wall / steps * 1e3
+    return dict(workload=f"mode_a_fp8_b{B}_l{T // B}_s{ld}_top512", rows=T,
+                candidates=T * n_vis, resident_entries_per_request=resident / B,
+                ms_per_step=step_ms, entries_per_s=T * n_vis / (step_ms * 1e-3),
+                level1_ms=l1_ms, level2_ms=l2_ms, level2_scoring_only_ms=score_ms,
+                level2_selection_share=max(0.0, 1 - score_ms / l2_ms),
+                level1_share=l1_ms / (l1_ms + l2_ms),
+                bracketed_ms=per,
+                level1_hbm_frac=l1_alg / (l1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                level2_hbm_frac=l2_alg / (l2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                alg_bytes=dict(level1=l1_alg, level2=l2_alg),
+                note="Level-1 mask (3 encoders) + masked top-512 of 21 layers, each over "
+                     "its own fp8 pool, in one call")
 
 
 def run_labels(torch, api, W, steps, warmup):

@@ -46,7 +46,8 @@ extern "C" {
 #endif
 
 #define FM_VERSION 100          /* 1.0.0 */
-#define FM_MAX_LAYERS 4
+#define FM_MAX_LAYERS 4          /* encoders of one fm_resident_mask call */
+#define FM_MAX_POOLS 32          /* key layers of one fm_kv_desc */
 #define FM_PAGE_SIZE 64         /* compressed entries per page */
 #define FM_HEAD_DIM 128
 #define FM_N_HEADS 64           /* indexer heads of every (q, key) dtype pair */
@@ -84,11 +85,12 @@ typedef enum {
  * [n_phys_pages][64][row] where row is 512 B (FM_F32), 256 B (FM_BF16) or 132 B
  * (FM_FP8_E4M3_SCALED132: bytes 0..127 E4M3FN codes, bytes 128..131 little-endian float32
  * scale; key = code * scale -- README "compressed_k format").  All layers share the block
- * table (each encoder scores its own keys at the same entry positions).  Pool bases must be
- * 16-byte aligned.  Requires bt_ld >= ceil(max_seq_len / 64).
+ * table (each encoder scores its own keys at the same entry positions).  Pools 0 .. n_pools-1
+ * must be non-NULL and 16-byte aligned (1 <= n_pools <= FM_MAX_POOLS).  Requires
+ * bt_ld >= ceil(max_seq_len / 64).
  */
 typedef struct {
-    const void *pool[FM_MAX_LAYERS];
+    const void *pool[FM_MAX_POOLS];
     int n_pools;
     fm_dtype key_dtype;         /* FM_F32, FM_BF16 or FM_FP8_E4M3_SCALED132 */
     int page_size;              /* must be 64 */
@@ -105,7 +107,14 @@ typedef struct {
  * Query rows of one encoder / layer.  q is [T, n_heads, head_dim] row-major; w is
  * [T, n_heads] and already includes any weight scale (the library applies none).
  * row_req maps a row to its request (NULL: row t is request t when T == B, or request 0
- * when B == 1).  With q_pos, row t may only use entries s < floor(q_pos[t] / compress_ratio)
+ * when B == 1).  row_pool maps a row to the key layer it scores (NULL: every row scores
+ * pool[0]), so one call can score the rows of many layers, each over its own pool, e.g. the
+ * 21 compressed-attention layers of Mode A (paper summary, section 6; README "Two-level
+ * recall": Level 2 runs in every c4 layer).  A row whose row_req or row_pool value is out of
+ * range ([0, B), [0, n_pools)) has no visible entries.  row_pool is honoured by
+ * fm_index_logits, fm_index_topk and the fm_score_resident calls; fm_resident_mask requires
+ * it NULL (encoder l always scores pool[l]).
+ * With q_pos, row t may only use entries s < floor(q_pos[t] / compress_ratio)
  * (DeepSeek-V4 CSA page, section 10: a token position maps to compressed block
  * floor(pos / ratio)); without it, every s < seq_len is visible.
  * Supported (q_dtype, key_dtype): (F32, F32), (BF16, BF16), (BF16, SCALED132),
@@ -126,20 +135,22 @@ typedef struct {
     const int32_t *row_req;     /* [T] or NULL */
     const int32_t *q_pos;       /* [T] or NULL */
     int compress_ratio;         /* > 0; used only with q_pos (4 for CSA) */
+    const int32_t *row_pool;    /* [T] or NULL: key layer of row t */
 } fm_query_desc;
 
 /*
  * Index logits.  For every row t and 0 <= s < ld:
  *   logits[t * ld + s] = L[t,s] (float32) if s < n_vis(t), else -inf,
  * where n_vis(t) = seq_len[b] (cut to floor(q_pos / ratio) with positions).  Entries of an
- * unmapped page score NaN.  Key layer 0 of `kv` is used.
+ * unmapped page score NaN.  Row t scores key layer row_pool[t] (layer 0 without row_pool).
  * Accuracy: bf16 / fp8 inputs are decoded exactly and products accumulate in float32.  With
- * FP8_E4M3 q over SCALED132 keys, one request and T >= 16 (prefill), each ReLU(q_h . k) term
- * is rounded to f16 on a per-row power-of-two scale set by the row's largest query code: the
- * term's error is at most 2^-11 relative, or 2^(E-15) code-product units absolute with E the
- * largest E4M3 exponent field among the row's codes (one unit for codes that fill the E4M3
- * range, 2^-10 units for codes below 1, as with q_scale = 1).  Key codes are assumed to use
- * the E4M3 range (scale = absmax / 448, as the compressed_k quantiser produces them).
+ * FP8_E4M3 q over SCALED132 keys, one request, T >= 16 and no row_pool (prefill), each
+ * ReLU(q_h . k) term is rounded to f16 on a per-row power-of-two scale set by the row's
+ * largest query code: the term's error is at most 2^-11 relative, or 2^(E-15) code-product
+ * units absolute with E the largest E4M3 exponent field among the row's codes (one unit for
+ * codes that fill the E4M3 range, 2^-10 units for codes below 1, as with q_scale = 1).  Key
+ * codes are assumed to use the E4M3 range (scale = absmax / 448, as the compressed_k
+ * quantiser produces them).
  */
 fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *logits,
                           int64_t ld, void *stream);

@@ -120,6 +120,11 @@ def logits_call(q, kv, ld=1000):
     (lambda q, kv: setattr(kv, "B", 0), api.FM_ERR_INVALID_ARG),
     (lambda q, kv: setattr(kv, "max_seq_len", -1), api.FM_ERR_INVALID_ARG),
     (lambda q, kv: setattr(kv, "n_phys_pages", 0), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "n_pools", 0), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "n_pools", api.FM_MAX_POOLS + 1), api.FM_ERR_INVALID_ARG),
+    (lambda q, kv: setattr(kv, "n_pools", 2), api.FM_ERR_INVALID_ARG),   # pool[1] NULL
+    (lambda q, kv: (setattr(kv, "n_pools", 2), kv.pool.__setitem__(1, FAKE + 4)),
+     api.FM_ERR_INVALID_ARG),                                              # pool[1] misaligned
     (lambda q, kv: setattr(kv, "block_table", None), api.FM_ERR_INVALID_ARG),
     (lambda q, kv: setattr(q, "T", -1), api.FM_ERR_INVALID_ARG),
     (lambda q, kv: setattr(q, "T", 3), api.FM_ERR_INVALID_ARG),      # T != B, no row_req
@@ -269,6 +274,51 @@ def test_resident_mask_validation():
     for q in wide_bf16:
         q.n_heads = 128
     assert mask_call(wide_bf16, good_kv("bf16", n_pools=3)) == api.FM_ERR_UNSUPPORTED
+    pooled = [good_q() for _ in range(3)]
+    pooled[2].row_pool = FAKE                   # encoder l always scores pool[l]
+    assert mask_call(pooled, kv) == api.FM_ERR_INVALID_ARG
+
+
+def test_descriptor_layout_matches_header(tmp_path):
+    """The ctypes descriptors have the C structs' size and field offsets (compiled with gcc
+    against include/fm.h)."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    structs = {"fm_kv_desc": api.KvDesc, "fm_query_desc": api.QueryDesc,
+               "fm_encoder_desc": api.EncoderDesc}
+    lines = []
+    for cname, cls in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f in cls._fields_:
+            lines.append(f'printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"fm.h\"\n"
+                   "int main(void) {\n" + "\n".join(lines) + "\nreturn 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True,
+                             text=True).stdout.split("\n"):
+        if ln:
+            a, b, c = ln.split()
+            got[(a, b)] = int(c)
+    for cname, cls in structs.items():
+        assert got[(cname, "sizeof")] == C.sizeof(cls), cname
+        for f in cls._fields_:
+            assert got[(cname, f[0])] == getattr(cls, f[0]).offset, (cname, f[0])
+
+
+def test_max_pools_pass_validation():
+    """FM_MAX_POOLS pools validate (a T = 0 call returns before any launch); one more does not."""
+    assert api.FM_MAX_POOLS == 32
+    kv = good_kv(n_pools=api.FM_MAX_POOLS)
+    api.fm_index_logits(good_q(T=0), kv, FAKE, 1000, 0)
+    assert api.fm_last_error() == ""
+    kv.n_pools = api.FM_MAX_POOLS + 1
+    assert logits_call(good_q(T=0), kv)[0] == api.FM_ERR_INVALID_ARG
 
 
 def good_enc(**kw):

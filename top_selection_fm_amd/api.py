@@ -21,6 +21,7 @@ FM_F32, FM_BF16, FM_FP8_E4M3, FM_FP8_E4M3_SCALED132 = range(4)
 FM_UNION_MAX, FM_UNION_MEAN = 0, 1
 FM_OP_INDEX_LOGITS, FM_OP_TOPK, FM_OP_RESIDENT_MASK, FM_OP_SCORE_RESIDENT, FM_OP_INDEX_TOPK = range(5)
 FM_MAX_LAYERS = 4
+FM_MAX_POOLS = 32
 PAGE = 64
 
 KEY_DTYPES = {"f32": FM_F32, "bf16": FM_BF16, "fp8x132": FM_FP8_E4M3_SCALED132}
@@ -39,7 +40,7 @@ class FmError(RuntimeError):
 
 
 class KvDesc(C.Structure):
-    _fields_ = [("pool", C.c_void_p * FM_MAX_LAYERS), ("n_pools", C.c_int),
+    _fields_ = [("pool", C.c_void_p * FM_MAX_POOLS), ("n_pools", C.c_int),
                 ("key_dtype", C.c_int), ("page_size", C.c_int), ("head_dim", C.c_int),
                 ("block_table", C.c_void_p), ("bt_ld", C.c_int64), ("seq_lens", C.c_void_p),
                 ("B", C.c_int), ("max_seq_len", C.c_int64), ("n_phys_pages", C.c_int64)]
@@ -48,7 +49,8 @@ class KvDesc(C.Structure):
 class QueryDesc(C.Structure):
     _fields_ = [("q", C.c_void_p), ("q_dtype", C.c_int), ("q_scale", C.c_void_p),
                 ("w", C.c_void_p), ("w_dtype", C.c_int), ("T", C.c_int), ("n_heads", C.c_int),
-                ("row_req", C.c_void_p), ("q_pos", C.c_void_p), ("compress_ratio", C.c_int)]
+                ("row_req", C.c_void_p), ("q_pos", C.c_void_p), ("compress_ratio", C.c_int),
+                ("row_pool", C.c_void_p)]
 
 
 class EncoderDesc(C.Structure):
@@ -146,7 +148,7 @@ def kv_desc(pools, key_dtype: str, block_table, seq_lens, max_seq_len: int,
 
 
 def query_desc(q, q_dtype: str, w, w_dtype: str, q_scale=None, row_req=None, q_pos=None,
-               compress_ratio: int = 4) -> QueryDesc:
+               compress_ratio: int = 4, row_pool=None) -> QueryDesc:
     d = QueryDesc()
     d.q = _ptr(q)
     d.q_dtype = Q_DTYPES[q_dtype]
@@ -158,6 +160,7 @@ def query_desc(q, q_dtype: str, w, w_dtype: str, q_scale=None, row_req=None, q_p
     d.row_req = _ptr(row_req)
     d.q_pos = _ptr(q_pos)
     d.compress_ratio = compress_ratio
+    d.row_pool = _ptr(row_pool)
     return d
 
 
@@ -305,6 +308,8 @@ class DeviceWorkload:
                 row_req=None if qq.row_req is None else _dev(qq.row_req.astype(np.int32),
                                                              self.device),
                 q_pos=None if qq.q_pos is None else _dev(qq.q_pos.astype(np.int32), self.device),
+                row_pool=None if qq.row_pool is None else _dev(qq.row_pool.astype(np.int32),
+                                                               self.device),
                 q_dtype=qq.q_dtype, w_dtype=qq.w_dtype, ratio=qq.compress_ratio))
         self.resident_pages = None if wl.resident_pages is None else _dev(
             wl.resident_pages.astype(np.int32), self.device)
@@ -321,4 +326,5 @@ class DeviceWorkload:
     def query(self, layer: int = 0) -> QueryDesc:
         d = self.q[layer]
         return query_desc(d["q"], d["q_dtype"], d["w"], d["w_dtype"], q_scale=d["q_scale"],
-                          row_req=d["row_req"], q_pos=d["q_pos"], compress_ratio=d["ratio"])
+                          row_req=d["row_req"], q_pos=d["q_pos"], compress_ratio=d["ratio"],
+                          row_pool=d["row_pool"])

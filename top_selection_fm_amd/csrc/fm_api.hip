@@ -67,9 +67,9 @@ fm_status check_kv(const fm_kv_desc *kv, int n_pools_needed) {
                 kv->key_dtype == FM_FP8_E4M3_SCALED132,
             FM_ERR_UNSUPPORTED, "key dtype %d", (int)kv->key_dtype);
     REQUIRE(kv->B >= 1, FM_ERR_INVALID_ARG, "B = %d", kv->B);
-    REQUIRE(kv->n_pools >= n_pools_needed && kv->n_pools <= FM_MAX_LAYERS, FM_ERR_INVALID_ARG,
-            "n_pools = %d, need %d..%d", kv->n_pools, n_pools_needed, FM_MAX_LAYERS);
-    for (int l = 0; l < n_pools_needed; ++l) {
+    REQUIRE(kv->n_pools >= n_pools_needed && kv->n_pools <= FM_MAX_POOLS, FM_ERR_INVALID_ARG,
+            "n_pools = %d, need %d..%d", kv->n_pools, n_pools_needed, FM_MAX_POOLS);
+    for (int l = 0; l < kv->n_pools; ++l) {
         REQUIRE(kv->pool[l], FM_ERR_INVALID_ARG, "pool[%d] is NULL", l);
         REQUIRE(aligned(kv->pool[l], 16), FM_ERR_INVALID_ARG, "pool[%d] not 16-byte aligned", l);
     }
@@ -124,13 +124,15 @@ fm::QArgs make_q(const fm_query_desc *q, const fm_kv_desc *kv) {
     a.b_is_zero = (!q->row_req && kv->B == 1) ? 1 : 0;
     a.q_pos = q->q_pos;
     a.ratio = q->compress_ratio >= 1 ? q->compress_ratio : 1;
+    a.row_pool = q->row_pool;
     return a;
 }
 
 fm::KvArgs make_kv(const fm_kv_desc *kv) {
     fm::KvArgs a;
-    for (int l = 0; l < FM_MAX_LAYERS; ++l)
+    for (int l = 0; l < FM_MAX_POOLS; ++l)
         a.pool[l] = l < kv->n_pools ? (const uint8_t *)kv->pool[l] : nullptr;
+    a.n_pools = kv->n_pools;
     a.bt = kv->block_table;
     a.bt_ld = kv->bt_ld;
     a.seq_lens = kv->seq_lens;
@@ -233,7 +235,8 @@ fm_status score_select(const fm_query_desc *q, const fm_kv_desc *kv, const int32
     const int kf = key_fmt(kv->key_dtype);
     const int qf = q->q_dtype == FM_FP8_E4M3 ? fm::Q_FP8 : q->q_dtype == FM_BF16 ? fm::Q_BF16 : fm::Q_F32;
     const fm::FuseShape fs = fm::fuse_shape(kf, qf, q->n_heads);
-    const bool prefill = q->q_dtype == FM_FP8_E4M3 && kv->B == 1 && q->T >= 16 && !res_pages;
+    const bool prefill = q->q_dtype == FM_FP8_E4M3 && kv->B == 1 && q->T >= 16 && !res_pages &&
+                         !q->row_pool;
     const FusePlan p = prefill ? FusePlan{false, 0, 0, 0} : fuse_plan(q->T, n_slots, k, fs.waves, fs.round);
     if (p.fused) {
         fm::ScoreArgs a;
@@ -484,7 +487,7 @@ fm_status fm_index_logits(const fm_query_desc *q, const fm_kv_desc *kv, float *l
     REQUIRE(aligned(logits, 4), FM_ERR_INVALID_ARG, "logits not 4-byte aligned");
     if (q->T == 0) return ok();
     const int64_t n_pages = (ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE;
-    if (q->q_dtype == FM_FP8_E4M3 && kv->B == 1 && q->T >= 16) {
+    if (q->q_dtype == FM_FP8_E4M3 && kv->B == 1 && q->T >= 16 && !q->row_pool) {
         // many rows over one request's keys (prefill): tiled for key reuse across rows
         fm::PrefillArgs a;
         a.q = make_q(q, kv);
@@ -630,6 +633,8 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
     REQUIRE(q_layers, FM_ERR_INVALID_ARG, "q_layers is NULL");
     for (int l = 0; l < n_layers; ++l) {
         CHECK(check_q(&q_layers[l], kv, "q_layers[l]"));
+        REQUIRE(!q_layers[l].row_pool, FM_ERR_INVALID_ARG,
+                "q_layers[%d].row_pool must be NULL (encoder l scores pool[l])", l);
         REQUIRE(q_layers[l].T == kv->B, FM_ERR_INVALID_ARG,
                 "q_layers[%d].T = %d, must equal B = %d (one row per request)", l,
                 q_layers[l].T, kv->B);

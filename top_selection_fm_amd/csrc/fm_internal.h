@@ -32,10 +32,12 @@ struct QArgs {
     int b_is_zero;          // row_req null and B == 1: every row is request 0
     const int32_t *q_pos;   // [T] or null
     int ratio;
+    const int32_t *row_pool; // [T] or null: key layer of row t (null: layer 0)
 };
 
 struct KvArgs {
-    const uint8_t *pool[FM_MAX_LAYERS];
+    const uint8_t *pool[FM_MAX_POOLS];
+    int n_pools;
     const int32_t *bt;
     int64_t bt_ld;
     const int32_t *seq_lens;

@@ -84,10 +84,21 @@ constexpr int kMaskPpw = FM_MASK_MAXPPW;   // pages per wave of the fp8 mask ker
 
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// request of row t; -1 when row_req points outside [0, B)
+// request of row t; -1 when row_req points outside [0, B) or row_pool outside [0, n_pools)
 __device__ __forceinline__ int row_request(const QArgs &q, const KvArgs &kv, int t) {
     const int b = q.row_req ? q.row_req[t] : (q.b_is_zero ? 0 : t);
+    if (q.row_pool) {
+        const int l = q.row_pool[t];
+        if (l < 0 || l >= kv.n_pools) return -1;
+    }
     return (b >= 0 && b < kv.B) ? b : -1;
+}
+
+// key pool of row t (rows are wave-uniform); pool 0 for a row that row_request rejects
+__device__ __forceinline__ const uint8_t *row_pool(const QArgs &q, const KvArgs &kv, int t) {
+    if (!q.row_pool) return kv.pool[0];
+    const int l = __builtin_amdgcn_readfirstlane(q.row_pool[t]);
+    return kv.pool[(l >= 0 && l < kv.n_pools) ? l : 0];
 }
 
 // entries row t may use (0 for a row whose request is out of range)
@@ -404,7 +415,7 @@ void score_kernel(ScoreArgs A) {
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
-    const uint8_t *pool = A.kv.pool[0];
+    const uint8_t *pool = row_pool(A.q, A.kv, t);
     const uint8_t *qrow = (const uint8_t *)A.q.q + (int64_t)t * kHeads * kDim * (QF == Q_FP8 ? 1 : 2);
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
@@ -459,7 +470,7 @@ void score_bf16_ring_kernel(ScoreArgs A) {
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
-    const uint8_t *pool = A.kv.pool[0];
+    const uint8_t *pool = row_pool(A.q, A.kv, t);
     int lp_l = -1, phys_l = kSlotEmpty;
     if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
     u32x4 qf[4];
@@ -1048,7 +1059,7 @@ void score_topk_bf16_kernel(ScoreArgs A, FuseArgs F) {
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
-    const uint8_t *pool = A.kv.pool[0];
+    const uint8_t *pool = row_pool(A.q, A.kv, t);
     int lp_l = -1, phys_l = kSlotEmpty;
     if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
     constexpr int QPW = NW >= 16 ? 1 : 16 / NW;             // query fragments a wave stages
@@ -1381,7 +1392,7 @@ __device__ __forceinline__ void score_f8_slots(const ScoreArgs &A, const QF &Q, 
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
-    const uint8_t *pool = A.kv.pool[0];
+    const uint8_t *pool = row_pool(A.q, A.kv, t);
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(A.out + (int64_t)t * A.out_ld), (short)0, (int)(A.out_ld * 4), 0x00020000);
     int lp_l = -1, phys_l = kSlotEmpty;
@@ -1450,7 +1461,7 @@ void score_topk_f8_kernel(ScoreArgs A, FuseArgs F) {
     const int64_t nvis = n_visible(A.q, A.kv, t, braw);
     const int b = braw < 0 ? 0 : braw;
     const int64_t nres = (A.res_pages && braw >= 0) ? A.n_res[b] : 0;
-    const uint8_t *pool = A.kv.pool[0];
+    const uint8_t *pool = row_pool(A.q, A.kv, t);
     int lp_l = -1, phys_l = kSlotEmpty;
     if (ln < nslot) phys_l = resolve_slot(A, b, nvis, nres, slot0 + ln, lp_l);
     for (int i = tid; i < kBins; i += NT) S.hist[i] = 0u;
@@ -1514,7 +1525,8 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs A) {
     const int64_t s = (int64_t)lp * kPage + col % kPage;
     float v;
     if (phys >= 0 && s < nvis) {
-        const float *k = (const float *)A.kv.pool[0] + ((int64_t)phys * kPage + col % kPage) * kDim;
+        const float *k = (const float *)row_pool(A.q, A.kv, t) +
+                         ((int64_t)phys * kPage + col % kPage) * kDim;
         float kr[kDim];
 #pragma unroll
         for (int d = 0; d < kDim; ++d) kr[d] = k[d];

@@ -119,6 +119,7 @@ class Queries:
     row_req: np.ndarray | None = None   # int32 [T]; None: row t is request t
     q_pos: np.ndarray | None = None     # int32 [T] absolute token positions; None: no causal cut
     compress_ratio: int = 4
+    row_pool: np.ndarray | None = None  # int32 [T] key layer of row t; None: layer 0
 
     @property
     def T(self) -> int:
@@ -268,6 +269,38 @@ def three_layer_mask_fp8(seed: int = 1003, B: int = 8, seq_len: int = 262144,
     return Workload(f"three_layer_mask_fp8_b{B}_s{seq_len}", kv, queries,
                     meta=dict(hot_pages=hot, shared_keys=shared_keys,
                               entries=int(seq_lens.sum())))
+
+
+def mode_a_fp8(seed: int = 1009, B: int = 8, seq_len: int = 262144, n_layers: int = 21,
+               ragged: bool = False) -> Workload:
+    """Mode A: a Level-1 mask from three encoders, then Level-2 rows of n_layers layers.
+
+    pools[0..2] and queries[0..2] are three_layer_mask_fp8(seed, B, seq_len) (the encoders
+    that decide residency).  pools[3 + l] is layer l's own fp8 key pool: encoder pool l mod 3
+    with its physical pages permuted by a seeded permutation, so each layer holds different
+    keys at every entry (no hot structure is planted for Level 2).  queries[3] holds the
+    n_layers * B Level-2 rows, layer-major: row l*B + b has row_req b and row_pool 3 + l;
+    q ~ N(0, 1/sqrt(128)) and w ~ N(0.05, 0.125) per head, as in decode_bf16.
+    """
+    base = three_layer_mask_fp8(seed, B=B, seq_len=seq_len, ragged=ragged)
+    rng = make_rng(seed + 7919)
+    kv = base.kv
+    pools = list(kv.pools)
+    for l in range(n_layers):
+        perm = rng.permutation(kv.n_phys_pages)
+        pool = pools[l % 3][perm]
+        _clear_tail(pool, kv.block_table, kv.seq_lens)
+        pools.append(pool)
+    T = n_layers * B
+    q32 = _normal(rng, (T, HEADS, DIM), std=1.0 / np.sqrt(DIM))
+    w32 = _normal(rng, (T, HEADS), mean=0.05, std=0.125)
+    rows = np.arange(T, dtype=np.int32)
+    level2 = Queries(bf16_bits(q32), "bf16", bf16_bits(w32), "bf16", row_req=rows % B,
+                     row_pool=3 + rows // B)
+    meta = dict(base.meta, n_layers=n_layers, level2_rows=T)
+    return Workload(f"mode_a_fp8_b{B}_l{n_layers}_s{seq_len}",
+                    KeyPool(pools, "fp8x132", kv.block_table, kv.seq_lens),
+                    list(base.queries) + [level2], meta=meta)
 
 
 def two_level_resident_fp8(seed: int = 1004, B: int = 30, seq_len: int = 262144,
