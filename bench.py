@@ -1,6 +1,11 @@
 """Benchmark of the compressed-key indexer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--no-cpu-baseline]
+                    [--only NAME] [--copy-calibration]
+
+--only NAME runs one secondary workload alone and prints its line (for profiler runs of one
+kernel); --copy-calibration runs plain 1 GiB device copies (the reference for scaling the
+profiler's FETCH_SIZE / WRITE_SIZE counters).
 
 Headline step: decode scoring of 32 requests x 65,536 bf16 compressed entries (256K-token
 context at 4:1 compression, 1,024 pages of 64 per request, pages scattered by a permuted block
@@ -19,7 +24,8 @@ roofline object reports the fused call against HBM peak (8 TB/s) with its algori
 (keys once, q/w once, block table, indices written) over its average duration: HIP events
 around the same calls launched back to back (events around each single call, which add a
 few microseconds, are reported beside it as bracketed_ms).  Secondary entries measure the other
-workloads (one call a step, timed over the calls back to back): the three-layer fp8 mask with 64 heads and with the retriever's 128,
+workloads (one call a step, timed over the calls back to back): the three-layer fp8 mask with
+64 heads, with one pool shared by the three encoders, and with the retriever's 128 heads,
 two-level fp8 scoring over 384 resident pages, causal fp8 prefill, Mode A end to end (the
 three-encoder mask, then the masked top-512 of 21 layers x 8 requests over 262,144 entries,
 every layer scoring its own fp8 pool), the retriever's query encoder at
@@ -44,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CPU_BASELINES = True         # oracle timings beside each secondary line (off: --no-cpu-baseline)
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 FLOP_PER_PAIR = 2 * 64 * 128
@@ -212,8 +219,11 @@ def run_decode(torch, api, W, steps, warmup, replicas=3):
                         / 1e9 / HBM_PEAK_GBS))
 
 
-def run_mask(torch, api, W, steps, warmup, replicas=2, heads=64):
-    wl = W.three_layer_mask_fp8(heads=heads)
+def run_mask(torch, api, W, steps, warmup, replicas=2, heads=64, shared=False):
+    """Level-1 mask of three encoders over 8 x 262,144 fp8 entries.  shared: the three
+    encoders score one pool (passed three times), so each key is read once for all of them
+    and the call is bounded by bf16 MFMA rather than HBM."""
+    wl = W.three_layer_mask_fp8(heads=heads, shared_keys=shared)
     dw = api.DeviceWorkload(wl, "cuda:0", pool_copies=replicas)
     B = wl.kv.B
     ld = wl.kv.block_table.shape[1] * 64
@@ -222,7 +232,11 @@ def run_mask(torch, api, W, steps, warmup, replicas=2, heads=64):
     cnt = torch.empty(B, dtype=torch.int32, device="cuda:0")
     plist = torch.empty((B, n_pages), dtype=torch.int32, device="cuda:0")
     qs = [dw.query(l) for l in range(3)]
-    kvs = [dw.kv(r) for r in range(replicas)]
+    if shared:
+        kvs = [api.kv_desc([dw.replicas[r][0]] * 3, "fp8x132", dw.block_table, dw.seq_lens,
+                           dw.max_seq_len) for r in range(replicas)]
+    else:
+        kvs = [dw.kv(r) for r in range(replicas)]
 
     def step(s, tm):
         if tm: tm.mark(s, 0)
@@ -232,15 +246,23 @@ def run_mask(torch, api, W, steps, warmup, replicas=2, heads=64):
 
     wall, per = timed(torch, ["mask+compact"], step, steps, warmup)
     entries = int(wl.kv.seq_lens.sum())
-    alg = 3 * entries * 132 + 3 * B * (heads * 128 * 2 + heads * 2) + wl.kv.block_table.nbytes + \
-        B * ld + B * n_pages * 4
+    cpu = None
+    if CPU_BASELINES and heads == 64 and not shared:
+        import oracle
+        dt, cores, _ = cpu_time(lambda: oracle.resident_mask(wl))
+        cpu = dict(value=entries / dt, unit="entries/s", cores=cores, kind="oracle",
+                   sample=f"whole workload (3 encoders x {entries} entries, fp64), {dt:.1f} s")
+    alg = (1 if shared else 3) * entries * 132 + 3 * B * (heads * 128 * 2 + heads * 2) + \
+        wl.kv.block_table.nbytes + B * ld + B * n_pages * 4
     flops = 3 * entries * 2 * heads * 128
     sec = per["mask+compact"] * 1e-3
-    return dict(workload=wl.name + ("" if heads == 64 else f"_h{heads}"), entries=entries,
+    return dict(workload=wl.name + ("" if heads == 64 else f"_h{heads}") +
+                ("_shared_keys" if shared else ""), entries=entries,
+                bound="bf16 mfma" if shared else "hbm",
                 layers=3, heads=heads, ms=per["mask+compact"], entries_per_s=entries / sec,
                 hbm_gbs=alg / sec / 1e9, hbm_frac=alg / sec / 1e9 / HBM_PEAK_GBS,
                 alg_bytes=alg, mfma_tflops=flops / sec / 1e12,
-                bf16_mfma_frac=flops / sec / 1e12 / BF16_PEAK_TFLOPS, resident_pages_mean=None)
+                bf16_mfma_frac=flops / sec / 1e12 / BF16_PEAK_TFLOPS, cpu_baseline=cpu)
 
 
 def run_two_level(torch, api, W, steps, warmup, replicas=12):
@@ -262,12 +284,19 @@ def run_two_level(torch, api, W, steps, warmup, replicas=12):
 
     wall, per = timed(torch, ["score_resident"], step, steps, warmup)
     entries = int(wl.n_resident.sum()) * 64
+    cpu = None
+    if CPU_BASELINES:
+        import oracle
+        dt, cores, _ = cpu_time(lambda: oracle.score_resident(wl))
+        cpu = dict(value=entries / dt, unit="entries/s", cores=cores, kind="oracle",
+                   sample=f"whole workload ({entries} resident entries, fp64 + top-512), "
+                          f"{dt:.2f} s")
     alg = entries * 132 + T * (64 * 128 * 2 + 64 * 2) + wl.resident_pages.nbytes + \
         int(wl.n_resident.sum()) * 4 + T * 512 * 4
     ms = per["score_resident"]
     return dict(workload=wl.name, entries=entries, ms=ms, entries_per_s=entries / (ms * 1e-3),
                 hbm_gbs=alg / (ms * 1e-3) / 1e9, hbm_frac=alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                alg_bytes=alg, note="score + top-512 in one call (two kernels)")
+                alg_bytes=alg, note="score + top-512 in one call (two kernels)", cpu_baseline=cpu)
 
 
 def run_prefill(torch, api, W, steps, warmup):
@@ -293,11 +322,26 @@ def run_prefill(torch, api, W, steps, warmup):
 
     wall, per = timed(torch, ["score", "topk"], step, steps, warmup)
     pairs = int(sum(min(ld, p // 4) for p in wl.queries[0].q_pos.tolist()))
+    cpu = None
+    if CPU_BASELINES:
+        import oracle
+        rows = np.arange(0, T, 16, dtype=np.int32)          # every 16th row: 1/16 of the pairs
+        sub = int(sum(min(ld, int(wl.queries[0].q_pos[r]) // 4) for r in rows))
+
+        def run():
+            oracle.topk_rows(oracle.logits(wl, rows=rows))
+
+        dt, cores, _ = cpu_time(run)
+        cpu = dict(value=sub / dt, unit="pairs/s", cores=cores, kind="oracle",
+                   sample=f"{rows.size} of {T} rows (every 16th; {sub} of {pairs} visible "
+                          f"pairs, fp64 logits + top-512) in {dt:.1f} s; whole workload "
+                          f"scaled linearly: {dt * pairs / sub:.0f} s")
     flops = pairs * FLOP_PER_PAIR
     return dict(workload=wl.name, visible_pairs=pairs, score_ms=per["score"],
                 topk_ms=per["topk"], pairs_per_s=pairs / ((per["score"] + per["topk"]) * 1e-3),
                 mfma_tflops=flops / (per["score"] * 1e-3) / 1e12,
-                mfma_frac=flops / (per["score"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS)
+                mfma_frac=flops / (per["score"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+                cpu_baseline=cpu)
 
 
 def run_mode_a(torch, api, W, steps, warmup):
@@ -459,6 +503,38 @@ def cpu_baseline(wl, budget_s=12.0):
                        f"({done_entries} entries, fp64 logits + top-512), {dt:.1f} s")
 
 
+def cpu_c1_single_thread(W, budget_s=1.0):
+    """The 4,096-entry fp32 single-query workload: fp64 logits + top-512 on one thread."""
+    import oracle
+
+    wl = W.tiny_single_query()
+    n0 = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.topk_rows(oracle.logits(wl))
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(n0)
+    n = int(wl.kv.seq_lens.sum())
+    return dict(value=n * reps / dt, unit="entries/s", cores=1, kind="oracle",
+                sample=f"{reps} passes over the whole workload ({n} entries), {dt:.2f} s",
+                ms_per_pass=dt / reps * 1e3)
+
+
+def cpu_time(fn):
+    import oracle
+
+    oracle.lib()
+    t0 = time.perf_counter()
+    out = fn()
+    return time.perf_counter() - t0, oracle.num_threads(), out
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_(0, 255)
@@ -487,6 +563,7 @@ def main():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--only", default=None)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -503,6 +580,19 @@ def main():
     api.lib()
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    global CPU_BASELINES
+    CPU_BASELINES = not args.no_cpu_baseline
+    secondaries = {
+        "mask": run_mask, "mask_shared_keys": lambda *a: run_mask(*a, shared=True),
+        "mask_h128": lambda *a: run_mask(*a, heads=128),   # the retriever's head count
+        "two_level": run_two_level, "prefill": run_prefill, "mode_a": run_mode_a,
+        "encoder": run_encoder, "labels": run_labels}
+    if args.only:
+        if args.only not in secondaries:
+            sys.exit(f"--only: one of {sorted(secondaries)}")
+        print(json.dumps(secondaries[args.only](torch, api, W, args.steps, args.warmup)),
+              flush=True)
         return
 
     log("headline: decode bf16 B=32 x 65536 ...")
@@ -546,10 +636,7 @@ def main():
     }
     if not args.headline_only:
         sec = []
-        run_mask_h128 = lambda *a: run_mask(*a, heads=128)   # the retriever's head count
-        for name, fn in (("mask", run_mask), ("mask_h128", run_mask_h128), ("two_level", run_two_level),
-                         ("prefill", run_prefill), ("mode_a", run_mode_a),
-                         ("encoder", run_encoder), ("labels", run_labels)):
+        for name, fn in secondaries.items():
             log(f"secondary: {name} ...")
             try:
                 sec.append(fn(torch, api, W, max(5, args.steps // 2), 2))
@@ -560,6 +647,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(wl)
+        line["cpu_baseline_single_thread_tiny"] = cpu_c1_single_thread(W)
     print(json.dumps(line), flush=True)
 
 

@@ -112,7 +112,9 @@ def densest_pages(density, kmax, n_pages=None):
 
 
 def resident_mask(dw, mode=api.FM_UNION_MAX, threshold=0.5, n_sink=0, n_recent=0,
-                  mask_ld=None, layers=None, with_union=True):
+                  mask_ld=None, layers=None, with_union=True, kv=None):
+    """fm_resident_mask over the workload's layers (kv: another key descriptor, e.g. one pool
+    passed for every layer)."""
     layers = list(range(len(dw.wl.queries))) if layers is None else layers
     B = dw.wl.kv.B
     mask_ld = dw.wl.kv.block_table.shape[1] * 64 if mask_ld is None else mask_ld
@@ -124,7 +126,8 @@ def resident_mask(dw, mode=api.FM_UNION_MAX, threshold=0.5, n_sink=0, n_recent=0
                page_density=torch.empty((B, n_pages), dtype=torch.int32, device=dev),
                union=torch.empty((B, mask_ld), dtype=torch.float32, device=dev)
                if with_union else None)
-    api.fm_resident_mask([dw.query(l) for l in layers], dw.kv(0, layers), mode, threshold,
+    api.fm_resident_mask([dw.query(l) for l in layers], dw.kv(0, layers) if kv is None else kv,
+                         mode, threshold,
                          n_sink, n_recent, out["mask"], mask_ld, out["page_count"],
                          out["page_list"], n_pages, out["page_density"], out["union"])
     return out

@@ -670,6 +670,14 @@ fm_status fm_resident_mask(const fm_query_desc *q_layers, int n_layers, const fm
     a.mask_ld = mask_ld;
     a.union_score = union_score;
     a.n_pages = (mask_ld + FM_PAGE_SIZE - 1) / FM_PAGE_SIZE;
+    // one pool passed for every encoder (fp8 keys, bf16 queries of 64 heads): read it once
+    a.shared_keys = 0;
+    if (n_layers >= 2 && kv->key_dtype == FM_FP8_E4M3_SCALED132 &&
+        q_layers[0].q_dtype == FM_BF16 && q_layers[0].n_heads == FM_N_HEADS) {
+        a.shared_keys = 1;
+        for (int l = 1; l < n_layers; ++l)
+            if (kv->pool[l] != kv->pool[0]) a.shared_keys = 0;
+    }
     // fp8 pools: the scoring kernel leaves each page's resident count in page_density (or, as
     // scratch, in page_list when that is wide enough), so compaction reads one word a page
     a.dens_out = nullptr;

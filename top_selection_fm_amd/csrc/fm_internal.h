@@ -86,6 +86,7 @@ struct MaskArgs {
     int ppw;             // pages per wave (set by the launcher)
     int32_t *dens_out;   // nullable: resident entries of every page, [B, dens_ld] (fp8 kernel)
     int64_t dens_ld;
+    int shared_keys;     // every layer's pool is the same array (fp8, 64 heads): read it once
 };
 
 struct CompactArgs {

@@ -65,6 +65,18 @@
 #ifndef FM_MASK_F8
 #define FM_MASK_F8 1   // fp8 mask: layers-per-wave kernel (0: one wave per layer)
 #endif
+#ifndef FM_SHARED_AHEAD
+#define FM_SHARED_AHEAD 3  // fp8 mask over one shared pool: rounds a wave's tile loads run ahead
+#endif
+#ifndef FM_SHARED_WPE
+#define FM_SHARED_WPE 2    // fp8 mask over one shared pool: waves per SIMD the registers are sized for
+#endif
+#ifndef FM_SHARED_PPW
+#define FM_SHARED_PPW 8    // fp8 mask over one shared pool: pages a workgroup, at most
+#endif
+#ifndef FM_SHARED_WG
+#define FM_SHARED_WG 512   // fp8 mask over one shared pool: workgroups to spread the pages over
+#endif
 
 namespace fm {
 namespace {
@@ -524,7 +536,10 @@ void score_bf16_ring_kernel(ScoreArgs A) {
     // tiles 0 .. 4 nslot - 1 in order; slots past nslot are empty (zero-size loads)
     TileBf16 T[RING];
 #pragma unroll
-    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+    for (int v = 0; v < RING - 1; ++v) {
+        fetch(T[v], v);
+        __builtin_amdgcn_sched_barrier(0);     // tiles issue in ring order, as the loop refills them
+    }
 #pragma unroll
     for (int f = 0; f < 4; ++f) s_q[wave * 4 + f][ln] = qf[f];
     __syncthreads();
@@ -1104,7 +1119,10 @@ void score_topk_bf16_kernel(ScoreArgs A, FuseArgs F) {
 
     TileBf16 T[RING];
 #pragma unroll
-    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+    for (int v = 0; v < RING - 1; ++v) {
+        fetch(T[v], v);
+        __builtin_amdgcn_sched_barrier(0);     // tiles issue in ring order, as the loop refills them
+    }
 #pragma unroll
     for (int f = 0; f < QPW; ++f) {
         const int fi = wave * QPW + f;
@@ -1366,7 +1384,10 @@ __device__ __forceinline__ void stream_tiles_f8(int n, const QF &Q, Fetch fetch,
     static_assert(RING % 2 == 0, "the ring holds whole pages");
     TileF8 T[RING];
 #pragma unroll
-    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+    for (int v = 0; v < RING - 1; ++v) {
+        fetch(T[v], v);
+        __builtin_amdgcn_sched_barrier(0);     // tiles issue in ring order, as the loop refills them
+    }
     float t0 = 0.f;
     for (int x0 = 0; x0 < 2 * n; x0 += 2 * RING) {
 #pragma unroll
@@ -1638,7 +1659,10 @@ __device__ __forceinline__ void stream_tiles_rows(int n, const QF &Q, uint8_t *b
     const int ln = __lane_id();
     TileF8 T[RING];
 #pragma unroll
-    for (int v = 0; v < RING - 1; ++v) fetch(T[v], v);
+    for (int v = 0; v < RING - 1; ++v) {
+        fetch(T[v], v);
+        __builtin_amdgcn_sched_barrier(0);     // tiles issue in ring order, as the loop refills them
+    }
     float t0 = 0.f, sc = 1.f;
     for (int x0 = 0; x0 < 2 * n; x0 += 2 * RING) {
 #pragma unroll
@@ -1711,6 +1735,9 @@ void mask_f8_kernel(MaskArgs A) {
         if constexpr (MT == 2) {
             QF8Reg Q;
             Q.init(qrow, A.q[l].w, A.q[l].w_bf16, b, ln);
+            // the query loads complete before the tile ring starts, so that the stream's waits
+            // count ring loads only (otherwise each pass of its loop waits for every load)
+            __builtin_amdgcn_s_waitcnt(0);
             stream_tiles_rows<RING>(np, Q, s_tile[wave], fetch, take);
         } else {
             __shared__ u32x4 s_qa[8 * MT * 64];
@@ -1759,6 +1786,158 @@ void mask_f8_kernel(MaskArgs A) {
         }
     } else {
         for (int e = ln; e < nb; e += 64) mrow[s0 + e] = decide(e) ? 1 : 0;
+    }
+}
+
+// The union over NL encoders that all score one pool (the pools are the same array), fp8 keys,
+// bf16 queries, 64 heads.  A workgroup of NL waves streams up to FM_SHARED_PPW pages of request
+// blockIdx.y, and each key tile leaves HBM once for all encoders: in round r wave w loads tile
+// NL r + w (coalesced rows, FM_SHARED_AHEAD rounds ahead in registers) and writes it to the
+// workgroup's LDS (double-buffered by round); after the round's barrier every wave scores all NL
+// tiles of the round with its own encoder's query operands and head weights (wave l = encoder
+// l, held in registers).  Each logit is the same float the per-layer kernel computes, and the
+// union is formed in the same layer order, so the result equals mask_f8_kernel's.
+template <int NL>
+__global__ __launch_bounds__(64 * NL) __attribute__((amdgpu_waves_per_eu(FM_SHARED_WPE)))
+void mask_f8_shared_kernel(MaskArgs A) {
+    constexpr int D = FM_SHARED_AHEAD;
+    constexpr int PPW = FM_SHARED_PPW;
+    constexpr int NT = 64 * NL;
+    __shared__ float s_l[NL][PPW][kPage];                                   // logits, then union
+    __shared__ float s_sc[PPW][kPage];                                      // entry scales
+    __shared__ __attribute__((aligned(16))) uint8_t s_t[2][NL][32 * kTileLdsRow];   // tiles
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x, ln = __lane_id();
+    const int l = __builtin_amdgcn_readfirstlane(tid >> 6);                // this wave's encoder
+    const int64_t page0 = (int64_t)blockIdx.x * A.ppw;
+    const int np = (int)max((int64_t)0, min((int64_t)A.ppw, A.n_pages - page0));
+    const int64_t seq = A.kv.seq_lens[b];
+    int phys_l = kSlotInvisible;            // lane i: page page0 + i (as in mask_f8_kernel)
+    if (ln < np) {
+        const int64_t lp = page0 + ln;
+        if (lp * kPage >= seq) phys_l = kSlotInvisible;
+        else if (lp >= A.kv.bt_ld) phys_l = kSlotUnmapped;
+        else {
+            const int p = A.kv.bt[(int64_t)b * A.kv.bt_ld + lp];
+            phys_l = (p < 0 || p >= A.kv.n_phys) ? kSlotUnmapped : p;
+        }
+    }
+    const uint8_t *pool = A.kv.pool[0];
+    // tile x of the workgroup's pages (past the last page: a zero-size load), as load_tile_rows
+    // loads it, except that every tile issues the scale load (the second half's through a
+    // zero-size descriptor): the same number of loads per tile keeps the loop's waits exact
+    auto fetch = [&](TileF8 &T, int x) {
+        const int phys = __builtin_amdgcn_readlane(phys_l, x >> 1);
+        const __amdgpu_buffer_rsrc_t rs = page_rsrc(pool, phys, kPage * kRowFp8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t row = (uint32_t)(32 * (x & 1) + 8 * k + (ln >> 3));
+            T.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, row * kRowFp8 + 16 * (ln & 7), 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t rsc = page_rsrc(pool, (x & 1) ? -1 : phys, kPage * kRowFp8);
+        T.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, (uint32_t)ln * kRowFp8 + kDim, 0, 0));
+    };
+    const int ntile = 2 * np;
+    const int nround = (ntile + NL - 1) / NL;
+    QF8Reg Q;
+    Q.init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, A.q[l].w, A.q[l].w_bf16, b, ln);
+    // the query loads complete before the tile ring starts, so that the loop's waits count
+    // ring loads only (otherwise every round waits for all loads in flight)
+    __builtin_amdgcn_s_waitcnt(0);
+    TileF8 T[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+        fetch(T[u], NL * u + l);
+        __builtin_amdgcn_sched_barrier(0);     // tiles issue in ring order, as the loop refills them
+    }
+    // every pass of the loop refills all D ring slots (rounds past the last one load nothing),
+    // so the loads in flight at its head are the same on every pass
+    for (int r0 = 0; r0 < nround; r0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int r = r0 + u;
+            const bool live = r < nround;
+            const int x = NL * r + l;
+            if (live && x < ntile) {
+                uint8_t *buf = s_t[r & 1][l];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    *(u32x4 *)(buf + (8 * k + (ln >> 3)) * kTileLdsRow + 16 * (ln & 7)) = T[u].c[k];
+                if ((x & 1) == 0) s_sc[x >> 1][ln] = T[u].scale;
+            }
+            fetch(T[u], NL * (r + D) + l);
+            if (!live) continue;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const int xj = NL * r + j;
+                if (xj >= ntile) break;
+                const uint8_t *src = s_t[r & 1][j];
+                TileF8 B;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    B.c[k] = *(const u32x4 *)(src + (ln & 31) * kTileLdsRow + 64 * (ln >> 5) + 16 * k);
+                B.scale = 1.f;
+                const float tl = tile_logit_f8(Q, B);
+                const int e = 32 * (xj & 1) + (ln & 31);
+                if (ln < 32) s_l[l][xj >> 1][e] = tl * s_sc[xj >> 1][e];
+            }
+        }
+    }
+    __syncthreads();
+    // union of each entry over the encoders, in layer order, into s_l[0]
+    const float inv_n = 1.0f / (float)NL;
+    for (int e = tid; e < np * kPage; e += NT) {
+        const int i = __builtin_amdgcn_readfirstlane(e >> 6), x = e & 63;
+        const int phys = __builtin_amdgcn_readlane(phys_l, i);
+        float u = 0.f;
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const float L = phys >= 0 ? s_l[k][i][x] : (phys == kSlotUnmapped ? __builtin_nanf("") : -INFINITY);
+            if (A.mean_mode) {
+                const float p = inv_n / (1.0f + expf(-L));
+                u = k == 0 ? p : u + p;
+            } else {
+                u = k == 0 ? L : ((L != L || u != u) ? __builtin_nanf("") : fmaxf(u, L));
+            }
+        }
+        s_l[0][i][x] = u;
+    }
+    __syncthreads();
+    uint8_t *mrow = A.mask + (int64_t)b * A.mask_ld;
+    const int64_t s0 = page0 * kPage;
+    const int nb = (int)max((int64_t)0, min((int64_t)np * kPage, A.mask_ld - s0));
+    auto decide = [&](int e) -> bool {     // entry s0 + e of the workgroup's span
+        const int64_t s = s0 + e;
+        const float u = s_l[0][e >> 6][e & 63];
+        return s < seq && (u >= A.cut || s < A.n_sink || s >= seq - A.n_recent);
+    };
+    if (A.dens_out) {
+        for (int i = l; i < np; i += NL) {
+            const int e = i * kPage + ln;
+            const uint64_t m = __ballot(e < nb && decide(e));
+            if (ln == 0) A.dens_out[(int64_t)b * A.dens_ld + page0 + i] = (int32_t)__popcll(m);
+        }
+    }
+    if (A.union_score)
+        for (int e = tid; e < nb; e += NT) {
+            const int64_t s = s0 + e;
+            A.union_score[(int64_t)b * A.mask_ld + s] = s < seq ? s_l[0][e >> 6][e & 63] : -INFINITY;
+        }
+    if (nb % 16 == 0 && ((uintptr_t)(mrow + s0) % 16) == 0) {
+        for (int c = tid; 16 * c < nb; c += NT) {
+            u32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w |= (decide(16 * c + 4 * q + k) ? 1u : 0u) << (8 * k);
+                v[q] = w;
+            }
+            *(u32x4 *)(mrow + s0 + 16 * c) = v;
+        }
+    } else {
+        for (int e = tid; e < nb; e += NT) mrow[s0 + e] = decide(e) ? 1 : 0;
     }
 }
 
@@ -1888,6 +2067,13 @@ hipError_t launch_mask(const MaskArgs &a0, int key_fmt, int B, hipStream_t s) {
         else if (a.n_layers == 2) mask_f8_kernel<2, 4><<<grid, 256, 0, s>>>(a);
         else if (a.n_layers == 3) mask_f8_kernel<3, 4><<<grid, 256, 0, s>>>(a);
         else mask_f8_kernel<4, 4><<<grid, 256, 0, s>>>(a);
+    } else if (key_fmt == KEY_FP8 && a.shared_keys && a.n_layers >= 2) {
+        // one pool for every encoder: workgroups of n_layers waves, each key tile read once
+        a.ppw = (int)std::min<int64_t>(FM_SHARED_PPW, std::max<int64_t>(1, (total + FM_SHARED_WG - 1) / FM_SHARED_WG));
+        dim3 grid((unsigned)((a.n_pages + a.ppw - 1) / a.ppw), (unsigned)B);
+        if (a.n_layers == 2) mask_f8_shared_kernel<2><<<grid, 128, 0, s>>>(a);
+        else if (a.n_layers == 3) mask_f8_shared_kernel<3><<<grid, 192, 0, s>>>(a);
+        else mask_f8_shared_kernel<4><<<grid, 256, 0, s>>>(a);
     } else if (key_fmt == KEY_FP8 && FM_MASK_F8) {
         dim3 grid((unsigned)((a.n_pages + 4 * a.ppw - 1) / (4 * a.ppw)), (unsigned)B);
         if (a.n_layers == 1) mask_f8_kernel<1, 2><<<grid, 256, 0, s>>>(a);
