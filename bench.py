@@ -625,7 +625,8 @@ def main():
         "graph_event_ms_per_step": h["graph_ms"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "score_topk_bf16_kernel<4,16> (bf16 keys, bf16 q, fused top-512)",
+                     "kernel": "fm_index_topk call: score_topk_bf16_kernel<4,16> (scoring + chunk "
+                               "selection) then merge_chunks_kernel<1024,8> (row merge)",
                      "alg_bytes_per_launch": h["alg_bytes"], "avg_kernel_ms": kern_ms,
                      "timing": "events around back-to-back launches of the fused call",
                      "bracketed_ms": h["per"]["index_topk"],

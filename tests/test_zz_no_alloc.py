@@ -1,7 +1,8 @@
 """fm_score_resident_noalloc (the library's static workspace) against fm_score_resident (a
 caller-allocated workspace): the same kernels, so the outputs must be identical, bit for bit.
-Two calls in a row, the second with a smaller input (the static array keeps the first call's
-contents); then a call whose workspace would not fit the static array is refused on the host.
+Calls in a row, the second with a smaller input (the static array keeps the first call's
+contents) and the third with more rows again; then a call whose workspace would not fit the
+static array is refused on the host.
 """
 import numpy as np
 import pytest
@@ -28,7 +29,9 @@ def test_noalloc_matches_score_resident_twice():
     big = W.two_level_resident_fp8(seed=2050, B=30, seq_len=64 * 2000 + 17, kmax=384,
                                    shuffled=True, ragged=True)
     small = W.two_level_resident_fp8(seed=2051, B=3, seq_len=64 * 70 + 5, kmax=21, ragged=True)
-    for tag, wl in (("30 requests x 384 pages", big), ("3 requests x 21 pages", small)):
+    more = W.two_level_resident_fp8(seed=2053, B=40, seq_len=64 * 300 + 3, kmax=64, ragged=True)
+    for tag, wl in (("30 requests x 384 pages", big), ("3 requests x 21 pages", small),
+                    ("40 requests x 64 pages", more)):
         dw = api.DeviceWorkload(wl, "cuda:0")
         i_ref, v_ref = G.score_resident(dw)
         i_na, v_na = _noalloc(dw)
