@@ -945,20 +945,49 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
     auto select = [&](bool take, float x, int32_t en) {
         append(take, x, en, &S.n_sel, S.sel_v, S.sel_e, (uint32_t)FM_MAX_K, true);
     };
-    if (m <= k) {
+    // append this thread's slots u with take(u) set, one slot reservation per wave for all of
+    // them (the reservations are serial LDS round trips)
+    auto append_all = [&](auto &&take, uint32_t *counter, float *xs, int32_t *es, uint32_t cap_n,
+                          bool sel) {
+        uint64_t mk[SPT];
+        uint32_t tot = 0;
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) select(ok[u], v[u], e[u]);
+        for (int u = 0; u < SPT; ++u) {
+            mk[u] = __ballot(take(u));
+            tot += (uint32_t)__popcll(mk[u]);
+        }
+        if (tot == 0) return;
+        uint32_t b0 = 0;
+        if (ln == 0) b0 = atomicAdd(counter, tot);
+        b0 = __shfl(b0, 0);
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            if ((mk[u] >> ln) & 1ull) {
+                const uint32_t p = b0 + (uint32_t)__popcll(mk[u] & lt);
+                if (p < cap_n) {
+                    es[p] = e[u];
+                    xs[p] = v[u];
+                }
+                if (sel && (uint32_t)e[u] < 32u * (uint32_t)F.bit_words)
+                    atomicOr(&S.bits[e[u] >> 5], 1u << (e[u] & 31));
+            }
+            b0 += (uint32_t)__popcll(mk[u]);
+        }
+    };
+    auto select_all = [&](auto &&take) {
+        append_all(take, &S.n_sel, S.sel_v, S.sel_e, (uint32_t)FM_MAX_K, true);
+    };
+    if (m <= k) {
+        select_all([&](int u) { return ok[u]; });
     } else {
         if (!radix) {
             top_bin<NT>(k, S);
             const int bstar = (int)S.misc[0];
             const uint32_t need = k - S.misc[1], nb = S.hist[bstar];
             if (nb <= (uint32_t)kBnd) {
-#pragma unroll
-                for (int u = 0; u < SPT; ++u) {
-                    select(bn[u] > bstar, v[u], e[u]);
-                    append(bn[u] == bstar, v[u], e[u], &S.n_bnd, S.bnd_v, S.bnd_e, (uint32_t)kBnd, false);
-                }
+                select_all([&](int u) { return bn[u] > bstar; });
+                append_all([&](int u) { return bn[u] == bstar; }, &S.n_bnd, S.bnd_v, S.bnd_e,
+                           (uint32_t)kBnd, false);
                 __syncthreads();
                 for (uint32_t a0 = 0; a0 < nb; a0 += NT) {
                     const uint32_t a = a0 + tid;
@@ -984,9 +1013,7 @@ __global__ __launch_bounds__(NT) void merge_chunks_kernel(FuseArgs F) {
             const RegSrc<SPT> src{v, e, ok};
             const Rule rule = radix_rule<NT>(src, k, S.hist, S.sh, S.misc);
             __syncthreads();
-#pragma unroll
-            for (int u = 0; u < SPT; ++u)
-                select(ok[u] && (full_key(v[u], e[u]) & rule.M) >= rule.P, v[u], e[u]);
+            select_all([&](int u) { return ok[u] && (full_key(v[u], e[u]) & rule.M) >= rule.P; });
         }
     }
     __syncthreads();
