@@ -66,10 +66,10 @@
 #define FM_MASK_F8 1   // fp8 mask: layers-per-wave kernel (0: one wave per layer)
 #endif
 #ifndef FM_SHARED_AHEAD
-#define FM_SHARED_AHEAD 3  // fp8 mask over one shared pool: rounds a wave's tile loads run ahead
+#define FM_SHARED_AHEAD 2  // fp8 mask over one shared pool: rounds a wave's tile loads run ahead
 #endif
 #ifndef FM_SHARED_WPE
-#define FM_SHARED_WPE 2    // fp8 mask over one shared pool: waves per SIMD the registers are sized for
+#define FM_SHARED_WPE 3    // fp8 mask over one shared pool: waves per SIMD the registers are sized for
 #endif
 #ifndef FM_SHARED_PPW
 #define FM_SHARED_PPW 8    // fp8 mask over one shared pool: pages a workgroup, at most
@@ -1280,6 +1280,35 @@ struct QF8Reg {
     static constexpr int kAhead = 4;
 };
 
+// The A operands in registers, the head weights in LDS ([lane half][16 m + v], as QWideLds lays
+// them out; every lane of a half reads the same words): 32 fewer registers than QF8Reg.
+struct QF8RegW {
+    u32x4 a[2][8];
+    const f32x4 *w;
+    // wave-wide: lane l writes one weight of the row into lds_w[64] (the caller synchronises
+    // the workgroup before the first use)
+    __device__ void init(const uint8_t *qrow, float *lds_w, const void *wp, int w_bf16, int t, int ln) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int st = 0; st < 8; ++st) a[m][st] = qa_frag(qrow, m, st, ln);
+        const int h = ln >> 5, m = (ln >> 4) & 1, v = ln & 15;
+        const int64_t head = (int64_t)t * kHeads + 32 * m + 8 * (v >> 2) + 4 * h + (v & 3);
+        lds_w[ln] = w_bf16 ? bf16f(((const uint16_t *)wp)[head]) : ((const float *)wp)[head];
+        w = (const f32x4 *)lds_w;
+    }
+    __device__ __forceinline__ const u32x4 *frags() const { return nullptr; }
+    __device__ __forceinline__ u32x4 get(const u32x4 *, int m, int st) const { return a[m][st]; }
+    __device__ __forceinline__ const f32x4 *weights() const {
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        return w + 8 * (__lane_id() >> 5) + z;
+    }
+    static constexpr int kMT = 2;
+    static constexpr bool kLds = false;
+    static constexpr int kAhead = 4;
+};
+
 // One query row's A operands and head weights for 32 MT heads, both in LDS, staged by the whole
 // workgroup (its waves all score that row): fragment (m, s) at a[(8 m + s) * 64 + lane] as
 // qa_frag lays it out, weights as [lane half h][16 m + v] = head 32 m + 8 (v / 4) + 4 h + v % 4,
@@ -1833,6 +1862,7 @@ void mask_f8_shared_kernel(MaskArgs A) {
     __shared__ float s_l[NL][PPW][kPage];                                   // logits, then union
     __shared__ float s_sc[PPW][kPage];                                      // entry scales
     __shared__ __attribute__((aligned(16))) uint8_t s_t[2][NL][32 * kTileLdsRow];   // tiles
+    __shared__ __align__(16) float s_w[NL][64];                             // head weights
     const int b = blockIdx.y;
     const int tid = threadIdx.x, ln = __lane_id();
     const int l = __builtin_amdgcn_readfirstlane(tid >> 6);                // this wave's encoder
@@ -1866,8 +1896,9 @@ void mask_f8_shared_kernel(MaskArgs A) {
     };
     const int ntile = 2 * np;
     const int nround = (ntile + NL - 1) / NL;
-    QF8Reg Q;
-    Q.init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, A.q[l].w, A.q[l].w_bf16, b, ln);
+    QF8RegW Q;
+    Q.init((const uint8_t *)A.q[l].q + (int64_t)b * kHeads * kDim * 2, s_w[l], A.q[l].w,
+           A.q[l].w_bf16, b, ln);
     // the query loads complete before the tile ring starts, so that the loop's waits count
     // ring loads only (otherwise every round waits for all loads in flight)
     __builtin_amdgcn_s_waitcnt(0);
