@@ -134,6 +134,33 @@ def test_labels_ties_split_by_index():
     assert idx[ptr[2]:ptr[3]].tolist() == list(range(55))
 
 
+@pytest.mark.parametrize("p", [0.3, 0.5, 0.7])
+def test_labels_ties_in_small_boundary_bin(p):
+    """Ten equal scores carry most of each row's mass and the boundary falls among them, with
+    few scores in their bin: the boundary is resolved by one wave comparing the gathered scores
+    pairwise, and the tied entries are split by entry index (floor(p Z / w) of them)."""
+    rng = np.random.default_rng(34)
+    T, ld = 6, 4096
+    S = rng.standard_normal((T, 1, ld)).astype(np.float32)
+    for t in range(T):
+        S[t, 0, rng.choice(ld, 10, replace=False)] = np.float32(8.0)
+    got = gpu_labels(S, None, p=p, min_votes=1, tau=1)
+    check_labels(f"ties in a small bin p={p}", S, None, p, 1, 1, got)
+
+
+def test_labels_far_from_zero():
+    """Scores near +-10,000 (the boundary-bin gather compares every entry exactly there) and a
+    row whose whole mass sits on one entry (an empty nucleus for p below 1)."""
+    rng = np.random.default_rng(35)
+    T, L, ld = 4, 2, 3000
+    S = (rng.standard_normal((T, L, ld)) * 2).astype(np.float32)
+    S[0] += np.float32(10000.0)
+    S[1] -= np.float32(10000.0)
+    S[2, :, 17] = np.float32(60.0)
+    got = gpu_labels(S, None, p=0.6, min_votes=1, tau=1)
+    check_labels("far from zero", S, None, 0.6, 1, 1, got)
+
+
 def test_labels_boundary_bin_overflow():
     """More than 4,096 candidates share the boundary's score bin (here: equal scores), so the
     radix search reads the row again from memory instead of the gathered list."""

@@ -11,15 +11,18 @@
 //                   the nucleus boundary exactly: softmax masses in 2^-44 fixed point summed
 //                   as integers (so the sums, and with them every decision, are independent of
 //                   the summation order), a mass histogram over linear score bins to find the
-//                   boundary bin, then a 32-bit radix search over the scores of that bin
-//                   (gathered in LDS)
-//                   for the boundary score; equal scores at the boundary are taken by lower
-//                   entry.  Membership goes out as one bit per entry.
+//                   boundary bin, then the boundary score among that bin's scores (gathered in
+//                   LDS): by one wave comparing every pair when they are at most 64, else by a
+//                   32-bit radix search.  Equal scores at the boundary are taken by lower entry.
+//                   Membership goes out as one bit per entry.  The kernel is bound by vector
+//                   instruction issue (a wave64 instruction takes four cycles), so every pass
+//                   over the row is branch-free or skips its rare work behind one compare.
 //   golden_kernel   votes across layers, one thread per 32-entry word: the golden bits A[i].
 //   window kernels  per (window t, 256-word chunk): the OR of tau golden words and its count,
 //                   an exclusive scan of the counts into label_ptr and chunk positions, then
 //                   the ascending indices with their scores, the fraction of the window's
 //                   tokens whose golden set holds the entry.
+#include <float.h>
 #include <math.h>
 
 #include "fm_internal.h"
@@ -107,6 +110,14 @@ __device__ __forceinline__ float key_score(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
+// the largest float below a finite x: y > float_below(x) exactly when y >= x, for every non-NaN
+// y (-0 and +0 count as equal)
+__device__ __forceinline__ float float_below(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) == 0u) return -__uint_as_float(1u);     // below +-0: -(smallest denormal)
+    return __uint_as_float((u & 0x80000000u) ? u + 1u : u - 1u);
+}
+
 // The row's registers pass through an empty asm statement before each sweep over them, so the
 // compiler cannot keep per-entry results (keys, bins, masses) of one sweep alive for the next:
 // 64 values a thread already fill half the registers.
@@ -157,6 +168,15 @@ __device__ void find_boundary_bin(NucLds &L, int nb, u64 room) {
     __syncthreads();
 }
 
+// OR of x over each group of eight neighbouring lanes (every lane of the group gets it): two
+// quad permutations and a mirror within each half row, all on the DPP path
+__device__ __forceinline__ uint32_t or8(uint32_t x) {
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // lanes ^ 1
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // lanes ^ 2
+    x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);  // 7 - lane
+    return x;
+}
+
 __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
     constexpr int NT = kNucNT, NW = NT / 64, VEC = kNucVec;
     __shared__ NucLds L;
@@ -168,15 +188,25 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
     for (int b = tid; b < kNucBins; b += NT) L.hm[b] = 0ull;
     if (tid == 0) L.list_n = 0u;
 
-    // the row; entries past n, -inf and NaN are not candidates (-inf here)
+    // the row, every load issued before any is used; entries past n, -inf and NaN are not
+    // candidates (-inf here)
     float v[VEC][4];
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, n * 4, 0x00020000);
+    {
+        f32x4 raw[VEC];
 #pragma unroll
-    for (int u = 0; u < VEC; ++u) {
-        const int j = 4 * (u * NT + tid);
-        const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 4u, 0, 0));
+        for (int u = 0; u < VEC; ++u)
+            raw[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs, (uint32_t)(4 * (u * NT + tid)) * 4u, 0, 0));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) v[u][c] = (j + c < n && x[c] == x[c]) ? x[c] : -INFINITY;
+        for (int u = 0; u < VEC; ++u) {
+            const int j = 4 * (u * NT + tid);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float x = raw[u][c];
+                v[u][c] = ((j + c < n) & (x == x)) ? x : -INFINITY;
+            }
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -196,18 +226,17 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
     }
     const RowConst K{mx, (kNucSpan - mx) * kBinsPerUnit};
 
-    // masses, their total and the mass histogram over linear score bins
+    // masses, their total and the mass histogram over linear score bins, branch-free: a
+    // non-candidate's mass is exp2(-inf) = 0 and adds nothing to the bin it lands in
     u64 zt = 0;
 #pragma unroll
     for (int u = 0; u < VEC; ++u)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float x = v[u][c];
-            if (x > -INFINITY) {
-                const u64 q = mass_fx(x, K);
-                zt += q;
-                if (q) atomicAdd(&L.hm[score_bin(x, K)], q);
-            }
+            const u64 q = mass_fx(x, K);
+            zt += q;
+            atomicAdd(&L.hm[score_bin(x, K)], q);
         }
     u64 Z;
     (void)block_excl_scan_t<u64, NT>(zt, L.sh64, Z);   // also orders the histogram's atomics
@@ -220,76 +249,128 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
         find_boundary_bin<NT>(L, kNucBins, room);
         const int b1 = (int)L.m32[0];
         u64 above = L.m64[0];
-        // the boundary bin's scores, gathered in LDS (few: the bins are narrow)
+        // the boundary bin's scores, gathered in LDS (few: the bins are narrow).  A score of
+        // bin b1 is at least the bin's lower edge; one compare against the edge less a bin
+        // (far wider than the rounding of the bin arithmetic for scores below 2^13) skips the
+        // bin arithmetic for nearly every entry.
+        const float xe = (b1 > 0 && fabsf(mx) < 8192.f) ? mx - kNucSpan + (float)(b1 - 1) / kBinsPerUnit
+                                                         : -FLT_MAX;
         opaque_row<VEC>(v);
 #pragma unroll
         for (int u = 0; u < VEC; ++u)
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float x = v[u][c];
-                if (x > -INFINITY && score_bin(x, K) == b1) {
-                    const uint32_t e = atomicAdd(&L.list_n, 1u);
-                    if (e < (uint32_t)kNucList) L.lx[e] = x;
+                if (x >= xe) {
+                    if ((x > -INFINITY) & (score_bin(x, K) == b1)) {
+                        const uint32_t e = atomicAdd(&L.list_n, 1u);
+                        if (e < (uint32_t)kNucList) L.lx[e] = x;
+                    }
                 }
             }
         __syncthreads();
-        const uint32_t nlist = L.list_n;
-        // the exact boundary score inside bin b1: radix over the 32-bit key, 11 + 11 + 10 bits,
-        // over the gathered scores (or, if the bin overflowed the list, over the row in memory)
-        uint32_t prefix = 0u, pmask = 0u, dig = 0u;
-        auto radix_pass = [&](int pass, auto &&sweep) {
-            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-            const int nb = pass == 2 ? 1024 : 2048;
-            for (int b = tid; b < kNucBins; b += NT) {
-                L.hm[b] = 0ull;
-                L.hc[b] = 0u;
+        const uint32_t nlist = (uint32_t)__builtin_amdgcn_readfirstlane((int)L.list_n);
+        bool resolved = false;
+        if (nlist <= 64u) {
+            // One wave, a gathered score a lane: the mass of larger scores and of equal ones
+            // (exact sums), and the lane whose score holds the boundary: gt <= room - above
+            // < gt + eq.  Its score is the boundary score, every entry of it weighs eq / cnt.
+            if (w == 0) {
+                const bool has = (uint32_t)ln < nlist;
+                const float x = has ? L.lx[ln] : -INFINITY;
+                const uint32_t key = has ? score_key(x) : 0u;
+                const u64 q = has ? mass_fx(x, K) : 0ull;
+                u64 gt = 0, eq = 0;
+                uint32_t cnt = 0;
+                for (int j = 0; j < (int)nlist; ++j) {
+                    const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+                    const u64 qj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(q >> 32), j) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)q, j);
+                    gt += kj > key ? qj : 0ull;
+                    eq += kj == key ? qj : 0ull;
+                    cnt += kj == key ? 1u : 0u;
+                }
+                const u64 rp = room - above;
+                const uint64_t bm = __ballot(has && gt <= rp && rp < gt + eq);
+                if (ln == 0) L.m32[1] = bm ? 1u : 0u;
+                if (bm && ln == __ffsll((long long)bm) - 1) {
+                    L.m32[0] = key;
+                    L.hc[0] = cnt;
+                    L.m64[0] = rp - gt;
+                    L.m64[1] = eq;
+                }
             }
             __syncthreads();
-            sweep([&](float x) {
-                const uint32_t key = score_key(x);
-                if ((key & pmask) == prefix) {
-                    const uint32_t d = (key >> shift) & (uint32_t)(nb - 1);
-                    atomicAdd(&L.hm[d], mass_fx(x, K));
-                    atomicAdd(&L.hc[d], 1u);
+            if (L.m32[1]) {
+                resolved = true;
+                xstar = key_score(L.m32[0]);
+                g = L.hc[0];
+                const u64 wq = L.m64[1] / g;
+                const u64 rr = L.m64[0] / (wq ? wq : 1ull);
+                r = (uint32_t)(rr < (u64)g ? rr : (u64)g);
+            }
+            __syncthreads();                    // L.m32 / L.m64 / L.hc are read before reuse
+        }
+        if (!resolved) {
+            // the exact boundary score inside bin b1: radix over the 32-bit key, 11 + 11 + 10
+            // bits, over the gathered scores (or, if the bin overflowed the list, over the row
+            // in memory)
+            uint32_t prefix = 0u, pmask = 0u, dig = 0u;
+            auto radix_pass = [&](int pass, auto &&sweep) {
+                const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+                const int nb = pass == 2 ? 1024 : 2048;
+                for (int b = tid; b < kNucBins; b += NT) {
+                    L.hm[b] = 0ull;
+                    L.hc[b] = 0u;
                 }
-            });
-            __syncthreads();
-            find_boundary_bin<NT>(L, nb, room - above);
-            dig = L.m32[0];
-            above += L.m64[0];
-            prefix |= dig << shift;
-            pmask |= (uint32_t)(nb - 1) << shift;
-        };
-        if (nlist <= (uint32_t)kNucList) {
-#pragma unroll 1
-            for (int pass = 0; pass < 3; ++pass)
-                radix_pass(pass, [&](auto &&add) {
-                    for (uint32_t e = tid; e < nlist; e += NT) add(L.lx[e]);
-                });
-        } else {
-#pragma unroll 1
-            for (int pass = 0; pass < 3; ++pass)
-                radix_pass(pass, [&](auto &&add) {
-                    // the row again from memory (the bin overflowed the list: many equal or
-                    // nearly equal scores), so the registers stay as they are
-                    for (int j = 4 * tid; j < n; j += 4 * NT) {
-                        const f32x4 x4 = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 4u, 0, 0));
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const float x = x4[c];
-                            if (j + c < n && x == x && x > -INFINITY && score_bin(x, K) == b1) add(x);
-                        }
+                __syncthreads();
+                sweep([&](float x) {
+                    const uint32_t key = score_key(x);
+                    if ((key & pmask) == prefix) {
+                        const uint32_t d = (key >> shift) & (uint32_t)(nb - 1);
+                        atomicAdd(&L.hm[d], mass_fx(x, K));
+                        atomicAdd(&L.hc[d], 1u);
                     }
                 });
+                __syncthreads();
+                find_boundary_bin<NT>(L, nb, room - above);
+                dig = L.m32[0];
+                above += L.m64[0];
+                prefix |= dig << shift;
+                pmask |= (uint32_t)(nb - 1) << shift;
+            };
+            if (nlist <= (uint32_t)kNucList) {
+#pragma unroll 1
+                for (int pass = 0; pass < 3; ++pass)
+                    radix_pass(pass, [&](auto &&add) {
+                        for (uint32_t e = tid; e < nlist; e += NT) add(L.lx[e]);
+                    });
+            } else {
+#pragma unroll 1
+                for (int pass = 0; pass < 3; ++pass)
+                    radix_pass(pass, [&](auto &&add) {
+                        // the row again from memory (the bin overflowed the list: many equal or
+                        // nearly equal scores), so the registers stay as they are
+                        for (int j = 4 * tid; j < n; j += 4 * NT) {
+                            const f32x4 x4 = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 4u, 0, 0));
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const float x = x4[c];
+                                if (j + c < n && x == x && x > -INFINITY && score_bin(x, K) == b1) add(x);
+                            }
+                        }
+                    });
+            }
+            // every entry of the boundary score has the same mass wq; r of its g entries are
+            // members
+            xstar = key_score(prefix);
+            g = L.hc[dig];
+            const u64 wq = g ? L.hm[dig] / g : 1ull;   // g > 0 and wq > 0: the bin holds the boundary
+            const u64 rr = (room - above) / (wq ? wq : 1ull);
+            r = (uint32_t)(rr < (u64)g ? rr : (u64)g);
+            __syncthreads();                    // L.hc / L.hm are read before anything reuses them
         }
-        // every entry of the boundary score has the same mass wq; r of its g entries are members
-        xstar = key_score(prefix);
-        g = L.hc[dig];
-        const u64 wq = g ? L.hm[dig] / g : 1ull;   // g > 0 and wq > 0: the bin holds the boundary
-        const u64 rr = (room - above) / (wq ? wq : 1ull);
-        r = (uint32_t)(rr < (u64)g ? rr : (u64)g);
-        __syncthreads();                        // L.hc / L.hm are read before anything reuses them
     }
 
     // membership bits: score > xstar, or score == xstar among the first r of those by entry
@@ -297,34 +378,42 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
     // (u NT + tid) / 8: eight neighbouring lanes assemble a word.
     const bool split = !all && r > 0u && r < g;  // workgroup-uniform
     const bool take_eq = all || r == g;
-    uint32_t run = 0u;                          // boundary entries in earlier slabs
     opaque_row<VEC>(v);
+    if (!split) {
+        // one compare an entry: x > thr, with thr = -inf (every candidate), the float below
+        // xstar (ties taken) or xstar
+        const float thr = all ? -INFINITY : (take_eq ? float_below(xstar) : xstar);
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) {
+            uint32_t nib = 0u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) nib |= (v[u][c] > thr ? 1u : 0u) << c;
+            const uint32_t word = or8(nib << (4 * (tid & 7)));
+            const int wd = (u * NT + tid) >> 3;
+            if ((tid & 7) == 0 && wd < A.words) mout[wd] = word;
+        }
+        return;
+    }
+    uint32_t run = 0u;                          // boundary entries in earlier slabs
 #pragma unroll
     for (int u = 0; u < VEC; ++u) {
         uint32_t nib = 0u, eq_mask = 0u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float x = v[u][c];
-            const bool cand = x > -INFINITY;
-            const bool in = cand && (all || x > xstar || (x == xstar && take_eq));
-            nib |= (in ? 1u : 0u) << c;
-            eq_mask |= (cand && x == xstar ? 1u : 0u) << c;
+            nib |= (x > xstar ? 1u : 0u) << c;
+            eq_mask |= (x == xstar ? 1u : 0u) << c;
         }
-        if (split) {
-            uint32_t tot;
-            const uint32_t before = run + block_excl_scan_t<uint32_t, NT>((uint32_t)__popc(eq_mask), L.sh32, tot);
+        uint32_t tot;
+        const uint32_t before = run + block_excl_scan_t<uint32_t, NT>((uint32_t)__popc(eq_mask), L.sh32, tot);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if ((eq_mask >> c) & 1u) {
-                    const uint32_t rank = before + (uint32_t)__popc(eq_mask & ((1u << c) - 1u));
-                    nib |= (rank < r ? 1u : 0u) << c;
-                }
-            run += tot;
-        }
-        uint32_t word = nib << (4 * (tid & 7));
-        word |= __shfl_xor(word, 1);
-        word |= __shfl_xor(word, 2);
-        word |= __shfl_xor(word, 4);
+        for (int c = 0; c < 4; ++c)
+            if ((eq_mask >> c) & 1u) {
+                const uint32_t rank = before + (uint32_t)__popc(eq_mask & ((1u << c) - 1u));
+                nib |= (rank < r ? 1u : 0u) << c;
+            }
+        run += tot;
+        const uint32_t word = or8(nib << (4 * (tid & 7)));
         const int wd = (u * NT + tid) >> 3;
         if ((tid & 7) == 0 && wd < A.words) mout[wd] = word;
     }
