@@ -113,6 +113,16 @@ def test_encoder_prefill_wide_tiles():
     check("encoder 600 rows x 256 heads, wide tiles (sampled)", qg[rows], wg[rows], qr, wr)
 
 
+def test_encoder_prefill_256_tiles():
+    """1,100 rows x 256 heads: the second product (32,768 columns, 640 tiles of 256 x 256) takes
+    the eight-wave 256 x 256 tiles, the last row tile holding 76 rows."""
+    e = W.query_encoder(seed=3109, T=1100, n_heads=256, d_model=256, q_rank=512)
+    qg, wg = run_encoder(e)
+    rows = np.array([0, 63, 64, 255, 256, 700, 1023, 1024, 1099])
+    qr, wr = oracle_encoder(e, rows=rows)
+    check("encoder 1100 rows x 256 heads, 256 x 256 tiles (sampled)", qg[rows], wg[rows], qr, wr)
+
+
 @pytest.mark.parametrize("T", [255, 256, 257])
 def test_encoder_around_the_tiled_threshold(T):
     """The second product: 255 rows take the per-32x32-tile kernel, 256 and 257 the LDS-tiled

@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E, int hp
 #ifndef FM_ENC_TK
 #define FM_ENC_TK 32
 #endif
-constexpr int kTM = 128, kTK = FM_ENC_TK, kTLd = kTK + 8;
+constexpr int kTK = FM_ENC_TK, kTLd = kTK + 8;
 #ifndef FM_ENC_WIDE_TILES
 #define FM_ENC_WIDE_TILES 512
 #endif
@@ -260,28 +260,30 @@ constexpr int kWideTiles = FM_ENC_WIDE_TILES;
 #endif
 constexpr int kTGroupM = FM_ENC_GROUP_M;
 
-template <int BN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int BM, int BN, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void enc_gemm_tiled_kernel(EncGemmArgs G) {
-    // PR 16-byte pieces a row of a k-slab; PA / PW pieces a thread loads of A / W; WJ MFMA
-    // column tiles a wave (its quarter is 64 x BN / 2)
-    constexpr int PR = kTK / 8, PA = kTM * PR / 256, PW = BN * PR / 256, WJ = BN / 64;
-    static_assert(PA >= 1 && PW >= 1 && kTM * PR % 256 == 0 && BN * PR % 256 == 0, "slab layout");
-    __shared__ __align__(16) uint16_t sA[2][kTM * kTLd];
+    // NT threads; WM x WN waves, each 64 x BN / WN of the tile (2 x WJ MFMA tiles); PR 16-byte
+    // pieces a row of a k-slab; PA / PW pieces a thread loads of A / W
+    constexpr int NT = 64 * NW, WM = BM / 64, WN = NW / WM, WJ = BN / WN / 32;
+    constexpr int PR = kTK / 8, PA = BM * PR / NT, PW = BN * PR / NT;
+    static_assert(WM * WN == NW && WJ >= 1 && BN % (WN * 32) == 0, "wave grid");
+    static_assert(PA >= 1 && PW >= 1 && BM * PR % NT == 0 && BN * PR % NT == 0, "slab layout");
+    __shared__ __align__(16) uint16_t sA[2][BM * kTLd];
     __shared__ __align__(16) uint16_t sW[2][BN * kTLd];
     const int tid = threadIdx.x, ln = __lane_id(), j = ln & 31, h = ln >> 5, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int N = G.N0 + G.N1;
     // Tile order: the chip's 8 XCDs (each with its own L2) take consecutive workgroup ids in
     // turn, so workgroup b runs on XCD b % 8; each XCD is given a contiguous run of tiles, and
     // within it tiles go in groups of kTGroupM row tiles by every column tile, so the
     // workgroups an L2 serves at once share their activation rows and weight rows.
-    const int mT = (G.M + kTM - 1) / kTM, nTl = (N + BN - 1) / BN, total = mT * nTl;
+    const int mT = (G.M + BM - 1) / BM, nTl = (N + BN - 1) / BN, total = mT * nTl;
     const int b = blockIdx.x, x = b % 8, per = total / 8, rem = total % 8;
     const int t = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + b / 8;
     const int grp = t / (kTGroupM * nTl), fm = grp * kTGroupM, gs = min(kTGroupM, mT - fm);
     const int within = t - grp * kTGroupM * nTl;
-    const int m0 = (fm + within % gs) * kTM, n0 = (within / gs) * BN;
+    const int m0 = (fm + within % gs) * BM, n0 = (within / gs) * BN;
     // this thread's slab pieces: piece p = tid P + e is row p / PR, k values 8 (p % PR) .. + 7
     const uint16_t *ap[PA];
     const uint16_t *wp[PW];
@@ -339,7 +341,7 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
                 a[i] = *(const u32x4 *)&sA[buf][(wm * 64 + 32 * i + j) * kTLd + 16 * ks + 8 * h];
 #pragma unroll
             for (int jj = 0; jj < WJ; ++jj)
-                bw[jj] = *(const u32x4 *)&sW[buf][(wn * (BN / 2) + 32 * jj + j) * kTLd + 16 * ks + 8 * h];
+                bw[jj] = *(const u32x4 *)&sW[buf][(wn * (BN / WN) + 32 * jj + j) * kTLd + 16 * ks + 8 * h];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -353,7 +355,7 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < WJ; ++jj) {
-            const int col = n0 + wn * (BN / 2) + 32 * jj + j;
+            const int col = n0 + wn * (BN / WN) + 32 * jj + j;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -366,14 +368,18 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
 
 hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
     if (g.S == 1 && g.Z == 1 && g.M >= kTiledMinRows) {
-        // 128 x 256 tiles (a wave 64 x 128: fewer LDS reads per MFMA) when they still give
-        // at least kWideTiles workgroups, else 128 x 128
-        const int mt = (g.M + kTM - 1) / kTM, n = g.N0 + g.N1;
-        const int wide = mt * ((n + 255) / 256);
-        if (wide >= kWideTiles)
-            enc_gemm_tiled_kernel<256><<<dim3((unsigned)wide), 256, 0, s>>>(g);
+        // the largest tile that still gives enough workgroups to fill the chip: 256 x 256
+        // (eight waves of 64 x 128), 128 x 256 (four waves of 64 x 128: fewer LDS reads per
+        // MFMA than 64 x 64), else 128 x 128
+        const int n = g.N0 + g.N1;
+        const int t256 = ((g.M + 255) / 256) * ((n + 255) / 256);
+        const int wide = ((g.M + 127) / 128) * ((n + 255) / 256);
+        if (t256 >= kWideTiles)
+            enc_gemm_tiled_kernel<256, 256, 8><<<dim3((unsigned)t256), 512, 0, s>>>(g);
+        else if (wide >= kWideTiles)
+            enc_gemm_tiled_kernel<128, 256, 4><<<dim3((unsigned)wide), 256, 0, s>>>(g);
         else
-            enc_gemm_tiled_kernel<128><<<dim3((unsigned)(mt * ((n + 127) / 128))), 256, 0, s>>>(g);
+            enc_gemm_tiled_kernel<128, 128, 4><<<dim3((unsigned)(((g.M + 127) / 128) * ((n + 127) / 128))), 256, 0, s>>>(g);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((g.N0 + g.N1) / 32), (unsigned)((g.M + 31) / 32), (unsigned)g.Z);
