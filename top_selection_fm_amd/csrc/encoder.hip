@@ -259,20 +259,26 @@ constexpr int kWideTiles = FM_ENC_WIDE_TILES;
 #define FM_ENC_GROUP_M 4
 #endif
 constexpr int kTGroupM = FM_ENC_GROUP_M;
+#ifndef FM_ENC_T256_WGM
+#define FM_ENC_T256_WGM 4            // 256 x 256 tiles: 4 x 2 waves of 64 x 128
+#endif
+#ifndef FM_ENC_T256_WPE
+#define FM_ENC_T256_WPE 2
+#endif
 
-template <int BM, int BN, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+template <int BM, int BN, int WGM, int WGN, int WPE>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE)))
 void enc_gemm_tiled_kernel(EncGemmArgs G) {
-    // NT threads; WM x WN waves, each 64 x BN / WN of the tile (2 x WJ MFMA tiles); PR 16-byte
-    // pieces a row of a k-slab; PA / PW pieces a thread loads of A / W
-    constexpr int NT = 64 * NW, WM = BM / 64, WN = NW / WM, WJ = BN / WN / 32;
+    // NT threads in WGM x WGN waves, each BM / WGM x BN / WGN of the tile (TI x TJ MFMA tiles);
+    // PR 16-byte pieces a row of a k-slab; PA / PW pieces a thread loads of A / W
+    constexpr int NW = WGM * WGN, NT = 64 * NW, TI = BM / WGM / 32, TJ = BN / WGN / 32;
     constexpr int PR = kTK / 8, PA = BM * PR / NT, PW = BN * PR / NT;
-    static_assert(WM * WN == NW && WJ >= 1 && BN % (WN * 32) == 0, "wave grid");
+    static_assert(TI >= 1 && TJ >= 1 && BM % (WGM * 32) == 0 && BN % (WGN * 32) == 0, "wave grid");
     static_assert(PA >= 1 && PW >= 1 && BM * PR % NT == 0 && BN * PR % NT == 0, "slab layout");
     __shared__ __align__(16) uint16_t sA[2][BM * kTLd];
     __shared__ __align__(16) uint16_t sW[2][BN * kTLd];
     const int tid = threadIdx.x, ln = __lane_id(), j = ln & 31, h = ln >> 5, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int wm = wave / WGN, wn = wave % WGN;
     const int N = G.N0 + G.N1;
     // Tile order: the chip's 8 XCDs (each with its own L2) take consecutive workgroup ids in
     // turn, so workgroup b runs on XCD b % 8; each XCD is given a contiguous run of tiles, and
@@ -291,7 +297,7 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
 #pragma unroll
     for (int e = 0; e < PA; ++e) {
         const int p = tid * PA + e, r = p / PR, kp = 8 * (p % PR);
-        ap[e] = G.A + (int64_t)min(m0 + r, G.M - 1) * G.lda + kp;
+        ap[e] = G.A + (int64_t)min(m0 + r, G.M - 1) * G.lda;
         aofs[e] = r * kTLd + kp;
         akp[e] = kp;
     }
@@ -299,66 +305,82 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
     for (int e = 0; e < PW; ++e) {
         const int p = tid * PW + e, r = p / PR, kp = 8 * (p % PR);
         const int n = min(n0 + r, N - 1);
-        wp[e] = (n < G.N0 ? G.W0 + (int64_t)n * G.K : G.W1 + (int64_t)(n - G.N0) * G.K) + kp;
+        wp[e] = n < G.N0 ? G.W0 + (int64_t)n * G.K : G.W1 + (int64_t)(n - G.N0) * G.K;
         wofs[e] = r * kTLd + kp;
         wkp[e] = kp;
     }
-    u32x4 ra[PA], rw[PW];
-    auto load = [&](int k0) {   // K is a multiple of 16, so a piece is wholly in or out
+    // Two register stages: the loads of slab kt + 2 are issued while slab kt is multiplied and
+    // slab kt + 1, loaded a step earlier, waits to be written to LDS.  Every load is issued
+    // (a piece past K reads the row's last piece and is zeroed when written), so the wait
+    // before a stage's LDS write covers only that stage's loads.
+    u32x4 ra[2][PA], rw[2][PW];
+    auto load = [&](int st, int k0) {   // K is a multiple of 16, so a piece is wholly in or out
 #pragma unroll
-        for (int e = 0; e < PA; ++e)
-            ra[e] = k0 + akp[e] < G.K ? *(const u32x4 *)(ap[e] + k0) : u32x4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < PA; ++e) ra[st][e] = *(const u32x4 *)(ap[e] + min(k0 + akp[e], G.K - 8));
 #pragma unroll
-        for (int e = 0; e < PW; ++e)
-            rw[e] = k0 + wkp[e] < G.K ? *(const u32x4 *)(wp[e] + k0) : u32x4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < PW; ++e) rw[st][e] = *(const u32x4 *)(wp[e] + min(k0 + wkp[e], G.K - 8));
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int st, int buf, int k0) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < PA; ++e) *(u32x4 *)&sA[buf][aofs[e]] = ra[e];
+        for (int e = 0; e < PA; ++e) *(u32x4 *)&sA[buf][aofs[e]] = k0 + akp[e] < G.K ? ra[st][e] : zero;
 #pragma unroll
-        for (int e = 0; e < PW; ++e) *(u32x4 *)&sW[buf][wofs[e]] = rw[e];
+        for (int e = 0; e < PW; ++e) *(u32x4 *)&sW[buf][wofs[e]] = k0 + wkp[e] < G.K ? rw[st][e] : zero;
     };
-    f32x16 acc[2][WJ];
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < WJ; ++jj)
+        for (int jj = 0; jj < TJ; ++jj)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
-
-    const int nk = (G.K + kTK - 1) / kTK;
-    load(0);
-    stash(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load((kt + 1) * kTK);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < kTK / 16; ++ks) {
-            u32x4 a[2], bw[WJ];
+            u32x4 a[TI], bw[TJ];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *(const u32x4 *)&sA[buf][(wm * 64 + 32 * i + j) * kTLd + 16 * ks + 8 * h];
+            for (int i = 0; i < TI; ++i)
+                a[i] = *(const u32x4 *)&sA[buf][(wm * (BM / WGM) + 32 * i + j) * kTLd + 16 * ks + 8 * h];
 #pragma unroll
-            for (int jj = 0; jj < WJ; ++jj)
-                bw[jj] = *(const u32x4 *)&sW[buf][(wn * (BN / WN) + 32 * jj + j) * kTLd + 16 * ks + 8 * h];
+            for (int jj = 0; jj < TJ; ++jj)
+                bw[jj] = *(const u32x4 *)&sW[buf][(wn * (BN / WGN) + 32 * jj + j) * kTLd + 16 * ks + 8 * h];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
-                for (int jj = 0; jj < WJ; ++jj) acc[i][jj] = mma(a[i], bw[jj], acc[i][jj]);
+                for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = mma(a[i], bw[jj], acc[i][jj]);
         }
-        if (kt + 1 < nk) stash(buf ^ 1);
+    };
+    const int nk = (G.K + kTK - 1) / kTK;
+    // Slab kt is in LDS buffer kt & 1; slab kt + 1 is in register stage s1; stage s0 is free.
+    // The loads are issued unconditionally (past the last slab they read the last piece of
+    // each row and are never written), and the loop runs whole pairs of steps, so that every
+    // path reaching a stage's LDS write has the same loads in flight.
+    auto step = [&](int kt, int s1, int s0) {
+        load(s0, (kt + 2) * kTK);
+        __builtin_amdgcn_sched_barrier(0);     // the loads go out before the step's MFMAs
+        compute(kt & 1);
+        if (kt + 1 < nk) stash(s1, (kt + 1) & 1, (kt + 1) * kTK);
         __syncthreads();
+    };
+    load(0, 0);
+    load(1, kTK);
+    stash(0, 0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        step(kt, 1, 0);
+        step(kt + 1, 0, 1);
     }
+    if (kt < nk) step(kt, 1, 0);
     // accumulator v of lane j + 32 h: row 8 (v / 4) + 4 h + v % 4, column j of its MFMA tile
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < WJ; ++jj) {
-            const int col = n0 + wn * (BN / WN) + 32 * jj + j;
+        for (int jj = 0; jj < TJ; ++jj) {
+            const int col = n0 + wn * (BN / WGN) + 32 * jj + j;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int row = m0 + wm * (BM / WGM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (row < G.M && col < N) G.C[(int64_t)row * N + col] = acc[i][jj][v];
             }
         }
@@ -375,11 +397,11 @@ hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
         const int t256 = ((g.M + 255) / 256) * ((n + 255) / 256);
         const int wide = ((g.M + 127) / 128) * ((n + 255) / 256);
         if (t256 >= kWideTiles)
-            enc_gemm_tiled_kernel<256, 256, 8><<<dim3((unsigned)t256), 512, 0, s>>>(g);
+            enc_gemm_tiled_kernel<256, 256, FM_ENC_T256_WGM, 2, FM_ENC_T256_WPE><<<dim3((unsigned)t256), 128 * FM_ENC_T256_WGM, 0, s>>>(g);
         else if (wide >= kWideTiles)
-            enc_gemm_tiled_kernel<128, 256, 4><<<dim3((unsigned)wide), 256, 0, s>>>(g);
+            enc_gemm_tiled_kernel<128, 256, 2, 2, 2><<<dim3((unsigned)wide), 256, 0, s>>>(g);
         else
-            enc_gemm_tiled_kernel<128, 128, 4><<<dim3((unsigned)(((g.M + 127) / 128) * ((n + 127) / 128))), 256, 0, s>>>(g);
+            enc_gemm_tiled_kernel<128, 128, 2, 2, 2><<<dim3((unsigned)(((g.M + 127) / 128) * ((n + 127) / 128))), 256, 0, s>>>(g);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((g.N0 + g.N1) / 32), (unsigned)((g.M + 31) / 32), (unsigned)g.Z);
