@@ -220,6 +220,7 @@ struct LabelArgs {
     int words;                // ceil(ld / 32)
     uint32_t *mbits;          // workspace [T, n_layers, words]: nucleus membership
     uint32_t *gbits;          // workspace [T, words]: golden sets
+    uint32_t *pbits, *sbits;  // workspace [T, words]: prefix / suffix ORs within tau-blocks
     uint32_t *ybits;          // workspace [T - tau + 1, words]: label sets of the windows
     int32_t *counts;          // workspace [T - tau + 1, chunks]: labels, then first positions
     int chunks;               // 256-word chunks of a row

@@ -17,11 +17,13 @@
 //                   Membership goes out as one bit per entry.  The kernel is bound by vector
 //                   instruction issue (a wave64 instruction takes four cycles), so every pass
 //                   over the row is branch-free or skips its rare work behind one compare.
-//   golden_kernel   votes across layers, one thread per 32-entry word: the golden bits A[i].
-//   window kernels  per (window t, 256-word chunk): the OR of tau golden words and its count,
-//                   an exclusive scan of the counts into label_ptr and chunk positions, then
-//                   the ascending indices with their scores, the fraction of the window's
-//                   tokens whose golden set holds the entry.
+//   golden_kernel   votes across layers, one thread per 32-entry word (bit-sliced counts):
+//                   the golden bits A[i].
+//   window kernels  prefix and suffix ORs of the golden words within blocks of tau tokens;
+//                   per (window t, 256-word chunk): the window's OR from one suffix and one
+//                   prefix and its count, an exclusive scan of the counts into label_ptr and
+//                   chunk positions, then the ascending indices with their scores, the
+//                   fraction of the window's tokens whose golden set holds the entry.
 #include <float.h>
 #include <math.h>
 
@@ -294,10 +296,17 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
                 const uint64_t bm = __ballot(has && gt <= rp && rp < gt + eq);
                 if (ln == 0) L.m32[1] = bm ? 1u : 0u;
                 if (bm && ln == __ffsll((long long)bm) - 1) {
+                    // r = floor((rp - gt) / (eq / cnt)) of the cnt equal entries, below cnt as
+                    // rp - gt < eq; a single entry (the usual case) leaves r = 0
+                    uint32_t rr = 0u;
+                    if (cnt > 1u) {
+                        const u64 wq = eq / cnt;
+                        const u64 q = (rp - gt) / (wq ? wq : 1ull);
+                        rr = (uint32_t)(q < (u64)cnt ? q : (u64)cnt);
+                    }
                     L.m32[0] = key;
                     L.hc[0] = cnt;
-                    L.m64[0] = rp - gt;
-                    L.m64[1] = eq;
+                    L.hc[1] = rr;
                 }
             }
             __syncthreads();
@@ -305,11 +314,9 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
                 resolved = true;
                 xstar = key_score(L.m32[0]);
                 g = L.hc[0];
-                const u64 wq = L.m64[1] / g;
-                const u64 rr = L.m64[0] / (wq ? wq : 1ull);
-                r = (uint32_t)(rr < (u64)g ? rr : (u64)g);
+                r = L.hc[1];
             }
-            __syncthreads();                    // L.m32 / L.m64 / L.hc are read before reuse
+            __syncthreads();                    // L.m32 / L.hc are read before reuse
         }
         if (!resolved) {
             // the exact boundary score inside bin b1: radix over the 32-bit key, 11 + 11 + 10
@@ -419,34 +426,67 @@ __global__ __launch_bounds__(kNucNT) void nucleus_kernel(LabelArgs A) {
     }
 }
 
-// votes of token blockIdx.y across layers, one thread per 32-entry word
+// votes of token blockIdx.y across layers, one thread per 32-entry word.  The 32 entries' vote
+// counts are kept as seven bit planes (at most 64 layers): a layer's word enters through a
+// ripple of half adders, and count >= min_votes is the absence of a borrow out of
+// count - min_votes, taken plane by plane.
 __global__ __launch_bounds__(256) void golden_kernel(LabelArgs A) {
     const int wd = blockIdx.x * 256 + threadIdx.x, i = blockIdx.y;
     if (wd >= A.words) return;
-    uint32_t cnt[32];
-#pragma unroll
-    for (int b = 0; b < 32; ++b) cnt[b] = 0u;
     const uint32_t *m = A.mbits + (int64_t)i * A.n_layers * A.words + wd;
+    uint32_t c[7] = {0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll 8
     for (int l = 0; l < A.n_layers; ++l) {
-        const uint32_t x = m[(int64_t)l * A.words];
+        uint32_t carry = m[(int64_t)l * A.words];
 #pragma unroll
-        for (int b = 0; b < 32; ++b) cnt[b] += (x >> b) & 1u;
+        for (int q = 0; q < 7; ++q) {
+            const uint32_t t = c[q] & carry;
+            c[q] ^= carry;
+            carry = t;
+        }
     }
     uint32_t gw = 0u;
+    if (A.min_votes < 128) {
+        uint32_t borrow = 0u;
 #pragma unroll
-    for (int b = 0; b < 32; ++b) gw |= (cnt[b] >= (uint32_t)A.min_votes ? 1u : 0u) << b;
+        for (int q = 0; q < 7; ++q) {
+            const uint32_t mb = ((A.min_votes >> q) & 1) ? ~0u : 0u;
+            borrow = (~c[q] & (mb | borrow)) | (mb & borrow);
+        }
+        gw = ~borrow;
+    }
     A.gbits[(int64_t)i * A.words + wd] = gw;
 }
 
-// Window t = blockIdx.x, words [256 c, 256 c + 256) with c = blockIdx.y: the label words
-// (OR of the window's tau golden words) to the workspace, and their label count.
+// Prefix and suffix ORs of the golden words within blocks of tau consecutive tokens (block b
+// is tokens b tau .. b tau + tau - 1, the last one possibly shorter): P[i] = OR of the block's
+// tokens up to i, S[i] = OR of its tokens from i.  Thread: one word of one block.
+__global__ __launch_bounds__(256) void window_ps_kernel(LabelArgs A) {
+    const int wd = blockIdx.x * 256 + threadIdx.x, blk = blockIdx.y;
+    if (wd >= A.words) return;
+    const int i0 = blk * A.tau, i1 = min(A.T, i0 + A.tau);
+    uint32_t x = 0u;
+    for (int i = i0; i < i1; ++i) {
+        x |= A.gbits[(int64_t)i * A.words + wd];
+        A.pbits[(int64_t)i * A.words + wd] = x;
+    }
+    x = 0u;
+    for (int i = i1 - 1; i >= i0; --i) {
+        x |= A.gbits[(int64_t)i * A.words + wd];
+        A.sbits[(int64_t)i * A.words + wd] = x;
+    }
+}
+
+// Window t = blockIdx.x, words [256 c, 256 c + 256) with c = blockIdx.y: the label words (the
+// OR of the window's tau golden words) to the workspace, and their label count.  Tokens t ..
+// t + tau - 1 span the end of t's block and the start of the next, so the OR is S[t] |
+// P[t + tau - 1] (both S[t] when t starts a block).
 __global__ __launch_bounds__(kWinNT) void window_or_kernel(LabelArgs A) {
     __shared__ uint32_t sh[kWinNT / 64 + 1];
     const int t = blockIdx.x, c = blockIdx.y, wd = c * kWinNT + (int)threadIdx.x;
     uint32_t y = 0u;
     if (wd < A.words) {
-        const uint32_t *gb = A.gbits + (int64_t)t * A.words + wd;
-        for (int k = 0; k < A.tau; ++k) y |= gb[(int64_t)k * A.words];
+        y = A.sbits[(int64_t)t * A.words + wd] | A.pbits[(int64_t)(t + A.tau - 1) * A.words + wd];
         A.ybits[(int64_t)t * A.words + wd] = y;
     }
     uint32_t tot;
@@ -493,6 +533,7 @@ __global__ __launch_bounds__(kWinNT) void window_write_kernel(LabelArgs A) {
             A.label_idx[pos] = 32 * wd + b;
             if (A.label_score) {
                 int hits = 0;
+#pragma unroll 16
                 for (int k = 0; k < A.tau; ++k) hits += (gb[(int64_t)k * A.words] >> b) & 1u;
                 A.label_score[pos] = (float)hits / (float)A.tau;
             }
@@ -506,7 +547,7 @@ __global__ __launch_bounds__(kWinNT) void window_write_kernel(LabelArgs A) {
 size_t labels_ws_bytes(int T, int n_layers, int64_t ld, int tau) {
     const size_t words = (size_t)((ld + 31) / 32), windows = (size_t)(T - tau + 1);
     const size_t chunks = (words + kWinNT - 1) / kWinNT;
-    return align_up((size_t)T * n_layers * words * 4, 256) + align_up((size_t)T * words * 4, 256) +
+    return align_up((size_t)T * n_layers * words * 4, 256) + 3 * align_up((size_t)T * words * 4, 256) +
            align_up(windows * words * 4, 256) + align_up(windows * chunks * 4, 256);
 }
 
@@ -518,6 +559,10 @@ void labels_ws_carve(LabelArgs &a, void *ws) {
     p += align_up((size_t)a.T * a.n_layers * words * 4, 256);
     a.gbits = (uint32_t *)p;
     p += align_up((size_t)a.T * words * 4, 256);
+    a.pbits = (uint32_t *)p;
+    p += align_up((size_t)a.T * words * 4, 256);
+    a.sbits = (uint32_t *)p;
+    p += align_up((size_t)a.T * words * 4, 256);
     a.ybits = (uint32_t *)p;
     p += align_up(windows * words * 4, 256);
     a.counts = (int32_t *)p;
@@ -528,6 +573,8 @@ hipError_t launch_labels(const LabelArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     golden_kernel<<<dim3((unsigned)((a.words + 255) / 256), (unsigned)a.T), dim3(256), 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    window_ps_kernel<<<dim3((unsigned)((a.words + 255) / 256), (unsigned)((a.T + a.tau - 1) / a.tau)), dim3(256), 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 wgrid((unsigned)(a.T - a.tau + 1), (unsigned)a.chunks);
     window_or_kernel<<<wgrid, dim3(kWinNT), 0, s>>>(a);
