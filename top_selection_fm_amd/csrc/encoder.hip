@@ -190,16 +190,32 @@ __global__ __launch_bounds__(kNormNT) void enc_norm_kernel(EncNormArgs E) {
     }
 }
 
-// One wave per (row, hpw heads), four waves a workgroup: lane l holds dims 2 l, 2 l + 1 of each
-// head in turn.  The RoPE angle pos * theta_i is formed and reduced in fp64 (positions reach
-// millions of radians), once per row and pair: every head of the row turns by the same angles.
-__global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E, int hpw) {
+// One wave per (row, HPW heads), four waves a workgroup: lane l holds dims 2 l, 2 l + 1 of each
+// head in turn.  Every load of the wave's heads is issued before the first head is turned.  The
+// RoPE angle pos * theta_i is formed and reduced in fp64 (positions reach millions of radians),
+// once per row and pair: every head of the row turns by the same angles.
+template <int HPW>
+__global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E) {
     const int ln = __lane_id();
-    const int groups = E.n_heads / hpw;
+    const int groups = E.n_heads / HPW;
     const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (item >= (int64_t)E.M * groups) return;
-    const int m = (int)(item / groups), h0 = (int)(item % groups) * hpw;
+    const int m = (int)(item / groups), h0 = (int)(item % groups) * HPW;
     const int N = E.n_heads * kDim;
+    float2 xv[HPW];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) xv[hh] = make_float2(0.f, 0.f);
+    for (int z = 0; z < E.Z; ++z) {
+        const float *row = E.C + ((int64_t)z * E.M + m) * N + h0 * kDim + 2 * ln;
+        float2 p[HPW];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) p[hh] = *(const float2 *)&row[hh * kDim];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+            xv[hh].x += p[hh].x;
+            xv[hh].y += p[hh].y;
+        }
+    }
     // the rotation of pair ln at this row's position: the same for every head of the row
     const int first = (kDim - E.rope_dim) / 2;          // the first rotated pair
     float c = 1.f, sn = 0.f;
@@ -208,14 +224,9 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E, int hp
         c = (float)cos(ang);
         sn = (float)sin(ang);
     }
-    for (int hh = h0; hh < h0 + hpw; ++hh) {
-        float x0 = 0.f, x1 = 0.f;
-#pragma unroll 4
-        for (int z = 0; z < E.Z; ++z) {
-            const float2 xv = *(const float2 *)&E.C[((int64_t)z * E.M + m) * N + hh * kDim + 2 * ln];
-            x0 += xv.x;
-            x1 += xv.y;
-        }
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        float x0 = xv[hh].x, x1 = xv[hh].y;
         if (ln >= first) {
             const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
             x0 = y0;
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E, int hp
         }
         const float nrm = 0.08838834764831845f;              // 1 / sqrt(128)
         const uint32_t packed = (uint32_t)bf16_rne(x0 * nrm) | ((uint32_t)bf16_rne(x1 * nrm) << 16);
-        *(uint32_t *)&E.q[((int64_t)m * E.n_heads + hh) * kDim + 2 * ln] = packed;
+        *(uint32_t *)&E.q[((int64_t)m * E.n_heads + h0 + hh) * kDim + 2 * ln] = packed;
     }
 }
 
@@ -422,9 +433,13 @@ hipError_t launch_enc_norm(const EncNormArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_enc_rope_had(const EncRopeArgs &a, hipStream_t s) {
-    const int hpw = a.M >= 256 ? kRopeHeadsPerWave : 1;
-    const int64_t items = (int64_t)a.M * (a.n_heads / hpw);
-    enc_rope_had_kernel<<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a, hpw);
+    if (a.M >= 256) {
+        const int64_t items = (int64_t)a.M * (a.n_heads / kRopeHeadsPerWave);
+        enc_rope_had_kernel<kRopeHeadsPerWave><<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a);
+    } else {
+        const int64_t items = (int64_t)a.M * a.n_heads;
+        enc_rope_had_kernel<1><<<dim3((unsigned)((items + 3) / 4)), 256, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
