@@ -113,6 +113,18 @@ def test_encoder_prefill_wide_tiles():
     check("encoder 600 rows x 256 heads, wide tiles (sampled)", qg[rows], wg[rows], qr, wr)
 
 
+@pytest.mark.timeout(300)
+def test_encoder_benchmarked_shape_sampled():
+    """The benchmarked prefill call: 4,096 rows at the page's sizes (d_model 4,096, q_rank
+    2,048, 128 heads), the same seeded inputs: sampled rows from every 256-row tile group
+    against the oracle."""
+    e = W.query_encoder(T=4096)
+    qg, wg = run_encoder(e)
+    rows = np.array([0, 1, 255, 256, 1000, 2047, 2048, 3071, 3072, 4094, 4095])
+    qr, wr = oracle_encoder(e, rows=rows)
+    check("encoder 4096 rows at the page's sizes (sampled)", qg[rows], wg[rows], qr, wr)
+
+
 def test_encoder_prefill_256_tiles():
     """1,100 rows x 256 heads: the second product (32,768 columns, 640 tiles of 256 x 256) takes
     the eight-wave 256 x 256 tiles, the last row tile holding 76 rows."""

@@ -174,12 +174,14 @@ def test_labels_boundary_bin_overflow():
     assert idx[ptr[0]:ptr[1]].tolist() == list(range(11000))
 
 
+@pytest.mark.timeout(300)
 def test_labels_page_shapes():
-    """21 layers x 65,536 entries (256K context at 4:1), 72 future tokens, p = 0.6, 3 votes,
-    tau = 64: nine windows, against the oracle; a repeat call is bit-identical."""
-    g = W.selector_scores(seed=2201, T=72)
+    """The benchmarked call: 128 future tokens x 21 layers x 65,536 entries (256K context at
+    4:1), p = 0.6, 3 votes, tau = 64 (65 windows), on the same seeded scores, against the
+    oracle; a repeat call is bit-identical."""
+    g = W.selector_scores()
     got = gpu_labels(g.scores, g.n_valid)
-    check_labels("labels 72 x 21 x 65536", g.scores, g.n_valid, 0.6, 3, 64, got)
+    check_labels("labels 128 x 21 x 65536", g.scores, g.n_valid, 0.6, 3, 64, got)
     again = gpu_labels(g.scores, g.n_valid)
     for a, b in zip(got, again):
         assert np.array_equal(a, b)
