@@ -465,15 +465,31 @@ __global__ __launch_bounds__(256) void window_ps_kernel(LabelArgs A) {
     const int wd = blockIdx.x * 256 + threadIdx.x, blk = blockIdx.y;
     if (wd >= A.words) return;
     const int i0 = blk * A.tau, i1 = min(A.T, i0 + A.tau);
+    const uint32_t *g = A.gbits + wd;
+    // sixteen tokens' words are loaded before any of their ORs is stored (the stores could
+    // alias the loads as far as the compiler knows)
+    constexpr int kB = 16;
     uint32_t x = 0u;
-    for (int i = i0; i < i1; ++i) {
-        x |= A.gbits[(int64_t)i * A.words + wd];
-        A.pbits[(int64_t)i * A.words + wd] = x;
+    for (int b0 = i0; b0 < i1; b0 += kB) {
+        uint32_t v[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) v[u] = b0 + u < i1 ? g[(int64_t)(b0 + u) * A.words] : 0u;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            x |= v[u];
+            if (b0 + u < i1) A.pbits[(int64_t)(b0 + u) * A.words + wd] = x;
+        }
     }
     x = 0u;
-    for (int i = i1 - 1; i >= i0; --i) {
-        x |= A.gbits[(int64_t)i * A.words + wd];
-        A.sbits[(int64_t)i * A.words + wd] = x;
+    for (int b1 = i1; b1 > i0; b1 -= kB) {
+        uint32_t v[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) v[u] = b1 - 1 - u >= i0 ? g[(int64_t)(b1 - 1 - u) * A.words] : 0u;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            x |= v[u];
+            if (b1 - 1 - u >= i0) A.sbits[(int64_t)(b1 - 1 - u) * A.words + wd] = x;
+        }
     }
 }
 
