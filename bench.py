@@ -640,7 +640,7 @@ def main():
         for name, fn in secondaries.items():
             log(f"secondary: {name} ...")
             try:
-                sec.append(fn(torch, api, W, max(5, args.steps // 2), 2))
+                sec.append(fn(torch, api, W, max(5, args.steps // 2), max(10, args.warmup)))
             except Exception as e:  # report and keep the headline
                 sec.append(dict(workload=name, error=repr(e)))
             torch.cuda.empty_cache()
