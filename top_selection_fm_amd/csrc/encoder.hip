@@ -19,7 +19,9 @@
 // activation (A) and the weight (B) alike, and the 32x32 accumulator register v of lane j + 32 h
 // is output row 8 (v / 4) + 4 h + v % 4, column j.  Decode-sized inputs (tens of rows) make
 // the products weight-bandwidth bound: Z workgroups of S waves share a 32 x 32 output tile, each
-// wave a K range, so that enough waves on enough CUs stream the weight matrix at once.
+// wave a K range, so that enough waves on enough CUs stream the weight matrix at once.  From
+// FM_ENC_TILED_MIN_ROWS rows the products are MFMA-bound and take enc_gemm_tiled_kernel (LDS
+// tiles, below) instead.
 #include <math.h>
 
 #include "fm_internal.h"
@@ -252,12 +254,13 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E) {
     }
 }
 
-// Prefill-sized products (hundreds of rows and more): a 128 x 128 output tile a workgroup,
-// staged through LDS 32 k-values at a time, so each A row and each weight row is read from
-// memory once per tile instead of once per 32 x 32 tile.  Four waves, each a 64 x 64 quarter
-// as 2 x 2 MFMA tiles; the next k-slab's global loads are in flight while the current one is
-// multiplied from the other LDS buffer.  LDS rows are padded to 40 bf16 (80 B), which keeps
-// the 16-byte operand reads of a wave conflict-free.  Z = 1 (no partial sums).
+// Prefill-sized products (hundreds of rows and more): a BM x BN output tile a workgroup
+// (256 x 256 with eight waves of 64 x 128, 128 x 256 with four of 64 x 128, or 128 x 128 with
+// four of 64 x 64), staged through LDS 32 k-values at a time, so each A row and each weight row
+// is read from memory once per tile instead of once per 32 x 32 tile.  The global loads run two
+// k-slabs ahead in two register stages while the current slab is multiplied from one of two
+// LDS buffers.  LDS rows are padded to 40 bf16 (80 B), which keeps the 16-byte operand reads of
+// a wave conflict-free.  Z = 1 (no partial sums).
 #ifndef FM_ENC_TK
 #define FM_ENC_TK 32
 #endif

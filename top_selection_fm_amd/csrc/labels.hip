@@ -6,7 +6,7 @@
 //   V[i,s]   = the number of layers whose nucleus holds s;  A[i] = {s : V[i,s] >= min_votes};
 //   Y[t]     = the union of A[i] over the lookahead window i = t .. t + tau - 1, as CSR.
 //
-// Four steps, each a kernel:
+// Three steps (the last one four kernels):
 //   nucleus_kernel  one workgroup per (token, layer) row holds the row in registers and finds
 //                   the nucleus boundary exactly: softmax masses in 2^-44 fixed point summed
 //                   as integers (so the sums, and with them every decision, are independent of
