@@ -566,9 +566,9 @@ def main():
     ap.add_argument("--only", default=None)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the indexer path shards by request with no communication; see the design "
-              f"notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the "
+              f"indexer path would shard by request across GPUs with no communication, so one "
+              f"GPU's throughput is the per-GPU figure).", file=sys.stderr)
         sys.exit(2)
 
     import torch
