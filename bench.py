@@ -31,7 +31,9 @@ two-level fp8 scoring over 384 resident pages, causal fp8 prefill, Mode A end to
 three-encoder mask, then the masked top-512 of 21 layers x 8 requests over 262,144 entries,
 every layer scoring its own fp8 pool), the retriever's query encoder at
 decode and prefill batch sizes, and golden-label construction from 128 tokens x 21 layers x
-65,536 selector scores.  cpu_baseline times the fp64 oracle on a bounded sample of
+65,536 selector scores.  Beside the published peaks, the line carries measured ceilings: a
+plain 1 GiB device copy (HBM) and the vendor GEMM library's fp8 and bf16 rates on random
+8192^3 products (dense MFMA); the MFMA-bound secondaries report their fraction of the latter.  cpu_baseline times the fp64 oracle on a bounded sample of
 the headline workload on the host cores.
 
 Prints exactly one JSON line on stdout.
@@ -558,6 +560,37 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     log(f"copy calibration: {reps} copies of {nbytes} bytes")
 
 
+def vendor_gemm_tflops(torch, n=8192, reps=20):
+    """Measured dense-MFMA ceilings on this GPU: the vendor GEMM library (through torch) on
+    n x n x n products of random operands, fp8 E4M3 (scaled, bf16 output) and bf16.  Random
+    operands matter: the chip's clock drops under their power, so zero or constant operands
+    would overstate the ceiling.  None where the library offers no kernel."""
+    def rate(fn):
+        for _ in range(3):
+            fn()
+        ms = b2b_ms(torch, lambda s: fn(), reps, 0)
+        return 2.0 * n * n * n / (ms * 1e-3) / 1e12
+    out = {}
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    a = torch.randn(n, n, device="cuda:0", generator=g) * 0.5
+    b = torch.randn(n, n, device="cuda:0", generator=g) * 0.5
+    try:
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn).t()
+        one = torch.tensor(1.0, device="cuda:0")
+        out["fp8_gemm_tflops"] = rate(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
+                                                               out_dtype=torch.bfloat16))
+        del a8, b8
+    except Exception as e:  # no fp8 GEMM in this build: report the gap, keep the rest
+        out["fp8_gemm_tflops"] = None
+        log(f"fp8 GEMM ceiling unavailable: {e!r}")
+    ab, bb = a.to(torch.bfloat16), b.to(torch.bfloat16)
+    out["bf16_gemm_tflops"] = rate(lambda: ab @ bb)
+    out["how"] = f"vendor GEMM {n}^3, random operands, events around {reps} back-to-back calls"
+    del a, b, ab, bb
+    torch.cuda.empty_cache()
+    return out
+
+
 def stream_copy_gbs(torch, nbytes=1 << 30, reps=10):
     """Measured HBM rate of a plain 1 GiB device-to-device copy (bytes read + written)."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_(0, 255)
@@ -659,6 +692,18 @@ def main():
                 sec.append(dict(workload=name, error=repr(e)))
             torch.cuda.empty_cache()
         line["secondary"] = sec
+        # the MFMA-bound lines against the measured GEMM ceilings beside the published peaks
+        ceil = vendor_gemm_tflops(torch)
+        line["measured_mfma_ceilings"] = ceil
+        for r in sec:
+            wname = r.get("workload", "")
+            if wname.startswith("prefill") and ceil.get("fp8_gemm_tflops") and "mfma_tflops" in r:
+                r["frac_of_vendor_fp8_gemm"] = r["mfma_tflops"] / ceil["fp8_gemm_tflops"]
+            if wname.endswith("shared_keys") and "mfma_tflops" in r:
+                r["frac_of_vendor_bf16_gemm"] = r["mfma_tflops"] / ceil["bf16_gemm_tflops"]
+            if wname.startswith("query_encoder") and "t4096" in r:
+                r["t4096"]["frac_of_vendor_bf16_gemm"] = (r["t4096"]["mfma_tflops"] /
+                                                          ceil["bf16_gemm_tflops"])
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(wl)
