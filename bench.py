@@ -592,10 +592,15 @@ def vendor_gemm_tflops(torch, n=8192, reps=20):
     except Exception as e:  # no fp8 GEMM in this build: report the gap, keep the rest
         out["fp8_gemm_tflops"] = None
         log(f"fp8 GEMM ceiling unavailable: {e!r}")
-    ab, bb = a.to(torch.bfloat16), b.to(torch.bfloat16)
-    out["bf16_gemm_tflops"] = rate(lambda: ab @ bb)
+    try:
+        ab, bb = a.to(torch.bfloat16), b.to(torch.bfloat16)
+        out["bf16_gemm_tflops"] = rate(lambda: ab @ bb)
+        del ab, bb
+    except Exception as e:
+        out["bf16_gemm_tflops"] = None
+        log(f"bf16 GEMM ceiling unavailable: {e!r}")
     out["how"] = f"vendor GEMM {n}^3, random operands, events around {reps} back-to-back calls"
-    del a, b, ab, bb
+    del a, b
     torch.cuda.empty_cache()
     return out
 
@@ -704,15 +709,15 @@ def main():
         # the MFMA-bound lines against the measured GEMM ceilings beside the published peaks
         ceil = vendor_gemm_tflops(torch)
         line["measured_mfma_ceilings"] = ceil
+        f8, b16 = ceil.get("fp8_gemm_tflops"), ceil.get("bf16_gemm_tflops")
         for r in sec:
             wname = r.get("workload", "")
-            if wname.startswith("prefill") and ceil.get("fp8_gemm_tflops") and "mfma_tflops" in r:
-                r["frac_of_vendor_fp8_gemm"] = r["mfma_tflops"] / ceil["fp8_gemm_tflops"]
-            if wname.endswith("shared_keys") and "mfma_tflops" in r:
-                r["frac_of_vendor_bf16_gemm"] = r["mfma_tflops"] / ceil["bf16_gemm_tflops"]
-            if wname.startswith("query_encoder") and "t4096" in r:
-                r["t4096"]["frac_of_vendor_bf16_gemm"] = (r["t4096"]["mfma_tflops"] /
-                                                          ceil["bf16_gemm_tflops"])
+            if wname.startswith("prefill") and f8 and "mfma_tflops" in r:
+                r["frac_of_vendor_fp8_gemm"] = r["mfma_tflops"] / f8
+            if wname.endswith("shared_keys") and b16 and "mfma_tflops" in r:
+                r["frac_of_vendor_bf16_gemm"] = r["mfma_tflops"] / b16
+            if wname.startswith("query_encoder") and b16 and "t4096" in r:
+                r["t4096"]["frac_of_vendor_bf16_gemm"] = r["t4096"]["mfma_tflops"] / b16
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(wl)
