@@ -303,7 +303,8 @@ size_t fm_workspace_bytes(fm_op op, int T, int64_t max_candidates);
  *     over rope_orig_len (YaRN's per-dimension interpolation; no temperature factor)
  *   q[t] = x . H / sqrt(head_dim), H Sylvester's Hadamard matrix (per head)
  *   w[t] = (hidden[t] . w_proj^T) * head_dim^-0.5 * n_heads^-0.5
- * Weights are Linear weights ([out, in] row-major bf16), all device pointers.  The products
+ * Weights are Linear weights ([out, in] row-major bf16; wq_a, wq_b and w_proj 16-byte
+ * aligned), all device pointers.  The products
  * accumulate in float32, r is rounded to bf16 (the operand of the second product), q is
  * rounded to bf16 at the end; w is float32.  q and w are the fm_query_desc inputs of the
  * scoring calls (q_dtype FM_BF16, w_dtype FM_F32) when n_heads is 64.

@@ -346,6 +346,9 @@ def test_encode_queries_validation():
     assert st(e=good_enc(rope_factor=0.5)) == api.FM_ERR_INVALID_ARG
     assert st(e=good_enc(beta_fast=0.5)) == api.FM_ERR_INVALID_ARG
     assert st(e=good_enc(wq_b=None)) == api.FM_ERR_INVALID_ARG
+    assert st(e=good_enc(wq_a=FAKE + 8)) == api.FM_ERR_INVALID_ARG     # weights 16-byte aligned
+    assert st(e=good_enc(wq_b=FAKE + 8)) == api.FM_ERR_INVALID_ARG
+    assert st(e=good_enc(w_proj=FAKE + 8)) == api.FM_ERR_INVALID_ARG
     assert st(T=-1) == api.FM_ERR_INVALID_ARG
     assert st(h=None) == api.FM_ERR_INVALID_ARG
     assert st(pos=None) == api.FM_ERR_INVALID_ARG

@@ -93,9 +93,10 @@ def test_encoder_many_rows_sampled():
 
 
 def test_encoder_prefill_tiled_products():
-    """1,000 rows: both products take the LDS-tiled kernel (128 x 128 tiles, the last row tile
-    and, with 2,112 columns, the last column tile partial; d_model 528 leaves a 16-wide K tail;
-    the first product's columns straddle the wq_a / w_proj boundary inside a tile)."""
+    """1,000 rows: d_model 528 leaves a 16-wide K tail, so the first product takes the
+    register-staged 128 x 128 tiles (the last row tile and, with 2,112 columns, the last column
+    tile partial; its columns straddle the wq_a / w_proj boundary inside a tile); the second
+    (8,192 columns) takes the direct-copy 128 x 128 tiles, 512 of them."""
     e = W.query_encoder(seed=3106, T=1000, n_heads=64, d_model=528, q_rank=2048)
     qg, wg = run_encoder(e)
     rows = np.array([0, 1, 127, 128, 255, 500, 896, 999])
@@ -104,8 +105,8 @@ def test_encoder_prefill_tiled_products():
 
 
 def test_encoder_prefill_wide_tiles():
-    """600 rows x 256 heads: the second product (32,768 columns) takes the 128 x 256 tiles
-    (a partial last row tile)."""
+    """600 rows x 256 heads: the second product (32,768 columns) takes the 128 x 256
+    direct-copy tiles (a partial last row tile), with three LDS stages."""
     e = W.query_encoder(seed=3107, T=600, n_heads=256, d_model=256, q_rank=512)
     qg, wg = run_encoder(e)
     rows = np.array([0, 63, 64, 127, 128, 300, 511, 512, 599])
@@ -117,7 +118,9 @@ def test_encoder_prefill_wide_tiles():
 def test_encoder_benchmarked_shape_sampled():
     """The benchmarked prefill call: 4,096 rows at the page's sizes (d_model 4,096, q_rank
     2,048, 128 heads), the same seeded inputs: sampled rows from every 256-row tile group
-    against the oracle."""
+    against the oracle.  Both products take the 256 x 256 direct-copy tiles; the first has 144
+    of them (2,176 columns, the last column tile half full, the wq_a / w_proj boundary inside
+    it)."""
     e = W.query_encoder(T=4096)
     qg, wg = run_encoder(e)
     rows = np.array([0, 1, 255, 256, 1000, 2047, 2048, 3071, 3072, 4094, 4095])

@@ -20,9 +20,13 @@
 // is output row 8 (v / 4) + 4 h + v % 4, column j.  Decode-sized inputs (tens of rows) make
 // the products weight-bandwidth bound: Z workgroups of S waves share a 32 x 32 output tile, each
 // wave a K range, so that enough waves on enough CUs stream the weight matrix at once.  From
-// FM_ENC_TILED_MIN_ROWS rows the products are MFMA-bound and take enc_gemm_tiled_kernel (LDS
-// tiles, below) instead.
+// FM_ENC_TILED_MIN_ROWS rows the products are MFMA-bound and take LDS-tiled kernels (below):
+// enc_gemm_dma_kernel, whose operands are copied from memory straight into LDS, when K is a
+// multiple of 32 and the operands are 16-byte aligned, else enc_gemm_tiled_kernel, which
+// stages them through registers.
 #include <math.h>
+
+#include <type_traits>
 
 #include "fm_internal.h"
 
@@ -257,10 +261,11 @@ __global__ __launch_bounds__(256) void enc_rope_had_kernel(EncRopeArgs E) {
 // Prefill-sized products (hundreds of rows and more): a BM x BN output tile a workgroup
 // (256 x 256 with eight waves of 64 x 128, 128 x 256 with four of 64 x 128, or 128 x 128 with
 // four of 64 x 64), staged through LDS 32 k-values at a time, so each A row and each weight row
-// is read from memory once per tile instead of once per 32 x 32 tile.  The global loads run two
-// k-slabs ahead in two register stages while the current slab is multiplied from one of two
-// LDS buffers.  LDS rows are padded to 40 bf16 (80 B), which keeps the 16-byte operand reads of
-// a wave conflict-free.  Z = 1 (no partial sums).
+// is read from memory once per tile instead of once per 32 x 32 tile.  This kernel (128 x 128,
+// for K not a multiple of 32) runs the global loads two k-slabs ahead in two register stages
+// while the current slab is multiplied from one of two LDS buffers, zeroing the pieces past K.
+// LDS rows are padded to 40 bf16 (80 B), which keeps the 16-byte operand reads of a wave
+// conflict-free.  Z = 1 (no partial sums).
 #ifndef FM_ENC_TK
 #define FM_ENC_TK 32
 #endif
@@ -269,16 +274,14 @@ constexpr int kTK = FM_ENC_TK, kTLd = kTK + 8;
 #define FM_ENC_WIDE_TILES 512
 #endif
 constexpr int kWideTiles = FM_ENC_WIDE_TILES;
+#ifndef FM_ENC_BIG_TILES_MIN
+#define FM_ENC_BIG_TILES_MIN 128
+#endif
+constexpr int kBigTilesMin = FM_ENC_BIG_TILES_MIN;
 #ifndef FM_ENC_GROUP_M
 #define FM_ENC_GROUP_M 4
 #endif
 constexpr int kTGroupM = FM_ENC_GROUP_M;
-#ifndef FM_ENC_T256_WGM
-#define FM_ENC_T256_WGM 4            // 256 x 256 tiles: 4 x 2 waves of 64 x 128
-#endif
-#ifndef FM_ENC_T256_WPE
-#define FM_ENC_T256_WPE 2
-#endif
 
 template <int BM, int BN, int WGM, int WGN, int WPE>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE)))
@@ -400,6 +403,152 @@ void enc_gemm_tiled_kernel(EncGemmArgs G) {
         }
 }
 
+
+// Prefill-sized products with the operands copied straight from memory into LDS: each wave
+// instruction of global_load_lds_dwordx4 lands 64 pieces of 16 bytes contiguously in LDS, so
+// no register staging is needed and S - 1 slabs of 32 k values stay in flight while one is
+// multiplied.  Tiles and waves as in enc_gemm_tiled_kernel.  A slab row is 64 bytes; its four
+// 16-byte pieces are stored in the order piece ^ dma_swz(row), which puts the 16-byte operand
+// reads of any 8 or 16 consecutive rows on distinct bank groups.  Each stage is an LDS array
+// of its own, chosen at compile time (the slab loop is unrolled by S), and each step waits for
+// its own slab's copies only (vmcnt) before a plain barrier: a barrier with the workgroup
+// fence would wait for every copy in flight.  Copies past the last slab reload it into stages
+// that no later step reads, so every step waits for the same count.  Both 16-wide k steps'
+// operands of a slab are read before its first MFMA.  Taken when K is a multiple of 32 and
+// the operands (rows of A included) are 16-byte aligned.
+__device__ __forceinline__ int dma_swz(int r) { return ((r >> 1) & 2) | (((r >> 1) ^ (r >> 3)) & 1); }
+
+template <int BM, int BN, int WGM, int WGN, int WPE, int S>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE)))
+void enc_gemm_dma_kernel(EncGemmArgs G) {
+    constexpr int NW = WGM * WGN, TI = BM / WGM / 32, TJ = BN / WGN / 32;
+    constexpr int PA = BM / 16 / NW, PW = BN / 16 / NW;     // 1 KB row blocks a wave copies
+    static_assert(PA * 16 * NW == BM && PW * 16 * NW == BN && PA >= 1 && PW >= 1, "copy layout");
+    static_assert(S >= 2 && S <= 4, "stages");
+    typedef __attribute__((address_space(3))) void lds_void;
+    __shared__ __align__(16) uint8_t sA0[BM * 64], sW0[BN * 64], sA1[BM * 64], sW1[BN * 64];
+    __shared__ __align__(16) uint8_t sA2[S > 2 ? BM * 64 : 16], sW2[S > 2 ? BN * 64 : 16];
+    __shared__ __align__(16) uint8_t sA3[S > 3 ? BM * 64 : 16], sW3[S > 3 ? BN * 64 : 16];
+    auto stA = [&](auto st) -> uint8_t * {
+        if constexpr (decltype(st)::value == 0) return sA0;
+        else if constexpr (decltype(st)::value == 1) return sA1;
+        else if constexpr (decltype(st)::value == 2) return sA2;
+        else return sA3;
+    };
+    auto stW = [&](auto st) -> uint8_t * {
+        if constexpr (decltype(st)::value == 0) return sW0;
+        else if constexpr (decltype(st)::value == 1) return sW1;
+        else if constexpr (decltype(st)::value == 2) return sW2;
+        else return sW3;
+    };
+    const int tid = threadIdx.x, ln = __lane_id(), j = ln & 31, h = ln >> 5, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int N = G.N0 + G.N1;
+    // tile order as in enc_gemm_tiled_kernel
+    const int mT = (G.M + BM - 1) / BM, nTl = (N + BN - 1) / BN, total = mT * nTl;
+    const int b = blockIdx.x, x = b % 8, per = total / 8, rem = total % 8;
+    const int t = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + b / 8;
+    const int grp = t / (kTGroupM * nTl), fm = grp * kTGroupM, gs = min(kTGroupM, mT - fm);
+    const int within = t - grp * kTGroupM * nTl;
+    const int m0 = (fm + within % gs) * BM, n0 = (within / gs) * BN;
+    // wave w copies row blocks w P .. w P + P - 1 (16 rows each) of each tile; lane l carries
+    // row 16 block + l / 4 and LDS piece l % 4, i.e. the row's piece (l % 4) ^ dma_swz(row)
+    const uint16_t *srcA[PA], *srcW[PW];
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+        const int r = 16 * (PA * wave + i) + (ln >> 2);
+        srcA[i] = G.A + (int64_t)min(m0 + r, G.M - 1) * G.lda + 8 * ((ln & 3) ^ dma_swz(r));
+    }
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+        const int r = 16 * (PW * wave + i) + (ln >> 2);
+        const int n = min(n0 + r, N - 1);
+        srcW[i] = (n < G.N0 ? G.W0 + (int64_t)n * G.K : G.W1 + (int64_t)(n - G.N0) * G.K) +
+                  8 * ((ln & 3) ^ dma_swz(r));
+    }
+    const int nk = G.K / 32;
+    auto issue = [&](auto st, int slab) {
+        const int k0 = 32 * min(slab, nk - 1);
+#pragma unroll
+        for (int i = 0; i < PA; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(srcA[i] + k0),
+                                             (lds_void *)(stA(st) + 1024 * (PA * wave + i)), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < PW; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(srcW[i] + k0),
+                                             (lds_void *)(stW(st) + 1024 * (PW * wave + i)), 16, 0, 0);
+    };
+    f32x16 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TJ; ++jj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
+    auto compute = [&](auto st) {
+        const uint8_t *a_s = stA(st), *w_s = stW(st);
+        u32x4 a[2][TI], bw[2][TJ];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int r = wm * (BM / WGM) + 32 * i + j;
+                a[ks][i] = *(const u32x4 *)(a_s + 64 * r + 16 * ((2 * ks + h) ^ dma_swz(r)));
+            }
+#pragma unroll
+            for (int jj = 0; jj < TJ; ++jj) {
+                const int r = wn * (BN / WGN) + 32 * jj + j;
+                bw[ks][jj] = *(const u32x4 *)(w_s + 64 * r + 16 * ((2 * ks + h) ^ dma_swz(r)));
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int jj = 0; jj < TJ; ++jj) acc[i][jj] = mma(a[ks][i], bw[ks][jj], acc[i][jj]);
+    };
+    // s_waitcnt vmcnt(n), the other counters left alone (vmcnt in bits 3:0 and 15:14)
+    constexpr int kWaitN = (PA + PW) * (S - 2);
+    constexpr int kWaitImm = (kWaitN & 15) | ((kWaitN >> 4) << 14) | (7 << 4) | (15 << 8);
+    auto step = [&](auto st, int slab) {
+        __builtin_amdgcn_s_waitcnt(kWaitImm);              // this wave's copies of the slab
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();                      // every wave's; and the stage refilled
+        __builtin_amdgcn_sched_barrier(0);                 // below was last read a step ago
+        asm volatile("" ::: "memory");
+        issue(std::integral_constant<int, (decltype(st)::value + S - 1) % S>(), slab + S - 1);
+        compute(st);
+    };
+    issue(std::integral_constant<int, 0>(), 0);           // S - 1 slabs in flight
+    if constexpr (S > 2) issue(std::integral_constant<int, 1>(), 1);
+    if constexpr (S > 3) issue(std::integral_constant<int, 2>(), 2);
+    int kt = 0;
+    for (; kt + S <= nk; kt += S) {
+        step(std::integral_constant<int, 0>(), kt);
+        step(std::integral_constant<int, 1>(), kt + 1);
+        if constexpr (S > 2) step(std::integral_constant<int, 2>(), kt + 2);
+        if constexpr (S > 3) step(std::integral_constant<int, 3>(), kt + 3);
+    }
+    const int left = nk - kt;                              // the last nk % S slabs
+    if (left > 0) step(std::integral_constant<int, 0>(), kt);
+    if constexpr (S > 2) if (left > 1) step(std::integral_constant<int, 1>(), kt + 1);
+    if constexpr (S > 3) if (left > 2) step(std::integral_constant<int, 2>(), kt + 2);
+    __builtin_amdgcn_s_waitcnt(0);                         // no copy outlives the workgroup
+    // accumulator v of lane j + 32 h: row 8 (v / 4) + 4 h + v % 4, column j of its MFMA tile
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < TJ; ++jj) {
+            const int col = n0 + wn * (BN / WGN) + 32 * jj + j;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * (BM / WGM) + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (row < G.M && col < N) G.C[(int64_t)row * N + col] = acc[i][jj][v];
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
@@ -410,12 +559,24 @@ hipError_t launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
         const int n = g.N0 + g.N1;
         const int t256 = ((g.M + 255) / 256) * ((n + 255) / 256);
         const int wide = ((g.M + 127) / 128) * ((n + 255) / 256);
-        if (t256 >= kWideTiles)
-            enc_gemm_tiled_kernel<256, 256, FM_ENC_T256_WGM, 2, FM_ENC_T256_WPE><<<dim3((unsigned)t256), 128 * FM_ENC_T256_WGM, 0, s>>>(g);
+        const unsigned t128 = (unsigned)(((g.M + 127) / 128) * ((n + 127) / 128));
+        // copies straight into LDS need whole 32-wide slabs and 16-byte aligned rows
+        const bool dma = g.K % 32 == 0 && g.lda % 8 == 0 && (uintptr_t)g.A % 16 == 0 &&
+                         (uintptr_t)g.W0 % 16 == 0 && (uintptr_t)g.W1 % 16 == 0;
+        // The largest tiles that give kWideTiles workgroups: 256 x 256, then 128 x 256, then
+        // 128 x 128 (two workgroups a CU).  When 128 x 128 tiles would spill past one round of
+        // two a CU, 256 x 256 tiles are faster down to kBigTilesMin workgroups (half the CUs
+        // idle).  The register-staged kernel takes the rest (K not a multiple of 32: the first
+        // product when d_model is an odd multiple of 16).
+        if (!dma)
+            enc_gemm_tiled_kernel<128, 128, 2, 2, 2><<<dim3(t128), 256, 0, s>>>(g);
+        else if (t256 >= kWideTiles ||
+                 (wide < kWideTiles && (int)t128 > kWideTiles && t256 >= kBigTilesMin))
+            enc_gemm_dma_kernel<256, 256, 4, 2, 2, 4><<<dim3((unsigned)t256), 512, 0, s>>>(g);
         else if (wide >= kWideTiles)
-            enc_gemm_tiled_kernel<128, 256, 2, 2, 2><<<dim3((unsigned)wide), 256, 0, s>>>(g);
+            enc_gemm_dma_kernel<128, 256, 2, 2, 2, 3><<<dim3((unsigned)wide), 256, 0, s>>>(g);
         else
-            enc_gemm_tiled_kernel<128, 128, 2, 2, 2><<<dim3((unsigned)(((g.M + 127) / 128) * ((n + 127) / 128))), 256, 0, s>>>(g);
+            enc_gemm_dma_kernel<128, 128, 2, 2, 2, 4><<<dim3(t128), 256, 0, s>>>(g);
         return hipGetLastError();
     }
     dim3 grid((unsigned)((g.N0 + g.N1) / 32), (unsigned)((g.M + 31) / 32), (unsigned)g.Z);

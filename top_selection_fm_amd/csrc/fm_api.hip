@@ -382,6 +382,8 @@ fm_status check_enc(const fm_encoder_desc *e) {
     REQUIRE(e, FM_ERR_INVALID_ARG, "encoder descriptor is NULL");
     REQUIRE(e->wq_a && e->q_norm && e->wq_b && e->w_proj, FM_ERR_INVALID_ARG,
             "encoder weight pointer is NULL");
+    REQUIRE(aligned(e->wq_a, 16) && aligned(e->wq_b, 16) && aligned(e->w_proj, 16),
+            FM_ERR_INVALID_ARG, "wq_a, wq_b and w_proj must be 16-byte aligned");
     REQUIRE(e->head_dim == FM_HEAD_DIM, FM_ERR_UNSUPPORTED, "head_dim %d (only %d)", e->head_dim,
             FM_HEAD_DIM);
     REQUIRE(e->d_model >= 16 && e->d_model % 16 == 0 && e->d_model <= (1 << 20),
