@@ -2,7 +2,7 @@
 
     python -m top_selection_fm_amd.profile_summary stats  TRACE_DIR  [--cmd "..."]
     python -m top_selection_fm_amd.profile_summary hbm    FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR [--cmd "..."]
-    python -m top_selection_fm_amd.profile_summary sq     TRACE_DIR PASS_DIR [PASS_DIR ...] --kernel NAME [--cmd "..."]
+    python -m top_selection_fm_amd.profile_summary sq     TRACE_DIR PASS_DIR [PASS_DIR ...] --kernel NAME[@GRID] [--cmd "..."]
     python -m top_selection_fm_amd.profile_summary traffic FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR --kernel NAME[@GRID] [...] [--cmd "..."]
 
 Each DIR is a rocprofv3 output directory written with --output-format csv (the
@@ -148,7 +148,11 @@ def cmd_traffic(a):
 
 
 def cmd_sq(a):
-    ds = [d for (n, g), v in trace(a.dirs[0]).items() if n == a.kernel[0] for d in v]
+    # NAME or NAME@GRID: the dispatches of one kernel, or of one kernel at one grid size
+    name, grid = (a.kernel[0].split("@")[0], int(a.kernel[0].split("@")[1])) if "@" in a.kernel[0] \
+        else (a.kernel[0], None)
+    pick = lambda n, g: n == name and (grid is None or g == grid)
+    ds = [d for (n, g), v in trace(a.dirs[0]).items() if pick(n, g) for d in v]
     if not ds:
         sys.exit("kernel not in the trace")
     us = statistics.median(ds)
@@ -156,11 +160,12 @@ def cmd_sq(a):
     vals = {}
     for d in a.dirs[1:]:
         per = counters(d)
-        keys = [k for k in per if k[0] == a.kernel[0]]
+        keys = [k for k in per if pick(k[0], k[1])]
         for c in per[keys[0]]:
             vals[c] = statistics.median(per[k][c] for k in keys)
     q = lambda c: 4 * vals[c] / (SIMDS * cyc)
-    out = [f"# rocprofv3 SQ counters of {a.kernel[0]}, median over its dispatches, MI355X",
+    what = name + (f" (grid {grid})" if grid is not None else "")
+    out = [f"# rocprofv3 SQ counters of {what}, median over its dispatches, MI355X",
            f"# command: {a.cmd}" if a.cmd else "# command: (not given)",
            f"# kernel_sources: {kernel_sources_digest(a.root)}",
            f"# kernel time: median {us:.1f} us over {len(ds)} traced dispatches = {cyc:.4g} cycles at 2.4 GHz",
