@@ -202,11 +202,11 @@ struct FusePlan {
     bool fused;
     int ppw, n_chunks, ppw_pad;
 };
-FusePlan fuse_plan(int T, int64_t n_slots, int k, int nw, int ring) {
+FusePlan fuse_plan(int T, int64_t n_slots, int k, int nw, int ring, int max_ppw) {
     FusePlan p{false, 0, 0, 0};
     if (nw <= 0 || T <= 0 || n_slots <= 0) return p;
     constexpr int64_t kWgTarget = 256;
-    auto clamp_ppw = [](int64_t x) { return x < 1 ? (int64_t)1 : (x > 16 ? (int64_t)16 : x); };
+    auto clamp_ppw = [&](int64_t x) { return x < 1 ? (int64_t)1 : (x > max_ppw ? (int64_t)max_ppw : x); };
     auto chunks_of = [&](int64_t ppw) { return (n_slots + nw * ppw - 1) / (nw * ppw); };
     int64_t ppw = clamp_ppw(((int64_t)T * n_slots + kWgTarget * nw - 1) / (kWgTarget * nw));
     int64_t ch = chunks_of(ppw);
@@ -237,7 +237,7 @@ fm_status score_select(const fm_query_desc *q, const fm_kv_desc *kv, const int32
     const fm::FuseShape fs = fm::fuse_shape(kf, qf, q->n_heads);
     const bool prefill = q->q_dtype == FM_FP8_E4M3 && kv->B == 1 && q->T >= 16 && !res_pages &&
                          !q->row_pool;
-    const FusePlan p = prefill ? FusePlan{false, 0, 0, 0} : fuse_plan(q->T, n_slots, k, fs.waves, fs.round);
+    const FusePlan p = prefill ? FusePlan{false, 0, 0, 0} : fuse_plan(q->T, n_slots, k, fs.waves, fs.round, fs.max_ppw);
     if (p.fused) {
         fm::ScoreArgs a;
         a.q = make_q(q, kv);

@@ -240,7 +240,7 @@ hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t 
 // Fused scoring + top-k (ScoreArgs.out: the logits too, or null).  fuse_shape: W waves a
 // workgroup (0: no fused kernel for the format) and the page count a wave's slots are padded to.
 struct FuseShape {
-    int waves, round;
+    int waves, round, max_ppw;    // waves a workgroup, ring (page slots a multiple of), slots a wave
 };
 FuseShape fuse_shape(int key_fmt, int q_fmt, int n_heads);
 hipError_t launch_score_topk(const ScoreArgs &a, const FuseArgs &f, int key_fmt, int q_fmt,

@@ -91,6 +91,8 @@ constexpr int kSlotInvisible = -1;  // every entry of the page is past the visib
 constexpr int kSlotUnmapped = -2;   // the block table (or resident list) points nowhere valid
 constexpr int kSlotEmpty = -3;      // resident-list slot beyond n_resident: nothing to write
 constexpr int kMaxPpw = 16;         // page slots per wave, at most
+constexpr int kF8FuseMaxPpw = 24;   // ... in the fused fp8 kernel, so that Mode A's 4,096-page
+                                    // rows fit 16 chunks (12 waves x 22 slots)
 constexpr int kStorePolicy = 0;     // logit stores: default cache policy (see store_wave_logits)
 constexpr int kMaskPpw = FM_MASK_MAXPPW;   // pages per wave of the fp8 mask kernel, at most
 
@@ -1511,13 +1513,13 @@ void score_f8_kernel(ScoreArgs A) {
 // fp8 keys x bf16 queries, 64 heads (two-level scoring, Mode A over fp8 pools), NW waves a
 // workgroup scoring one row's chunk: the 32-entry tile stream of score_f8_kernel with the
 // query fragments staged in LDS for the workgroup, logits into LDS, then the fused selection.
-template <int RING, int NW>
+template <int RING, int NW, int MAXPPW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FM_F8_WPE)))
 void score_topk_f8_kernel(ScoreArgs A, FuseArgs F) {
     constexpr int NT = 64 * NW;
     extern __shared__ __align__(16) float s_dyn[];          // [NW][ppw_pad][64] logits
     __shared__ u32x4 s_qa[16 * 64];                          // fragment (m, s) at (8 m + s) 64
-    __shared__ int32_t s_base[NW * kMaxPpw];
+    __shared__ int32_t s_base[NW * MAXPPW];
     __shared__ FuseLds<NT> S;
     // workgroup (chunk, row) = (id / T8, id % T8), T8 = T rounded up to 8: the workgroups go to
     // the 8 XCDs in turn, so every chunk of row t runs on the XCD of the merge workgroup t
@@ -1574,7 +1576,8 @@ void score_topk_f8_kernel(ScoreArgs A, FuseArgs F) {
     if (ppw_pad <= 4) sel(std::integral_constant<int, 4>());
     else if (ppw_pad <= 8) sel(std::integral_constant<int, 8>());
     else if (ppw_pad <= 12) sel(std::integral_constant<int, 12>());
-    else sel(std::integral_constant<int, 16>());
+    else if (MAXPPW <= 16 || ppw_pad <= 16) sel(std::integral_constant<int, 16>());
+    else sel(std::integral_constant<int, MAXPPW>());
 }
 
 // ---------------------------------------------------------------- fp32 path (VALU)
@@ -2073,9 +2076,10 @@ hipError_t launch_score(const ScoreArgs &a, int key_fmt, int q_fmt, hipStream_t 
 #endif
 FuseShape fuse_shape(int key_fmt, int q_fmt, int n_heads) {
     if (key_fmt == KEY_BF16 && q_fmt == Q_BF16 && n_heads == kHeads)
-        return FuseShape{16, FM_BF16_RING ? FM_BF16_RING : 4};
-    if (key_fmt == KEY_FP8 && q_fmt == Q_BF16 && n_heads == kHeads) return FuseShape{FM_FUSE_F8_WAVES, 4};
-    return FuseShape{0, 1};                          // no fused kernel for this format
+        return FuseShape{16, FM_BF16_RING ? FM_BF16_RING : 4, kMaxPpw};
+    if (key_fmt == KEY_FP8 && q_fmt == Q_BF16 && n_heads == kHeads)
+        return FuseShape{FM_FUSE_F8_WAVES, 4, kF8FuseMaxPpw};
+    return FuseShape{0, 1, 1};                       // no fused kernel for this format
 }
 
 hipError_t launch_score_topk(const ScoreArgs &a, const FuseArgs &f, int key_fmt, int q_fmt,
@@ -2086,8 +2090,13 @@ hipError_t launch_score_topk(const ScoreArgs &a, const FuseArgs &f, int key_fmt,
         score_topk_bf16_kernel<FM_BF16_RING ? FM_BF16_RING : 4, NW>
             <<<grid, 64 * NW, (size_t)NW * f.ppw_pad * 64 * 4, s>>>(a, f);
     } else if (key_fmt == KEY_FP8 && q_fmt == Q_BF16 && a.q.n_heads == kHeads) {
+        // rows longer than 16 slots a wave (Mode A's 4,096-page rows) take their own
+        // instantiation, so the shorter rows' kernel keeps its registers
         constexpr int NW = FM_FUSE_F8_WAVES;
-        score_topk_f8_kernel<FM_F8_RING, NW><<<grid, 64 * NW, (size_t)NW * f.ppw_pad * 64 * 4, s>>>(a, f);
+        if (f.ppw_pad <= kMaxPpw)
+            score_topk_f8_kernel<FM_F8_RING, NW, kMaxPpw><<<grid, 64 * NW, (size_t)NW * f.ppw_pad * 64 * 4, s>>>(a, f);
+        else
+            score_topk_f8_kernel<FM_F8_RING, NW, kF8FuseMaxPpw><<<grid, 64 * NW, (size_t)NW * f.ppw_pad * 64 * 4, s>>>(a, f);
     } else {
         return hipErrorInvalidValue;
     }
