@@ -411,7 +411,7 @@ def run_mode_a(torch, api, W, steps, warmup):
     logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
     score_ms = b2b_ms(torch, lambda s: api.fm_index_logits(q2, kv_all, logits, ld), steps, warmup)
     del logits
-    n_vis = int(wl.kv.seq_lens.sum())                  # per layer
+    n_vis = int(wl.kv.seq_lens.sum())     # entries of one layer over all requests (a row sees its own)
     resident = int(mask.sum().item())
     l1_alg = n_enc * n_vis * 132 + n_enc * B * (64 * 128 * 2 + 64 * 2) + \
         wl.kv.block_table.nbytes + B * ld + B * n_pages * 4
@@ -421,8 +421,8 @@ def run_mode_a(torch, api, W, steps, warmup):
         wl.kv.block_table.nbytes + B * ld) + T * 512 * 4
     step_ms = wall / steps * 1e3
     return dict(workload=f"mode_a_fp8_b{B}_l{T // B}_s{ld}_top512", rows=T,
-                candidates=T * n_vis, resident_entries_per_request=resident / B,
-                ms_per_step=step_ms, entries_per_s=T * n_vis / (step_ms * 1e-3),
+                candidates=(T // B) * n_vis, resident_entries_per_request=resident / B,
+                ms_per_step=step_ms, entries_per_s=(T // B) * n_vis / (step_ms * 1e-3),
                 level1_ms=l1_ms, level2_ms=l2_ms, level2_scoring_only_ms=score_ms,
                 level2_selection_share=max(0.0, 1 - score_ms / l2_ms),
                 level1_share=l1_ms / (l1_ms + l2_ms),
