@@ -411,7 +411,7 @@ def run_mode_a(torch, api, W, steps, warmup):
     logits = torch.empty((T, ld), dtype=torch.float32, device=dev)
     score_ms = b2b_ms(torch, lambda s: api.fm_index_logits(q2, kv_all, logits, ld), steps, warmup)
     del logits
-    n_vis = int(wl.kv.seq_lens.sum())     # entries of one layer over all requests (a row sees its own)
+    n_vis = int(wl.kv.seq_lens.sum())     # one layer over all requests (a row sees its own)
     resident = int(mask.sum().item())
     l1_alg = n_enc * n_vis * 132 + n_enc * B * (64 * 128 * 2 + 64 * 2) + \
         wl.kv.block_table.nbytes + B * ld + B * n_pages * 4
