@@ -188,8 +188,9 @@ def test_row_pool_two_level(small, small_dev):
 @pytest.mark.timeout(600)
 def test_mode_a_full_size_sampled():
     """8 requests x 21 layers x 262,144 entries, as timed: the mask, then one fm_index_topk
-    call over the 168 rows.  Sampled rows against the oracle; every row's result is checked
-    for what any correct answer satisfies (ascending, resident, visible, count)."""
+    call over the 168 rows.  Every row equals fm_index_logits + fm_topk512 under the mask bit
+    for bit and satisfies what any correct answer does (ascending, resident, visible, count);
+    sampled rows against the oracle."""
     wl = W.mode_a_fp8()
     dw = api.DeviceWorkload(wl, "cuda:0")
     B, n_layers = wl.kv.B, wl.meta["n_layers"]
@@ -208,6 +209,18 @@ def test_mode_a_full_size_sampled():
         assert np.all(np.diff(sel) > 0) and np.all(ig[t][sel.size:] == -1)
         assert np.all(mask_np[b, sel] != 0) and np.all(sel < wl.kv.seq_lens[b])
         assert np.all(np.isfinite(vg[t][:sel.size])) and np.all(np.isneginf(vg[t][sel.size:]))
+    # the call runs fused (24 page slots a wave, 15 chunks a row): it equals the logits written
+    # by fm_index_logits and selected by fm_topk512 under the mask, bit for bit, on every row
+    ld = wl.kv.block_table.shape[1] * 64
+    L = torch.empty((B * n_layers, ld), dtype=torch.float32, device="cuda:0")
+    api.fm_index_logits(dw.query(N_ENC), dw.kv(), L, ld)
+    row_req = torch.from_numpy(np.ascontiguousarray(wl.queries[N_ENC].row_req)).to("cuda:0")
+    i2, v2 = G.topk(L, k=512, mask=m["mask"], row_req=row_req)
+    del L
+    assert torch.equal(idx, i2), "fused and two-call indices differ"
+    assert torch.equal(val.view(torch.int32), v2.view(torch.int32)), \
+        "fused and two-call values differ"
+    G.note("mode A full", step="fused equals two calls")
     for t in (0, 8 * 10 + 3, B * n_layers - 1):
         l, b = divmod(t, B)
         view = layer_view(wl, l)
