@@ -119,8 +119,8 @@ def test_encoder_benchmarked_shape_sampled():
     """The benchmarked prefill call: 4,096 rows at the page's sizes (d_model 4,096, q_rank
     2,048, 128 heads), the same seeded inputs: sampled rows from every 256-row tile group
     against the oracle.  Both products take the 256 x 256 direct-copy tiles; the first has 144
-    of them (2,176 columns, the last column tile half full, the wq_a / w_proj boundary inside
-    it)."""
+    of them (2,176 columns: the last column tile holds the 128 w_proj columns and is half
+    full)."""
     e = W.query_encoder(T=4096)
     qg, wg = run_encoder(e)
     rows = np.array([0, 1, 255, 256, 1000, 2047, 2048, 3071, 3072, 4094, 4095])
@@ -136,6 +136,24 @@ def test_encoder_prefill_256_tiles():
     rows = np.array([0, 63, 64, 255, 256, 700, 1023, 1024, 1099])
     qr, wr = oracle_encoder(e, rows=rows)
     check("encoder 1100 rows x 256 heads, 256 x 256 tiles (sampled)", qg[rows], wg[rows], qr, wr)
+
+
+@pytest.mark.parametrize("T,n_heads,d_model,q_rank", [
+    (300, 64, 32, 96),      # both products 128 x 128: one k slab (the first), three (the second)
+    (600, 256, 32, 32),     # one k slab each; the second product on 128 x 256 tiles
+    (1100, 256, 64, 160),   # the second product on 256 x 256 tiles: one round of slabs + one
+    (2100, 64, 96, 4000),   # the first on 256 x 256 tiles (3 slabs), the second on 128 x 256
+])                          # (125 slabs: 41 rounds of three + two)
+def test_encoder_direct_copy_slab_tails(T, n_heads, d_model, q_rank):
+    """The direct-copy products when K has fewer 32-wide slabs than the kernel has LDS stages,
+    or leaves a partial round of them, and when the wq_a / w_proj boundary (column q_rank)
+    falls inside a column tile rather than on a tile edge; partial row and column tiles."""
+    e = W.query_encoder(seed=3120 + q_rank, T=T, n_heads=n_heads, d_model=d_model, q_rank=q_rank)
+    qg, wg = run_encoder(e)
+    rows = np.unique(np.array([0, 1, 127, 128, 255, 256, T // 2, T - 2, T - 1]))
+    qr, wr = oracle_encoder(e, rows=rows)
+    check(f"encoder {T} x {n_heads} heads, d_model {d_model}, q_rank {q_rank} (sampled)",
+          qg[rows], wg[rows], qr, wr)
 
 
 @pytest.mark.parametrize("T", [255, 256, 257])
