@@ -589,7 +589,7 @@ def vendor_gemm_tflops(torch, n=8192, reps=20):
         out["fp8_gemm_tflops"] = rate(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
                                                                out_dtype=torch.bfloat16))
         del a8, b8
-    except Exception as e:  # no fp8 GEMM in this build: report the gap, keep the rest
+    except Exception as e:  # torch without an fp8 GEMM: report the gap, keep the rest
         out["fp8_gemm_tflops"] = None
         log(f"fp8 GEMM ceiling unavailable: {e!r}")
     try:
