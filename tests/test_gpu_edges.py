@@ -246,3 +246,34 @@ def test_resident_pages_out_of_range_are_skipped():
     sel = ig[1][ig[1] >= 0]
     assert sel.size == 5 * 64 and np.all(np.isfinite(vg[1][:sel.size]))
     assert set((sel // 64).tolist()) == set(rp[1].tolist()) - {10 ** 6}
+
+
+@pytest.mark.parametrize("cells", [False, True])
+def test_two_level_empty_and_short_resident_lists(cells):
+    """Per-request resident counts of 0 (nothing to select: all -1 / -inf), 3 pages (fewer
+    entries than k: every visible entry, ascending), and 12 pages (a real top-512), with list
+    positions past each count holding clean pages that must be ignored and every page outside
+    the lists poisoned; entries (or reserve cells) against the oracle."""
+    wl = W.two_level_resident_fp8(seed=3005, B=3, seq_len=64 * 40 + 5, kmax=12, poison=True)
+    nres = np.array([0, 3, 12], np.int32)
+    dw = api.DeviceWorkload(wl, "cuda:0")
+    call = G.score_resident_cells if cells else G.score_resident
+    idx, val = call(dw, n_resident=torch.from_numpy(nres).cuda())
+    ig, vg = idx.cpu().numpy(), val.cpu().numpy()
+    ri, rv, rc = oracle.score_resident(wl, n_resident=nres, cells=cells)
+    assert np.all(ig[0] == -1) and np.all(np.isneginf(vg[0])), "empty list selects nothing"
+    for t in (1, 2):
+        sel = ig[t][ig[t] >= 0]
+        assert np.all(np.isfinite(vg[t][:sel.size])), f"row {t}: a poisoned page was read"
+        scale = float(np.max(np.abs(rv[t, :rc[t]])))
+        of = (lambda e, t=t: oracle.logits_at(wl, np.full(len(e), t),
+                                              wl.resident_pages[t][np.asarray(e) // 64] * 64
+                                              + np.asarray(e) % 64)) if cells else \
+             (lambda e, t=t: oracle.logits_at(wl, np.full(len(e), t), e))
+        G.check_topk_row(ig[t], vg[t], ri[t], rc[t], of, scale, 512, f"row {t} cells={cells}")
+        listed = wl.resident_pages[t][:nres[t]]
+        if cells:
+            assert np.all(sel // 64 < nres[t]), f"row {t}: a cell past the list's count"
+        else:
+            assert set((sel // 64).tolist()) <= set(listed.tolist()), f"row {t}: unlisted page"
+    assert rc[1] < 512 and rc[2] >= 512, "the cases must cover a short and a full row"
