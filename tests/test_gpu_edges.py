@@ -277,3 +277,26 @@ def test_two_level_empty_and_short_resident_lists(cells):
         else:
             assert set((sel // 64).tolist()) <= set(listed.tolist()), f"row {t}: unlisted page"
     assert rc[1] < 512 and rc[2] >= 512, "the cases must cover a short and a full row"
+
+
+@pytest.mark.parametrize("sink,recent", [(0, 0), (5, 100)])
+def test_mask_empty_and_one_page_requests(sink, recent):
+    """One fm_resident_mask call over requests of 0 entries, 37 entries (one partial page) and
+    64 * 30 + 11 entries, with and without sink / recent forcing (the recent window longer
+    than the short request): the empty request has no mask bit and no page, the forced
+    entries are resident, and every output matches the oracle under the band rule."""
+    wl = W.three_layer_mask_fp8(seed=3006, B=3, seq_len=64 * 30 + 11)
+    wl.kv.seq_lens[:] = np.array([0, 37, 64 * 30 + 11], np.int32)
+    dw = api.DeviceWorkload(wl, "cuda:0")
+    m = G.resident_mask(dw, n_sink=sink, n_recent=recent)
+    r = oracle.resident_mask(wl, n_sink=sink, n_recent=recent)
+    tag = f"mask lengths 0 / 37 / 1931, sink {sink}, recent {recent}"
+    mg = m["mask"].cpu().numpy()
+    G.check_mask(mg, r["mask"], r["union"], 0.0, wl.kv.seq_lens, tag)
+    G.check_pages(m, r, 0.0, wl.kv.seq_lens, tag)
+    assert not mg[0].any() and int(m["page_count"][0]) == 0
+    assert np.all(m["page_list"][0].cpu().numpy() == -1)
+    if recent:
+        assert mg[1, :37].all() and not mg[1, 37:].any()
+        n = int(wl.kv.seq_lens[2])
+        assert mg[2, :sink].all() and mg[2, n - recent:n].all() and not mg[2, n:].any()
